@@ -1,0 +1,369 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes a loaded oracle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with:
+  * exact rational arithmetic on tiny inputs (Python ``fractions``), with the
+    operands sliced out of the packed layout by numpy reshapes, an indexing
+    route independent of the oracle's pointer arithmetic;
+  * the closed form of the ramp inputs of the tensor-core study blog
+    ("Tensor Core学习", the sgemm_wmma_naive test main: A = i/256 and
+    B = (i+1.25)/128 read as an NT pair);
+  * the worked tiling example of the kernl notebook "1 - tiled matmul"
+    (864 loads, 135 writes, stored in tests/golden/);
+  * identity, zero and empty products, and the closed forms of the tile
+    counts on ragged shapes;
+  * invariants of the causal scores (lower triangle = scaled dense product,
+    NaN count, non-negative diagonal when Q = K) and thread-count
+    independence;
+  * library conversions of bfloat16 / binary16 (torch, numpy).
+
+The same functions run against mutated copies of the oracle in
+test_oracle_mutations.py, which checks that every planted mistake is caught.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from causal_attention_score_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+QNAN = 0x7FC00000
+
+
+# ------------------------------------------------------------------ helpers
+
+def f32_round(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest binary32 value, ties to even."""
+    if fr == 0:
+        return np.float32(0.0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    # choose e so that 2^23 <= a / 2^(e-23) < 2^24
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = max(e - 23, -149)  # quantum; subnormals keep the fixed -149 quantum
+    n = round(a / Fraction(2) ** q)  # Fraction.__round__ is ties-to-even
+    return np.float32(sign * n * 2.0 ** q)
+
+
+def ulp32(x: float) -> float:
+    x = np.float32(abs(x))
+    return float(np.nextafter(x, np.float32(np.inf)) - x) if x != 0 else 2.0 ** -149
+
+
+def bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def decoded(orc, a, dtype):
+    return orc.decode(a, dtype) if dtype != "f32" else np.asarray(a, dtype=np.float64)
+
+
+def exact_gemm(X, W, dtype, orc):
+    """Exact rational Y = X W^T and sum |x w|, operands widened by the library
+    conversions (numpy for fp32/f16, torch for bf16), not by the oracle."""
+    Xd, Wd = lib_decode(X, dtype), lib_decode(W, dtype)
+    M, K = Xd.shape
+    N = Wd.shape[0]
+    Y = [[None] * N for _ in range(M)]
+    S = [[None] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            asum = Fraction(0)
+            for k in range(K):
+                p = Fraction(float(Xd[m, k])) * Fraction(float(Wd[n, k]))
+                acc += p
+                asum += abs(p)
+            Y[m][n], S[m][n] = acc, asum
+    return Y, S
+
+
+def lib_decode(a, dtype) -> np.ndarray:
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f16":
+        return a.view(np.float16).astype(np.float64)
+    import torch
+    t = torch.from_numpy(a.astype(np.int16).copy()).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def scale_is_nearest(s: np.float32, hs: int) -> bool:
+    """s is the binary32 value nearest to 1/sqrt(hs): 1/hs lies between the
+    squares of the midpoints to s's neighbours (exact rationals)."""
+    lo = np.nextafter(s, np.float32(0))
+    hi = np.nextafter(s, np.float32(np.inf))
+    fs, flo, fhi = Fraction(float(s)), Fraction(float(lo)), Fraction(float(hi))
+    target = Fraction(1, hs)
+    return ((flo + fs) / 2) ** 2 <= target <= ((fs + fhi) / 2) ** 2
+
+
+# ------------------------------------------------------------- gemm pins
+
+def pin_gemm_bruteforce_int(orc):
+    for (M, N, K, seed) in [(1, 1, 1, 0), (3, 5, 7, 1), (8, 8, 8, 2), (5, 2, 6, 3)]:
+        for dtype in ("f32", "bf16", "f16"):
+            X, W = synth.gemm_inputs(M, N, K, dtype, seed, dist="int")
+            Y, bound = orc.gemm_nt(X, W, dtype)
+            Ye, Se = exact_gemm(X, W, dtype, orc)
+            for m in range(M):
+                for n in range(N):
+                    assert bits(Y[m, n]) == bits(f32_round(Ye[m][n])), (dtype, M, N, K, m, n)
+                    assert Fraction(float(bound[m, n])) == Se[m][n], (dtype, m, n)
+
+
+def pin_gemm_bruteforce_random(orc):
+    for (M, N, K, seed) in [(4, 3, 5, 10), (7, 6, 8, 11)]:
+        for dtype in ("f32", "bf16"):
+            X, W = synth.gemm_inputs(M, N, K, dtype, seed, dist="normal")
+            Y, bound = orc.gemm_nt(X, W, dtype)
+            Ye, Se = exact_gemm(X, W, dtype, orc)
+            for m in range(M):
+                for n in range(N):
+                    ref = f32_round(Ye[m][n])
+                    # one rounding of the exact sum; a double-sum error can tip
+                    # a near-tie by at most one unit in the last place
+                    assert abs(float(Y[m, n]) - float(ref)) <= ulp32(float(ref)), (dtype, m, n)
+                    assert abs(Fraction(float(bound[m, n])) - Se[m][n]) <= Se[m][n] * Fraction(1, 2 ** 48)
+
+
+def pin_gemm_strided(orc):
+    """Row pitches larger than K: only the first K entries of a row count."""
+    M, N, K, ldx, ldw, ldy = 5, 4, 3, 7, 6, 9
+    g = np.random.default_rng(5)
+    Xf = g.integers(-3, 4, size=(M, ldx)).astype(np.float32)
+    Wf = g.integers(-3, 4, size=(N, ldw)).astype(np.float32)
+    Y, _ = orc.gemm_nt(Xf, Wf, "f32", M=M, N=N, K=K, ldx=ldx, ldw=ldw, ldy=ldy)
+    ref = Xf[:, :K].astype(np.int64) @ Wf[:, :K].astype(np.int64).T
+    assert np.array_equal(Y[:, :N], ref.astype(np.float32))
+    assert np.all(Y[:, N:] == 0)  # columns past N are never written
+
+
+def pin_gemm_ramp_closed_form(orc):
+    """Ramp inputs of the tensor-core blog's WMMA test, read as NT:
+    A[m,k] = (mK+k)/256, W[n,k] = (nK+k+1.25)/128. With a = mK and
+    c = nK + 1.25, Y = (K a c + (a+c) K(K-1)/2 + (K-1)K(2K-1)/6) / 32768."""
+    for (M, N, K) in [(16, 16, 16), (5, 7, 13), (1, 3, 64)]:
+        A = (np.arange(M * K, dtype=np.float64) / 256.0).astype(np.float32).reshape(M, K)
+        W = ((np.arange(N * K, dtype=np.float64) + 1.25) / 128.0).astype(np.float32).reshape(N, K)
+        Y, _ = orc.gemm_nt(A, W, "f32")
+        for m in range(M):
+            for n in range(N):
+                a = Fraction(m * K)
+                c = Fraction(n * K) + Fraction(5, 4)
+                exact = (K * a * c + (a + c) * Fraction(K * (K - 1), 2)
+                         + Fraction((K - 1) * K * (2 * K - 1), 6)) / 32768
+                assert bits(Y[m, n]) == bits(f32_round(exact)), (M, N, K, m, n)
+
+
+def pin_gemm_identity_zero_empty(orc):
+    g = np.random.default_rng(7)
+    X = g.standard_normal((6, 9)).astype(np.float32)
+    Y, _ = orc.gemm_nt(X, np.eye(9, dtype=np.float32), "f32")
+    assert np.array_equal(bits(Y), bits(X))
+    Y, _ = orc.gemm_nt(np.eye(6, dtype=np.float32), X.T.copy(), "f32")  # I . (X^T)^T = X
+    assert np.array_equal(bits(Y), bits(X))
+    Y, _ = orc.gemm_nt(np.zeros((4, 5), np.float32), g.standard_normal((3, 5)).astype(np.float32), "f32")
+    assert np.all(Y == 0)
+    Y, b = orc.gemm_nt(np.zeros((4, 0), np.float32), np.zeros((3, 0), np.float32), "f32")
+    assert Y.shape == (4, 3) and np.all(Y == 0) and np.all(b == 0)  # empty sum
+
+
+# ------------------------------------------------------------ trimul pins
+
+def qk_views(qkv, B, T, NH, HS, dtype):
+    """Q and K as (B, NH, T, HS) via numpy reshape of the packed
+    (B, T, 3, NH, HS) layout, decoded by the library conversions."""
+    d = lib_decode(qkv, dtype).reshape(B, T, 3, NH, HS)
+    return d[:, :, 0].transpose(0, 2, 1, 3), d[:, :, 1].transpose(0, 2, 1, 3)
+
+
+def pin_trimul_scale(orc):
+    for hs in (1, 2, 3, 5, 8, 40, 64, 80, 96, 128, 255):
+        s = orc.trimul_scale(hs)
+        assert scale_is_nearest(s, hs), hs
+    assert orc.trimul_scale(64) == np.float32(0.125)
+
+
+def pin_trimul_bruteforce(orc):
+    for (B, T, NH, HS, seed, dist, dtype) in [
+        (1, 1, 1, 1, 0, "int", "f32"),
+        (2, 9, 2, 5, 1, "int", "f32"),
+        (1, 7, 3, 4, 2, "int", "bf16"),
+        (2, 5, 2, 3, 3, "normal", "f32"),
+        (1, 6, 2, 8, 4, "normal", "f16"),
+    ]:
+        C = NH * HS
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed, dist)
+        out, bound = orc.trimul_causal(qkv, B, T, C, NH, dtype)
+        Q, Kt = qk_views(qkv, B, T, NH, HS, dtype)
+        s = Fraction(float(orc.trimul_scale(HS)))
+        for b in range(B):
+            for h in range(NH):
+                for t in range(T):
+                    for t2 in range(T):
+                        v = out[b, h, t, t2]
+                        if t2 > t:
+                            assert bits(v) == QNAN, (b, h, t, t2)
+                            continue
+                        dot = sum((Fraction(float(Q[b, h, t, i])) * Fraction(float(Kt[b, h, t2, i]))
+                                   for i in range(HS)), Fraction(0))
+                        asum = sum((abs(Fraction(float(Q[b, h, t, i])) * Fraction(float(Kt[b, h, t2, i])))
+                                    for i in range(HS)), Fraction(0))
+                        ref = f32_round(dot * s)
+                        tol = 0 if dist == "int" else ulp32(float(ref))
+                        assert abs(float(v) - float(ref)) <= tol, (dtype, b, h, t, t2, v, ref)
+                        assert abs(Fraction(float(bound[b, h, t, t2])) - asum * s) <= asum * s * Fraction(1, 2 ** 48)
+
+
+def pin_trimul_vs_numpy_matmul(orc):
+    """Lower triangle equals scale * (Q @ K^T) from numpy's float64 matmul."""
+    B, T, NH, HS = 2, 37, 3, 16
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 21)
+    out, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+    Q, Kt = qk_views(qkv, B, T, NH, HS, "f32")
+    ref = (Q @ Kt.transpose(0, 1, 3, 2)) * float(orc.trimul_scale(HS))
+    low = np.tril(np.ones((T, T), dtype=bool))
+    err = np.abs(out.astype(np.float64) - ref)[..., low]
+    assert np.all(err <= 1e-6 * bound[..., low] + 1e-30), err.max()
+    assert np.all(bits(out[..., ~low]) == QNAN)
+
+
+def pin_trimul_equals_dense_lower(orc):
+    """trimul = scale * lower(gemm_nt(Q, K)) per (b, nh); with HS = 64 the
+    scale is 1/8, a power of two, so the two agree bit for bit."""
+    B, T, NH, HS = 2, 19, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 22)
+    out, _ = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+    d = qkv.reshape(B, T, 3, NH, HS)
+    low = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(NH):
+            Y, _ = orc.gemm_nt(np.ascontiguousarray(d[b, :, 0, h]), np.ascontiguousarray(d[b, :, 1, h]), "f32")
+            assert np.array_equal(bits(out[b, h][low]), bits((Y * np.float32(0.125))[low]))
+
+
+def pin_trimul_mask_counts(orc):
+    for (B, T, NH, HS) in [(1, 1, 1, 4), (2, 13, 3, 4), (1, 64, 2, 8)]:
+        qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 23)
+        out, _ = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+        u = bits(out)
+        assert int(np.sum(u == QNAN)) == B * NH * T * (T - 1) // 2
+        assert int(np.sum(np.isfinite(out))) == B * NH * T * (T + 1) // 2
+
+
+def pin_trimul_q_equals_k(orc):
+    """With K = Q the diagonal is scale * |q_t|^2 >= 0 and the lower triangle
+    is symmetric with the transposed product."""
+    B, T, NH, HS = 1, 11, 2, 6
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 24).reshape(B, T, 3, NH, HS)
+    qkv[:, :, 1] = qkv[:, :, 0]
+    out, _ = orc.trimul_causal(qkv.reshape(B, T, -1), B, T, NH * HS, NH, "f32")
+    Q = qkv[0, :, 0].astype(np.float64)          # (T, NH, HS)
+    s = float(orc.trimul_scale(HS))
+    for h in range(NH):
+        diag = np.diagonal(out[0, h])
+        assert np.all(diag >= 0)
+        ref = s * np.sum(Q[:, h] ** 2, axis=1)
+        assert np.allclose(diag, ref, rtol=1e-6, atol=0)
+
+
+def pin_trimul_rows_match_full(orc):
+    B, T, NH, HS = 2, 21, 3, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", 25)
+    full, _ = orc.trimul_causal(qkv, B, T, NH * HS, NH, "bf16")
+    part, _ = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, 1, 2, 5, 17, "bf16")
+    assert np.array_equal(bits(part), bits(full[1, 2, 5:17]))
+
+
+def pin_thread_independence(orc):
+    n0 = orc.num_threads()
+    try:
+        X, W = synth.gemm_inputs(67, 45, 129, "f32", 26)
+        qkv = synth.trimul_inputs(2, 70, 2, 24, "bf16", 27)
+        orc.set_threads(1)
+        y1, _ = orc.gemm_nt(X, W, "f32")
+        o1, _ = orc.trimul_causal(qkv, 2, 70, 48, 2, "bf16")
+        orc.set_threads(max(2, os.cpu_count() or 2))
+        y2, _ = orc.gemm_nt(X, W, "f32")
+        o2, _ = orc.trimul_causal(qkv, 2, 70, 48, 2, "bf16")
+        assert np.array_equal(bits(y1), bits(y2)) and np.array_equal(bits(o1), bits(o2))
+    finally:
+        orc.set_threads(n0)
+
+
+# ------------------------------------------------------- tiled-count pins
+
+def read_golden_counts():
+    vals = {}
+    with open(os.path.join(GOLDEN, "kernl_tiled_matmul_counts.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = int(v)
+    return vals
+
+
+def pin_tiled_worked_example(orc):
+    g = read_golden_counts()
+    M, N, K = g["M"], g["N"], g["K"]
+    wl = synth.WORKLOADS["dense_f32_15x9x12"]
+    A, Wt = wl.inputs()
+    Bm = np.ascontiguousarray(Wt.T)
+    out, loads, writes, ploads, pwrites = orc.tiled_matmul_count(A, Bm, g["block_M"], g["block_N"], g["block_K"])
+    assert (loads, writes) == (g["total_load"], g["total_write"])
+    assert (ploads, pwrites) == (g["total_load"], g["total_write"])  # tiles divide the shape
+    assert np.allclose(out, A.astype(np.float64) @ Bm.astype(np.float64), rtol=1e-6, atol=0)
+    Y, _ = orc.gemm_nt(A, Wt, "f32")
+    assert np.max(np.abs(Y - out)) <= 2 * np.max(np.abs(Y)) * 2.0 ** -24
+
+
+def pin_tiled_closed_forms(orc):
+    cdiv = lambda a, b: -(-a // b)
+    for (M, N, K, bm, bn, bk) in [(17, 10, 13, 5, 3, 6), (15, 9, 12, 5, 3, 6), (1, 1, 1, 4, 4, 4),
+                                  (33, 21, 7, 8, 16, 4)]:
+        g = np.random.default_rng(M + N + K)
+        A = g.integers(-3, 4, (M, K)).astype(np.float32)
+        Bm = g.integers(-3, 4, (K, N)).astype(np.float32)
+        out, loads, writes, ploads, pwrites = orc.tiled_matmul_count(A, Bm, bm, bn, bk)
+        assert loads == M * K * cdiv(N, bn) + K * N * cdiv(M, bm)
+        assert writes == M * N
+        assert ploads == (bm * bk + bk * bn) * cdiv(M, bm) * cdiv(N, bn) * cdiv(K, bk)
+        assert pwrites == bm * bn * cdiv(M, bm) * cdiv(N, bn)
+        assert np.array_equal(out, (A.astype(np.int64) @ Bm.astype(np.int64)).astype(np.float32))
+
+
+# ----------------------------------------------------------- decode pins
+
+def pin_decode_all_16bit(orc):
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dtype in ("bf16", "f16"):
+        mine = orc.decode(pats, dtype)
+        ref = lib_decode(pats, dtype)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(mine), nan), dtype
+        assert np.array_equal(mine[~nan], ref[~nan]), dtype
+
+
+def pin_rejects_bad_arguments(orc):
+    import ctypes
+    lib = orc.lib
+    buf = np.zeros(64, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert lib.oracle_trimul_causal(p, p, None, 1, 2, 10, 3, 0) == -1   # C % NH != 0
+    assert lib.oracle_trimul_causal(p, p, None, 1, 2, 12, 3, 7) == -1   # bad dtype
+    assert lib.oracle_gemm_nt(p, p, p, None, 2, 2, 3, 2, 3, 2, 0) == -1  # ldx < K
+    assert lib.oracle_trimul_causal(p, p, None, 0, 5, 12, 3, 0) == 0    # empty batch
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
