@@ -1,0 +1,256 @@
+"""Throughput of the tiled-matmul hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * gemm_nt       fp32 X [960, 770] . W [1024, 770]^T (the DietCode dense layer
+                  with H = 1024; N(0,1)/sqrt(770) inputs), and
+  * trimul_causal fp32 causal scores from packed QKV (8, 1024, 3, 12, 64)
+                  (the llm.c trimat_forward.cu benchmark shape; N(0,1)).
+
+value = useful TFLOP/s of the step (2MNK for the dense product, the lower
+triangle including the diagonal, 2*HS*B*NH*T(T+1)/2, for the scores), with
+inputs resident in HBM. The JSON line also carries the roofline of the
+dominant kernel (timed with HIP events on its own stream), the oracle's
+throughput on the host cores, and the bf16 workloads (4096^3 dense, causal
+scores (4, 4096, 3, 25, 64)) timed the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # dense MFMA
+METRIC = "useful TFLOP/s (gemm_nt, trimul_causal) + % of MI355X MFMA/HBM roofline"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def device_tensor(a, dtype):
+    import numpy as np
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(a).cuda()
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a.view(np.float16)).cuda()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_attention_score_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    `kernel`, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sources_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Part:
+    """One entry point on one workload, with device buffers ready."""
+
+    def __init__(self, wl):
+        import torch
+
+        import causal_attention_score_amd as cas
+        self.wl = wl
+        self.cas = cas
+        if wl.kind == "gemm_nt":
+            X, W = wl.inputs()
+            self.x, self.w = device_tensor(X, wl.dtype), device_tensor(W, wl.dtype)
+            M, N, _ = wl.dims
+            self.out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        else:
+            (qkv,) = wl.inputs()
+            B, T, NH, _ = wl.dims
+            self.qkv = device_tensor(qkv, wl.dtype)
+            self.NH = NH
+            self.out = torch.empty((B, NH, T, T), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        if self.wl.kind == "gemm_nt":
+            self.cas.gemm_nt(self.x, self.w, out=self.out)
+        else:
+            self.cas.trimul_causal(self.qkv, self.NH, out=self.out)
+
+
+def time_parts(parts, steps: int, warmup: int):
+    """Warm up, then time `steps` steps; every part is bracketed by HIP events
+    on the stream it is launched on. Returns (ms per step, [avg ms per part])."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for p in parts:
+            p()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, p in enumerate(parts):
+            p()
+            ev[s][i + 1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    total = start.elapsed_time(stop)
+    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps for i in range(len(parts))]
+    return total / steps, per, wall / steps
+
+
+def roofline_of(wl, ms: float, traffic):
+    t = ms * 1e-3
+    if wl.kind == "trimul_causal":
+        achieved = wl.algorithmic_bytes() / t / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": f"trimul_causal {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
+                "algorithmic_bytes": wl.algorithmic_bytes()}
+    achieved = wl.useful_flops() / t / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": f"gemm_nt {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
+            "useful_flops": wl.useful_flops()}
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of
+    the step: the whole dense product, then causal-score planes (one (b, nh)
+    plane at a time) until the time budget is spent."""
+    import oracle
+    from causal_attention_score_amd import synth
+    orc = oracle.get()
+    wg = synth.WORKLOADS["dense_f32_960x1024x770"]
+    wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
+    X, W = wg.inputs()
+    (qkv,) = wt.inputs()
+    B, T, NH, HS = wt.dims
+    t0 = time.perf_counter()
+    orc.gemm_nt(X, W, "f32", with_bound=False)
+    flops = wg.useful_flops()
+    planes = 0
+    for p in range(B * NH):
+        b, h = divmod(p, NH)
+        orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, "f32", with_bound=False)
+        planes += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops += planes * 2 * HS * T * (T + 1) // 2
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"dense fp32 960x1024x770 in full + {planes} of {B * NH} causal-score planes "
+                      f"(T={T}, HS={HS}) of the step, fp64 accumulation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the hot path shards with no communication "
+              "and this build measures one GPU's share; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_attention_score_amd import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    digest = kernel_sources_digest()
+
+    wg = synth.WORKLOADS["dense_f32_960x1024x770"]
+    wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
+    log("preparing inputs")
+    parts = [Part(wg), Part(wt)]
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_step, per, wall_ms = time_parts(parts, args.steps, args.warmup)
+    flops = wg.useful_flops() + wt.useful_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    dom = max(range(2), key=lambda i: per[i])
+    dom_wl = [wg, wt][dom]
+    kname = "trimul_f32_B8_T1024" if dom_wl.kind == "trimul_causal" else "gemm_nt_f32_960x1024x770"
+    roof = roofline_of(dom_wl, per[dom], read_traffic(kname, digest))
+    parts_report = {wl.name: {"avg_launch_us": round(ms * 1e3, 2),
+                              "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
+                              "roofline": roofline_of(wl, ms, None)}
+                    for wl, ms in zip([wg, wt], per)}
+    del parts
+    torch.cuda.empty_cache()
+
+    bf16 = None
+    if not args.no_bf16:
+        bf16 = {}
+        for name in ("dense_bf16_4096", "trimul_bf16_B4_T4096_NH25_HS64"):
+            wl = synth.WORKLOADS[name]
+            log(f"timing {name}")
+            p = Part(wl)
+            _, (ms,), _ = time_parts([p], max(5, args.steps // 5), 2)
+            bf16[name] = {"avg_launch_us": round(ms * 1e3, 2),
+                          "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
+                          "roofline": roofline_of(wl, ms, None)}
+            del p
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) inputs of the pages' shapes)",
+        "config": {"workload": "dense fp32 960x1024x770 + causal scores fp32 B=8 T=1024 NH=12 HS=64",
+                   "gemm_nt": {"M": 960, "N": 1024, "K": 770, "dtype": "f32"},
+                   "trimul_causal": {"B": 8, "T": 1024, "NH": 12, "HS": 64, "dtype": "f32"}},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parts": parts_report,
+        "bf16_workloads": bf16,
+        "wall_ms_per_step": round(wall_ms, 5),
+        "device": torch.cuda.get_device_name(0),
+        "sources_digest": digest,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,143 @@
-"""MI355X-native tiled-matmul hot path: dense Y = X W^T and causal attention scores."""
+"""MI355X-native tiled-matmul hot path: dense Y = X W^T and causal attention
+scores, as hand-written gfx950 HIP kernels behind a C ABI (``include/cas.h``).
+
+This module is the thin binding: it marshals torch tensors (device memory and
+the current HIP stream) into the C ABI of ``libcas.so`` and raises on a
+non-zero status. Every step of the computation runs in the HIP kernels; there
+is no CPU fallback, and the calls raise if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcas.so")
+
+CAS_F32, CAS_BF16, CAS_F16 = 0, 1, 2
+STATUS = {0: "CAS_OK", -1: "CAS_ERR_NULL", -2: "CAS_ERR_SHAPE", -3: "CAS_ERR_DTYPE",
+          -4: "CAS_ERR_ALIAS", -5: "CAS_ERR_DEVICE", -6: "CAS_ERR_HIP"}
+EXPORTS = ("cas_gemm_nt", "cas_trimul_causal", "cas_status_string", "cas_last_hip_error", "cas_version")
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class CasError(RuntimeError):
+    def __init__(self, op: str, status: int, message: str):
+        super().__init__(f"{op}: {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.cas_gemm_nt.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [ctypes.c_int, ctypes.c_int, _vp]
+        L.cas_gemm_nt.restype = ctypes.c_int
+        L.cas_trimul_causal.argtypes = [_vp, _vp] + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
+        L.cas_trimul_causal.restype = ctypes.c_int
+        L.cas_status_string.argtypes = [ctypes.c_int]
+        L.cas_status_string.restype = ctypes.c_char_p
+        L.cas_last_hip_error.restype = ctypes.c_int
+        L.cas_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().cas_status_string(status).decode()
+
+
+def _check(op: str, status: int) -> None:
+    if status != 0:
+        msg = status_string(status)
+        if status in (-5, -6):
+            msg += f" (hipError {lib().cas_last_hip_error()})"
+        raise CasError(op, status, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: CAS_F32, torch.bfloat16: CAS_BF16, torch.float16: CAS_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported input dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream_ptr(dev) -> int:
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _require_device(*ts) -> None:
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must live on the same GPU")
+
+
+def gemm_nt(x, w, out=None):
+    """Y = x @ w.T with fp32 accumulation and fp32 output.
+
+    x: [M, K] and w: [N, K] of one dtype (float32, bfloat16, float16), rows
+    contiguous (any row pitch); out: optional [M, N] float32 with contiguous
+    rows. The kernel runs on the current stream of x's device."""
+    import torch
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("gemm_nt expects x [M, K] and w [N, K]")
+    if x.dtype != w.dtype:
+        raise TypeError("x and w must share a dtype")
+    if x.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("rows of x and w must be contiguous")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a float32 [M, N] tensor with contiguous rows")
+    _require_device(x, w, out)
+    ldx = x.stride(0) if M > 1 else K
+    ldw = w.stride(0) if N > 1 else K
+    ldy = out.stride(0) if M > 1 else N
+    st = lib().cas_gemm_nt(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, ldx, ldw, ldy,
+                           _dtype_code(x), CAS_F32, _stream_ptr(x.device))
+    _check("cas_gemm_nt", st)
+    return out
+
+
+def trimul_causal(qkv, NH: int, out=None):
+    """Causal attention scores from packed QKV.
+
+    qkv: contiguous (B, T, 3*C) or (B, T, 3, NH, HS) tensor (float32,
+    bfloat16 or float16); returns out (B, NH, T, T) float32 with
+    scale * Q.K on and below the diagonal and NaN above it."""
+    import torch
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous")
+    if qkv.dim() == 5:
+        B, T, three, nh, HS = qkv.shape
+        if three != 3 or nh != NH:
+            raise ValueError("qkv must be (B, T, 3, NH, HS)")
+        C = NH * HS
+    elif qkv.dim() == 3:
+        B, T, C3 = qkv.shape
+        if C3 % 3:
+            raise ValueError("last dim of qkv must be 3*C")
+        C = C3 // 3
+    else:
+        raise ValueError("qkv must be (B, T, 3C) or (B, T, 3, NH, HS)")
+    if out is None:
+        out = torch.empty((B, NH, T, T), dtype=torch.float32, device=qkv.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, NH, T, T) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 (B, NH, T, T) tensor")
+    _require_device(qkv, out)
+    st = lib().cas_trimul_causal(qkv.data_ptr(), out.data_ptr(), B, T, C, NH,
+                                 _dtype_code(qkv), CAS_F32, _stream_ptr(qkv.device))
+    _check("cas_trimul_causal", st)
+    return out

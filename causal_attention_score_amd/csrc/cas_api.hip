@@ -1,0 +1,185 @@
+// cas_api.hip -- the C ABI (include/cas.h): argument validation, variant
+// choice and launch on the caller's stream.
+//
+// Every check that can be made without the GPU happens before the first HIP
+// call, so a rejected call returns its status on any machine. No exception
+// crosses the ABI and the library keeps no state besides a per-device
+// "is this gfx950" answer and the per-thread last HIP error.
+#include "cas.h"
+#include "launch.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#define CAS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr int MAX_DEVICES = 64;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_add_overflow(a, b, r); }
+
+int elem_size(cas_dtype d) { return d == CAS_F32 ? 4 : 2; }
+
+bool dtype_pair_ok(cas_dtype in, cas_dtype out)
+{
+    return (in == CAS_F32 || in == CAS_BF16 || in == CAS_F16) && out == CAS_F32;
+}
+
+// Byte extent of `rows` rows of `cols` elements at pitch `ld`: ((rows-1)*ld + cols)*es.
+bool extent(int64_t rows, int64_t cols, int64_t ld, int es, int64_t *bytes)
+{
+    if (rows == 0 || cols == 0) {
+        *bytes = 0;
+        return true;
+    }
+    int64_t t;
+    return mul_ok(rows - 1, ld, &t) && add_ok(t, cols, &t) && mul_ok(t, es, bytes) && *bytes < (INT64_C(1) << 62);
+}
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)na;
+    const uintptr_t b0 = (uintptr_t)b, b1 = b0 + (uintptr_t)nb;
+    return a0 < b1 && b0 < a1;
+}
+
+int device_check()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip = (int)e;
+        return CAS_ERR_DEVICE;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) return CAS_ERR_DEVICE;
+    static std::once_flag once[MAX_DEVICES];
+    static bool is_gfx950[MAX_DEVICES];
+    std::call_once(once[dev], [dev] {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) == hipSuccess)
+            is_gfx950[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    });
+    return is_gfx950[dev] ? CAS_OK : CAS_ERR_DEVICE;
+}
+
+// Widest load (in elements, at most 16 bytes) that divides every length and
+// pitch and the alignment of every base address.
+int pick_vec(int es, const int64_t *lens, int nlens, const void *const *ptrs, int nptrs)
+{
+    for (int v = 16 / es; v > 1; v /= 2) {
+        bool ok = true;
+        for (int i = 0; i < nlens; ++i) ok = ok && (lens[i] % v == 0);
+        for (int i = 0; i < nptrs; ++i) ok = ok && ((uintptr_t)ptrs[i] % (uintptr_t)(v * es) == 0);
+        if (ok) return v;
+    }
+    return 1;
+}
+
+// CAS_GEMM_TILE=64|128 forces the dense tile shape (tests and tuning);
+// anything else leaves the automatic choice.
+int gemm_tile_override()
+{
+    const char *v = std::getenv("CAS_GEMM_TILE");
+    if (!v) return cas::GEMM_TILE_AUTO;
+    if (std::strcmp(v, "64") == 0) return cas::GEMM_TILE_64;
+    if (std::strcmp(v, "128") == 0) return cas::GEMM_TILE_128;
+    return cas::GEMM_TILE_AUTO;
+}
+
+int launch_status(hipError_t e)
+{
+    if (e == hipSuccess) return CAS_OK;
+    g_last_hip = (int)e;
+    return CAS_ERR_HIP;
+}
+
+} // namespace
+
+CAS_EXPORT int cas_gemm_nt(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int64_t ldx,
+                           int64_t ldw, int64_t ldy, cas_dtype in_dtype, cas_dtype out_dtype, void *stream)
+{
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || ldx < K || ldw < K || ldy < N) return CAS_ERR_SHAPE;
+    if (M == 0 || N == 0) return CAS_OK;
+    if (!Y || (K > 0 && (!X || !W))) return CAS_ERR_NULL;
+    const int es = elem_size(in_dtype);
+    int64_t xb, wb, yb;
+    if (!extent(M, K, ldx, es, &xb) || !extent(N, K, ldw, es, &wb) || !extent(M, N, ldy, 4, &yb))
+        return CAS_ERR_SHAPE;
+    if (overlap(Y, yb, X, xb) || overlap(Y, yb, W, wb)) return CAS_ERR_ALIAS;
+
+    cas::GemmArgs a{X, W, (float *)Y, M, N, K, ldx, ldw, ldy};
+    const int tile = gemm_tile_override();
+    if (cas::gemm_nt_workgroups(a, in_dtype, tile) > INT32_MAX) return CAS_ERR_SHAPE;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+
+    const int64_t lens[3] = {K, ldx, ldw};
+    const void *ptrs[2] = {X, W};
+    const int vec = K > 0 ? pick_vec(es, lens, 3, ptrs, 2) : 1;
+    return launch_status(cas::launch_gemm_nt(a, in_dtype, vec, tile, (hipStream_t)stream));
+}
+
+CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t T, int64_t C, int64_t NH,
+                                 cas_dtype in_dtype, cas_dtype out_dtype, void *stream)
+{
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (B < 0 || T < 0 || C < 0 || NH < 0) return CAS_ERR_SHAPE;
+    if (B == 0 || T == 0 || NH == 0) return CAS_OK;
+    if (C == 0 || C % NH != 0) return CAS_ERR_SHAPE;
+    if (!qkv || !out) return CAS_ERR_NULL;
+    const int es = elem_size(in_dtype);
+    int64_t in_elems, out_elems, t, c3, inb, outb;
+    if (!mul_ok(3, C, &c3) || !mul_ok(B, T, &t) || !mul_ok(t, c3, &in_elems) || !mul_ok(in_elems, es, &inb))
+        return CAS_ERR_SHAPE;
+    if (!mul_ok(B, NH, &t) || !mul_ok(t, T, &t) || !mul_ok(t, T, &out_elems) || !mul_ok(out_elems, 4, &outb))
+        return CAS_ERR_SHAPE;
+    if (inb >= (INT64_C(1) << 62) || outb >= (INT64_C(1) << 62)) return CAS_ERR_SHAPE;
+    if (overlap(out, outb, qkv, inb)) return CAS_ERR_ALIAS;
+    if (cas::trimul_workgroups(B, T, NH) > INT32_MAX) return CAS_ERR_SHAPE;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+
+    const int64_t HS = C / NH;
+    cas::TrimulArgs a{};
+    a.qkv = qkv;
+    a.out = (float *)out;
+    a.B = B;
+    a.T = T;
+    a.C = C;
+    a.NH = NH;
+    a.HS = HS;
+    a.scale = (float)(1.0 / std::sqrt((double)HS)); // nearest fp32 to 1/sqrt(HS)
+    a.vec_store = (T % 4 == 0) && ((uintptr_t)out % 16 == 0);
+    const int64_t lens[2] = {HS, C};
+    const void *ptrs[1] = {qkv};
+    const int vec = pick_vec(es, lens, 2, ptrs, 1);
+    return launch_status(cas::launch_trimul(a, in_dtype, vec, (hipStream_t)stream));
+}
+
+CAS_EXPORT const char *cas_status_string(int status)
+{
+    switch (status) {
+    case CAS_OK: return "ok";
+    case CAS_ERR_NULL: return "a required pointer is NULL";
+    case CAS_ERR_SHAPE: return "invalid shape: negative size, pitch smaller than the row, C % NH != 0, or overflow";
+    case CAS_ERR_DTYPE: return "unsupported (in_dtype, out_dtype) pair";
+    case CAS_ERR_ALIAS: return "output bytes overlap input bytes";
+    case CAS_ERR_DEVICE: return "the current HIP device is not a gfx950 (MI355X) GPU or is unavailable";
+    case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+CAS_EXPORT int cas_last_hip_error(void) { return g_last_hip; }
+
+CAS_EXPORT int cas_version(void) { return 100; }

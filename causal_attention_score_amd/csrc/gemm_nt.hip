@@ -1,0 +1,127 @@
+// gemm_nt.hip -- dense Y = X W^T on gfx950 MFMA, ragged shapes by local padding.
+//
+// Workload: the dense layer of DietCode's test_1_local_padding.py
+// (test_local_padding docstring), Y[i,j] += X[i,k] * W[j,k]. Each workgroup
+// owns one BM x BN output tile and runs the shared fetch -> LDS -> MFMA
+// pipeline over K; edge tiles are zero-filled at fetch and masked at
+// writeback, so the MFMA loop itself has no predicates.
+//
+// Tile order (the blog "Tensor Core学习", GEMM optimisation notes on L2
+// locality and grid raster): workgroup ids are first regrouped per XCD, then
+// walked in groups of GROUP_M tile rows so that neighbouring workgroups share
+// X and W panels in L2.
+#include "launch.hpp"
+#include "tile_engine.hpp"
+
+namespace cas {
+
+namespace {
+
+constexpr int GROUP_M = 4;
+
+template <class E> struct GemmBK;
+template <> struct GemmBK<KF32> { static constexpr int v = 32; };
+template <> struct GemmBK<KBF16> { static constexpr int v = 64; };
+template <> struct GemmBK<KF16> { static constexpr int v = 64; };
+
+template <class E, int BM, int BN, int WGM, int WGN, int VEC>
+__global__ void __launch_bounds__(WGM *WGN * 64)
+gemm_nt_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
+               int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+               int64_t tiles_m, int64_t tiles_n)
+{
+    using G = Engine<E, BM, BN, GemmBK<E>::v, WGM, WGN, VEC>;
+    __shared__ __attribute__((aligned(16))) char lds[2 * G::STAGE];
+
+    const int tid = threadIdx.x;
+    const int64_t nwg = tiles_m * tiles_n;
+    const int64_t pid = xcd_remap(blockIdx.x, nwg);
+    const int64_t group = GROUP_M * tiles_n;
+    const int64_t first_m = (pid / group) * GROUP_M;
+    const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    const int64_t tm = first_m + (pid % group) % gm;
+    const int64_t tn = (pid % group) / gm;
+
+    f32x16 acc[G::MB][G::NB];
+    G::template mainloop<2>(acc, lds, X, ldx, M, tm * BM, W, ldw, N, tn * BN, K, tid);
+
+    // Writeback stage: predicated on the true M and N.
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wave_m = wave / WGN, wave_n = wave % WGN;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb) {
+            const int64_t col = tn * BN + wave_n * G::WN + nb * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = tm * BM + wave_m * G::WM + mb * 32 + acc_row(r, lane);
+                if (row < M && col < N) Y[row * ldy + col] = acc[mb][nb][r];
+            }
+        }
+    }
+}
+
+template <int BM, int BN> struct TileCfg;
+template <> struct TileCfg<64, 64> { static constexpr int WGM = 2, WGN = 2; };
+template <> struct TileCfg<128, 128> { static constexpr int WGM = 2, WGN = 2; };
+
+template <class E, int BM, int BN, int VEC>
+hipError_t launch_tile(const GemmArgs &a, hipStream_t s)
+{
+    using C = TileCfg<BM, BN>;
+    const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC>), dim3((unsigned)(tm * tn)),
+                       dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
+                       a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+    return hipGetLastError();
+}
+
+template <class E, int BM, int BN>
+hipError_t launch_vec(const GemmArgs &a, int vec, hipStream_t s)
+{
+    constexpr int VMAX = 16 / E::ES;
+    if (vec >= VMAX) return launch_tile<E, BM, BN, VMAX>(a, s);
+    if (vec >= VMAX / 2) return launch_tile<E, BM, BN, VMAX / 2>(a, s);
+    if constexpr (VMAX / 4 >= 1) {
+        if (vec >= VMAX / 4) return launch_tile<E, BM, BN, VMAX / 4>(a, s);
+    }
+    if constexpr (VMAX / 8 >= 1) {
+        if (vec >= VMAX / 8) return launch_tile<E, BM, BN, VMAX / 8>(a, s);
+    }
+    return launch_tile<E, BM, BN, 1>(a, s);
+}
+
+int pick_tile(const GemmArgs &a, int tile)
+{
+    if (tile != GEMM_TILE_AUTO) return tile;
+    // Largest tile that still gives every CU (256) about one workgroup.
+    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    return t128 >= 256 ? GEMM_TILE_128 : GEMM_TILE_64;
+}
+
+template <class E>
+hipError_t launch_elem(const GemmArgs &a, int vec, int tile, hipStream_t s)
+{
+    if (pick_tile(a, tile) == GEMM_TILE_128) return launch_vec<E, 128, 128>(a, vec, s);
+    return launch_vec<E, 64, 64>(a, vec, s);
+}
+
+} // namespace
+
+int64_t gemm_nt_workgroups(const GemmArgs &a, int /*elem*/, int tile)
+{
+    const int bm = pick_tile(a, tile) == GEMM_TILE_128 ? 128 : 64;
+    return ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm);
+}
+
+hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s)
+{
+    switch (elem) {
+    case E_F32: return launch_elem<KF32>(a, vec, tile, s);
+    case E_BF16: return launch_elem<KBF16>(a, vec, tile, s);
+    default: return launch_elem<KF16>(a, vec, tile, s);
+    }
+}
+
+} // namespace cas

@@ -1,0 +1,37 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cas {
+
+enum ElemCode { E_F32 = 0, E_BF16 = 1, E_F16 = 2 };
+
+struct GemmArgs {
+    const void *X;
+    const void *W;
+    float *Y;
+    int64_t M, N, K, ldx, ldw, ldy;
+};
+
+struct TrimulArgs {
+    const void *qkv;
+    float *out;
+    int64_t B, T, C, NH, HS;
+    float scale;
+    bool vec_store; // T % 4 == 0 and out is 16-byte aligned
+};
+
+// Tile shapes the dense launcher can pick (exposed for tests and tuning).
+enum GemmTile { GEMM_TILE_AUTO = 0, GEMM_TILE_64 = 1, GEMM_TILE_128 = 2 };
+
+// vec: elements per global load (a power of two that divides K, both pitches
+// and both base addresses' alignment in elements). Returns the launch error.
+hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s);
+int64_t gemm_nt_workgroups(const GemmArgs &a, int elem, int tile);
+
+hipError_t launch_trimul(const TrimulArgs &a, int elem, int vec, hipStream_t s);
+int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);
+
+} // namespace cas

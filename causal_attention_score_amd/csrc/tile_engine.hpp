@@ -1,0 +1,219 @@
+// tile_engine.hpp -- the fetch -> LDS -> MFMA pipeline shared by the dense NT
+// product and the causal score kernels (gfx950, wave64).
+//
+// Stage model (DietCode test_1_local_padding.py, test_local_padding
+// docstring: Fetch, Compute, Writeback): every bounds predicate lives in the
+// Fetch stage, which zero-fills rows past the matrix and contraction indices
+// past K, and in the Writeback stage of each kernel. The Compute stage below
+// runs over full tiles with no predicates ("local padding"); it never shrinks
+// the LDS workspace for edge tiles (test_local_padding_ii docstring).
+//
+// Both operands arrive as rows that are contiguous along the contraction
+// index ("NT": X rows and W rows, or Q rows and K rows), so one 16-byte LDS
+// read per lane feeds an MFMA operand directly with no transposition.
+//
+// MFMA shapes: fp32 inputs use v_mfma_f32_32x32x2_f32 (4 per 16-byte chunk),
+// bf16 / f16 inputs use v_mfma_f32_32x32x16_{bf16,f16} (1 per chunk). The
+// accumulators are fp32 in every case.
+//
+// Contraction-order permutation: lane half h = lane/32 is the MFMA's k-slot.
+// Within one BK chunk, half h feeds the contraction indices
+// [h*BK/2, (h+1)*BK/2) in ascending order, so a lane reads contiguous bytes.
+// A and B use the same permutation, so every product a_k*b_k is formed
+// exactly once; only the fp32 summation order differs from the plain loop.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cas {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Element kinds of the inputs (outputs are always fp32).
+struct KF32 { static constexpr int ES = 4; };
+struct KBF16 { static constexpr int ES = 2; };
+struct KF16 { static constexpr int ES = 2; };
+
+// One 16-byte chunk of A and of B per lane -> accumulate into a 32x32 tile.
+template <class E> __device__ __forceinline__ void mfma_chunk(f32x16 &acc, u32x4 a, u32x4 b);
+
+template <> __device__ __forceinline__ void mfma_chunk<KF32>(f32x16 &acc, u32x4 a, u32x4 b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+template <> __device__ __forceinline__ void mfma_chunk<KBF16>(f32x16 &acc, u32x4 a, u32x4 b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+template <> __device__ __forceinline__ void mfma_chunk<KF16>(f32x16 &acc, u32x4 a, u32x4 b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+// Global-load vector types by byte width.
+template <int BYTES> struct VecT;
+template <> struct VecT<16> { using T = u32x4; };
+template <> struct VecT<8> { using T = u32x2; };
+template <> struct VecT<4> { using T = unsigned int; };
+template <> struct VecT<2> { using T = unsigned short; };
+
+// Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
+// row 8*(r/4) + 4*(l/32) + r%4 (an A row) and column l%32 (a B row).
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// E: element kind. BM x BN output tile, BK contraction chunk, WGM x WGN waves,
+// VEC elements per global load.
+template <class E, int BM, int BN, int BK, int WGM, int WGN, int VEC>
+struct Engine {
+    static constexpr int ES = E::ES;
+    static constexpr int NT = WGM * WGN * 64;          // threads per workgroup
+    static constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
+    static constexpr int MB = WM / 32, NB = WN / 32;   // 32x32 MFMA tiles per wave
+    static constexpr int ROWB = BK * ES + 16;          // LDS row pitch: +16 B skews banks
+    static constexpr int A_BYTES = BM * ROWB;
+    static constexpr int B_BYTES = BN * ROWB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int VB = VEC * ES;                // bytes per global load
+    static constexpr int VPR = BK / VEC;               // loads per tile row
+    static constexpr int A_IT = BM * VPR / NT;
+    static constexpr int B_IT = BN * VPR / NT;
+    static constexpr int HALF_B = BK * ES / 2;         // bytes of one k-slot half row
+    static constexpr int CHUNKS = HALF_B / 16;
+    using V = typename VecT<VB>::T;
+
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+    static_assert(HALF_B % 16 == 0, "half row must be whole 16-byte chunks");
+    static_assert((BM * VPR) % NT == 0 && (BN * VPR) % NT == 0, "fetch must divide evenly");
+    static_assert(ROWB % 16 == 0 && ((ROWB / 16) & 1) == 1, "odd 16-byte pitch keeps 8 lanes on distinct banks");
+
+    struct Regs {
+        V a[A_IT];
+        V b[B_IT];
+    };
+
+    // Fetch stage: rows [ra0, ra0+BM) of A and [rb0, rb0+BN) of B, contraction
+    // indices [k0, k0+BK); anything outside (rows >= rows*, k >= K) is zero.
+    // Host guarantees K % VEC == 0, pitches % VEC == 0 and VB-aligned bases, so
+    // a vector is either wholly inside or wholly outside.
+    __device__ static __forceinline__ void fetch(Regs &R, const char *A, int64_t lda, int64_t rowsA, int64_t ra0,
+                                                 const char *B, int64_t ldb, int64_t rowsB, int64_t rb0,
+                                                 int64_t K, int64_t k0, int tid)
+    {
+#pragma unroll
+        for (int it = 0; it < A_IT; ++it) {
+            const int v = it * NT + tid;
+            const int r = v / VPR, c = v % VPR;
+            const int64_t gr = ra0 + r, gk = k0 + (int64_t)c * VEC;
+            V val = {};
+            if (gr < rowsA && gk < K) val = *reinterpret_cast<const V *>(A + (gr * lda + gk) * ES);
+            R.a[it] = val;
+        }
+#pragma unroll
+        for (int it = 0; it < B_IT; ++it) {
+            const int v = it * NT + tid;
+            const int r = v / VPR, c = v % VPR;
+            const int64_t gr = rb0 + r, gk = k0 + (int64_t)c * VEC;
+            V val = {};
+            if (gr < rowsB && gk < K) val = *reinterpret_cast<const V *>(B + (gr * ldb + gk) * ES);
+            R.b[it] = val;
+        }
+    }
+
+    __device__ static __forceinline__ void stash(const Regs &R, char *lds, int tid)
+    {
+#pragma unroll
+        for (int it = 0; it < A_IT; ++it) {
+            const int v = it * NT + tid;
+            *reinterpret_cast<V *>(lds + (v / VPR) * ROWB + (v % VPR) * VB) = R.a[it];
+        }
+#pragma unroll
+        for (int it = 0; it < B_IT; ++it) {
+            const int v = it * NT + tid;
+            *reinterpret_cast<V *>(lds + A_BYTES + (v / VPR) * ROWB + (v % VPR) * VB) = R.b[it];
+        }
+    }
+
+    // Compute stage: no predicates; every wave multiplies its WM x WN slice.
+    __device__ static __forceinline__ void compute(f32x16 (&acc)[MB][NB], const char *lds, int wave_m, int wave_n,
+                                                   int lane)
+    {
+        const int r32 = lane & 31, h = lane >> 5;
+        const char *a0 = lds + (wave_m * WM + r32) * ROWB + h * HALF_B;
+        const char *b0 = lds + A_BYTES + (wave_n * WN + r32) * ROWB + h * HALF_B;
+#pragma unroll
+        for (int u = 0; u < CHUNKS; ++u) {
+            u32x4 af[MB], bfr[NB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4 *>(a0 + mb * 32 * ROWB + u * 16);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) bfr[nb] = *reinterpret_cast<const u32x4 *>(b0 + nb * 32 * ROWB + u * 16);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) mfma_chunk<E>(acc[mb][nb], af[mb], bfr[nb]);
+        }
+    }
+
+    // Full contraction over K for one output tile, STAGES = 1 or 2 LDS buffers.
+    template <int STAGES>
+    __device__ static __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], char *lds,
+                                                    const char *A, int64_t lda, int64_t rowsA, int64_t ra0,
+                                                    const char *B, int64_t ldb, int64_t rowsB, int64_t rb0,
+                                                    int64_t K, int tid)
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wave_m = wave / WGN, wave_n = wave % WGN;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+
+        const int64_t nk = (K + BK - 1) / BK;
+        Regs R;
+        if constexpr (STAGES == 2) {
+            if (nk > 0) {
+                fetch(R, A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, 0, tid);
+                stash(R, lds, tid);
+            }
+            __syncthreads();
+            for (int64_t kc = 0; kc < nk; ++kc) {
+                const char *cur = lds + (kc & 1) * STAGE;
+                if (kc + 1 < nk) fetch(R, A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, (kc + 1) * BK, tid);
+                compute(acc, cur, wave_m, wave_n, lane);
+                if (kc + 1 < nk) stash(R, lds + ((kc + 1) & 1) * STAGE, tid);
+                __syncthreads();
+            }
+        } else {
+            for (int64_t kc = 0; kc < nk; ++kc) {
+                fetch(R, A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, kc * BK, tid);
+                if (kc > 0) __syncthreads(); // every wave is done reading the previous chunk
+                stash(R, lds, tid);
+                __syncthreads();
+                compute(acc, lds, wave_m, wave_n, lane);
+            }
+        }
+    }
+};
+
+// Map the hardware workgroup id so that the ids dispatched to one XCD
+// (round-robin: id % 8) become one contiguous range of logical ids; the
+// logical order then keeps tiles that share operand panels on one L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t n)
+{
+    const int64_t q = n / 8, rem = n % 8, x = w % 8;
+    return x * q + (x < rem ? x : rem) + w / 8;
+}
+
+} // namespace cas

@@ -1,0 +1,100 @@
+/*
+ * cas.h -- C ABI of the MI355X (gfx950) tiled-matmul hot path.
+ *
+ * Two operations, both hand-written CDNA4 kernels with fp32 accumulation:
+ *
+ *   cas_gemm_nt        dense Y = X W^T over ragged shapes
+ *   cas_trimul_causal  causal attention scores read straight from packed QKV
+ *
+ * Conventions shared by every entry point
+ *   - Pointers X, W, Y, qkv, out are DEVICE pointers (hipMalloc or any
+ *     allocator of device memory). The caller owns every buffer; the library
+ *     allocates nothing, keeps no pointer after returning and never
+ *     synchronises. Buffers must stay alive until the stream reaches the
+ *     kernel.
+ *   - stream is a hipStream_t passed as void*; NULL selects the default
+ *     (null) stream. The kernel is enqueued and the call returns at once.
+ *   - Shapes and pitches are int64 counts of ELEMENTS.
+ *   - Arguments are validated before any HIP call; a rejected call returns a
+ *     negative cas_status and writes nothing. A failed launch returns
+ *     CAS_ERR_HIP and cas_last_hip_error() gives the hipError_t (per thread).
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Accepted (in_dtype, out_dtype) pairs: (F32, F32), (BF16, F32),
+ *     (F16, F32). 16-bit inputs are raw bfloat16 / IEEE binary16 patterns.
+ *   - The output byte range may not overlap an input byte range.
+ *   - Any alignment is accepted; 16-byte aligned bases and pitches select
+ *     wider loads and stores, with the same results.
+ */
+#ifndef CAS_H
+#define CAS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CAS_F32 = 0, CAS_BF16 = 1, CAS_F16 = 2 } cas_dtype;
+
+typedef enum {
+    CAS_OK = 0,
+    CAS_ERR_NULL = -1,   /* a required pointer is NULL                       */
+    CAS_ERR_SHAPE = -2,  /* negative dim, pitch too small, C % NH != 0, overflow */
+    CAS_ERR_DTYPE = -3,  /* unsupported (in_dtype, out_dtype) pair           */
+    CAS_ERR_ALIAS = -4,  /* output bytes overlap input bytes                 */
+    CAS_ERR_DEVICE = -5, /* current device is not gfx950, or no device       */
+    CAS_ERR_HIP = -6     /* the HIP launch failed; see cas_last_hip_error()  */
+} cas_status;
+
+/*
+ * Dense NT product (DietCode tests/codegen/test_1_local_padding.py,
+ * test_local_padding docstring: the dense layer Y = X W^T with X [B*T, I],
+ * W [H, I], Y [B*T, H], i.e. Y[i,j] += X[i,k] * W[j,k]):
+ *
+ *   Y[m*ldy + n] = sum_{k<K} X[m*ldx + k] * W[n*ldw + k],   m < M, n < N
+ *
+ * X: M rows of pitch ldx (>= K), W: N rows of pitch ldw (>= K), both of
+ * in_dtype; Y: M rows of pitch ldy (>= N), fp32, written only at n < N.
+ * Shapes need not be tile multiples: out-of-range rows and columns are
+ * zero-filled when fetched and masked when written back.
+ * M == 0 or N == 0: nothing is written (OK). K == 0: Y = 0 (the empty sum).
+ */
+int cas_gemm_nt(const void *X, const void *W, void *Y,
+                int64_t M, int64_t N, int64_t K,
+                int64_t ldx, int64_t ldw, int64_t ldy,
+                cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * Causal attention scores (llm.c dev/cuda/trimat_forward.cu, trimul_cpu, the
+ * "Referee" of Chapter I; launched per (batch, head) as in trimul_global of
+ * Chapter II):
+ *
+ *   qkv  (B, T, 3, NH, HS) contiguous, C = NH*HS; Q row t of head nh starts at
+ *        element b*T*3C + t*3C + nh*HS, K row t2 at the same place + C; the V
+ *        third is never read.
+ *   out  (B, NH, T, T) contiguous fp32:
+ *        out[b,nh,t,t2] = fp32(Q.K) * s  for t2 <= t, s = fp32 nearest 1/sqrt(HS)
+ *        out[b,nh,t,t2] = quiet NaN, bits 0x7FC00000, for t2 > t
+ *
+ * Only tiles on or below the diagonal are computed; the tiles above it are
+ * filled with the NaN pattern by the same launch. Any T >= 1 is accepted.
+ * Requires C > 0 and C % NH == 0. B == 0, T == 0 or NH == 0: nothing is
+ * written (OK). Offsets are 64-bit: outputs above 2^32 bytes are fine.
+ */
+int cas_trimul_causal(const void *qkv, void *out,
+                      int64_t B, int64_t T, int64_t C, int64_t NH,
+                      cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *cas_status_string(int status);
+
+/* hipError_t of this thread's last CAS_ERR_HIP / CAS_ERR_DEVICE, else 0. */
+int cas_last_hip_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int cas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CAS_H */

@@ -1,0 +1,122 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+symbol include/cas.h declares, and rejects bad arguments before any HIP call."""
+import os
+import re
+
+import pytest
+
+import causal_attention_score_amd as cas
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cas.h")
+
+F32, BF16, F16 = cas.CAS_F32, cas.CAS_BF16, cas.CAS_F16
+OK, ENULL, ESHAPE, EDTYPE, EALIAS, EDEV = 0, -1, -2, -3, -4, -5
+
+# Fake, distinct, aligned addresses: validation never dereferences them.
+PX, PW, PY = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cas.LIB_PATH):
+        pytest.skip("libcas.so not built")
+    return cas.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cas_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(cas.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in list(cas.STATUS) + [7, -99]:
+        s = cas.status_string(code)
+        assert isinstance(s, str) and s
+    assert L.cas_version() >= 100
+
+
+def g(L, X=PX, W=PW, Y=PY, M=4, N=5, K=6, ldx=None, ldw=None, ldy=None, ind=F32, outd=F32):
+    return L.cas_gemm_nt(X, W, Y, M, N, K, K if ldx is None else ldx, K if ldw is None else ldw,
+                         N if ldy is None else ldy, ind, outd, None)
+
+
+def t(L, qkv=PX, out=PY, B=2, T=5, C=12, NH=3, ind=F32, outd=F32):
+    return L.cas_trimul_causal(qkv, out, B, T, C, NH, ind, outd, None)
+
+
+def test_gemm_rejections(L):
+    assert g(L, ind=7) == EDTYPE
+    assert g(L, outd=BF16) == EDTYPE
+    assert g(L, M=-1) == ESHAPE
+    assert g(L, K=-2) == ESHAPE
+    assert g(L, ldx=5) == ESHAPE            # ldx < K
+    assert g(L, ldw=3) == ESHAPE            # ldw < K
+    assert g(L, ldy=4) == ESHAPE            # ldy < N
+    assert g(L, Y=None) == ENULL
+    assert g(L, X=None) == ENULL
+    assert g(L, W=None) == ENULL
+    assert g(L, Y=PX + 8) == EALIAS         # output starts inside X
+    assert g(L, X=PY + 4 * 5 * 4 - 4) == EALIAS  # X starts at Y's last element
+    assert g(L, M=2**40, ldx=2**40, K=6) == ESHAPE  # byte extent above 2^62
+    assert g(L, M=2**62, N=4, K=4) == ESHAPE  # byte extent overflows
+
+
+def test_gemm_empty_is_ok_without_a_device(L):
+    assert g(L, M=0) == OK
+    assert g(L, N=0, ldy=0) == OK
+    assert g(L, X=None, W=None, Y=None, M=0) == OK
+
+
+def test_gemm_k0_needs_no_inputs(L):
+    # K == 0 writes zeros: X and W may be NULL; with no GPU the call stops at
+    # the device check.
+    assert g(L, X=None, W=None, K=0) == EDEV
+
+
+def test_trimul_rejections(L):
+    assert t(L, ind=3) == EDTYPE
+    assert t(L, outd=F16) == EDTYPE
+    assert t(L, B=-1) == ESHAPE
+    assert t(L, C=10, NH=3) == ESHAPE       # C % NH != 0
+    assert t(L, C=0) == ESHAPE
+    assert t(L, qkv=None) == ENULL
+    assert t(L, out=None) == ENULL
+    assert t(L, out=PX + 64) == EALIAS
+    assert t(L, B=2**40, T=2**20) == ESHAPE
+
+
+def test_trimul_empty_is_ok(L):
+    assert t(L, B=0) == OK
+    assert t(L, T=0) == OK
+    assert t(L, NH=0, C=0) == OK
+
+
+def test_valid_calls_reach_the_device_check(L):
+    # On a machine with no GPU a valid call fails at the device check only.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert g(L) == EDEV
+    assert t(L) == EDEV
+
+
+def test_binding_validates_shapes():
+    import torch
+    x = torch.zeros(3, 4)
+    with pytest.raises(ValueError):
+        cas.gemm_nt(x, torch.zeros(5, 3))
+    with pytest.raises(TypeError):
+        cas.gemm_nt(x, torch.zeros(5, 4, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        cas.trimul_causal(torch.zeros(2, 3, 10), 2)

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+element by element on the same seeded inputs.
+
+Sizes span several tiles and ragged tails; the workload tests run the
+full-size configurations in the launch configuration the benchmark times and
+compare every element the oracle can afford (sampled rows / planes at the two
+largest sizes, plus whole-output mask counts)."""
+import numpy as np
+import pytest
+import torch
+
+import causal_attention_score_amd as cas
+from causal_attention_score_amd import synth
+from gpu_util import (QNAN, SENTINEL, assert_close, assert_exact, assert_scores, bits, case, check_guards,
+                      guarded_output, to_device)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "bf16", "f16"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gemm(X, W, dtype, M, N, K, label, ldy=None):
+    ldy = N if ldy is None else ldy
+    n = M * ldy
+    buf, flat = guarded_output(n)
+    y = flat.view(M, ldy)[:, :N]
+    case(f"{label} gemm_nt {dtype} M={M} N={N} K={K} ldy={ldy}")
+    cas.gemm_nt(to_device(X, dtype), to_device(W, dtype), out=y)
+    torch.cuda.synchronize()
+    check_guards(buf, n)
+    return flat.view(M, ldy).cpu().numpy()
+
+
+# ------------------------------------------------------------------ gemm_nt
+
+GEMM_SHAPES = [(1, 1, 1), (2, 3, 7), (7, 15, 31), (15, 9, 12), (33, 63, 65), (65, 33, 127), (127, 129, 255),
+               (129, 127, 257), (255, 257, 33), (257, 255, 770), (1, 257, 129), (300, 1, 64), (64, 64, 64),
+               (128, 128, 128), (96, 160, 770), (200, 72, 3)]
+
+
+@pytest.mark.parametrize("tile", ["64", "128"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_ragged(orc, monkeypatch, shape, dtype, tile):
+    monkeypatch.setenv("CAS_GEMM_TILE", tile)
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, dtype, seed=M * 7 + N * 3 + K)
+    ref, bound = orc.gemm_nt(X, W, dtype)
+    y = run_gemm(X, W, dtype, M, N, K, f"tile{tile}")
+    assert_close(y, ref, bound, dtype, f"gemm {shape} {dtype} tile{tile}")
+
+
+@pytest.mark.parametrize("tile", ["64", "128"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_exact_small_integers(orc, monkeypatch, dtype, tile):
+    """Integer inputs: every partial sum is an exact integer, so the GPU must
+    equal the oracle bit for bit whatever its summation order."""
+    monkeypatch.setenv("CAS_GEMM_TILE", tile)
+    for (M, N, K) in [(131, 67, 770), (64, 256, 129), (5, 300, 1000)]:
+        X, W = synth.gemm_inputs(M, N, K, dtype, seed=K, dist="int")
+        ref, _ = orc.gemm_nt(X, W, dtype)
+        y = run_gemm(X, W, dtype, M, N, K, "exact")
+        assert_exact(y, ref, f"gemm exact {(M, N, K)} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_strided_misaligned(orc, dtype):
+    """Row pitches above K, bases one element off 16-byte alignment, and an
+    output pitch above N: the narrow-load variants and the writeback mask."""
+    M, N, K = 77, 45, 130
+    ldx, ldw, ldy = K + 3, K + 5, N + 7
+    g = np.random.default_rng(99)
+    Xf = synth.to_storage(g.standard_normal((M * ldx + 1,)).astype(np.float32), dtype)
+    Wf = synth.to_storage(g.standard_normal((N * ldw + 1,)).astype(np.float32), dtype)
+    ref, bound = orc.gemm_nt(Xf[1:], Wf[1:], dtype, M=M, N=N, K=K, ldx=ldx, ldw=ldw, ldy=ldy)
+    dx, dw = to_device(Xf, dtype), to_device(Wf, dtype)
+    x = dx[1:].as_strided((M, K), (ldx, 1))
+    w = dw[1:].as_strided((N, K), (ldw, 1))
+    buf, flat = guarded_output(M * ldy)
+    y = flat.view(M, ldy)[:, :N]
+    case(f"gemm strided/misaligned {dtype}")
+    cas.gemm_nt(x, w, out=y)
+    torch.cuda.synchronize()
+    check_guards(buf, M * ldy)
+    h = flat.view(M, ldy).cpu().numpy()
+    assert np.all(h[:, N:].view(np.int32) == SENTINEL), "wrote past N inside the output pitch"
+    assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
+
+
+def test_gemm_k0_writes_zeros():
+    x = torch.empty((5, 0), device="cuda")
+    w = torch.empty((7, 0), device="cuda")
+    buf, flat = guarded_output(35)
+    case("gemm K=0")
+    cas.gemm_nt(x, w, out=flat.view(5, 7))
+    torch.cuda.synchronize()
+    check_guards(buf, 35)
+    assert np.all(flat.cpu().numpy() == 0)
+
+
+def test_gemm_empty_is_noop():
+    x = torch.zeros((0, 4), device="cuda")
+    w = torch.zeros((3, 4), device="cuda")
+    y = cas.gemm_nt(x, w)
+    assert y.shape == (0, 3)
+
+
+def test_gemm_alias_rejected():
+    buf = torch.zeros(4096, device="cuda")
+    x = buf[:64].view(8, 8)
+    w = buf[64:128].view(8, 8)
+    with pytest.raises(cas.CasError) as e:
+        cas.gemm_nt(x, w, out=buf[32:96].view(8, 8))
+    assert e.value.status == -4
+
+
+def test_gemm_side_stream(orc):
+    X, W = synth.gemm_inputs(300, 200, 100, "f32", seed=5)
+    ref, bound = orc.gemm_nt(X, W, "f32")
+    s = torch.cuda.Stream()
+    x, w = to_device(X, "f32"), to_device(W, "f32")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        case("gemm on a side stream")
+        y = cas.gemm_nt(x, w)
+    s.synchronize()
+    assert_close(y.cpu().numpy(), ref, bound, "f32", "gemm side stream")
+
+
+# ------------------------------------------------------------ trimul_causal
+
+def run_trimul(qkv, dtype, B, T, NH, HS, label):
+    n = B * NH * T * T
+    buf, flat = guarded_output(n)
+    case(f"{label} trimul_causal {dtype} B={B} T={T} NH={NH} HS={HS}")
+    cas.trimul_causal(to_device(qkv, dtype).view(B, T, 3 * NH * HS), NH, out=flat.view(B, NH, T, T))
+    torch.cuda.synchronize()
+    check_guards(buf, n)
+    return flat.view(B, NH, T, T).cpu().numpy()
+
+
+TRI_T = [1, 2, 7, 63, 64, 65, 127, 128, 129, 300]
+TRI_HS = [1, 8, 40, 64, 80, 128]
+
+
+@pytest.mark.parametrize("HS", TRI_HS)
+@pytest.mark.parametrize("T", TRI_T)
+def test_trimul_ragged_f32(orc, T, HS):
+    for (B, NH) in [(1, 1), (2, 3)]:
+        qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 131 + HS)
+        ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+        out = run_trimul(qkv, "f32", B, T, NH, HS, "sweep")
+        assert_scores(out, ref, bound, "f32", f"trimul f32 B={B} T={T} NH={NH} HS={HS}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("HS", [8, 40, 64, 80, 128, 3])
+@pytest.mark.parametrize("T", [1, 65, 128, 300])
+def test_trimul_ragged_16bit(orc, T, HS, dtype):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 17 + HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul(qkv, dtype, B, T, NH, HS, "sweep16")
+    assert_scores(out, ref, bound, dtype, f"trimul {dtype} T={T} HS={HS}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_trimul_exact_small_integers(orc, dtype):
+    for (B, T, NH, HS) in [(2, 257, 2, 64), (1, 130, 3, 40)]:
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS, dist="int")
+        ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+        out = run_trimul(qkv, dtype, B, T, NH, HS, "exact")
+        # HS = 64 scales by 1/8 exactly; HS = 40 rounds once, like the oracle
+        assert_scores(out, ref, bound, dtype, f"trimul exact {dtype}", exact=(HS == 64))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_trimul_misaligned_base(orc, dtype):
+    """qkv one element past a 16-byte boundary: the narrow fetch variant."""
+    B, T, NH, HS = 2, 70, 2, 16
+    n = B * T * 3 * NH * HS
+    flat = synth.to_storage(synth.normal_f32(synth.rng(3), (n + 1,)), dtype)
+    qkv = flat[1:].reshape(B, T, 3 * NH * HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    d = to_device(flat, dtype)
+    buf, o = guarded_output(B * NH * T * T)
+    case(f"trimul misaligned {dtype}")
+    cas.trimul_causal(d[1:].view(B, T, -1), NH, out=o.view(B, NH, T, T))
+    torch.cuda.synchronize()
+    check_guards(buf, B * NH * T * T)
+    assert_scores(o.view(B, NH, T, T).cpu().numpy(), ref, bound, dtype, f"trimul misaligned {dtype}")
+
+
+def test_trimul_5d_input_and_side_stream(orc):
+    B, T, NH, HS = 1, 200, 4, 32
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=8)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "bf16")
+    d = to_device(qkv, "bf16").view(B, T, 3, NH, HS)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        case("trimul 5-d input on a side stream")
+        out = cas.trimul_causal(d, NH)
+    s.synchronize()
+    assert_scores(out.cpu().numpy(), ref, bound, "bf16", "trimul 5d")
+
+
+def test_trimul_alias_rejected():
+    buf = torch.zeros(1 << 16, device="cuda")
+    qkv = buf[:2 * 8 * 24].view(2, 8, 24)
+    with pytest.raises(cas.CasError) as e:
+        cas.trimul_causal(qkv, 2, out=buf[100:100 + 2 * 2 * 64].view(2, 2, 8, 8))
+    assert e.value.status == -4
+
+
+def test_trimul_rejects_bad_heads():
+    qkv = torch.zeros((1, 4, 30), device="cuda")
+    with pytest.raises(cas.CasError):
+        cas.trimul_causal(qkv, 4)  # C = 10 is not a multiple of NH = 4
+
+
+# ------------------------------------------------- the five workloads, full size
+
+def test_workload_dense_f32_15x9x12(orc):
+    wl = synth.WORKLOADS["dense_f32_15x9x12"]
+    X, W = wl.inputs()
+    ref, bound = orc.gemm_nt(X, W, "f32")
+    y = run_gemm(X, W, "f32", 15, 9, 12, wl.name)
+    assert_close(y, ref, bound, "f32", wl.name)
+    # the same product taken the notebook's tiled way
+    tiled, loads, writes, _, _ = orc.tiled_matmul_count(X, np.ascontiguousarray(W.T), 5, 3, 6)
+    assert (loads, writes) == (864, 135)
+    assert np.max(np.abs(y - tiled)) <= 1e-4 * np.max(bound) + 1e-6
+
+
+def test_workload_dense_f32_960x1024x770(orc):
+    wl = synth.WORKLOADS["dense_f32_960x1024x770"]
+    X, W = wl.inputs()
+    ref, bound = orc.gemm_nt(X, W, "f32")
+    y = run_gemm(X, W, "f32", 960, 1024, 770, wl.name)
+    r = assert_close(y, ref, bound, "f32", wl.name)
+    print(f"{wl.name}: max err/tol {r:.3g}")
+
+
+def test_workload_trimul_f32_B8_T1024(orc):
+    wl = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    out = run_trimul(qkv, "f32", B, T, NH, HS, wl.name)
+    worst = 0.0
+    for b in range(B):
+        for h in range(NH):
+            ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, "f32")
+            worst = max(worst, assert_scores(out[b, h], ref, bound, "f32", f"{wl.name} plane ({b},{h})"))
+    print(f"{wl.name}: max err/tol {worst:.3g}")
+
+
+def test_workload_dense_bf16_4096(orc):
+    wl = synth.WORKLOADS["dense_bf16_4096"]
+    M, N, K = wl.dims
+    X, W = wl.inputs()
+    x, w = to_device(X, "bf16"), to_device(W, "bf16")
+    case(f"{wl.name} gemm_nt full size")
+    y = cas.gemm_nt(x, w)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 255, 256, 1000, 2047, 2048, 3071, 4064, 4095]
+    ref, bound = orc.gemm_nt(np.ascontiguousarray(X[rows]), W, "bf16")
+    got = y[rows].cpu().numpy()
+    r = assert_close(got, ref, bound, "bf16", wl.name)
+    assert bool(torch.isfinite(y).all())
+    print(f"{wl.name}: sampled rows max err/tol {r:.3g}")
+
+
+def test_workload_trimul_bf16_B4_T4096(orc):
+    wl = synth.WORKLOADS["trimul_bf16_B4_T4096_NH25_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    d = to_device(qkv, "bf16")
+    out = torch.empty((B, NH, T, T), dtype=torch.float32, device="cuda")
+    out.view(torch.int32).fill_(SENTINEL)
+    case(f"{wl.name} trimul_causal full size")
+    cas.trimul_causal(d, NH, out=out)
+    torch.cuda.synchronize()
+    ob = out.view(torch.int32)
+    n_nan = int((ob == QNAN).sum())
+    n_fin = int(torch.isfinite(out).sum())
+    assert n_nan == B * NH * T * (T - 1) // 2
+    assert n_fin == B * NH * T * (T + 1) // 2
+    worst = 0.0
+    for (b, h) in [(0, 0), (1, 13), (3, 24)]:
+        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, "bf16")
+        worst = max(worst, assert_scores(out[b, h].cpu().numpy(), ref, bound, "bf16", f"{wl.name} plane ({b},{h})"))
+    # rows sampled from every other plane
+    for p in range(0, B * NH, 7):
+        b, h = divmod(p, NH)
+        t0 = (p * 613) % (T - 8)
+        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, "bf16")
+        worst = max(worst, assert_scores(out[b, h, t0:t0 + 8].cpu().numpy(), ref, bound, "bf16",
+                                         f"{wl.name} rows {t0}.. of plane ({b},{h})"))
+    print(f"{wl.name}: sampled max err/tol {worst:.3g}")
