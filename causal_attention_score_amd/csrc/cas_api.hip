@@ -144,6 +144,8 @@ CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t 
     if (!mul_ok(B, NH, &t) || !mul_ok(t, T, &t) || !mul_ok(t, T, &out_elems) || !mul_ok(out_elems, 4, &outb))
         return CAS_ERR_SHAPE;
     if (inb >= (INT64_C(1) << 62) || outb >= (INT64_C(1) << 62)) return CAS_ERR_SHAPE;
+    // The kernels address a 64-row tile with 31-bit buffer offsets.
+    if (c3 * es >= (INT64_C(1) << 24) || T >= (INT64_C(1) << 24)) return CAS_ERR_SHAPE;
     if (overlap(out, outb, qkv, inb)) return CAS_ERR_ALIAS;
     if (cas::trimul_workgroups(B, T, NH) > INT32_MAX) return CAS_ERR_SHAPE;
     const int dc = device_check();

@@ -1,0 +1,462 @@
+// trimul_kernel.hpp -- causal attention scores straight from packed QKV on gfx950.
+//
+// Semantics: llm.c dev/cuda/trimat_forward.cu, trimul_cpu ("the Referee",
+// Chapter I): out[b,nh,t,t2] = (Q[b,t,nh,:] . K[b,t2,nh,:]) * s for t2 <= t
+// and NaN above the diagonal, with s = fp32 nearest 1/sqrt(HS).
+//
+// Design (MI355X-first; differs from that file's GPU kernels on purpose):
+//  * Work item = one 64x64 score tile. Only on- and below-diagonal tiles are
+//    items: item -> (plane, i, j <= i) by inverting the triangular numbers. A
+//    diagonal tile skips the 32x32 block that lies wholly above the diagonal;
+//    an off-diagonal tile (i, j) also writes its mirror tile (j, i) as NaN, so
+//    one launch writes the whole (T, T) plane.
+//  * Wave specialisation. A workgroup holds four compute waves and four store
+//    waves (one of each per SIMD). A compute wave fetches its tile's Q and K
+//    rows straight from the packed (B, T, 3, NH, HS) rows (pitch 3C: no
+//    permute pass, V never read) into registers, prefetching the next pass
+//    while the MFMAs of the current one run, then writes the scaled, masked
+//    tile to LDS. A store wave streams the previous tile from LDS to HBM with
+//    16-byte non-temporal stores, plus the NaN mirror tile. Compute waves issue
+//    no global stores and store waves no global loads, so neither ever waits
+//    on the other's memory latency (one vmcnt counts both on CDNA); the two
+//    sides meet at one LDS-only barrier per step, double-buffered.
+//  * Persistent grid sized to residency; the item list is split into eight
+//    contiguous ranges, one per XCD (workgroups are dispatched to XCDs round
+//    robin), so the Q and K rows of a plane stay within one XCD's L2.
+//  * Any T >= 1, any HS >= 1: rows past T and head entries past HS are zero
+//    at fetch (local padding), writes are masked; offsets are 64-bit.
+//
+// Contraction-order permutation: in each 16-byte chunk pair of a row, lane
+// half h = lane/32 (the MFMA k-slot) takes chunk 2u + h, for A (Q) and B (K)
+// alike, so each product q_k * k_k is formed exactly once.
+#pragma once
+
+#include "launch.hpp"
+#include "tile_engine.hpp"
+
+#include <cstdlib>
+
+namespace cas {
+namespace tri {
+
+constexpr int TB = 64;         // score tile edge
+constexpr int NCOMP = 4;       // compute waves per workgroup (one per SIMD)
+constexpr int NTHREADS = 2 * NCOMP * 64;
+constexpr int TILE_BYTES = TB * TB * 4;
+constexpr unsigned QNAN_BITS = 0x7FC00000u;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt4(float *p, f32x4v v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4v *>(p)); }
+
+// Keep a value opaque to the optimiser inside the loop, so address arithmetic
+// built on it is recomputed cheaply instead of hoisted into a register per use.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// LDS-only workgroup barrier: outstanding global stores are not waited for.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One 64-row operand block of a wave in MFMA layout: block mb (rows
+// mb*32 + lane%32), chunk pair u (chunk 2u + lane/32 of the row's pass).
+template <int U> struct Operand {
+    u32x4 c[2][U];
+};
+
+// A work item, all fields wave-uniform.
+struct Tile {
+    const char *q; // Q row t0 of (b, nh)
+    const char *k; // K row s0 of (b, nh)
+    char *o;       // out plane (b, nh)
+    int64_t t0, s0;
+    int rl, cl;    // rows / columns of the tile inside the plane (<= 64)
+    bool diag;
+};
+
+__device__ __forceinline__ Tile make_tile(const char *qkv, float *out, int64_t id, int64_t L, int64_t T, int64_t C,
+                                          int64_t NH, int64_t HS, int es)
+{
+    Tile tl;
+    const int64_t plane = id / L;
+    const int64_t r = id - plane * L;
+    // r = i(i+1)/2 + j, 0 <= j <= i
+    int64_t i = (int64_t)((sqrtf(8.0f * (float)r + 1.0f) - 1.0f) * 0.5f);
+    while (i * (i + 1) / 2 > r) --i;
+    while ((i + 1) * (i + 2) / 2 <= r) ++i;
+    const int64_t j = r - i * (i + 1) / 2;
+    const int64_t b = plane / NH, nh = plane - b * NH;
+    const int64_t C3 = 3 * C;
+    tl.t0 = i * TB;
+    tl.s0 = j * TB;
+    tl.q = qkv + ((b * T + tl.t0) * C3 + nh * HS) * es;
+    tl.k = qkv + ((b * T + tl.s0) * C3 + C + nh * HS) * es;
+    tl.o = reinterpret_cast<char *>(out + plane * T * T);
+    tl.rl = (int)((T - tl.t0) < TB ? (T - tl.t0) : TB);
+    tl.cl = (int)((T - tl.s0) < TB ? (T - tl.s0) : TB);
+    tl.diag = i == j;
+    return tl;
+}
+
+// Buffer resource over `base` (wave-uniform). Offsets at or above OOB read
+// as zero: the hardware range check does the zero-fill of local padding.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const char *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// Fetch head entries [e0, e0 + U*32/ES) of 64 rows starting at `base`
+// (uniform), row pitch ldb bytes; rows at or past `rows` and entries at or
+// past HS are zero.
+//   VEC16 (16-byte aligned rows, HS*ES % 16 == 0): one unconditional 16-byte
+//   buffer load per chunk, out-of-range lanes pointed past the record count.
+//   Otherwise (unaligned or ragged head) elements are fetched one by one.
+template <class E, int U, bool VEC16>
+__device__ __forceinline__ void fetch_rows(Operand<U> &op, const char *__restrict__ base, uint32_t ldb, int rows,
+                                           int64_t HS, int64_t e0, int lane)
+{
+    constexpr int ES = E::ES;
+    constexpr int EPC = 16 / ES; // elements per chunk
+    const int h = lane >> 5;
+    if constexpr (VEC16) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc_at(base);
+        const bool full = e0 + (int64_t)U * 2 * EPC <= HS; // uniform
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int r = mb * 32 + (lane & 31);
+            const uint32_t ro = (uint32_t)r * ldb + (uint32_t)(e0 * ES) + (uint32_t)h * 16;
+            const uint32_t rv = r < rows ? ro : OOB;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                uint32_t vo = rv + u * 32;
+                if (!full) vo = (e0 + (int64_t)(2 * u + h) * EPC < HS) ? vo : OOB;
+                op.c[mb][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int r = mb * 32 + (lane & 31);
+            const bool row_ok = r < rows;
+            const char *rp0 = base + (uint64_t)r * ldb + e0 * ES;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t e = e0 + (int64_t)(2 * u + h) * EPC; // first head entry of the chunk
+                unsigned w[4] = {0u, 0u, 0u, 0u};
+                if (row_ok) {
+                    const char *rp = rp0 + (2 * u + h) * 16;
+#pragma unroll
+                    for (int x = 0; x < EPC; ++x) {
+                        if (e + x < HS) {
+                            unsigned bitsv;
+                            if constexpr (ES == 4) bitsv = *reinterpret_cast<const unsigned *>(rp + x * 4);
+                            else bitsv = *reinterpret_cast<const unsigned short *>(rp + x * 2);
+                            w[(x * ES) / 4] |= bitsv << (((x * ES) % 4) * 8);
+                        }
+                    }
+                }
+                op.c[mb][u] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+}
+
+template <class E, int U>
+__device__ __forceinline__ void mma_pass(f32x16 (&acc)[2][2], const Operand<U> &q, const Operand<U> &k, bool diag)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        mfma_chunk<E>(acc[0][0], q.c[0][u], k.c[0][u]);
+        if (!diag) mfma_chunk<E>(acc[0][1], q.c[0][u], k.c[1][u]); // wholly above the diagonal otherwise
+        mfma_chunk<E>(acc[1][0], q.c[1][u], k.c[0][u]);
+        mfma_chunk<E>(acc[1][1], q.c[1][u], k.c[1][u]);
+    }
+}
+
+// Scaled, masked tile -> LDS, row-major 64 x 64 fp32.
+__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, bool diag, int lane)
+{
+    const float qnan = __uint_as_float(QNAN_BITS);
+    const int c0 = lane & 31, h4 = 4 * (lane >> 5);
+    const uint32_t lo = opaque((uint32_t)(h4 * TB + c0) * 4);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = mb * 32 + 8 * (r >> 2) + (r & 3); // uniform part of the row
+                const int row = rr + h4, col = nb * 32 + c0;
+                float v = acc[mb][nb][r] * scale;
+                if (diag && col > row) v = qnan;
+                *reinterpret_cast<float *>(lds + lo + (uint32_t)(rr * TB + nb * 32) * 4) = v;
+            }
+}
+
+// LDS tile -> rows [t0, t0+rl) x columns [s0, s0+cl) of the plane. FULL:
+// a whole 64x64 tile with 16-byte stores and no masks.
+template <bool FULL>
+__device__ __forceinline__ void lds_to_out(const char *lds, const Tile &tl, uint32_t T4, int lane, bool vec4)
+{
+    char *dst = tl.o + ((uint64_t)tl.t0 * (T4 / 4) + (uint64_t)tl.s0) * 4;
+    if (FULL || vec4) { // T % 4 == 0 and 16-byte aligned: columns come in fours
+        const int r4 = lane >> 4, c = (lane & 15) * 4;
+        const uint32_t go = opaque((uint32_t)r4 * T4 + (uint32_t)c * 4);
+        f32x4v v[TB / 4];
+#pragma unroll
+        for (int s = 0; s < TB / 4; ++s) v[s] = *reinterpret_cast<const f32x4v *>(lds + lane * 16 + s * 1024);
+#pragma unroll
+        for (int s = 0; s < TB / 4; ++s) {
+            if (FULL || (c < tl.cl && s * 4 + r4 < tl.rl))
+                st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * T4 + go)), v[s]);
+        }
+    } else {
+        for (int s = 0; s < TB; ++s) {
+            const float v = *reinterpret_cast<const float *>(lds + (s * TB + lane) * 4);
+            if (s < tl.rl && lane < tl.cl) st_nt(reinterpret_cast<float *>(dst + ((uint32_t)s * T4 + (uint32_t)lane * 4)), v);
+        }
+    }
+}
+
+// NaN over the mirror tile (j, i): rows [s0, s0+cl) x columns [t0, t0+rl).
+template <bool FULL>
+__device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane, bool vec4)
+{
+    const float qnan = __uint_as_float(QNAN_BITS);
+    char *dst = tl.o + ((uint64_t)tl.s0 * (T4 / 4) + (uint64_t)tl.t0) * 4;
+    if (FULL || vec4) {
+        const f32x4v n4 = {qnan, qnan, qnan, qnan};
+        const int r4 = lane >> 4, c = (lane & 15) * 4;
+        const uint32_t go = opaque((uint32_t)r4 * T4 + (uint32_t)c * 4);
+#pragma unroll
+        for (int s = 0; s < TB / 4; ++s)
+            if (FULL || (c < tl.rl && s * 4 + r4 < tl.cl))
+                st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * T4 + go)), n4);
+    } else {
+        for (int s = 0; s < TB; ++s)
+            if (s < tl.cl && lane < tl.rl) st_nt(reinterpret_cast<float *>(dst + ((uint32_t)s * T4 + (uint32_t)lane * 4)), qnan);
+    }
+}
+
+// One step of a compute wave: the P register passes of tile `tl` (operands of
+// pass 0 already in ops[SB]), prefetching each next pass -- and after the last
+// pass the first pass of `nx` when has_next -- into the other buffer, then the
+// scaled, masked tile to LDS. Afterwards nx's first pass sits in ops[(SB+P)%2].
+// P == 0: any number of passes, each fetched and then multiplied (no prefetch).
+template <class E, int U, bool VEC16, int P, int SB>
+__device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile &tl, const Tile &nx, bool has_next,
+                                             char *lds, uint32_t ldb, int64_t HS, float scale, int lane)
+{
+    constexpr int64_t PASS = (int64_t)U * 32 / E::ES;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+    if constexpr (P == 0) {
+        for (int64_t e0 = 0; e0 < HS; e0 += PASS) {
+            fetch_rows<E, U, VEC16>(ops[0][0], tl.q, ldb, tl.rl, HS, e0, lane);
+            fetch_rows<E, U, VEC16>(ops[0][1], tl.k, ldb, tl.cl, HS, e0, lane);
+            mma_pass<E, U>(acc, ops[0][0], ops[0][1], tl.diag);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int cur = (SB + p) & 1, nxt = cur ^ 1;
+            if (p + 1 < P) {
+                fetch_rows<E, U, VEC16>(ops[nxt][0], tl.q, ldb, tl.rl, HS, (p + 1) * PASS, lane);
+                fetch_rows<E, U, VEC16>(ops[nxt][1], tl.k, ldb, tl.cl, HS, (p + 1) * PASS, lane);
+            } else if (has_next) {
+                fetch_rows<E, U, VEC16>(ops[nxt][0], nx.q, ldb, nx.rl, HS, 0, lane);
+                fetch_rows<E, U, VEC16>(ops[nxt][1], nx.k, ldb, nx.cl, HS, 0, lane);
+            }
+            mma_pass<E, U>(acc, ops[cur][0], ops[cur][1], tl.diag);
+        }
+    }
+    tile_to_lds(acc, lds, scale, tl.diag, lane);
+}
+
+template <class E, int U, bool VEC16, int P>
+__global__ void __launch_bounds__(NTHREADS)
+trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, int64_t C, int64_t NH, int64_t HS,
+              int64_t L, int64_t items, float scale, int vec_store)
+{
+    constexpr int ES = E::ES;
+    __shared__ __attribute__((aligned(16))) char lds[NCOMP * 2 * TILE_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool compute = wave < NCOMP;
+    const int slot = wave % NCOMP;
+    char *my_lds = lds + slot * 2 * TILE_BYTES;
+
+    // XCD-local contiguous item range (proportional to the workgroups on each
+    // XCD); the workgroups of an XCD take NCOMP consecutive items per step.
+    const int64_t nwg = gridDim.x;
+    const int64_t x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
+    const int64_t wg_before = x * q8 + (x < r8 ? x : r8);
+    const int64_t wg_on_x = q8 + (x < r8 ? 1 : 0);
+    const int64_t lo = items * wg_before / nwg, hi = items * (wg_before + wg_on_x) / nwg;
+    const int64_t first = lo + (blockIdx.x / 8) * NCOMP;
+    const int64_t stride = wg_on_x * NCOMP;
+    const int64_t steps = first < hi ? (hi - first + stride - 1) / stride : 0;
+
+    const uint32_t T4 = (uint32_t)T * 4u;
+    const uint32_t ldb = (uint32_t)(3 * C * ES);
+    const bool vec4 = vec_store != 0;
+
+    if (compute) {
+        // Items of this wave: first + n*stride + slot for n < steps (while < hi).
+        Operand<U> ops[2][2];
+        int64_t id = first + slot;
+        Tile tl = make_tile(qkv, out, id < hi ? id : lo, L, T, C, NH, HS, ES);
+        if (P > 0 && id < hi) {
+            fetch_rows<E, U, VEC16>(ops[0][0], tl.q, ldb, tl.rl, HS, 0, lane);
+            fetch_rows<E, U, VEC16>(ops[0][1], tl.k, ldb, tl.cl, HS, 0, lane);
+        }
+        // Two steps per iteration so the operand buffers alternate statically.
+        for (int64_t n = 0; n <= steps; n += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t m = n + half;
+                if (m <= steps) {
+                    if (m < steps && id < hi) {
+                        const int64_t nid = id + stride;
+                        const bool has_next = m + 1 < steps && nid < hi;
+                        const Tile nx = make_tile(qkv, out, has_next ? nid : id, L, T, C, NH, HS, ES);
+                        char *buf = my_lds + (m & 1) * TILE_BYTES;
+                        if (half == 0 || (P & 1) == 0)
+                            compute_tile<E, U, VEC16, P, 0>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane);
+                        else
+                            compute_tile<E, U, VEC16, P, 1>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane);
+                        tl = nx;
+                        id = nid;
+                    }
+                    lds_barrier();
+                }
+            }
+        }
+    } else {
+        for (int64_t n = 0; n <= steps; ++n) {
+            if (n >= 1) {
+                const int64_t pid = first + (n - 1) * stride + slot;
+                if (pid < hi) {
+                    const Tile tl = make_tile(qkv, out, pid, L, T, C, NH, HS, ES);
+                    const uint32_t t4 = opaque_s(T4);
+                    const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
+                    if (tl.rl == TB && tl.cl == TB && vec4) {
+                        lds_to_out<true>(buf, tl, t4, lane, vec4);
+                        if (!tl.diag) nan_mirror<true>(tl, t4, lane, vec4);
+                    } else {
+                        lds_to_out<false>(buf, tl, t4, lane, vec4);
+                        if (!tl.diag) nan_mirror<false>(tl, t4, lane, vec4);
+                    }
+                }
+            }
+            lds_barrier();
+        }
+    }
+}
+
+// Register pass width: chunk pairs per pass (U * 32 bytes of each row); the
+// two operand blocks take 16*U registers each, twice over with the prefetch.
+// CAS_TRIMUL_PASS=1|2|4 overrides the choice (tuning).
+inline int pick_u(int64_t HS, int es)
+{
+    if (const char *v = std::getenv("CAS_TRIMUL_PASS")) {
+        const int u = std::atoi(v);
+        if (u == 1 || u == 2 || u == 4) return u;
+    }
+    const int64_t row_bytes = HS * es;
+    if (row_bytes > 64) return 4;
+    if (row_bytes > 32) return 2;
+    return 1;
+}
+
+template <class E, int U, bool VEC16, int P>
+hipError_t launch_cfg(const TrimulArgs &a, hipStream_t s)
+{
+    auto kern = trimul_kernel<E, U, VEC16, P>;
+    const int64_t nt = (a.T + TB - 1) / TB;
+    const int64_t L = nt * (nt + 1) / 2;
+    const int64_t items = a.B * a.NH * L;
+
+    // Persistent grid: as many workgroups as stay resident on the device.
+    static int resident_per_cu[64] = {0};
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (resident_per_cu[dev] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NTHREADS, 0) != hipSuccess || n < 1) n = 1;
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
+        cus[dev] = cu;
+        resident_per_cu[dev] = n;
+    }
+    const int64_t want = (items + NCOMP - 1) / NCOMP;
+    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    if (grid > want) grid = want;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, a.out, a.T, a.C, a.NH,
+                       a.HS, L, items, a.scale, (int)a.vec_store);
+    return hipGetLastError();
+}
+
+// Passes per head: P = ceil(HS*ES / (32*U)). Prefetching variants exist for
+// P <= 4 at the full pass width (heads up to 512 bytes) and P == 1 at the
+// narrow widths chosen for short heads; anything else takes the P == 0 path.
+template <class E, int U, bool VEC16>
+hipError_t launch_p(const TrimulArgs &a, hipStream_t s)
+{
+    const int64_t pb = 32 * U;
+    const int64_t P = (a.HS * E::ES + pb - 1) / pb;
+    if constexpr (U == 4) {
+        switch (P) {
+        case 1: return launch_cfg<E, U, VEC16, 1>(a, s);
+        case 2: return launch_cfg<E, U, VEC16, 2>(a, s);
+        case 3: return launch_cfg<E, U, VEC16, 3>(a, s);
+        case 4: return launch_cfg<E, U, VEC16, 4>(a, s);
+        default: return launch_cfg<E, U, VEC16, 0>(a, s);
+        }
+    } else {
+        if (P == 1) return launch_cfg<E, U, VEC16, 1>(a, s);
+        return launch_cfg<E, U, VEC16, 0>(a, s);
+    }
+}
+
+template <class E, bool VEC16>
+hipError_t launch_u(const TrimulArgs &a, hipStream_t s)
+{
+    switch (pick_u(a.HS, E::ES)) {
+    case 4: return launch_p<E, 4, VEC16>(a, s);
+    case 2: return launch_p<E, 2, VEC16>(a, s);
+    default: return launch_p<E, 1, VEC16>(a, s);
+    }
+}
+
+template <class E>
+hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
+{
+    // 16-byte chunks need base, pitch and head offsets 16-byte aligned and
+    // HS*ES a multiple of 16 (vec = elements that divide all of them).
+    if (vec * E::ES >= 16) return launch_u<E, true>(a, s);
+    return launch_u<E, false>(a, s);
+}
+
+} // namespace tri
+} // namespace cas

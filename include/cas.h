@@ -78,7 +78,8 @@ int cas_gemm_nt(const void *X, const void *W, void *Y,
  *
  * Only tiles on or below the diagonal are computed; the tiles above it are
  * filled with the NaN pattern by the same launch. Any T >= 1 is accepted.
- * Requires C > 0 and C % NH == 0. B == 0, T == 0 or NH == 0: nothing is
+ * Requires C > 0, C % NH == 0, a QKV row of 3*C elements under 2^24 bytes and
+ * T < 2^24 (both far beyond what fits in memory as (T, T) planes). B == 0, T == 0 or NH == 0: nothing is
  * written (OK). Offsets are 64-bit: outputs above 2^32 bytes are fine.
  */
 int cas_trimul_causal(const void *qkv, void *out,

@@ -94,6 +94,8 @@ def test_trimul_rejections(L):
     assert t(L, out=None) == ENULL
     assert t(L, out=PX + 64) == EALIAS
     assert t(L, B=2**40, T=2**20) == ESHAPE
+    assert t(L, B=1, T=2**24, C=12, NH=3) == ESHAPE   # T at the 32-bit offset limit
+    assert t(L, B=1, T=4, C=2**22, NH=2) == ESHAPE    # QKV row of 3 * 2^24 fp32 bytes
 
 
 def test_trimul_empty_is_ok(L):
