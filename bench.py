@@ -130,18 +130,24 @@ def time_parts(parts, steps: int, warmup: int):
     return total / steps, per, wall / steps
 
 
-def roofline_of(wl, ms: float, traffic):
+def roofline_of(wl, ms: float, traffic_bytes):
+    """Roofline entry of one kernel from its average launch time. `traffic` is
+    the measured HBM bytes per launch (rocprofv3 counters, committed under
+    profiles/) over the same launch time, in the unit of `achieved` when the
+    bound is HBM; null when no counters match the current kernel sources."""
     t = ms * 1e-3
     if wl.kind == "trimul_causal":
         achieved = wl.algorithmic_bytes() / t / 1e9
+        traffic = round(traffic_bytes / t / 1e9, 1) if traffic_bytes else None
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "traffic_bytes_per_launch": traffic_bytes,
                 "kernel": f"trimul_causal {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
                 "algorithmic_bytes": wl.algorithmic_bytes()}
     achieved = wl.useful_flops() / t / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "frac": round(achieved / peak, 4), "traffic": None, "traffic_bytes_per_launch": traffic_bytes,
             "kernel": f"gemm_nt {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
             "useful_flops": wl.useful_flops()}
 
@@ -176,6 +182,29 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"(T={T}, HS={HS}) of the step, fp64 accumulation"}
 
 
+def traffic_probe() -> None:
+    """Kernels for the HBM-traffic counter runs (rocprofv3 --pmc FETCH_SIZE,
+    then WRITE_SIZE): one plain copy of 512 MiB, whose counters calibrate
+    the byte scale, then three launches of each part of the step."""
+    import torch
+
+    from causal_attention_score_amd import synth
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for name in ("dense_f32_960x1024x770", "trimul_f32_B8_T1024_NH12_HS64"):
+        p = Part(synth.WORKLOADS[name])
+        for _ in range(3):
+            p()
+        torch.cuda.synchronize()
+        del p
+    print("traffic probe done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +212,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the kernels for the rocprofv3 HBM-traffic counter runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the hot path shards with no communication "
@@ -193,6 +224,9 @@ def main():
 
     from causal_attention_score_amd import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.traffic_probe:
+        traffic_probe()
+        return
     digest = kernel_sources_digest()
 
     wg = synth.WORKLOADS["dense_f32_960x1024x770"]

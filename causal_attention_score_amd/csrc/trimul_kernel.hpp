@@ -7,9 +7,9 @@
 // Design (MI355X-first; differs from that file's GPU kernels on purpose):
 //  * Work item = one 64x64 score tile. Only on- and below-diagonal tiles are
 //    items: item -> (plane, i, j <= i) by inverting the triangular numbers. A
-//    diagonal tile skips the 32x32 block that lies wholly above the diagonal;
-//    an off-diagonal tile (i, j) also writes its mirror tile (j, i) as NaN, so
-//    one launch writes the whole (T, T) plane.
+//    diagonal tile masks its upper part to NaN; an off-diagonal tile (i, j)
+//    also writes its mirror tile (j, i) as NaN, so one launch writes the
+//    whole (T, T) plane.
 //  * Wave specialisation. A workgroup holds four compute waves and four store
 //    waves (one of each per SIMD). A compute wave fetches its tile's Q and K
 //    rows straight from the packed (B, T, 3, NH, HS) rows (pitch 3C: no
@@ -35,6 +35,7 @@
 #include "tile_engine.hpp"
 
 #include <cstdlib>
+#include <cstring>
 
 namespace cas {
 namespace tri {
@@ -175,13 +176,17 @@ __device__ __forceinline__ void fetch_rows(Operand<U> &op, const char *__restric
     }
 }
 
+// All four 32x32 blocks, also on diagonal tiles: there block (0, 1) lies
+// above the diagonal and is masked to NaN on the way out; a branch around its
+// MFMAs would make the compiler copy the accumulators, waiting on the matrix
+// pipe.
 template <class E, int U>
-__device__ __forceinline__ void mma_pass(f32x16 (&acc)[2][2], const Operand<U> &q, const Operand<U> &k, bool diag)
+__device__ __forceinline__ void mma_pass(f32x16 (&acc)[2][2], const Operand<U> &q, const Operand<U> &k)
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         mfma_chunk<E>(acc[0][0], q.c[0][u], k.c[0][u]);
-        if (!diag) mfma_chunk<E>(acc[0][1], q.c[0][u], k.c[1][u]); // wholly above the diagonal otherwise
+        mfma_chunk<E>(acc[0][1], q.c[0][u], k.c[1][u]);
         mfma_chunk<E>(acc[1][0], q.c[1][u], k.c[0][u]);
         mfma_chunk<E>(acc[1][1], q.c[1][u], k.c[1][u]);
     }
@@ -271,7 +276,7 @@ __device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile
         for (int64_t e0 = 0; e0 < HS; e0 += PASS) {
             fetch_rows<E, U, VEC16>(ops[0][0], tl.q, ldb, tl.rl, HS, e0, lane);
             fetch_rows<E, U, VEC16>(ops[0][1], tl.k, ldb, tl.cl, HS, e0, lane);
-            mma_pass<E, U>(acc, ops[0][0], ops[0][1], tl.diag);
+            mma_pass<E, U>(acc, ops[0][0], ops[0][1]);
         }
     } else {
 #pragma unroll
@@ -284,7 +289,7 @@ __device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile
                 fetch_rows<E, U, VEC16>(ops[nxt][0], nx.q, ldb, nx.rl, HS, 0, lane);
                 fetch_rows<E, U, VEC16>(ops[nxt][1], nx.k, ldb, nx.cl, HS, 0, lane);
             }
-            mma_pass<E, U>(acc, ops[cur][0], ops[cur][1], tl.diag);
+            mma_pass<E, U>(acc, ops[cur][0], ops[cur][1]);
         }
     }
     tile_to_lds(acc, lds, scale, tl.diag, lane);
@@ -372,6 +377,342 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Super-tile kernel (rows 16-byte aligned, HS*ES <= 256 bytes): a workgroup
+// step is one 128x128 super-tile (I, J <= I). Its 128 Q rows and 128 K rows
+// are fetched once, by all four compute waves with coalesced 16-byte loads
+// (8 or 16 lanes per row), into an XOR-swizzled LDS operand buffer: chunk c
+// of row r sits at position c ^ (r % 8), so the MFMA operand reads (32 rows,
+// one chunk) and the row writes are both free of bank conflicts. Compute wave
+// w multiplies sub-tile (w/2, w%2) as D = K Q^T (K rows are the MFMA A
+// operand), so a lane's four consecutive accumulators are four consecutive
+// output columns and the raw tile goes to LDS with 16-byte writes. Store wave
+// w reads it back, applies the scale and the causal mask, and streams it to
+// HBM with its NaN mirror, so the compute waves spend their time in MFMAs.
+// Two LDS-only barriers per step:
+//   compute: MFMA(n) | X | acc(n) -> out LDS, rows(n+1) -> operand LDS, fetch(n+2) | Y
+//   store:           | X |                                                    | Y | out LDS -> HBM (n)
+// The store waves stream step n while the MFMAs of step n+1 run, with no
+// barrier in between, so the write stream has no gaps; the output buffer is
+// rewritten only after the next X, which a store wave reaches once its reads
+// are done. The operand rows of step n+2 are requested right after those of
+// n+1 reach LDS, two steps ahead, between the store phases.
+// On a diagonal super-tile, sub-tile (0, 1) lies wholly above the diagonal
+// and is written as NaN; (0, 0) and (1, 1) are masked diagonal tiles.
+// ---------------------------------------------------------------------------
+constexpr int ST = 2 * TB;                    // super-tile edge
+constexpr int OP_ROWS = 2 * ST;               // 128 Q rows + 128 K rows
+constexpr int NCOMP_THREADS = NCOMP * 64;
+constexpr int OUT_PITCH = TB * 4 + 16;        // bytes per LDS output row (+16: bank skew)
+constexpr int OUT_BYTES = TB * OUT_PITCH;
+
+// Walks item ids first, first + step, ... as (plane, r) with 32-bit
+// arithmetic and one division at set-up.
+struct Cursor {
+    uint32_t plane, r, dp, dr, L;
+    __device__ __forceinline__ void init(uint32_t first, uint32_t step, uint32_t L_)
+    {
+        L = L_;
+        plane = first / L;
+        r = first - plane * L;
+        dp = step / L;
+        dr = step - dp * L;
+    }
+    __device__ __forceinline__ void advance()
+    {
+        r += dr;
+        plane += dp;
+        if (r >= L) {
+            r -= L;
+            ++plane;
+        }
+    }
+};
+
+struct Super {
+    uint32_t plane, T0, S0;
+    bool diag;
+};
+
+__device__ __forceinline__ Super decode_super(const Cursor &cu)
+{
+    Super sp;
+    const uint32_t r = cu.r;
+    // r = i(i+1)/2 + j, 0 <= j <= i
+    uint32_t i = (uint32_t)((sqrtf(8.0f * (float)r + 1.0f) - 1.0f) * 0.5f);
+    while (i * (i + 1) / 2 > r) --i;
+    while ((i + 1) * (i + 2) / 2 <= r) ++i;
+    const uint32_t j = r - i * (i + 1) / 2;
+    sp.plane = cu.plane;
+    sp.T0 = i * ST;
+    sp.S0 = j * ST;
+    sp.diag = i == j;
+    return sp;
+}
+
+// Rows of the next super-tile, NCH 16-byte chunks per row, in registers.
+template <int NCH> struct Staged {
+    u32x4 v[NCH];
+};
+
+// Coalesced fetch of the 256 operand rows of super-tile `sp` (compute lane
+// cl = wave*64 + lane of 256): chunk j*256 + cl is row (j*256 + cl) / NCH,
+// chunk (cl % NCH). Rows past T and chunks past the head read zero.
+template <class E, int NCH>
+__device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, const Super &sp, uint32_t T, uint32_t C,
+                                            uint32_t NH, uint32_t HS, uint32_t ldb, int cl)
+{
+    constexpr int ES = E::ES;
+    constexpr int RPJ = NCOMP_THREADS / NCH; // rows per j
+    const uint32_t b = sp.plane / NH, nh = sp.plane - b * NH;
+    const uint64_t rowq = (uint64_t)b * T + sp.T0, rowk = (uint64_t)b * T + sp.S0;
+    const char *qb = qkv + (rowq * (3u * C) + (uint64_t)nh * HS) * ES;
+    const char *kb = qkv + (rowk * (3u * C) + C + (uint64_t)nh * HS) * ES;
+    const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb), rk = rsrc_at(kb);
+    const int c = cl % NCH;
+    const bool chunk_ok = (uint32_t)(c * 16) < HS * ES;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int row = j * RPJ + cl / NCH; // 0..255
+        const bool isq = j < NCH / 2;       // uniform
+        const int rin = isq ? row : row - ST;
+        const uint32_t grow = (isq ? sp.T0 : sp.S0) + rin;
+        const uint32_t vo = (chunk_ok && grow < T) ? (uint32_t)rin * ldb + (uint32_t)(c * 16) : OOB;
+        st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(isq ? rq : rk, (int)vo, 0, 0);
+    }
+}
+
+template <int NCH>
+__device__ __forceinline__ void stage_store(const Staged<NCH> &st, char *opb, int cl)
+{
+    constexpr int RPJ = NCOMP_THREADS / NCH;
+    const int c = cl % NCH;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int row = j * RPJ + cl / NCH;
+        *reinterpret_cast<u32x4 *>(opb + row * (NCH * 16) + ((c ^ (row & 7)) << 4)) = st.v[j];
+    }
+}
+
+// Operand fragments of one chunk pair: K rows (A operand) and Q rows (B).
+struct Frag {
+    u32x4 k0, k1, q0, q1;
+};
+
+template <int NCH>
+__device__ __forceinline__ Frag read_frag(const char *krow, const char *qrow, int u, int h, int xr)
+{
+    constexpr int RB = NCH * 16;
+    const int pos = ((2 * u + h) ^ xr) << 4;
+    Frag f;
+    f.k0 = *reinterpret_cast<const u32x4 *>(krow + pos);
+    f.k1 = *reinterpret_cast<const u32x4 *>(krow + 32 * RB + pos);
+    f.q0 = *reinterpret_cast<const u32x4 *>(qrow + pos);
+    f.q1 = *reinterpret_cast<const u32x4 *>(qrow + 32 * RB + pos);
+    return f;
+}
+
+// Sub-tile (a, b) of the super-tile: acc[kb][qb] covers output columns
+// 32kb.. (K rows 128 + 64b + 32kb..) and output rows 32qb.. (Q rows
+// 64a + 32qb..). The LDS reads run two chunk pairs ahead of the MFMAs. On a
+// diagonal sub-tile the block (kb=1, qb=0) lies above the diagonal; it is
+// computed anyway and masked to NaN on the way out: a branch around its MFMAs
+// would make the compiler copy the accumulators, waiting on the matrix pipe.
+template <class E, int NCH>
+__device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, int a, int b, int lane)
+{
+    constexpr int RB = NCH * 16;
+    constexpr int NU = NCH / 2;
+    const int r32 = lane & 31, h = lane >> 5, xr = r32 & 7;
+    const char *qrow = opb + (a * TB + r32) * RB;
+    const char *krow = opb + (ST + b * TB + r32) * RB;
+    Frag f[3];
+    f[0] = read_frag<NCH>(krow, qrow, 0, h, xr);
+    if (NU > 1) f[1] = read_frag<NCH>(krow, qrow, 1, h, xr);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 2 < NU) f[(u + 2) % 3] = read_frag<NCH>(krow, qrow, u + 2, h, xr);
+        __builtin_amdgcn_sched_barrier(0);
+        const Frag &g = f[u % 3];
+        mfma_chunk<E>(acc[0][0], g.k0, g.q0);
+        mfma_chunk<E>(acc[0][1], g.k0, g.q1);
+        mfma_chunk<E>(acc[1][0], g.k1, g.q0);
+        mfma_chunk<E>(acc[1][1], g.k1, g.q1);
+    }
+}
+
+// Raw sub-tile -> LDS rows of OUT_PITCH bytes. Lane l holds output row
+// 32qb + l%32 and columns 32kb + 8g + 4(l/32) + 0..3 of acc[kb][qb][4g..].
+__device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, int lane)
+{
+    const int r32 = lane & 31, h4 = 4 * (lane >> 5);
+    const uint32_t lo = opaque((uint32_t)(r32 * OUT_PITCH + h4 * 4));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4v v = {acc[kb][qb][4 * g], acc[kb][qb][4 * g + 1], acc[kb][qb][4 * g + 2],
+                                  acc[kb][qb][4 * g + 3]};
+                *reinterpret_cast<f32x4v *>(lds + lo + (uint32_t)(32 * qb * OUT_PITCH + (32 * kb + 8 * g) * 4)) = v;
+            }
+}
+
+template <class E, int NCH>
+__global__ void __launch_bounds__(NTHREADS)
+trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
+                    uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store)
+{
+    constexpr int RB = NCH * 16;
+    __shared__ __attribute__((aligned(16))) char opb[OP_ROWS * RB];
+    __shared__ __attribute__((aligned(16))) char outb[NCOMP * OUT_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool compute = wave < NCOMP;
+    const int slot = wave % NCOMP;
+    const int sa = slot >> 1, sb = slot & 1; // sub-tile of this wave pair
+    char *my_out = outb + slot * OUT_BYTES;
+
+    // XCD-local contiguous item range; one super-tile per workgroup step.
+    const uint32_t nwg = gridDim.x;
+    const uint32_t x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
+    const uint32_t wg_before = x * q8 + (x < r8 ? x : r8);
+    const uint32_t wg_on_x = q8 + (x < r8 ? 1 : 0);
+    const uint32_t lo = (uint32_t)((uint64_t)items * wg_before / nwg);
+    const uint32_t hi = (uint32_t)((uint64_t)items * (wg_before + wg_on_x) / nwg);
+    const uint32_t first = lo + blockIdx.x / 8;
+    const uint32_t steps = first < hi ? (hi - first + wg_on_x - 1) / wg_on_x : 0;
+
+    const uint32_t T4 = T * 4u;
+    const uint32_t ldb = 3u * C * (uint32_t)E::ES;
+    const bool vec4 = vec_store != 0;
+    Cursor cur;
+    cur.init(first < hi ? first : 0, wg_on_x, L);
+
+    if (compute) {
+        const int cl = slot * 64 + lane;
+        Staged<NCH> st;
+        Super sp = decode_super(cur); // item of step n
+        Cursor nc = cur;              // item of step n + 2 (after the prologue)
+        if (steps > 0) {
+            stage_fetch<E, NCH>(st, qkv, sp, T, C, NH, HS, ldb, cl);
+            stage_store<NCH>(st, opb, cl);
+            if (steps > 1) {
+                nc.advance();
+                stage_fetch<E, NCH>(st, qkv, decode_super(nc), T, C, NH, HS, ldb, cl);
+            }
+        }
+        lds_barrier();
+        for (uint32_t n = 0; n < steps; ++n) {
+            // Diagonal sub-tile (0, 1) is all NaN: its store wave writes it directly.
+            const bool live = !(sp.diag && sa == 0 && sb == 1);
+            f32x16 acc[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+            if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
+            lds_barrier(); // X: operand rows consumed, previous outputs streamed out
+            if (live) subtile_to_lds(acc, my_out, lane);
+            if (n + 1 < steps) {
+                stage_store<NCH>(st, opb, cl); // rows of step n + 1
+                if (n + 2 < steps) {
+                    nc.advance();
+                    stage_fetch<E, NCH>(st, qkv, decode_super(nc), T, C, NH, HS, ldb, cl);
+                }
+            }
+            lds_barrier(); // Y: outputs and next operand rows in LDS
+            cur.advance();
+            sp = decode_super(cur);
+        }
+    } else {
+        lds_barrier(); // first operand rows staged (matches the compute waves)
+        const int r4 = lane >> 4, c = (lane & 15) * 4;
+        const uint32_t li = (uint32_t)(r4 * OUT_PITCH + c * 4);
+        const float qnan = __uint_as_float(QNAN_BITS);
+        for (uint32_t n = 0; n < steps; ++n) {
+            const Super sp = decode_super(cur);
+            cur.advance();
+            lds_barrier(); // X
+            lds_barrier(); // Y: tile n in LDS
+            Tile tl;
+            tl.t0 = sp.T0 + sa * TB;
+            tl.s0 = sp.S0 + sb * TB;
+            tl.o = reinterpret_cast<char *>(out + (uint64_t)sp.plane * T * T);
+            tl.rl = (int)((int64_t)T - tl.t0 < TB ? (int64_t)T - tl.t0 : TB);
+            tl.cl = (int)((int64_t)T - tl.s0 < TB ? (int64_t)T - tl.s0 : TB);
+            tl.diag = sp.diag;
+            if (tl.rl <= 0 || tl.cl <= 0) continue; // sub-tile past the plane edge
+            const uint32_t t4 = opaque_s(T4);
+            const bool full = tl.rl == TB && tl.cl == TB;
+            // the NaN mirror first: it needs nothing from LDS
+            if (!tl.diag) {
+                if (full && vec4) nan_mirror<true>(tl, t4, lane, vec4);
+                else nan_mirror<false>(tl, t4, lane, vec4);
+            }
+            const bool all_nan = sp.diag && sa == 0 && sb == 1; // wholly above the diagonal
+            const bool dsub = sp.diag && sa == sb;
+            char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * 4;
+            const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
+#pragma unroll
+            for (int s = 0; s < TB / 4; ++s) {
+                f32x4v v;
+                if (all_nan) {
+                    v = f32x4v{qnan, qnan, qnan, qnan};
+                } else {
+                    v = *reinterpret_cast<const f32x4v *>(my_out + li + s * 4 * OUT_PITCH);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = v[e] * scale;
+                        v[e] = (dsub && c + e > s * 4 + r4) ? qnan : y;
+                    }
+                }
+                const int row = s * 4 + r4;
+                if (vec4) {
+                    if (full || (c < tl.cl && row < tl.rl))
+                        st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * t4 + go)), v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row < tl.rl && c + e < tl.cl)
+                            st_nt(reinterpret_cast<float *>(dst + ((uint32_t)row * t4 + (uint32_t)(c + e) * 4)), v[e]);
+                }
+            }
+        }
+    }
+}
+
+template <class E, int NCH>
+hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
+{
+    auto kern = trimul_super_kernel<E, NCH>;
+    const int64_t nt = (a.T + ST - 1) / ST;
+    const int64_t L = nt * (nt + 1) / 2;
+    const int64_t items = a.B * a.NH * L;
+    static int resident_per_cu[64] = {0};
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (resident_per_cu[dev] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NTHREADS, 0) != hipSuccess || n < 1) n = 1;
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
+        cus[dev] = cu;
+        resident_per_cu[dev] = n;
+    }
+    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    if (grid > items) grid = items;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, a.out, (uint32_t)a.T,
+                       (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
+                       (int)a.vec_store);
+    return hipGetLastError();
+}
+
 // Register pass width: chunk pairs per pass (U * 32 bytes of each row); the
 // two operand blocks take 16*U registers each, twice over with the prefetch.
 // CAS_TRIMUL_PASS=1|2|4 overrides the choice (tuning).
@@ -452,6 +793,19 @@ hipError_t launch_u(const TrimulArgs &a, hipStream_t s)
 template <class E>
 hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
 {
+    // Super-tile kernel: 16-byte aligned rows and heads of at most 256 bytes.
+    // Measured choice: it leads for 16-bit inputs, whose time is all stores;
+    // for fp32 inputs, where MFMA time rivals the store time, the per-wave
+    // tile kernel overlaps the two better. CAS_TRIMUL_KERNEL=tile|super forces
+    // one (tests and tuning).
+    const char *kv = std::getenv("CAS_TRIMUL_KERNEL");
+    const bool force_tile = kv && std::strcmp(kv, "tile") == 0;
+    const bool force_super = kv && std::strcmp(kv, "super") == 0;
+    const int64_t nts = (a.T + ST - 1) / ST;
+    const bool ids_fit = a.B * a.NH * (nts * (nts + 1) / 2) <= INT32_MAX;
+    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 256;
+    if (super_ok && !force_tile && (force_super || E::ES == 2))
+        return a.HS * E::ES <= 128 ? launch_super<E, 8>(a, s) : launch_super<E, 16>(a, s);
     // 16-byte chunks need base, pitch and head offsets 16-byte aligned and
     // HS*ES a multiple of 16 (vec = elements that divide all of them).
     if (vec * E::ES >= 16) return launch_u<E, true>(a, s);

@@ -150,9 +150,14 @@ TRI_T = [1, 2, 7, 63, 64, 65, 127, 128, 129, 300]
 TRI_HS = [1, 8, 40, 64, 80, 128]
 
 
+@pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("HS", TRI_HS)
 @pytest.mark.parametrize("T", TRI_T)
-def test_trimul_ragged_f32(orc, T, HS):
+def test_trimul_ragged_f32(orc, monkeypatch, T, HS, kernel):
+    """Both score kernels: the super-tile kernel (used where rows are 16-byte
+    aligned and the head is at most 256 bytes; other shapes fall back) and the
+    per-wave tile kernel that serves every shape."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
     for (B, NH) in [(1, 1), (2, 3)]:
         qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 131 + HS)
         ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
@@ -160,10 +165,12 @@ def test_trimul_ragged_f32(orc, T, HS):
         assert_scores(out, ref, bound, "f32", f"trimul f32 B={B} T={T} NH={NH} HS={HS}")
 
 
+@pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("HS", [8, 40, 64, 80, 128, 3])
+@pytest.mark.parametrize("HS", [8, 40, 64, 80, 128, 136, 3])
 @pytest.mark.parametrize("T", [1, 65, 128, 300])
-def test_trimul_ragged_16bit(orc, T, HS, dtype):
+def test_trimul_ragged_16bit(orc, monkeypatch, T, HS, dtype, kernel):
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
     B, NH = 2, 3
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 17 + HS)
     ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
@@ -171,8 +178,10 @@ def test_trimul_ragged_16bit(orc, T, HS, dtype):
     assert_scores(out, ref, bound, dtype, f"trimul {dtype} T={T} HS={HS}")
 
 
+@pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_trimul_exact_small_integers(orc, dtype):
+def test_trimul_exact_small_integers(orc, monkeypatch, dtype, kernel):
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
     for (B, T, NH, HS) in [(2, 257, 2, 64), (1, 130, 3, 40)]:
         qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS, dist="int")
         ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
