@@ -238,9 +238,12 @@ __device__ __forceinline__ void lds_to_out(const char *lds, const Tile &tl, uint
 }
 
 // NaN over the mirror tile (j, i): rows [s0, s0+cl) x columns [t0, t0+rl).
-template <bool FULL>
+// H = 0 or 1 writes only the first or the second half of the mirror's rows,
+// H = -1 all of them.
+template <bool FULL, int H = -1>
 __device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane, bool vec4)
 {
+    constexpr int R0 = H == 1 ? TB / 2 : 0, R1 = H == 0 ? TB / 2 : TB; // mirror rows [R0, R1)
     const float qnan = __uint_as_float(QNAN_BITS);
     char *dst = tl.o + ((uint64_t)tl.s0 * (T4 / 4) + (uint64_t)tl.t0) * 4;
     if (FULL || vec4) {
@@ -248,11 +251,11 @@ __device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane
         const int r4 = lane >> 4, c = (lane & 15) * 4;
         const uint32_t go = opaque((uint32_t)r4 * T4 + (uint32_t)c * 4);
 #pragma unroll
-        for (int s = 0; s < TB / 4; ++s)
+        for (int s = R0 / 4; s < R1 / 4; ++s)
             if (FULL || (c < tl.rl && s * 4 + r4 < tl.cl))
                 st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * T4 + go)), n4);
     } else {
-        for (int s = 0; s < TB; ++s)
+        for (int s = R0; s < R1; ++s)
             if (s < tl.cl && lane < tl.rl) st_nt(reinterpret_cast<float *>(dst + ((uint32_t)s * T4 + (uint32_t)lane * 4)), qnan);
     }
 }
@@ -380,29 +383,39 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
 // ---------------------------------------------------------------------------
 // Super-tile kernel (rows 16-byte aligned, HS*ES <= 256 bytes): a workgroup
 // step is one 128x128 super-tile (I, J <= I). Its 128 Q rows and 128 K rows
-// are fetched once, by all four compute waves with coalesced 16-byte loads
-// (8 or 16 lanes per row), into an XOR-swizzled LDS operand buffer: chunk c
-// of row r sits at position c ^ (r % 8), so the MFMA operand reads (32 rows,
-// one chunk) and the row writes are both free of bank conflicts. Compute wave
-// w multiplies sub-tile (w/2, w%2) as D = K Q^T (K rows are the MFMA A
-// operand), so a lane's four consecutive accumulators are four consecutive
-// output columns and the raw tile goes to LDS with 16-byte writes. Store wave
-// w reads it back, applies the scale and the causal mask, and streams it to
-// HBM with its NaN mirror, so the compute waves spend their time in MFMAs.
+// are fetched once, with coalesced 16-byte loads (8 or 16 lanes per row), into
+// an XOR-swizzled LDS operand buffer: chunk c of row r sits at position
+// c ^ (r % 8), so the MFMA operand reads (32 rows, one chunk) and the row
+// writes are both free of bank conflicts. Three roles of four waves each, one
+// wave of every role per SIMD:
+//  * compute wave w multiplies sub-tile (w/2, w%2) as D = K Q^T (K rows are
+//    the MFMA A operand), so a lane's four consecutive accumulators are four
+//    consecutive output columns, and writes the raw tile to LDS with 16-byte
+//    writes. It issues no global memory instruction at all.
+//  * store wave w reads the tile back, applies the scale and the causal mask
+//    and streams it to HBM with its NaN mirror (non-temporal 16-byte stores).
+//  * loader wave w requests its quarter of the next step's operand rows into
+//    registers and writes them to the operand buffer once it is free.
+// On CDNA the loads and stores of a CU share one vector-memory queue, which
+// the store stream keeps full: a load waits behind the stores ahead of it.
+// Only the loader waves ever wait there, and they have a whole MFMA phase to
+// do so, so the waves that gate the barriers never stall on memory.
 // Two LDS-only barriers per step:
-//   compute: MFMA(n) | X | acc(n) -> out LDS, rows(n+1) -> operand LDS, fetch(n+2) | Y
-//   store:           | X |                                                    | Y | out LDS -> HBM (n)
-// The store waves stream step n while the MFMAs of step n+1 run, with no
-// barrier in between, so the write stream has no gaps; the output buffer is
-// rewritten only after the next X, which a store wave reaches once its reads
-// are done. The operand rows of step n+2 are requested right after those of
-// n+1 reach LDS, two steps ahead, between the store phases.
+//   compute: MFMA(n)                        | X | acc(n) -> out LDS       | Y
+//   loader:  fetch rows(n+1) -> registers   | X | rows(n+1) -> opnd LDS  | Y
+//   store:   tile(n-1), 1st half mirror(n-1)| X | 2nd half mirror(n-1)   | Y
+// A step lasts the longer side of each segment, added up. The store waves
+// keep the write stream busy through both: the NaN mirror needs nothing from
+// LDS, so half of it fills the short LDS segment and half follows tile n-1
+// through the long MFMA segment. The output buffer is rewritten only after
+// X, which a store wave reaches once its reads of the previous tile are done.
 // On a diagonal super-tile, sub-tile (0, 1) lies wholly above the diagonal
 // and is written as NaN; (0, 0) and (1, 1) are masked diagonal tiles.
 // ---------------------------------------------------------------------------
 constexpr int ST = 2 * TB;                    // super-tile edge
 constexpr int OP_ROWS = 2 * ST;               // 128 Q rows + 128 K rows
-constexpr int NCOMP_THREADS = NCOMP * 64;
+constexpr int NCOMP_THREADS = NCOMP * 64;   // lanes of one role
+constexpr int SUPER_THREADS = 3 * NCOMP_THREADS;
 constexpr int OUT_PITCH = TB * 4 + 16;        // bytes per LDS output row (+16: bank skew)
 constexpr int OUT_BYTES = TB * OUT_PITCH;
 
@@ -455,7 +468,7 @@ template <int NCH> struct Staged {
     u32x4 v[NCH];
 };
 
-// Coalesced fetch of the 256 operand rows of super-tile `sp` (compute lane
+// Coalesced fetch of the 256 operand rows of super-tile `sp` (loader lane
 // cl = wave*64 + lane of 256): chunk j*256 + cl is row (j*256 + cl) / NCH,
 // chunk (cl % NCH). Rows past T and chunks past the head read zero.
 template <class E, int NCH>
@@ -469,15 +482,14 @@ __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, co
     const char *qb = qkv + (rowq * (3u * C) + (uint64_t)nh * HS) * ES;
     const char *kb = qkv + (rowk * (3u * C) + C + (uint64_t)nh * HS) * ES;
     const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb), rk = rsrc_at(kb);
-    const int c = cl % NCH;
-    const bool chunk_ok = (uint32_t)(c * 16) < HS * ES;
+    const uint32_t c = (uint32_t)(cl % NCH), r0 = (uint32_t)(cl / NCH);
+    const uint32_t lim = c * 16 < HS * ES ? T : 0u; // a chunk past the head reads zero
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        const int row = j * RPJ + cl / NCH; // 0..255
-        const bool isq = j < NCH / 2;       // uniform
-        const int rin = isq ? row : row - ST;
-        const uint32_t grow = (isq ? sp.T0 : sp.S0) + rin;
-        const uint32_t vo = (chunk_ok && grow < T) ? (uint32_t)rin * ldb + (uint32_t)(c * 16) : OOB;
+        const bool isq = j < NCH / 2; // uniform: rows 0..127 are Q, 128..255 K
+        const uint32_t rin = (uint32_t)((isq ? j : j - NCH / 2) * RPJ) + r0;
+        const uint32_t ok = 0u - (uint32_t)((isq ? sp.T0 : sp.S0) + rin < lim); // all ones in range
+        const uint32_t vo = ((rin * ldb + c * 16) & ok) | (OOB & ~ok);
         st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(isq ? rq : rk, (int)vo, 0, 0);
     }
 }
@@ -561,7 +573,7 @@ __device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *
 }
 
 template <class E, int NCH>
-__global__ void __launch_bounds__(NTHREADS)
+__global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store)
 {
@@ -571,9 +583,9 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool compute = wave < NCOMP;
+    const int role = wave / NCOMP; // 0 compute, 1 store, 2 loader
     const int slot = wave % NCOMP;
-    const int sa = slot >> 1, sb = slot & 1; // sub-tile of this wave pair
+    const int sa = slot >> 1, sb = slot & 1; // sub-tile of this compute / store pair
     char *my_out = outb + slot * OUT_BYTES;
 
     // XCD-local contiguous item range; one super-tile per workgroup step.
@@ -592,21 +604,31 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
     Cursor cur;
     cur.init(first < hi ? first : 0, wg_on_x, L);
 
-    if (compute) {
+    // Every wave passes the same barriers: one after the prologue, then X and
+    // Y once per step.
+    if (role == 2) {
         const int cl = slot * 64 + lane;
         Staged<NCH> st;
-        Super sp = decode_super(cur); // item of step n
-        Cursor nc = cur;              // item of step n + 2 (after the prologue)
         if (steps > 0) {
-            stage_fetch<E, NCH>(st, qkv, sp, T, C, NH, HS, ldb, cl);
+            stage_fetch<E, NCH>(st, qkv, decode_super(cur), T, C, NH, HS, ldb, cl);
             stage_store<NCH>(st, opb, cl);
-            if (steps > 1) {
-                nc.advance();
-                stage_fetch<E, NCH>(st, qkv, decode_super(nc), T, C, NH, HS, ldb, cl);
-            }
         }
+        lds_barrier(); // operand rows of step 0 in LDS
+        for (uint32_t n = 0; n < steps; ++n) {
+            const bool more = n + 1 < steps;
+            if (more) {
+                cur.advance();
+                stage_fetch<E, NCH>(st, qkv, decode_super(cur), T, C, NH, HS, ldb, cl);
+            }
+            lds_barrier(); // X: operand rows of step n consumed
+            if (more) stage_store<NCH>(st, opb, cl);
+            lds_barrier(); // Y: operand rows of step n + 1 in LDS
+        }
+    } else if (role == 0) {
         lds_barrier();
         for (uint32_t n = 0; n < steps; ++n) {
+            const Super sp = decode_super(cur);
+            cur.advance();
             // Diagonal sub-tile (0, 1) is all NaN: its store wave writes it directly.
             const bool live = !(sp.diag && sa == 0 && sb == 1);
             f32x16 acc[2][2];
@@ -615,29 +637,20 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
 #pragma unroll
                 for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
             if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
-            lds_barrier(); // X: operand rows consumed, previous outputs streamed out
+            lds_barrier(); // X: operand rows consumed, previous tile read back
             if (live) subtile_to_lds(acc, my_out, lane);
-            if (n + 1 < steps) {
-                stage_store<NCH>(st, opb, cl); // rows of step n + 1
-                if (n + 2 < steps) {
-                    nc.advance();
-                    stage_fetch<E, NCH>(st, qkv, decode_super(nc), T, C, NH, HS, ldb, cl);
-                }
-            }
-            lds_barrier(); // Y: outputs and next operand rows in LDS
-            cur.advance();
-            sp = decode_super(cur);
+            lds_barrier(); // Y: tile n in LDS
         }
     } else {
-        lds_barrier(); // first operand rows staged (matches the compute waves)
+        lds_barrier();
         const int r4 = lane >> 4, c = (lane & 15) * 4;
         const uint32_t li = (uint32_t)(r4 * OUT_PITCH + c * 4);
         const float qnan = __uint_as_float(QNAN_BITS);
+        Tile pm;              // mirror of the previous step, second half pending
+        bool pm_live = false, pm_full = false;
         for (uint32_t n = 0; n < steps; ++n) {
             const Super sp = decode_super(cur);
             cur.advance();
-            lds_barrier(); // X
-            lds_barrier(); // Y: tile n in LDS
             Tile tl;
             tl.t0 = sp.T0 + sa * TB;
             tl.s0 = sp.S0 + sb * TB;
@@ -645,14 +658,17 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
             tl.rl = (int)((int64_t)T - tl.t0 < TB ? (int64_t)T - tl.t0 : TB);
             tl.cl = (int)((int64_t)T - tl.s0 < TB ? (int64_t)T - tl.s0 : TB);
             tl.diag = sp.diag;
-            if (tl.rl <= 0 || tl.cl <= 0) continue; // sub-tile past the plane edge
+            const bool inside = tl.rl > 0 && tl.cl > 0; // else the sub-tile lies past the plane edge
             const uint32_t t4 = opaque_s(T4);
             const bool full = tl.rl == TB && tl.cl == TB;
-            // the NaN mirror first: it needs nothing from LDS
-            if (!tl.diag) {
-                if (full && vec4) nan_mirror<true>(tl, t4, lane, vec4);
-                else nan_mirror<false>(tl, t4, lane, vec4);
+            lds_barrier(); // X
+            if (pm_live) { // second half of the previous step's mirror: needs nothing from LDS
+                if (pm_full) nan_mirror<true, 1>(pm, t4, lane, vec4);
+                else nan_mirror<false, 1>(pm, t4, lane, vec4);
             }
+            pm_live = false;
+            lds_barrier(); // Y: tile n in LDS
+            if (!inside) continue;
             const bool all_nan = sp.diag && sa == 0 && sb == 1; // wholly above the diagonal
             const bool dsub = sp.diag && sa == sb;
             char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * 4;
@@ -681,6 +697,18 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
                             st_nt(reinterpret_cast<float *>(dst + ((uint32_t)row * t4 + (uint32_t)(c + e) * 4)), v[e]);
                 }
             }
+            if (!tl.diag) { // first half of the mirror now, the second after the next X
+                pm = tl;
+                pm_live = true;
+                pm_full = full && vec4;
+                if (pm_full) nan_mirror<true, 0>(tl, t4, lane, vec4);
+                else nan_mirror<false, 0>(tl, t4, lane, vec4);
+            }
+        }
+        if (pm_live) {
+            const uint32_t t4 = opaque_s(T4);
+            if (pm_full) nan_mirror<true, 1>(pm, t4, lane, vec4);
+            else nan_mirror<false, 1>(pm, t4, lane, vec4);
         }
     }
 }
@@ -698,7 +726,7 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (resident_per_cu[dev] == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NTHREADS, 0) != hipSuccess || n < 1) n = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, SUPER_THREADS, 0) != hipSuccess || n < 1) n = 1;
         int cu = 0;
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
         cus[dev] = cu;
@@ -707,7 +735,7 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, a.out, (uint32_t)a.T,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, a.out, (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
                        (int)a.vec_store);
     return hipGetLastError();
