@@ -115,6 +115,7 @@ __device__ __forceinline__ Tile make_tile(const char *qkv, float *out, int64_t i
 // Buffer resource over `base` (wave-uniform). Offsets at or above OOB read
 // as zero: the hardware range check does the zero-fill of local padding.
 constexpr uint32_t OOB = 0x80000000u;
+constexpr int ST_NT = 2; // cache-policy operand of buffer stores: non-temporal
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const char *base)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
@@ -554,11 +555,14 @@ __device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, in
     }
 }
 
-// Raw sub-tile -> LDS rows of OUT_PITCH bytes. Lane l holds output row
+// Scaled sub-tile -> LDS rows of OUT_PITCH bytes. Lane l holds output row
 // 32qb + l%32 and columns 32kb + 8g + 4(l/32) + 0..3 of acc[kb][qb][4g..].
-__device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, int lane)
+// DIAG: a sub-tile on the diagonal, whose entries right of it become NaN.
+template <bool DIAG>
+__device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, int lane)
 {
     const int r32 = lane & 31, h4 = 4 * (lane >> 5);
+    const float qnan = __uint_as_float(QNAN_BITS);
     const uint32_t lo = opaque((uint32_t)(r32 * OUT_PITCH + h4 * 4));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -566,10 +570,27 @@ __device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4v v = {acc[kb][qb][4 * g], acc[kb][qb][4 * g + 1], acc[kb][qb][4 * g + 2],
-                                  acc[kb][qb][4 * g + 3]};
+                f32x4v v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = acc[kb][qb][4 * g + e] * scale;
+                    v[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? qnan : y;
+                }
                 *reinterpret_cast<f32x4v *>(lds + lo + (uint32_t)(32 * qb * OUT_PITCH + (32 * kb + 8 * g) * 4)) = v;
             }
+}
+
+// Rows [32H, 32H + 32) of the NaN mirror of a whole 64 x 64 tile, with
+// buffer stores whose row offset is a scalar: no vector ALU work per store.
+template <int H>
+__device__ __forceinline__ void nan_mirror_full(const Tile &tl, uint32_t T4, int lane)
+{
+    constexpr int S0 = H * TB / 8, S1 = S0 + TB / 8; // groups of four rows
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tl.o + ((uint64_t)tl.s0 * (T4 / 4) + (uint64_t)tl.t0) * 4);
+    const uint32_t go = opaque((uint32_t)(lane >> 4) * T4 + (uint32_t)(lane & 15) * 16);
+    const u32x4 n4 = {QNAN_BITS, QNAN_BITS, QNAN_BITS, QNAN_BITS};
+#pragma unroll
+    for (int s = S0; s < S1; ++s) __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * 4) * T4), ST_NT);
 }
 
 template <class E, int NCH>
@@ -638,7 +659,10 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
                 for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
             if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
             lds_barrier(); // X: operand rows consumed, previous tile read back
-            if (live) subtile_to_lds(acc, my_out, lane);
+            if (live) {
+                if (sp.diag && sa == sb) subtile_to_lds<true>(acc, my_out, scale, lane);
+                else subtile_to_lds<false>(acc, my_out, scale, lane);
+            }
             lds_barrier(); // Y: tile n in LDS
         }
     } else {
@@ -663,51 +687,62 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
             const bool full = tl.rl == TB && tl.cl == TB;
             lds_barrier(); // X
             if (pm_live) { // second half of the previous step's mirror: needs nothing from LDS
-                if (pm_full) nan_mirror<true, 1>(pm, t4, lane, vec4);
+                if (pm_full) nan_mirror_full<1>(pm, t4, lane);
                 else nan_mirror<false, 1>(pm, t4, lane, vec4);
             }
             pm_live = false;
             lds_barrier(); // Y: tile n in LDS
             if (!inside) continue;
             const bool all_nan = sp.diag && sa == 0 && sb == 1; // wholly above the diagonal
-            const bool dsub = sp.diag && sa == sb;
             char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * 4;
-            const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
-#pragma unroll
-            for (int s = 0; s < TB / 4; ++s) {
-                f32x4v v;
+            if (full && vec4) {
+                // Whole tile: one LDS read and one buffer store per four rows,
+                // the row offset a scalar, so no vector ALU work: the SIMD's
+                // vector issue belongs to the compute wave's MFMAs.
+                const __amdgpu_buffer_rsrc_t rs = rsrc_at(dst);
+                const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
                 if (all_nan) {
-                    v = f32x4v{qnan, qnan, qnan, qnan};
-                } else {
-                    v = *reinterpret_cast<const f32x4v *>(my_out + li + s * 4 * OUT_PITCH);
+                    const u32x4 n4 = {QNAN_BITS, QNAN_BITS, QNAN_BITS, QNAN_BITS};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float y = v[e] * scale;
-                        v[e] = (dsub && c + e > s * 4 + r4) ? qnan : y;
+                    for (int s = 0; s < TB / 4; ++s)
+                        __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * 4) * t4), ST_NT);
+                } else {
+#pragma unroll
+                    for (int s = 0; s < TB / 4; ++s) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(my_out + li + s * 4 * OUT_PITCH);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)go, (int)((uint32_t)(s * 4) * t4), ST_NT);
                     }
                 }
-                const int row = s * 4 + r4;
-                if (vec4) {
-                    if (full || (c < tl.cl && row < tl.rl))
-                        st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * t4 + go)), v);
-                } else {
+            } else {
+                const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (row < tl.rl && c + e < tl.cl)
-                            st_nt(reinterpret_cast<float *>(dst + ((uint32_t)row * t4 + (uint32_t)(c + e) * 4)), v[e]);
+                for (int s = 0; s < TB / 4; ++s) {
+                    f32x4v v;
+                    if (all_nan) v = f32x4v{qnan, qnan, qnan, qnan};
+                    else v = *reinterpret_cast<const f32x4v *>(my_out + li + s * 4 * OUT_PITCH);
+                    const int row = s * 4 + r4;
+                    if (vec4) {
+                        if (c < tl.cl && row < tl.rl)
+                            st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * t4 + go)), v);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (row < tl.rl && c + e < tl.cl)
+                                st_nt(reinterpret_cast<float *>(dst + ((uint32_t)row * t4 + (uint32_t)(c + e) * 4)), v[e]);
+                    }
                 }
             }
             if (!tl.diag) { // first half of the mirror now, the second after the next X
                 pm = tl;
                 pm_live = true;
                 pm_full = full && vec4;
-                if (pm_full) nan_mirror<true, 0>(tl, t4, lane, vec4);
+                if (pm_full) nan_mirror_full<0>(tl, t4, lane);
                 else nan_mirror<false, 0>(tl, t4, lane, vec4);
             }
         }
         if (pm_live) {
             const uint32_t t4 = opaque_s(T4);
-            if (pm_full) nan_mirror<true, 1>(pm, t4, lane, vec4);
+            if (pm_full) nan_mirror_full<1>(pm, t4, lane);
             else nan_mirror<false, 1>(pm, t4, lane, vec4);
         }
     }
@@ -821,18 +856,18 @@ hipError_t launch_u(const TrimulArgs &a, hipStream_t s)
 template <class E>
 hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
 {
-    // Super-tile kernel: 16-byte aligned rows and heads of at most 256 bytes.
-    // Measured choice: it leads for 16-bit inputs, whose time is all stores;
-    // for fp32 inputs, where MFMA time rivals the store time, the per-wave
-    // tile kernel overlaps the two better. CAS_TRIMUL_KERNEL=tile|super forces
-    // one (tests and tuning).
+    // Super-tile kernel wherever it applies (16-byte aligned rows, heads of
+    // at most 256 bytes): measured ahead of the per-wave tile kernel for every
+    // input type. CAS_TRIMUL_KERNEL=tile forces the tile kernel (tests and
+    // tuning).
     const char *kv = std::getenv("CAS_TRIMUL_KERNEL");
     const bool force_tile = kv && std::strcmp(kv, "tile") == 0;
-    const bool force_super = kv && std::strcmp(kv, "super") == 0;
     const int64_t nts = (a.T + ST - 1) / ST;
     const bool ids_fit = a.B * a.NH * (nts * (nts + 1) / 2) <= INT32_MAX;
-    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 256;
-    if (super_ok && !force_tile && (force_super || E::ES == 2))
+    // The super-tile kernel's buffer offsets within a 64-row tile reach 256 T
+    // bytes, under the 2^31 range of its buffer resources for T < 2^22.
+    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 256 && a.T < (int64_t(1) << 22);
+    if (super_ok && !force_tile)
         return a.HS * E::ES <= 128 ? launch_super<E, 8>(a, s) : launch_super<E, 16>(a, s);
     // 16-byte chunks need base, pitch and head offsets 16-byte aligned and
     // HS*ES a multiple of 16 (vec = elements that divide all of them).
