@@ -84,14 +84,16 @@ int pick_vec(int es, const int64_t *lens, int nlens, const void *const *ptrs, in
     return 1;
 }
 
-// CAS_GEMM_TILE=64|128 forces the dense tile shape (tests and tuning);
-// anything else leaves the automatic choice.
+// CAS_GEMM_TILE=64|128|256 forces the dense tile shape (tests and tuning;
+// 256 applies where its kernel does, see gemm_wide_fits); anything else leaves
+// the automatic choice.
 int gemm_tile_override()
 {
     const char *v = std::getenv("CAS_GEMM_TILE");
     if (!v) return cas::GEMM_TILE_AUTO;
     if (std::strcmp(v, "64") == 0) return cas::GEMM_TILE_64;
     if (std::strcmp(v, "128") == 0) return cas::GEMM_TILE_128;
+    if (std::strcmp(v, "256") == 0) return cas::GEMM_TILE_256;
     return cas::GEMM_TILE_AUTO;
 }
 

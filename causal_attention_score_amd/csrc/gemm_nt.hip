@@ -94,7 +94,7 @@ hipError_t launch_vec(const GemmArgs &a, int vec, hipStream_t s)
 
 int pick_tile(const GemmArgs &a, int tile)
 {
-    if (tile != GEMM_TILE_AUTO) return tile;
+    if (tile == GEMM_TILE_64 || tile == GEMM_TILE_128) return tile;
     // Largest tile that still gives every CU (256) about one workgroup.
     const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
     return t128 >= 256 ? GEMM_TILE_128 : GEMM_TILE_64;
@@ -117,6 +117,10 @@ int64_t gemm_nt_workgroups(const GemmArgs &a, int /*elem*/, int tile)
 
 hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s)
 {
+    // 256 x 256 tiles where every CU gets one (M = N = 4096 and up).
+    if (elem != E_F32 && gemm_wide_fits(a, 2, vec) &&
+        (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256)))
+        return launch_gemm_wide(a, elem, s);
     switch (elem) {
     case E_F32: return launch_elem<KF32>(a, vec, tile, s);
     case E_BF16: return launch_elem<KBF16>(a, vec, tile, s);

@@ -24,12 +24,18 @@ struct TrimulArgs {
 };
 
 // Tile shapes the dense launcher can pick (exposed for tests and tuning).
-enum GemmTile { GEMM_TILE_AUTO = 0, GEMM_TILE_64 = 1, GEMM_TILE_128 = 2 };
+enum GemmTile { GEMM_TILE_AUTO = 0, GEMM_TILE_64 = 1, GEMM_TILE_128 = 2, GEMM_TILE_256 = 3 };
 
 // vec: elements per global load (a power of two that divides K, both pitches
 // and both base addresses' alignment in elements). Returns the launch error.
 hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s);
 int64_t gemm_nt_workgroups(const GemmArgs &a, int elem, int tile);
+
+// 256 x 256 tiles with loads straight into LDS (gemm_nt_wide.hip): 16-bit
+// inputs whose rows split into 16-byte pieces (vec * es == 16).
+bool gemm_wide_fits(const GemmArgs &a, int es, int vec);
+int64_t gemm_wide_workgroups(const GemmArgs &a);
+hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s);
 
 hipError_t launch_trimul(const TrimulArgs &a, int elem, int vec, hipStream_t s);
 int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);

@@ -57,13 +57,43 @@ def test_gemm_ragged(orc, monkeypatch, shape, dtype, tile):
     assert_close(y, ref, bound, dtype, f"gemm {shape} {dtype} tile{tile}")
 
 
-@pytest.mark.parametrize("tile", ["64", "128"])
+# 256 x 256 tiles with loads straight into LDS (16-bit inputs, K a multiple of
+# 8): ragged M and N, K not a multiple of the 64-element chunk, one chunk, and
+# shapes with several tiles per dimension.
+WIDE_SHAPES = [(256, 256, 64), (300, 520, 136), (257, 255, 8), (513, 260, 264), (1, 300, 72), (600, 40, 1000),
+               (520, 513, 4104), (255, 1, 16), (768, 512, 192)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_wide_ragged(orc, monkeypatch, shape, dtype):
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, dtype, seed=M * 5 + N * 11 + K)
+    ref, bound = orc.gemm_nt(X, W, dtype)
+    y = run_gemm(X, W, dtype, M, N, K, "tile256")
+    assert_close(y, ref, bound, dtype, f"gemm wide {shape} {dtype}")
+
+
+def test_gemm_wide_k0_writes_zeros(monkeypatch):
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    x = torch.empty((300, 0), device="cuda", dtype=torch.bfloat16)
+    w = torch.empty((260, 0), device="cuda", dtype=torch.bfloat16)
+    buf, flat = guarded_output(300 * 260)
+    case("gemm wide K=0")
+    cas.gemm_nt(x, w, out=flat.view(300, 260))
+    torch.cuda.synchronize()
+    check_guards(buf, 300 * 260)
+    assert np.all(flat.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("tile", ["64", "128", "256"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gemm_exact_small_integers(orc, monkeypatch, dtype, tile):
     """Integer inputs: every partial sum is an exact integer, so the GPU must
     equal the oracle bit for bit whatever its summation order."""
     monkeypatch.setenv("CAS_GEMM_TILE", tile)
-    for (M, N, K) in [(131, 67, 770), (64, 256, 129), (5, 300, 1000)]:
+    for (M, N, K) in [(131, 67, 770), (64, 256, 129), (5, 300, 1000), (300, 257, 1024)]:
         X, W = synth.gemm_inputs(M, N, K, dtype, seed=K, dist="int")
         ref, _ = orc.gemm_nt(X, W, dtype)
         y = run_gemm(X, W, dtype, M, N, K, "exact")
