@@ -16,34 +16,34 @@
 //
 // Data path. A workgroup holds four waves, one per SIMD, in a 2 x 2 grid;
 // each wave accumulates a 128 x 128 block as 4 x 4 MFMA tiles of 32 x 32
-// (v_mfma_f32_32x32x16_{bf16,f16}, 256 fp32 accumulators per lane). Each
-// k-chunk of BK = 64 elements (128-byte rows) of the 256 X rows and 256 W rows
-// lands in LDS straight from the load unit: one load instruction fills 1 KB
-// of LDS (8 rows), lane i writing bytes [16i, 16i + 16). Chunk c of row r is
-// stored at 16-byte slot c ^ (r % 8) of its row: the loads pick their source
-// addresses accordingly, and the MFMA operand reads (32 rows, one chunk per
-// lane half) then hit 8 distinct bank groups per 8 lanes. Two LDS stages: the
-// load of chunk k+2 is issued right after the barrier inside chunk k, so it
-// has about a chunk of MFMAs (64 per wave) to arrive.
+// (v_mfma_f32_32x32x16_{bf16,f16}, 256 fp32 accumulators per lane, held in
+// the accumulation registers). Each k-chunk (BKB bytes of a row: 32 or 64
+// elements) of the 256 X rows and 256 W rows lands in LDS straight from the
+// load unit: one load instruction fills 1 KB of LDS, lane i writing bytes
+// [16i, 16i + 16). A row's 16-byte pieces are stored XOR-swizzled, the loads
+// picking their source addresses to match, so the MFMA operand reads are free
+// of bank conflicts. S LDS stages form a ring: the loads of chunk k + S are
+// issued as soon as every wave is done with chunk k, so they have S - 1
+// chunks of MFMAs to arrive.
 //
 // Contraction-order permutation: in a chunk, lane half h (the MFMA k-slot)
-// takes 16-byte pieces 4h..4h+3, for X and W alike, so every product
-// x_k * w_k is formed exactly once.
+// takes the 16-byte pieces of its half of the chunk, for X and W alike, so
+// every product x_k * w_k is formed exactly once.
 #include "launch.hpp"
 #include "tile_engine.hpp"
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <type_traits>
 
 namespace cas {
 
 namespace {
 
-constexpr int WB = 256;              // output tile edge
-constexpr int WBK_BYTES = 128;       // bytes of a row per k-chunk (64 16-bit elements)
-constexpr int WSLOTS = WBK_BYTES / 16;
-constexpr int WOP_BYTES = WB * WBK_BYTES;   // one operand tile per stage (32 KB)
-constexpr int WSTAGE = 2 * WOP_BYTES;       // X tile + W tile
-constexpr int WTHREADS = 256;
+constexpr int WB = 256;        // output tile edge
 constexpr int WGROUP_M = 4;
-constexpr uint32_t WOOB = 0x80000000u;      // buffer offset the load unit reads as zero
+constexpr uint32_t WOOB = 0x80000000u; // buffer offset the load unit reads as zero
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -52,35 +52,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const char *base)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Fetch stage of one operand: rows [0, 256) of the tile whose first row is at
-// `rs`, k-chunk k0 (elements). Wave w issues loads j = 0..7, each filling the
-// 1 KB of LDS that holds tile rows 8(8w + j) .. +8.
-__device__ __forceinline__ void fetch_operand(__amdgpu_buffer_rsrc_t rs, char *lds_tile, uint32_t ldb, int rows,
-                                              uint32_t k0b, uint32_t kb, int wave, int lane)
-{
-    const int rsub = lane >> 3, slot = lane & 7;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = (wave * 8 + j) * 8 + rsub;                 // tile row written by this lane
-        const uint32_t cb = k0b + (uint32_t)((slot ^ (r & 7)) * 16); // its source piece (bytes)
-        const uint32_t vo = (r < rows && cb < kb) ? (uint32_t)r * ldb + cb : WOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + (wave * 8 + j) * 1024), 16, (int)vo,
-                                                 0, 0, 0);
-    }
-}
+// s_waitcnt immediate for "at most N vector memory operations in flight and
+// no LDS operation" (vmcnt is split over bits 3:0 and 15:14).
+template <int N> constexpr int wait_vm_lgkm0 = (N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14);
 
-template <class E>
-__global__ void __launch_bounds__(WTHREADS)
+// Barrier that orders this wave's LDS accesses (already waited for) against
+// the other waves' without waiting for its loads still in flight.
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// BKB: bytes of a row per k-chunk (64 or 128); S: LDS stages; NW: waves.
+template <int BKB, int S, int NW> struct Wide {
+    static constexpr int SPR = BKB / 16;              // 16-byte pieces per row
+    static constexpr int OPB = WB * BKB;              // one operand tile per stage
+    static constexpr int STAGE = 2 * OPB;
+    static constexpr int ROWS_PER_LOAD = 1024 / BKB;  // rows one load instruction fills
+    static constexpr int LOADS = OPB / 1024 / NW;     // per wave and operand
+    static constexpr int PC = 2 * LOADS;              // per wave and chunk
+    static constexpr int NU = BKB / 32;               // k16 steps per chunk
+    static constexpr int SH = BKB == 128 ? 1 : 2;     // log2(256 / BKB)
+    static_assert(S * STAGE <= 160 * 1024, "LDS");
+
+    // Piece c of tile row r sits at slot c ^ f(r). The LDS serves 16-byte
+    // reads 16 lanes (256 bytes) at a time, so rows whose addresses share a
+    // 256-byte bank offset are 256 / BKB apart, and f steps once per such
+    // stride: 16 consecutive rows read at one piece hit 16 distinct 16-byte
+    // bank groups (the bank-conflict counter reads zero; with f stepping
+    // every row it does not). Rows 32i + r32 share f(r32).
+    __device__ static __forceinline__ int f(int r) { return (r >> SH) & (SPR - 1); }
+
+    // Load j (< LOADS) of one operand tile at `rs`, k-chunk at byte k0b: it
+    // fills the 1 KB of LDS of tile rows ROWS_PER_LOAD * (LOADS * wave + j)
+    // .. + ROWS_PER_LOAD.
+    __device__ static __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, char *tile, uint32_t ldb, int rows,
+                                                 uint32_t k0b, uint32_t kb, int wave, int lane, int j)
+    {
+        const int rsub = lane / SPR, slot = lane % SPR;
+        const int blk = wave * LOADS + j;
+        const int r = blk * ROWS_PER_LOAD + rsub;
+        const uint32_t cb = k0b + (uint32_t)((slot ^ f(r)) * 16);
+        const uint32_t vo = (r < rows && cb < kb) ? (uint32_t)r * ldb + cb : WOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + blk * 1024), 16, (int)vo, 0, 0, 0);
+    }
+};
+
+// NWN: waves along N (2: four waves with 128 x 128 blocks; 4: eight waves,
+// two per SIMD, with 128 x 64 blocks).
+template <class E, int BKB, int S, int NWN>
+__global__ void __launch_bounds__(2 * NWN * 64)
 gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
                     int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                     int64_t tiles_m, int64_t tiles_n)
 {
+    constexpr int NW = 2 * NWN, WN = 256 / NWN, NB = WN / 32; // waves; wave block 128 x WN
+    using G = Wide<BKB, S, NW>;
     constexpr int ES = E::ES;
-    __shared__ __attribute__((aligned(1024))) char lds[2 * WSTAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[S * G::STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / NWN, wn = wave % NWN;
 
     // XCD-aware raster: the workgroups of one XCD take a contiguous range of
     // logical ids, walked in groups of WGROUP_M tile rows, so the X and W
@@ -101,79 +131,125 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
     const __amdgpu_buffer_rsrc_t rx = wide_rsrc(X + m0 * ldx * ES);
     const __amdgpu_buffer_rsrc_t rw = wide_rsrc(W + n0 * ldw * ES);
     const uint32_t ldxb = (uint32_t)(ldx * ES), ldwb = (uint32_t)(ldw * ES), kb = (uint32_t)(K * ES);
-    const int64_t nk = (K * ES + WBK_BYTES - 1) / WBK_BYTES;
+    const int nk = (int)((K * ES + BKB - 1) / BKB);
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+        for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
 
-    const int r32 = lane & 31, h = lane >> 5;
-    // Fragments of k16 step u of a chunk: 16-byte piece 4h + u of rows
-    // 32i + r32 (which all share r32 % 8, hence one swizzled position).
-    auto read_frags = [&](const char *stage, int u, u32x4 (&af)[4], u32x4 (&bfr)[4]) {
-        const int pos = ((4 * h + u) ^ (r32 & 7)) * 16;
-        const char *xa = stage + (wm * 128 + r32) * WBK_BYTES + pos;
-        const char *wa = stage + WOP_BYTES + (wn * 128 + r32) * WBK_BYTES + pos;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(xa + i * 32 * WBK_BYTES);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bfr[i] = *reinterpret_cast<const u32x4 *>(wa + i * 32 * WBK_BYTES);
+    // Load q (< PC) of this wave for chunk c: the X tile's, then the W tile's.
+    // A chunk past the end reads as zeros (every piece out of range).
+    auto fetch_one = [&](int c, int q) {
+        char *stg = lds + (c % S) * G::STAGE;
+        const uint32_t kbv = c < nk ? kb : 0u;
+        if (q < G::LOADS) G::fetch(rx, stg, ldxb, rows_x, (uint32_t)c * BKB, kbv, wave, lane, q);
+        else G::fetch(rw, stg + G::OPB, ldwb, rows_w, (uint32_t)c * BKB, kbv, wave, lane, q - G::LOADS);
     };
-    // Stage s of LDS holds chunks s, s + 2, ... Per chunk one barrier, before
-    // its last step's MFMAs: by then every wave holds that step's fragments in
-    // registers, so after the barrier the chunk's stage takes the load of
-    // chunk + 2 while the next chunk's first fragments are read behind the
-    // MFMAs. The barrier's fence also waits for this wave's loads of
-    // chunk + 1 (the only ones in flight).
-    u32x4 fa[2][4], fb[2][4];
-    if (nk > 0) {
-        fetch_operand(rx, lds, ldxb, rows_x, 0, kb, wave, lane);
-        fetch_operand(rw, lds + WOP_BYTES, ldwb, rows_w, 0, kb, wave, lane);
-        __syncthreads(); // chunk 0 in LDS
-        if (nk > 1) {
-            fetch_operand(rx, lds + WSTAGE, ldxb, rows_x, WBK_BYTES, kb, wave, lane);
-            fetch_operand(rw, lds + WSTAGE + WOP_BYTES, ldwb, rows_w, WBK_BYTES, kb, wave, lane);
+    const int r32 = lane & 31, h = lane >> 5, fr = G::f(r32);
+    // Fragments of k16 step u: piece h * NU + u (lane half h is the MFMA
+    // k-slot) of rows 32i + r32.
+    auto read_frags = [&](const char *stage, int u, u32x4 (&af)[4], u32x4 (&bfr)[NB]) {
+        const int pos = ((h * G::NU + u) ^ fr) * 16;
+        const char *xa = stage + (wm * 128 + r32) * BKB + pos;
+        const char *wa = stage + G::OPB + (wn * WN + r32) * BKB + pos;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(xa + i * 32 * BKB);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bfr[i] = *reinterpret_cast<const u32x4 *>(wa + i * 32 * BKB);
+    };
+
+    // Pipeline: chunk c lives in stage c % S. One barrier per chunk, before
+    // its last k16 step's MFMAs: by then every wave holds that step's
+    // fragments in registers, so from the barrier inside chunk c on, the
+    // stage of chunk c is free for chunk c + S, and the next chunk's first
+    // fragments are read behind the MFMAs.
+    // Chunk c's loads: one step's worth (LPS) right after the barrier inside
+    // chunk c - S, the rest during steps 0 .. NU - 2 of chunk c - S + 1, one
+    // load after every P MFMAs. Chunks past the end are loaded too (as zeros,
+    // into stages nothing reads any more), so every step issues the same
+    // loads at the same places -- no branch among the MFMAs, where a taken
+    // branch stalls the matrix pipe -- and every barrier waits for the same
+    // count: this wave's loads of chunk kc + 1 are done once at most those of
+    // chunks kc + 2 .. kc + S - 1, (S - 2) PC loads, are in flight.
+    constexpr int MPS = 4 * NB;        // MFMAs per step
+    constexpr int LPS = G::PC / G::NU; // loads per step
+    constexpr int P = MPS / LPS;
+    static_assert(LPS * G::NU == G::PC && LPS <= MPS && MPS % LPS == 0, "load spread");
+    static_assert((S - 2) * G::PC + LPS <= 63, "vmcnt range");
+    u32x4 fa[2][4], fb[2][NB];
+    // One k16 step: MPS MFMAs; with c >= 0 (compile-time shape: c is only
+    // ever a chunk number or -1 for none), loads [q0, q0 + LPS) of chunk c.
+    auto mma_step = [&](int fi, int c, int q0, auto with_loads) {
+#pragma unroll
+        for (int i = 0; i < MPS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_chunk<E>(acc[i / NB][i % NB], fa[fi][i / NB], fb[fi][i % NB]);
+            if constexpr (decltype(with_loads)::value) {
+                if ((i + 1) % P == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    fetch_one(c, q0 + (i + 1) / P - 1);
+                }
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using loads = std::true_type;
+    using no_loads = std::false_type;
+    // The writeback's arguments, read from the kernel arguments now: a
+    // scalar load still in flight in the main loop would make every wait for
+    // the fragment reads a wait for all of them (scalar loads return out of
+    // order, in the same counter).
+    asm volatile("" ::"s"(Y), "s"(ldy));
+    if (nk > 0) {
+        for (int c = 0; c + 1 < S; ++c)
+            for (int q = 0; q < G::PC; ++q) fetch_one(c, q);
+        for (int q = 0; q < LPS; ++q) fetch_one(S - 1, q);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<(S - 2) * G::PC + LPS>); // chunk 0 landed
+        plain_barrier();
         read_frags(lds, 0, fa[0], fb[0]);
     }
-    for (int64_t kc = 0; kc < nk; ++kc) {
-        const char *cur = lds + (kc & 1) * WSTAGE;
+    for (int kc = 0; kc + 1 < nk; ++kc) {
+        const char *cur = lds + (kc % S) * G::STAGE;
 #pragma unroll
-        for (int u = 0; u < WSLOTS / 2; ++u) {
-            const int f = u & 1;
-            if (u + 1 < WSLOTS / 2) {
-                read_frags(cur, u + 1, fa[f ^ 1], fb[f ^ 1]);
-            } else if (kc + 1 < nk) {
-                __syncthreads(); // chunk kc + 1 in LDS; every wave done reading chunk kc
-                if (kc + 2 < nk) {
-                    char *stg = lds + (kc & 1) * WSTAGE;
-                    const uint32_t k0b = (uint32_t)(kc + 2) * WBK_BYTES;
-                    fetch_operand(rx, stg, ldxb, rows_x, k0b, kb, wave, lane);
-                    fetch_operand(rw, stg + WOP_BYTES, ldwb, rows_w, k0b, kb, wave, lane);
-                }
-                read_frags(lds + ((kc + 1) & 1) * WSTAGE, 0, fa[f ^ 1], fb[f ^ 1]);
+        for (int u = 0; u < G::NU; ++u) {
+            const int fi = u & 1;
+            if (u + 1 < G::NU) {
+                read_frags(cur, u + 1, fa[fi ^ 1], fb[fi ^ 1]);
+                mma_step(fi, kc - 1 + S, (u + 1) * LPS, loads{});
+            } else {
+                __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<(S - 2) * G::PC>); // chunk kc + 1 landed
+                plain_barrier(); // ... for every wave; every wave done reading chunk kc
+                read_frags(lds + ((kc + 1) % S) * G::STAGE, 0, fa[fi ^ 1], fb[fi ^ 1]);
+                mma_step(fi, kc + S, 0, loads{});
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) mfma_chunk<E>(acc[a][b], fa[f][a], fb[f][b]);
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // The last chunk: no barrier, no loads (out of the loop, which keeps the
+    // LDS waits of the loop body exact).
+    if (nk > 0) {
+        const char *cur = lds + ((nk - 1) % S) * G::STAGE;
+#pragma unroll
+        for (int u = 0; u < G::NU; ++u) {
+            const int fi = u & 1;
+            if (u + 1 < G::NU) read_frags(cur, u + 1, fa[fi ^ 1], fb[fi ^ 1]);
+            mma_step(fi, -1, 0, no_loads{});
+        }
+    }
+    // Loads of chunks past the end may still be writing LDS.
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<0>);
 
     // Writeback: lane l, register r of block (a, b) holds row
     // 32a + acc_row(r, l) and column 32b + l % 32 of this wave's block, so one
     // store instruction writes two whole 128-byte row pieces.
-    const int64_t row0 = m0 + wm * 128, col0 = n0 + wn * 128;
+    const int64_t row0 = m0 + wm * 128, col0 = n0 + wn * WN;
     float *yw = Y + row0 * ldy + col0 + r32;
-    if (row0 + 128 <= M && col0 + 128 <= N) {
+    if (row0 + 128 <= M && col0 + WN <= N) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     __builtin_nontemporal_store(acc[a][b][r], yw + (32 * a + acc_row(r, lane)) * ldy + 32 * b);
@@ -181,7 +257,7 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const bool col_ok = col0 + 32 * b + r32 < N;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -203,16 +279,35 @@ bool gemm_wide_fits(const GemmArgs &a, int es, int vec)
 
 int64_t gemm_wide_workgroups(const GemmArgs &a) { return ((a.M + WB - 1) / WB) * ((a.N + WB - 1) / WB); }
 
-hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s)
+namespace {
+template <class E, int BKB, int S, int NWN>
+hipError_t launch_wide_cfg(const GemmArgs &a, hipStream_t s)
 {
     const int64_t tm = (a.M + WB - 1) / WB, tn = (a.N + WB - 1) / WB;
-    if (elem == E_BF16)
-        hipLaunchKernelGGL(gemm_nt_wide_kernel<KBF16>, dim3((unsigned)(tm * tn)), dim3(WTHREADS), 0, s,
-                           (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn);
-    else
-        hipLaunchKernelGGL(gemm_nt_wide_kernel<KF16>, dim3((unsigned)(tm * tn)), dim3(WTHREADS), 0, s,
-                           (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+    hipLaunchKernelGGL((gemm_nt_wide_kernel<E, BKB, S, NWN>), dim3((unsigned)(tm * tn)), dim3(2 * NWN * 64), 0, s,
+                       (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn);
     return hipGetLastError();
+}
+
+// CAS_GEMM_WIDE=<chunk bytes>x<stages>[w8] picks the k-chunk width, the
+// stage count and four or eight waves (tuning); see the default below.
+template <class E>
+hipError_t launch_wide_elem(const GemmArgs &a, hipStream_t s)
+{
+    const char *v = std::getenv("CAS_GEMM_WIDE");
+    const std::string c = v ? v : "";
+    if (c == "128x2") return launch_wide_cfg<E, 128, 2, 2>(a, s);
+    if (c == "64x3") return launch_wide_cfg<E, 64, 3, 2>(a, s);
+    if (c == "64x4") return launch_wide_cfg<E, 64, 4, 2>(a, s);
+    if (c == "128x2w8") return launch_wide_cfg<E, 128, 2, 4>(a, s);
+    if (c == "64x3w8") return launch_wide_cfg<E, 64, 3, 4>(a, s);
+    return launch_wide_cfg<E, 64, 4, 4>(a, s);
+}
+} // namespace
+
+hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s)
+{
+    return elem == E_BF16 ? launch_wide_elem<KBF16>(a, s) : launch_wide_elem<KF16>(a, s);
 }
 
 } // namespace cas
