@@ -46,6 +46,7 @@ constexpr int WGROUP_M = 4;
 constexpr uint32_t WOOB = 0x80000000u; // buffer offset the load unit reads as zero
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const char *base)
 {
@@ -185,7 +186,9 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
 #pragma unroll
         for (int i = 0; i < MPS; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            mfma_chunk<E>(acc[i / NB][i % NB], fa[fi][i / NB], fb[fi][i % NB]);
+            // D = W X^T: W rows are the MFMA A operand, so a lane's four
+            // consecutive accumulators are four consecutive output columns.
+            mfma_chunk<E>(acc[i / NB][i % NB], fb[fi][i % NB], fa[fi][i / NB]);
             if constexpr (decltype(with_loads)::value) {
                 if ((i + 1) % P == 0) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -240,31 +243,34 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
     // Loads of chunks past the end may still be writing LDS.
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<0>);
 
-    // Writeback: lane l, register r of block (a, b) holds row
-    // 32a + acc_row(r, l) and column 32b + l % 32 of this wave's block, so one
-    // store instruction writes two whole 128-byte row pieces.
-    const int64_t row0 = m0 + wm * 128, col0 = n0 + wn * WN;
-    float *yw = Y + row0 * ldy + col0 + r32;
-    if (row0 + 128 <= M && col0 + WN <= N) {
+    // Writeback: lane l, registers 4g .. 4g+3 of block (a, b) hold row
+    // 32a + l % 32 and columns 32b + 8g + 4(l / 32) + 0..3 of this wave's
+    // block: one 16-byte store each where the row is 16-byte aligned.
+    const int64_t row0 = m0 + wm * 128 + r32, col0 = n0 + wn * WN + 4 * h;
+    float *yw = Y + row0 * ldy + col0;
+    const bool vec_ok = ((uintptr_t)Y % 16 == 0) && (ldy % 4 == 0);
+    if (vec_ok && m0 + wm * 128 + 128 <= M && n0 + wn * WN + WN <= N) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    __builtin_nontemporal_store(acc[a][b][r], yw + (32 * a + acc_row(r, lane)) * ldy + 32 * b);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4v v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+                    *reinterpret_cast<f32x4v *>(yw + 32 * a * ldy + 32 * b + 8 * g) = v;
+                }
     } else {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+            const bool row_ok = row0 + 32 * a < M;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const bool col_ok = col0 + 32 * b + r32 < N;
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int rr = 32 * a + acc_row(r, lane);
-                    if (col_ok && row0 + rr < M) __builtin_nontemporal_store(acc[a][b][r], yw + rr * ldy + 32 * b);
+                    const int cc = 32 * b + 8 * (r >> 2) + (r & 3);
+                    if (row_ok && col0 + cc < N) yw[32 * a * ldy + cc] = acc[a][b][r];
                 }
-            }
+        }
     }
 }
 
