@@ -10,10 +10,13 @@ value = useful TFLOP/s of the step (2MNK for the dense product, the lower
 triangle including the diagonal, 2*HS*B*NH*T(T+1)/2, for the scores), with
 inputs resident in HBM. The JSON line also carries the roofline of the
 dominant kernel (timed with HIP events on its own stream), the oracle's
-throughput on the host cores, and the bf16 workloads (4096^3 dense, causal
-scores (4, 4096, 3, 25, 64)) timed the same way.
+throughput on the host cores, the bf16 workloads (4096^3 dense, causal
+scores (4, 4096, 3, 25, 64)) timed the same way, and the local-padding A/B:
+the fp32 dense layer at H = 1024 and at DietCode's H = 2304, with the bounds
+checks removed from the MFMA loop (the product path) and kept there
+(CAS_VARIANT=predicated).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bf16]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bf16] [--no-ab]
 """
 from __future__ import annotations
 
@@ -46,18 +49,29 @@ def device_tensor(a, dtype):
     return torch.from_numpy(a.view(np.float16)).cuda()
 
 
-def kernel_sources_digest() -> str:
+# Sources each profiled kernel is built from (its translation unit, what it
+# includes, and the host dispatch in front of it).
+KERNEL_SOURCES = {
+    "trimul_f32_B8_T1024": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip", "trimul_f32.hip",
+                            "trimul_kernel.hpp"],
+    "gemm_nt_f32_960x1024x770": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip"],
+}
+
+
+def kernel_sources_digest(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the sources `kernel` is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "causal_attention_score_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[kernel]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, digest: str):
+def read_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    `kernel`, if it was taken on the current kernel sources; else None."""
+    `kernel`, if it was taken on the kernel's current sources; else None."""
+    digest = kernel_sources_digest(kernel)
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
     if not os.path.exists(path):
         return None
@@ -152,6 +166,39 @@ def roofline_of(wl, ms: float, traffic_bytes):
             "useful_flops": wl.useful_flops()}
 
 
+def local_padding_ab(steps: int):
+    """The dense fp32 layer with local padding (predicates only at fetch and
+    writeback) against the same kernel with the bounds checks kept inside the
+    MFMA loop (CAS_VARIANT=predicated), on the 1024-wide layer and on the
+    DietCode shape (H = 2304)."""
+    import torch
+
+    from causal_attention_score_amd import synth
+    out = {}
+    for name in ("dense_f32_960x1024x770", "dense_f32_960x2304x770"):
+        wl = synth.WORKLOADS[name]
+        log(f"local-padding A/B on {name}")
+        p = Part(wl)
+        res = {}
+        for variant in ("local_padding", "predicated"):
+            if variant == "predicated":
+                os.environ["CAS_VARIANT"] = "predicated"
+            else:
+                os.environ.pop("CAS_VARIANT", None)
+            _, (ms,), _ = time_parts([p], steps, 3)
+            res[variant] = {"avg_launch_us": round(ms * 1e3, 2),
+                            "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2)}
+        os.environ.pop("CAS_VARIANT", None)
+        res["speedup"] = round(res["predicated"]["avg_launch_us"] / res["local_padding"]["avg_launch_us"], 3)
+        if name.endswith("2304x770"):
+            res["pages_context"] = ("DietCode on NVIDIA RTX: 0.98 vs 11.6 TFLOP/s (3090), 0.43 vs 5.27 (2080 Ti), "
+                                    "baseline vs local padding; another machine, not a target")
+        out[name] = res
+        del p
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of
     the step: the whole dense product, then causal-score planes (one (b, nh)
@@ -212,6 +259,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-ab", action="store_true", help="skip the local-padding A/B")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the kernels for the rocprofv3 HBM-traffic counter runs")
     args = ap.parse_args()
@@ -227,8 +275,6 @@ def main():
     if args.traffic_probe:
         traffic_probe()
         return
-    digest = kernel_sources_digest()
-
     wg = synth.WORKLOADS["dense_f32_960x1024x770"]
     wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
     log("preparing inputs")
@@ -240,7 +286,7 @@ def main():
     dom = max(range(2), key=lambda i: per[i])
     dom_wl = [wg, wt][dom]
     kname = "trimul_f32_B8_T1024" if dom_wl.kind == "trimul_causal" else "gemm_nt_f32_960x1024x770"
-    roof = roofline_of(dom_wl, per[dom], read_traffic(kname, digest))
+    roof = roofline_of(dom_wl, per[dom], read_traffic(kname))
     parts_report = {wl.name: {"avg_launch_us": round(ms * 1e3, 2),
                               "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                               "roofline": roofline_of(wl, ms, None)}
@@ -262,6 +308,10 @@ def main():
             del p
             torch.cuda.empty_cache()
 
+    ab = None
+    if not args.no_ab:
+        ab = local_padding_ab(max(10, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
@@ -279,9 +329,10 @@ def main():
         "cpu_baseline": cpu,
         "parts": parts_report,
         "bf16_workloads": bf16,
+        "local_padding_ab": ab,
         "wall_ms_per_step": round(wall_ms, 5),
         "device": torch.cuda.get_device_name(0),
-        "sources_digest": digest,
+        "sources_digest": {k: kernel_sources_digest(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
 

@@ -97,6 +97,15 @@ int gemm_tile_override()
     return cas::GEMM_TILE_AUTO;
 }
 
+// CAS_VARIANT=predicated keeps the bounds checks inside the dense product's
+// MFMA loop (on the general tile kernel): the baseline of the local-padding
+// A/B measurement. Anything else is the local-padding path.
+bool gemm_predicated()
+{
+    const char *v = std::getenv("CAS_VARIANT");
+    return v && std::strcmp(v, "predicated") == 0;
+}
+
 int launch_status(hipError_t e)
 {
     if (e == hipSuccess) return CAS_OK;
@@ -119,7 +128,7 @@ CAS_EXPORT int cas_gemm_nt(const void *X, const void *W, void *Y, int64_t M, int
         return CAS_ERR_SHAPE;
     if (overlap(Y, yb, X, xb) || overlap(Y, yb, W, wb)) return CAS_ERR_ALIAS;
 
-    cas::GemmArgs a{X, W, (float *)Y, M, N, K, ldx, ldw, ldy};
+    cas::GemmArgs a{X, W, (float *)Y, M, N, K, ldx, ldw, ldy, gemm_predicated()};
     const int tile = gemm_tile_override();
     if (cas::gemm_nt_workgroups(a, in_dtype, tile) > INT32_MAX) return CAS_ERR_SHAPE;
     const int dc = device_check();

@@ -24,13 +24,13 @@ template <> struct GemmBK<KF32> { static constexpr int v = 32; };
 template <> struct GemmBK<KBF16> { static constexpr int v = 64; };
 template <> struct GemmBK<KF16> { static constexpr int v = 64; };
 
-template <class E, int BM, int BN, int WGM, int WGN, int VEC>
+template <class E, int BM, int BN, int WGM, int WGN, int VEC, bool PRED>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 gemm_nt_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
                int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                int64_t tiles_m, int64_t tiles_n)
 {
-    using G = Engine<E, BM, BN, GemmBK<E>::v, WGM, WGN, VEC>;
+    using G = Engine<E, BM, BN, GemmBK<E>::v, WGM, WGN, VEC, PRED>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::STAGE];
 
     const int tid = threadIdx.x;
@@ -71,9 +71,14 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s)
 {
     using C = TileCfg<BM, BN>;
     const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC>), dim3((unsigned)(tm * tn)),
-                       dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
-                       a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+    if (a.predicated)
+        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, true>), dim3((unsigned)(tm * tn)),
+                           dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
+                           a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+    else
+        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, false>), dim3((unsigned)(tm * tn)),
+                           dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
+                           a.K, a.ldx, a.ldw, a.ldy, tm, tn);
     return hipGetLastError();
 }
 
@@ -118,7 +123,7 @@ int64_t gemm_nt_workgroups(const GemmArgs &a, int /*elem*/, int tile)
 hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s)
 {
     // 256 x 256 tiles where every CU gets one (M = N = 4096 and up).
-    if (elem != E_F32 && gemm_wide_fits(a, 2, vec) &&
+    if (elem != E_F32 && !a.predicated && gemm_wide_fits(a, 2, vec) &&
         (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256)))
         return launch_gemm_wide(a, elem, s);
     switch (elem) {

@@ -13,6 +13,7 @@ struct GemmArgs {
     const void *W;
     float *Y;
     int64_t M, N, K, ldx, ldw, ldy;
+    bool predicated = false; // bounds checks inside the MFMA loop (local-padding A/B)
 };
 
 struct TrimulArgs {

@@ -73,9 +73,16 @@ template <> struct VecT<2> { using T = unsigned short; };
 // row 8*(r/4) + 4*(l/32) + r%4 (an A row) and column l%32 (a B row).
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// Bounds of one output tile's operands, seen by a predicated compute stage.
+struct TileBounds {
+    int64_t ra0, rowsA, rb0, rowsB, K;
+};
+
 // E: element kind. BM x BN output tile, BK contraction chunk, WGM x WGN waves,
-// VEC elements per global load.
-template <class E, int BM, int BN, int BK, int WGM, int WGN, int VEC>
+// VEC elements per global load. PRED: the compute stage re-checks every
+// operand element against the matrix bounds, zeroing those outside -- the
+// predicates that local padding removes, kept for the A/B measurement.
+template <class E, int BM, int BN, int BK, int WGM, int WGN, int VEC, bool PRED = false>
 struct Engine {
     static constexpr int ES = E::ES;
     static constexpr int NT = WGM * WGN * 64;          // threads per workgroup
@@ -145,9 +152,27 @@ struct Engine {
         }
     }
 
-    // Compute stage: no predicates; every wave multiplies its WM x WN slice.
+    // Zero the elements of one 16-byte operand chunk (contraction indices
+    // kidx .. kidx + 16/ES - 1 of row `row`) that lie outside the matrix.
+    __device__ static __forceinline__ u32x4 mask_chunk(u32x4 v, bool row_ok, int64_t kidx, int64_t K)
+    {
+        constexpr int EPD = 4 / ES; // elements per dword
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            unsigned m = 0;
+#pragma unroll
+            for (int e = 0; e < EPD; ++e)
+                if (row_ok && kidx + d * EPD + e < K) m |= (ES == 4 ? 0xFFFFFFFFu : 0xFFFFu << (16 * e));
+            v[d] &= m;
+        }
+        return v;
+    }
+
+    // Compute stage. PRED = false: no predicates; every wave multiplies its
+    // WM x WN slice. PRED = true: every operand chunk read from LDS is masked
+    // against the bounds first (tb, contraction offset k0 of this chunk).
     __device__ static __forceinline__ void compute(f32x16 (&acc)[MB][NB], const char *lds, int wave_m, int wave_n,
-                                                   int lane)
+                                                   int lane, const TileBounds &tb = {}, int64_t k0 = 0)
     {
         const int r32 = lane & 31, h = lane >> 5;
         const char *a0 = lds + (wave_m * WM + r32) * ROWB + h * HALF_B;
@@ -159,6 +184,15 @@ struct Engine {
             for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4 *>(a0 + mb * 32 * ROWB + u * 16);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) bfr[nb] = *reinterpret_cast<const u32x4 *>(b0 + nb * 32 * ROWB + u * 16);
+            if constexpr (PRED) {
+                const int64_t kidx = k0 + h * (BK / 2) + u * (16 / ES);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    af[mb] = mask_chunk(af[mb], tb.ra0 + wave_m * WM + mb * 32 + r32 < tb.rowsA, kidx, tb.K);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    bfr[nb] = mask_chunk(bfr[nb], tb.rb0 + wave_n * WN + nb * 32 + r32 < tb.rowsB, kidx, tb.K);
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -191,7 +225,7 @@ struct Engine {
             for (int64_t kc = 0; kc < nk; ++kc) {
                 const char *cur = lds + (kc & 1) * STAGE;
                 if (kc + 1 < nk) fetch(R, A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, (kc + 1) * BK, tid);
-                compute(acc, cur, wave_m, wave_n, lane);
+                compute(acc, cur, wave_m, wave_n, lane, TileBounds{ra0, rowsA, rb0, rowsB, K}, kc * BK);
                 if (kc + 1 < nk) stash(R, lds + ((kc + 1) & 1) * STAGE, tid);
                 __syncthreads();
             }
@@ -201,7 +235,7 @@ struct Engine {
                 if (kc > 0) __syncthreads(); // every wave is done reading the previous chunk
                 stash(R, lds, tid);
                 __syncthreads();
-                compute(acc, lds, wave_m, wave_n, lane);
+                compute(acc, lds, wave_m, wave_n, lane, TileBounds{ra0, rowsA, rb0, rowsB, K}, kc * BK);
             }
         }
     }

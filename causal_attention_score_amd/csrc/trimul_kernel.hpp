@@ -420,49 +420,54 @@ constexpr int SUPER_THREADS = 3 * NCOMP_THREADS;
 constexpr int OUT_PITCH = TB * 4 + 16;        // bytes per LDS output row (+16: bank skew)
 constexpr int OUT_BYTES = TB * OUT_PITCH;
 
-// Walks item ids first, first + step, ... as (plane, r) with 32-bit
-// arithmetic and one division at set-up.
-struct Cursor {
-    uint32_t plane, r, dp, dr, L;
-    __device__ __forceinline__ void init(uint32_t first, uint32_t step, uint32_t L_)
-    {
-        L = L_;
-        plane = first / L;
-        r = first - plane * L;
-        dp = step / L;
-        dr = step - dp * L;
-    }
-    __device__ __forceinline__ void advance()
-    {
-        r += dr;
-        plane += dp;
-        if (r >= L) {
-            r -= L;
-            ++plane;
-        }
-    }
-};
-
 struct Super {
     uint32_t plane, T0, S0;
     bool diag;
 };
 
-__device__ __forceinline__ Super decode_super(const Cursor &cu)
-{
-    Super sp;
-    const uint32_t r = cu.r;
-    // r = i(i+1)/2 + j, 0 <= j <= i
-    uint32_t i = (uint32_t)((sqrtf(8.0f * (float)r + 1.0f) - 1.0f) * 0.5f);
-    while (i * (i + 1) / 2 > r) --i;
-    while ((i + 1) * (i + 2) / 2 <= r) ++i;
-    const uint32_t j = r - i * (i + 1) / 2;
-    sp.plane = cu.plane;
-    sp.T0 = i * ST;
-    sp.S0 = j * ST;
-    sp.diag = i == j;
-    return sp;
-}
+// Walks the items first, first + step, ... of the per-plane triangles (row i
+// holds the i + 1 super-tiles j = 0..i) as (plane, i, j). The set-up decodes
+// `first` once; each advance moves whole planes, then row by row, with
+// scalar integer arithmetic only: the waves that share a SIMD with the fp32
+// MFMAs get few vector issue slots.
+struct Walker {
+    uint32_t plane, i, j, dp, dr, nt;
+    __device__ __forceinline__ void init(uint32_t first, uint32_t step, uint32_t L, uint32_t nt_)
+    {
+        nt = nt_;
+        plane = first / L;
+        const uint32_t r = first - plane * L;
+        dp = step / L;
+        dr = step - dp * L;
+        // r = i(i+1)/2 + j, 0 <= j <= i
+        uint32_t q = (uint32_t)((sqrtf(8.0f * (float)r + 1.0f) - 1.0f) * 0.5f);
+        while (q * (q + 1) / 2 > r) --q;
+        while ((q + 1) * (q + 2) / 2 <= r) ++q;
+        i = __builtin_amdgcn_readfirstlane(q);
+        j = __builtin_amdgcn_readfirstlane(r - q * (q + 1) / 2);
+    }
+    __device__ __forceinline__ void advance()
+    {
+        plane += dp;
+        j += dr;
+        while (j > i) {
+            j -= i + 1;
+            if (++i == nt) {
+                i = 0;
+                ++plane;
+            }
+        }
+    }
+    __device__ __forceinline__ Super item() const
+    {
+        Super sp;
+        sp.plane = plane;
+        sp.T0 = i * ST;
+        sp.S0 = j * ST;
+        sp.diag = i == j;
+        return sp;
+    }
+};
 
 // Rows of the next super-tile, NCH 16-byte chunks per row, in registers.
 template <int NCH> struct Staged {
@@ -622,8 +627,8 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
     const uint32_t T4 = T * 4u;
     const uint32_t ldb = 3u * C * (uint32_t)E::ES;
     const bool vec4 = vec_store != 0;
-    Cursor cur;
-    cur.init(first < hi ? first : 0, wg_on_x, L);
+    Walker cur;
+    cur.init(first < hi ? first : 0, wg_on_x, L, (T + ST - 1) / ST);
 
     // Every wave passes the same barriers: one after the prologue, then X and
     // Y once per step.
@@ -631,7 +636,7 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
         const int cl = slot * 64 + lane;
         Staged<NCH> st;
         if (steps > 0) {
-            stage_fetch<E, NCH>(st, qkv, decode_super(cur), T, C, NH, HS, ldb, cl);
+            stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
             stage_store<NCH>(st, opb, cl);
         }
         lds_barrier(); // operand rows of step 0 in LDS
@@ -639,7 +644,7 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
             const bool more = n + 1 < steps;
             if (more) {
                 cur.advance();
-                stage_fetch<E, NCH>(st, qkv, decode_super(cur), T, C, NH, HS, ldb, cl);
+                stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
             }
             lds_barrier(); // X: operand rows of step n consumed
             if (more) stage_store<NCH>(st, opb, cl);
@@ -648,7 +653,7 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
     } else if (role == 0) {
         lds_barrier();
         for (uint32_t n = 0; n < steps; ++n) {
-            const Super sp = decode_super(cur);
+            const Super sp = cur.item();
             cur.advance();
             // Diagonal sub-tile (0, 1) is all NaN: its store wave writes it directly.
             const bool live = !(sp.diag && sa == 0 && sb == 1);
@@ -673,7 +678,7 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
         Tile pm;              // mirror of the previous step, second half pending
         bool pm_live = false, pm_full = false;
         for (uint32_t n = 0; n < steps; ++n) {
-            const Super sp = decode_super(cur);
+            const Super sp = cur.item();
             cur.advance();
             Tile tl;
             tl.t0 = sp.T0 + sa * TB;

@@ -148,6 +148,10 @@ WORKLOADS = {
     "trimul_f32_B8_T1024_NH12_HS64": Workload("trimul_f32_B8_T1024_NH12_HS64", "trimul_causal",
                                               "f32", 3, (8, 1024, 12, 64)),
     "dense_bf16_4096": Workload("dense_bf16_4096", "gemm_nt", "bf16", 4, (4096, 4096, 4096)),
+    # The local-padding A/B shape of DietCode's test_local_padding (B=16,
+    # T=60, I=770, H=2304): the same inputs recipe as the 1024-wide layer.
+    "dense_f32_960x2304x770": Workload("dense_f32_960x2304x770", "gemm_nt", "f32", 6,
+                                       (960, 2304, 770), "normal", 1.0 / np.sqrt(770.0)),
     "trimul_bf16_B4_T4096_NH25_HS64": Workload("trimul_bf16_B4_T4096_NH25_HS64", "trimul_causal",
                                                "bf16", 5, (4, 4096, 25, 64)),
 }

@@ -87,6 +87,35 @@ def test_gemm_wide_k0_writes_zeros(monkeypatch):
     assert np.all(flat.cpu().numpy() == 0)
 
 
+# The local-padding A/B baseline: the same product with the bounds checks
+# kept inside the MFMA loop (CAS_VARIANT=predicated) must give the same results.
+PRED_SHAPES = [(15, 9, 12), (65, 33, 127), (129, 127, 257), (257, 255, 770), (200, 72, 3), (1, 257, 129),
+               (96, 160, 770)]
+
+
+@pytest.mark.parametrize("tile", ["64", "128"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", PRED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_predicated_ragged(orc, monkeypatch, shape, dtype, tile):
+    monkeypatch.setenv("CAS_VARIANT", "predicated")
+    monkeypatch.setenv("CAS_GEMM_TILE", tile)
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, dtype, seed=M * 7 + N * 3 + K)
+    ref, bound = orc.gemm_nt(X, W, dtype)
+    y = run_gemm(X, W, dtype, M, N, K, f"predicated tile{tile}")
+    assert_close(y, ref, bound, dtype, f"gemm predicated {shape} {dtype} tile{tile}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_predicated_exact_small_integers(orc, monkeypatch, dtype):
+    monkeypatch.setenv("CAS_VARIANT", "predicated")
+    for (M, N, K) in [(131, 67, 770), (300, 257, 1024)]:
+        X, W = synth.gemm_inputs(M, N, K, dtype, seed=K + 1, dist="int")
+        ref, _ = orc.gemm_nt(X, W, dtype)
+        y = run_gemm(X, W, dtype, M, N, K, "predicated exact")
+        assert_exact(y, ref, f"gemm predicated exact {(M, N, K)} {dtype}")
+
+
 @pytest.mark.parametrize("tile", ["64", "128", "256"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gemm_exact_small_integers(orc, monkeypatch, dtype, tile):
@@ -286,6 +315,21 @@ def test_workload_dense_f32_960x1024x770(orc):
     y = run_gemm(X, W, "f32", 960, 1024, 770, wl.name)
     r = assert_close(y, ref, bound, "f32", wl.name)
     print(f"{wl.name}: max err/tol {r:.3g}")
+
+
+@pytest.mark.parametrize("variant", ["local_padding", "predicated"])
+def test_workload_dense_f32_960x2304x770(orc, monkeypatch, variant):
+    """The local-padding A/B shape, both variants, in the launch configuration
+    bench.py times (automatic tile choice)."""
+    if variant == "predicated":
+        monkeypatch.setenv("CAS_VARIANT", "predicated")
+    wl = synth.WORKLOADS["dense_f32_960x2304x770"]
+    M, N, K = wl.dims
+    X, W = wl.inputs()
+    ref, bound = orc.gemm_nt(X, W, "f32")
+    y = run_gemm(X, W, "f32", M, N, K, f"{wl.name} {variant}")
+    r = assert_close(y, ref, bound, "f32", f"{wl.name} {variant}")
+    print(f"{wl.name} {variant}: max err/tol {r:.3g}")
 
 
 def test_workload_trimul_f32_B8_T1024(orc):
