@@ -98,11 +98,11 @@ class Part:
         import causal_attention_score_amd as cas
         self.wl = wl
         self.cas = cas
-        if wl.kind == "gemm_nt":
+        if wl.kind in ("gemm_nt", "batch_matmul_nt"):
             X, W = wl.inputs()
             self.x, self.w = device_tensor(X, wl.dtype), device_tensor(W, wl.dtype)
-            M, N, _ = wl.dims
-            self.out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            shape = wl.dims[:2] if wl.kind == "gemm_nt" else (wl.dims[0], wl.dims[1], wl.dims[2])
+            self.out = torch.empty(shape, dtype=torch.float32, device="cuda")
         else:
             (qkv,) = wl.inputs()
             B, T, NH, _ = wl.dims
@@ -113,6 +113,8 @@ class Part:
     def __call__(self):
         if self.wl.kind == "gemm_nt":
             self.cas.gemm_nt(self.x, self.w, out=self.out)
+        elif self.wl.kind == "batch_matmul_nt":
+            self.cas.batch_matmul_nt(self.x, self.w, out=self.out)
         else:
             self.cas.trimul_causal(self.qkv, self.NH, out=self.out)
 
@@ -169,13 +171,15 @@ def roofline_of(wl, ms: float, traffic_bytes):
 def local_padding_ab(steps: int):
     """The dense fp32 layer with local padding (predicates only at fetch and
     writeback) against the same kernel with the bounds checks kept inside the
-    MFMA loop (CAS_VARIANT=predicated), on the 1024-wide layer and on the
-    DietCode shape (H = 2304)."""
+    MFMA loop (CAS_VARIANT=predicated), on the 1024-wide layer, on the
+    DietCode shape (H = 2304), and on DietCode's BatchMatmulNT heads
+    (192 x 120 x 120 x 64, full-size LDS tiles at T = 120); plus the causal
+    scores of those heads (ragged T)."""
     import torch
 
     from causal_attention_score_amd import synth
     out = {}
-    for name in ("dense_f32_960x1024x770", "dense_f32_960x2304x770"):
+    for name in ("dense_f32_960x1024x770", "dense_f32_960x2304x770", "bmm_nt_f32_192x120x120x64"):
         wl = synth.WORKLOADS[name]
         log(f"local-padding A/B on {name}")
         p = Part(wl)
@@ -193,9 +197,20 @@ def local_padding_ab(steps: int):
         if name.endswith("2304x770"):
             res["pages_context"] = ("DietCode on NVIDIA RTX: 0.98 vs 11.6 TFLOP/s (3090), 0.43 vs 5.27 (2080 Ti), "
                                     "baseline vs local padding; another machine, not a target")
+        if name.startswith("bmm_nt"):
+            res["pages_context"] = ("DietCode on NVIDIA RTX: 3.5 vs 8.7 TFLOP/s (3090), 1.8 vs 5.5 (2080 Ti), "
+                                    "shrunk workspace vs local padding; another machine, not a target")
         out[name] = res
         del p
         torch.cuda.empty_cache()
+    wl = synth.WORKLOADS["trimul_f32_B16_T120_NH12_HS64"]
+    p = Part(wl)
+    _, (ms,), _ = time_parts([p], steps, 3)
+    out[wl.name] = {"avg_launch_us": round(ms * 1e3, 2),
+                    "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
+                    "roofline": roofline_of(wl, ms, None)}
+    del p
+    torch.cuda.empty_cache()
     return out
 
 

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libcas.so")
 CAS_F32, CAS_BF16, CAS_F16 = 0, 1, 2
 STATUS = {0: "CAS_OK", -1: "CAS_ERR_NULL", -2: "CAS_ERR_SHAPE", -3: "CAS_ERR_DTYPE",
           -4: "CAS_ERR_ALIAS", -5: "CAS_ERR_DEVICE", -6: "CAS_ERR_HIP"}
-EXPORTS = ("cas_gemm_nt", "cas_trimul_causal", "cas_status_string", "cas_last_hip_error", "cas_version")
+EXPORTS = ("cas_gemm_nt", "cas_batch_matmul_nt", "cas_trimul_causal", "cas_status_string", "cas_last_hip_error",
+           "cas_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -40,6 +41,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.cas_gemm_nt.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [ctypes.c_int, ctypes.c_int, _vp]
         L.cas_gemm_nt.restype = ctypes.c_int
+        L.cas_batch_matmul_nt.argtypes = [_vp, _vp, _vp] + [_i64] * 10 + [ctypes.c_int, ctypes.c_int, _vp]
+        L.cas_batch_matmul_nt.restype = ctypes.c_int
         L.cas_trimul_causal.argtypes = [_vp, _vp] + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
         L.cas_trimul_causal.restype = ctypes.c_int
         L.cas_status_string.argtypes = [ctypes.c_int]
@@ -108,6 +111,37 @@ def gemm_nt(x, w, out=None):
     st = lib().cas_gemm_nt(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, ldx, ldw, ldy,
                            _dtype_code(x), CAS_F32, _stream_ptr(x.device))
     _check("cas_gemm_nt", st)
+    return out
+
+
+def batch_matmul_nt(x, w, out=None):
+    """Y[b] = x[b] @ w[b].T for every b, fp32 accumulation and output.
+
+    x: [batch, M, K] and w: [batch, N, K] of one dtype (float32, bfloat16,
+    float16), rows contiguous (any row pitch and batch stride; a batch stride
+    of 0, as from expand(), repeats one block); out: optional [batch, M, N]
+    float32 with contiguous rows. Runs on the current stream of x's device."""
+    import torch
+    if x.dim() != 3 or w.dim() != 3 or x.shape[0] != w.shape[0] or x.shape[2] != w.shape[2]:
+        raise ValueError("batch_matmul_nt expects x [batch, M, K] and w [batch, N, K]")
+    if x.dtype != w.dtype:
+        raise TypeError("x and w must share a dtype")
+    if x.stride(2) != 1 or w.stride(2) != 1:
+        raise ValueError("rows of x and w must be contiguous")
+    Bt, M, K = x.shape
+    N = w.shape[1]
+    if out is None:
+        out = torch.empty((Bt, M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (Bt, M, N) or (N > 1 and out.stride(2) != 1):
+        raise ValueError("out must be a float32 [batch, M, N] tensor with contiguous rows")
+    _require_device(x, w, out)
+    ldx = x.stride(1) if M > 1 else K
+    ldw = w.stride(1) if N > 1 else K
+    ldy = out.stride(1) if M > 1 else N
+    st = lib().cas_batch_matmul_nt(x.data_ptr(), w.data_ptr(), out.data_ptr(), Bt, M, N, K, ldx, ldw, ldy,
+                                   x.stride(0), w.stride(0), out.stride(0), _dtype_code(x), CAS_F32,
+                                   _stream_ptr(x.device))
+    _check("cas_batch_matmul_nt", st)
     return out
 
 

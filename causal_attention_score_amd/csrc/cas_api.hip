@@ -44,6 +44,19 @@ bool extent(int64_t rows, int64_t cols, int64_t ld, int es, int64_t *bytes)
     return mul_ok(rows - 1, ld, &t) && add_ok(t, cols, &t) && mul_ok(t, es, bytes) && *bytes < (INT64_C(1) << 62);
 }
 
+// Byte extent of `batch` such blocks, block b starting bs elements after
+// block b-1: (batch-1)*bs*es + the extent of one block.
+bool batch_extent(int64_t batch, int64_t bs, int64_t block_bytes, int es, int64_t *bytes)
+{
+    if (batch == 0 || block_bytes == 0) {
+        *bytes = 0;
+        return true;
+    }
+    int64_t t;
+    return mul_ok(batch - 1, bs, &t) && mul_ok(t, es, &t) && add_ok(t, block_bytes, bytes) &&
+           *bytes < (INT64_C(1) << 62);
+}
+
 bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
 {
     if (na == 0 || nb == 0) return false;
@@ -137,6 +150,39 @@ CAS_EXPORT int cas_gemm_nt(const void *X, const void *W, void *Y, int64_t M, int
     const int64_t lens[3] = {K, ldx, ldw};
     const void *ptrs[2] = {X, W};
     const int vec = K > 0 ? pick_vec(es, lens, 3, ptrs, 2) : 1;
+    return launch_status(cas::launch_gemm_nt(a, in_dtype, vec, tile, (hipStream_t)stream));
+}
+
+CAS_EXPORT int cas_batch_matmul_nt(const void *X, const void *W, void *Y, int64_t batch, int64_t M, int64_t N,
+                                   int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int64_t bsx, int64_t bsw,
+                                   int64_t bsy, cas_dtype in_dtype, cas_dtype out_dtype, void *stream)
+{
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (batch < 0 || M < 0 || N < 0 || K < 0 || ldx < K || ldw < K || ldy < N || bsx < 0 || bsw < 0 || bsy < 0)
+        return CAS_ERR_SHAPE;
+    if (batch == 0 || M == 0 || N == 0) return CAS_OK;
+    if (!Y || (K > 0 && (!X || !W))) return CAS_ERR_NULL;
+    const int es = elem_size(in_dtype);
+    int64_t xb, wb, yb, xt, wt, yt;
+    if (!extent(M, K, ldx, es, &xb) || !extent(N, K, ldw, es, &wb) || !extent(M, N, ldy, 4, &yb))
+        return CAS_ERR_SHAPE;
+    // Output blocks may not overlap one another (inputs may: bs = 0 repeats one).
+    if (batch > 1 && bsy * 4 < yb) return CAS_ERR_SHAPE;
+    if (!batch_extent(batch, bsx, xb, es, &xt) || !batch_extent(batch, bsw, wb, es, &wt) ||
+        !batch_extent(batch, bsy, yb, 4, &yt))
+        return CAS_ERR_SHAPE;
+    if (overlap(Y, yt, X, xt) || overlap(Y, yt, W, wt)) return CAS_ERR_ALIAS;
+
+    cas::GemmArgs a{X, W, (float *)Y, M, N, K, ldx, ldw, ldy, gemm_predicated(), batch, bsx, bsw, bsy};
+    const int tile = gemm_tile_override();
+    if (cas::gemm_nt_workgroups(a, in_dtype, tile) > INT32_MAX) return CAS_ERR_SHAPE;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+
+    // Vector loads must stay aligned in every block: the batch strides count too.
+    const int64_t lens[5] = {K, ldx, ldw, bsx, bsw};
+    const void *ptrs[2] = {X, W};
+    const int vec = K > 0 ? pick_vec(es, lens, 5, ptrs, 2) : 1;
     return launch_status(cas::launch_gemm_nt(a, in_dtype, vec, tile, (hipStream_t)stream));
 }
 

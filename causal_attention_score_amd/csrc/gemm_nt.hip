@@ -28,14 +28,20 @@ template <class E, int BM, int BN, int WGM, int WGN, int VEC, bool PRED>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 gemm_nt_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
                int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-               int64_t tiles_m, int64_t tiles_n)
+               int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t bsx, int64_t bsw, int64_t bsy)
 {
     using G = Engine<E, BM, BN, GemmBK<E>::v, WGM, WGN, VEC, PRED>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::STAGE];
 
     const int tid = threadIdx.x;
-    const int64_t nwg = tiles_m * tiles_n;
-    const int64_t pid = xcd_remap(blockIdx.x, nwg);
+    // Logical id = batch * tiles + tile; each XCD takes a contiguous range of
+    // them, so the products of one batch share that XCD's L2.
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t lid = xcd_remap(blockIdx.x, tiles * batch);
+    const int64_t b = lid / tiles, pid = lid - b * tiles;
+    X += b * bsx * G::ES;
+    W += b * bsw * G::ES;
+    Y += b * bsy;
     const int64_t group = GROUP_M * tiles_n;
     const int64_t first_m = (pid / group) * GROUP_M;
     const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
@@ -71,14 +77,15 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s)
 {
     using C = TileCfg<BM, BN>;
     const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    const dim3 grid((unsigned)(tm * tn * a.batch));
     if (a.predicated)
-        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, true>), dim3((unsigned)(tm * tn)),
-                           dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
-                           a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, true>), grid, dim3(C::WGM * C::WGN * 64),
+                           0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm,
+                           tn, a.batch, a.bsx, a.bsw, a.bsy);
     else
-        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, false>), dim3((unsigned)(tm * tn)),
+        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, false>), grid,
                            dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
-                           a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+                           a.K, a.ldx, a.ldw, a.ldy, tm, tn, a.batch, a.bsx, a.bsw, a.bsy);
     return hipGetLastError();
 }
 
@@ -101,7 +108,7 @@ int pick_tile(const GemmArgs &a, int tile)
 {
     if (tile == GEMM_TILE_64 || tile == GEMM_TILE_128) return tile;
     // Largest tile that still gives every CU (256) about one workgroup.
-    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.batch;
     return t128 >= 256 ? GEMM_TILE_128 : GEMM_TILE_64;
 }
 
@@ -117,13 +124,13 @@ hipError_t launch_elem(const GemmArgs &a, int vec, int tile, hipStream_t s)
 int64_t gemm_nt_workgroups(const GemmArgs &a, int /*elem*/, int tile)
 {
     const int bm = pick_tile(a, tile) == GEMM_TILE_128 ? 128 : 64;
-    return ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm);
+    return ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm) * a.batch;
 }
 
 hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s)
 {
     // 256 x 256 tiles where every CU gets one (M = N = 4096 and up).
-    if (elem != E_F32 && !a.predicated && gemm_wide_fits(a, 2, vec) &&
+    if (elem != E_F32 && !a.predicated && a.batch == 1 && gemm_wide_fits(a, 2, vec) &&
         (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256)))
         return launch_gemm_wide(a, elem, s);
     switch (elem) {

@@ -14,6 +14,8 @@ struct GemmArgs {
     float *Y;
     int64_t M, N, K, ldx, ldw, ldy;
     bool predicated = false; // bounds checks inside the MFMA loop (local-padding A/B)
+    int64_t batch = 1;       // independent products; batch b reads X + b*bsx, W + b*bsw, writes Y + b*bsy
+    int64_t bsx = 0, bsw = 0, bsy = 0; // batch strides in elements
 };
 
 struct TrimulArgs {

@@ -102,10 +102,10 @@ def trimul_inputs(B: int, T: int, NH: int, HS: int, dtype: str = "f32", seed: in
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "gemm_nt" or "trimul_causal"
+    kind: str            # "gemm_nt", "batch_matmul_nt" or "trimul_causal"
     dtype: str           # input storage type; outputs are fp32
     seed: int
-    dims: tuple          # gemm: (M, N, K); trimul: (B, T, NH, HS)
+    dims: tuple          # gemm: (M, N, K); batched: (batch, M, N, K); trimul: (B, T, NH, HS)
     dist: str = "normal"
     scale: float = 1.0   # multiplier applied in double before rounding
 
@@ -120,6 +120,10 @@ class Workload:
                 Bm = uniform01_f32(g, (K, N))
                 return to_storage(A, self.dtype), to_storage(np.ascontiguousarray(Bm.T), self.dtype)
             return gemm_inputs(M, N, K, self.dtype, self.seed, self.dist, self.scale)
+        if self.kind == "batch_matmul_nt":
+            Bt, M, N, K = self.dims
+            X, W = gemm_inputs(Bt * M, Bt * N, K, self.dtype, self.seed, self.dist, self.scale)
+            return X.reshape(Bt, M, K), W.reshape(Bt, N, K)
         B, T, NH, HS = self.dims
         return (trimul_inputs(B, T, NH, HS, self.dtype, self.seed, self.dist),)
 
@@ -127,6 +131,9 @@ class Workload:
         if self.kind == "gemm_nt":
             M, N, K = self.dims
             return 2 * M * N * K
+        if self.kind == "batch_matmul_nt":
+            Bt, M, N, K = self.dims
+            return 2 * Bt * M * N * K
         B, T, NH, HS = self.dims
         return 2 * HS * B * NH * T * (T + 1) // 2
 
@@ -137,6 +144,9 @@ class Workload:
         if self.kind == "gemm_nt":
             M, N, K = self.dims
             return es * (M * K + N * K) + 4 * M * N
+        if self.kind == "batch_matmul_nt":
+            Bt, M, N, K = self.dims
+            return Bt * (es * (M * K + N * K) + 4 * M * N)
         B, T, NH, HS = self.dims
         return es * 2 * B * T * NH * HS + 4 * B * NH * T * T
 
@@ -152,6 +162,13 @@ WORKLOADS = {
     # T=60, I=770, H=2304): the same inputs recipe as the 1024-wide layer.
     "dense_f32_960x2304x770": Workload("dense_f32_960x2304x770", "gemm_nt", "f32", 6,
                                        (960, 2304, 770), "normal", 1.0 / np.sqrt(770.0)),
+    # BatchMatmulNT of DietCode's test_local_padding_ii (B=16, T=120, H=768,
+    # NH=12: B*NH = 192 heads of 120 x 120 x 64), and the causal scores of the
+    # same heads read from packed QKV (ragged T: 120 is not a tile multiple).
+    "bmm_nt_f32_192x120x120x64": Workload("bmm_nt_f32_192x120x120x64", "batch_matmul_nt", "f32", 7,
+                                          (192, 120, 120, 64)),
+    "trimul_f32_B16_T120_NH12_HS64": Workload("trimul_f32_B16_T120_NH12_HS64", "trimul_causal", "f32", 8,
+                                              (16, 120, 12, 64)),
     "trimul_bf16_B4_T4096_NH25_HS64": Workload("trimul_bf16_B4_T4096_NH25_HS64", "trimul_causal",
                                                "bf16", 5, (4, 4096, 25, 64)),
 }

@@ -1,10 +1,11 @@
 /*
  * cas.h -- C ABI of the MI355X (gfx950) tiled-matmul hot path.
  *
- * Two operations, both hand-written CDNA4 kernels with fp32 accumulation:
+ * Hand-written CDNA4 kernels with fp32 accumulation:
  *
- *   cas_gemm_nt        dense Y = X W^T over ragged shapes
- *   cas_trimul_causal  causal attention scores read straight from packed QKV
+ *   cas_gemm_nt          dense Y = X W^T over ragged shapes
+ *   cas_batch_matmul_nt  the same over a batch of independent products
+ *   cas_trimul_causal    causal attention scores read straight from packed QKV
  *
  * Conventions shared by every entry point
  *   - Pointers X, W, Y, qkv, out are DEVICE pointers (hipMalloc or any
@@ -63,6 +64,27 @@ int cas_gemm_nt(const void *X, const void *W, void *Y,
                 int64_t M, int64_t N, int64_t K,
                 int64_t ldx, int64_t ldw, int64_t ldy,
                 cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * Batched NT product (DietCode tests/codegen/test_1_local_padding.py,
+ * test_local_padding_ii docstring: BatchMatmulNT over B*NH independent heads,
+ * Y[i,j,k] += X[i,j,l] * W[i,k,l]):
+ *
+ *   Y[b*bsy + m*ldy + n] = sum_{k<K} X[b*bsx + m*ldx + k] * W[b*bsw + n*ldw + k]
+ *                                       for b < batch, m < M, n < N
+ *
+ * Each block b is the dense product of cas_gemm_nt, with the same pitches,
+ * dtypes, ragged-shape handling and K == 0 behaviour. Batch strides bsx, bsw,
+ * bsy are in elements, >= 0; an input stride of 0 repeats one block for every
+ * b. Output blocks may not overlap (bsy must cover one block:
+ * bsy >= (M-1)*ldy + N when batch > 1), else CAS_ERR_SHAPE.
+ * batch == 0, M == 0 or N == 0: nothing is written (OK).
+ */
+int cas_batch_matmul_nt(const void *X, const void *W, void *Y, int64_t batch,
+                        int64_t M, int64_t N, int64_t K,
+                        int64_t ldx, int64_t ldw, int64_t ldy,
+                        int64_t bsx, int64_t bsw, int64_t bsy,
+                        cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
 
 /*
  * Causal attention scores (llm.c dev/cuda/trimat_forward.cu, trimul_cpu, the

@@ -96,6 +96,21 @@ class Oracle:
             raise ValueError("oracle_gemm_nt rejected its arguments")
         return Y, bound
 
+    def batch_matmul_nt(self, X: np.ndarray, W: np.ndarray, dtype: str = "f32", with_bound: bool = True):
+        """BatchMatmulNT (DietCode test_1_local_padding.py, test_local_padding_ii
+        docstring): Y[i] = X[i] W[i]^T for every batch index i, each block the
+        dense product above. X is [batch, M, K], W is [batch, N, K]."""
+        Bt, M, K = X.shape
+        N = W.shape[1]
+        Y = np.zeros((Bt, M, N), dtype=np.float32)
+        bound = np.zeros((Bt, M, N), dtype=np.float64) if with_bound else None
+        for i in range(Bt):
+            y, b = self.gemm_nt(X[i], W[i], dtype, with_bound=with_bound)
+            Y[i] = y
+            if with_bound:
+                bound[i] = b
+        return Y, bound
+
     def trimul_causal(self, qkv: np.ndarray, B: int, T: int, C: int, NH: int,
                       dtype: str = "f32", with_bound: bool = True):
         raw = self._raw(qkv, dtype)

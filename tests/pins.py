@@ -136,6 +136,22 @@ def pin_gemm_bruteforce_random(orc):
                     assert abs(Fraction(float(bound[m, n])) - Se[m][n]) <= Se[m][n] * Fraction(1, 2 ** 48)
 
 
+def pin_batch_matmul_bruteforce(orc):
+    """Every block of the batched product is its own exact dense product
+    (a wrong batch index for X or W, or a transposed block, fails)."""
+    for dtype in ("f32", "bf16"):
+        Bt, M, N, K = 3, 2, 3, 5
+        X, W = synth.gemm_inputs(Bt * M, Bt * N, K, dtype, 21, dist="int")
+        X, W = X.reshape(Bt, M, K), W.reshape(Bt, N, K)
+        Y, bound = orc.batch_matmul_nt(X, W, dtype)
+        for i in range(Bt):
+            Ye, Se = exact_gemm(X[i], W[i], dtype, orc)
+            for m in range(M):
+                for n in range(N):
+                    assert bits(Y[i, m, n]) == bits(f32_round(Ye[m][n])), (dtype, i, m, n)
+                    assert Fraction(float(bound[i, m, n])) == Se[m][n], (dtype, i, m, n)
+
+
 def pin_gemm_strided(orc):
     """Row pitches larger than K: only the first K entries of a row count."""
     M, N, K, ldx, ldw, ldy = 5, 4, 3, 7, 6, 9

@@ -51,6 +51,16 @@ def g(L, X=PX, W=PW, Y=PY, M=4, N=5, K=6, ldx=None, ldw=None, ldy=None, ind=F32,
                          N if ldy is None else ldy, ind, outd, None)
 
 
+def bm(L, X=PX, W=PW, Y=PY, batch=3, M=4, N=5, K=6, ldx=None, ldw=None, ldy=None, bsx=None, bsw=None, bsy=None,
+       ind=F32, outd=F32):
+    ldx = K if ldx is None else ldx
+    ldw = K if ldw is None else ldw
+    ldy = N if ldy is None else ldy
+    return L.cas_batch_matmul_nt(X, W, Y, batch, M, N, K, ldx, ldw, ldy,
+                                 M * ldx if bsx is None else bsx, N * ldw if bsw is None else bsw,
+                                 M * ldy if bsy is None else bsy, ind, outd, None)
+
+
 def t(L, qkv=PX, out=PY, B=2, T=5, C=12, NH=3, ind=F32, outd=F32):
     return L.cas_trimul_causal(qkv, out, B, T, C, NH, ind, outd, None)
 
@@ -82,6 +92,30 @@ def test_gemm_k0_needs_no_inputs(L):
     # K == 0 writes zeros: X and W may be NULL; with no GPU the call stops at
     # the device check.
     assert g(L, X=None, W=None, K=0) == EDEV
+
+
+def test_batch_matmul_rejections(L):
+    assert bm(L, ind=9) == EDTYPE
+    assert bm(L, outd=F16) == EDTYPE
+    assert bm(L, batch=-1) == ESHAPE
+    assert bm(L, bsx=-1) == ESHAPE
+    assert bm(L, ldy=4) == ESHAPE
+    assert bm(L, bsy=4 * 5 - 1) == ESHAPE   # output blocks would overlap
+    assert bm(L, Y=None) == ENULL
+    assert bm(L, W=None) == ENULL
+    assert bm(L, Y=PX + 2 * 4 * 6 * 4) == EALIAS   # output starts inside the third X block
+    assert bm(L, X=PY + 2 * 4 * 5 * 4, bsx=0) == EALIAS  # X inside the last output block
+    assert bm(L, batch=2**40, bsy=2**30) == ESHAPE      # byte extent above 2^62
+
+
+def test_batch_matmul_empty_and_broadcast_reach_the_device_check(L):
+    import torch
+    assert bm(L, batch=0) == OK
+    assert bm(L, M=0) == OK
+    assert bm(L, X=None, W=None, Y=None, batch=0) == OK
+    if not torch.cuda.is_available():
+        assert bm(L, bsw=0) == EDEV     # one W block for every batch: valid
+        assert bm(L, batch=1, bsy=0) == EDEV
 
 
 def test_trimul_rejections(L):

@@ -153,6 +153,94 @@ def test_gemm_strided_misaligned(orc, dtype):
     assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
 
 
+# ------------------------------------------------------- batch_matmul_nt
+
+BMM_SHAPES = [(192, 120, 120, 64), (3, 65, 33, 127), (5, 1, 257, 129), (7, 200, 72, 3), (2, 128, 128, 128),
+              (4, 15, 9, 12)]
+
+
+def run_bmm(X, W, dtype, label):
+    Bt, M, K = X.shape
+    N = W.shape[1]
+    n = Bt * M * N
+    buf, flat = guarded_output(n)
+    case(f"{label} batch_matmul_nt {dtype} batch={Bt} M={M} N={N} K={K}")
+    cas.batch_matmul_nt(to_device(X, dtype), to_device(W, dtype), out=flat.view(Bt, M, N))
+    torch.cuda.synchronize()
+    check_guards(buf, n)
+    return flat.view(Bt, M, N).cpu().numpy()
+
+
+@pytest.mark.parametrize("tile", ["64", "128"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", BMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bmm_ragged(orc, monkeypatch, shape, dtype, tile):
+    monkeypatch.setenv("CAS_GEMM_TILE", tile)
+    Bt, M, N, K = shape
+    X, W = synth.gemm_inputs(Bt * M, Bt * N, K, dtype, seed=Bt + M + N + K)
+    X, W = X.reshape(Bt, M, K), W.reshape(Bt, N, K)
+    ref, bound = orc.batch_matmul_nt(X, W, dtype)
+    y = run_bmm(X, W, dtype, f"tile{tile}")
+    assert_close(y, ref, bound, dtype, f"bmm {shape} {dtype} tile{tile}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bmm_predicated(orc, monkeypatch, dtype):
+    monkeypatch.setenv("CAS_VARIANT", "predicated")
+    Bt, M, N, K = 24, 120, 120, 64
+    X, W = synth.gemm_inputs(Bt * M, Bt * N, K, dtype, seed=31)
+    X, W = X.reshape(Bt, M, K), W.reshape(Bt, N, K)
+    ref, bound = orc.batch_matmul_nt(X, W, dtype)
+    y = run_bmm(X, W, dtype, "predicated")
+    assert_close(y, ref, bound, dtype, f"bmm predicated {dtype}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bmm_strides_and_broadcast(orc, dtype):
+    """Batch strides above one block, odd row pitches, one W block for every
+    batch (stride 0), and an output batch stride that leaves gaps: the gaps
+    and the pitch padding keep their sentinel."""
+    Bt, M, N, K = 5, 37, 29, 50
+    ldx, ldw, ldy = K + 3, K + 1, N + 5
+    bsx, bsy = M * ldx + 7, M * ldy + 11
+    g = np.random.default_rng(7)
+    Xf = synth.to_storage(g.standard_normal((Bt * bsx,)).astype(np.float32), dtype)
+    Wf = synth.to_storage(g.standard_normal((N * ldw,)).astype(np.float32), dtype)
+    Xb = np.stack([Xf[b * bsx:b * bsx + M * ldx].reshape(M, ldx)[:, :K] for b in range(Bt)])
+    Wb = np.stack([Wf.reshape(N, ldw)[:, :K]] * Bt)
+    ref, bound = orc.batch_matmul_nt(np.ascontiguousarray(Xb), np.ascontiguousarray(Wb), dtype)
+    dx, dw = to_device(Xf, dtype), to_device(Wf, dtype)
+    x = dx.as_strided((Bt, M, K), (bsx, ldx, 1))
+    w = dw.as_strided((Bt, N, K), (0, ldw, 1))
+    n = Bt * bsy
+    buf, flat = guarded_output(n)
+    y = flat.as_strided((Bt, M, N), (bsy, ldy, 1))
+    case(f"bmm strides/broadcast {dtype}")
+    cas.batch_matmul_nt(x, w, out=y)
+    torch.cuda.synchronize()
+    check_guards(buf, n)
+    h = flat.cpu().numpy()
+    got = np.stack([h[b * bsy:b * bsy + M * ldy].reshape(M, ldy)[:, :N] for b in range(Bt)])
+    assert_close(got, ref, bound, dtype, "bmm strides")
+    mask = np.ones(n, dtype=bool)
+    for b in range(Bt):
+        for m in range(M):
+            mask[b * bsy + m * ldy:b * bsy + m * ldy + N] = False
+    assert np.all(h[mask].view(np.int32) == SENTINEL), "wrote outside the output blocks"
+
+
+def test_bmm_k0_and_empty():
+    x = torch.empty((3, 5, 0), device="cuda")
+    w = torch.empty((3, 7, 0), device="cuda")
+    buf, flat = guarded_output(105)
+    case("bmm K=0")
+    cas.batch_matmul_nt(x, w, out=flat.view(3, 5, 7))
+    torch.cuda.synchronize()
+    check_guards(buf, 105)
+    assert np.all(flat.cpu().numpy() == 0)
+    assert cas.batch_matmul_nt(torch.zeros((0, 4, 8), device="cuda"), torch.zeros((0, 3, 8), device="cuda")).shape == (0, 4, 3)
+
+
 def test_gemm_k0_writes_zeros():
     x = torch.empty((5, 0), device="cuda")
     w = torch.empty((7, 0), device="cuda")
@@ -330,6 +418,32 @@ def test_workload_dense_f32_960x2304x770(orc, monkeypatch, variant):
     y = run_gemm(X, W, "f32", M, N, K, f"{wl.name} {variant}")
     r = assert_close(y, ref, bound, "f32", f"{wl.name} {variant}")
     print(f"{wl.name} {variant}: max err/tol {r:.3g}")
+
+
+@pytest.mark.parametrize("variant", ["local_padding", "predicated"])
+def test_workload_bmm_nt_f32_192x120x120x64(orc, monkeypatch, variant):
+    """DietCode's BatchMatmulNT heads, whole output, both variants, in the
+    launch configuration bench.py times."""
+    if variant == "predicated":
+        monkeypatch.setenv("CAS_VARIANT", "predicated")
+    wl = synth.WORKLOADS["bmm_nt_f32_192x120x120x64"]
+    X, W = wl.inputs()
+    ref, bound = orc.batch_matmul_nt(X, W, "f32")
+    y = run_bmm(X, W, "f32", f"{wl.name} {variant}")
+    r = assert_close(y, ref, bound, "f32", f"{wl.name} {variant}")
+    print(f"{wl.name} {variant}: max err/tol {r:.3g}")
+
+
+def test_workload_trimul_f32_B16_T120(orc):
+    """Ragged-T causal scores of the same heads, from packed QKV, whole output."""
+    wl = synth.WORKLOADS["trimul_f32_B16_T120_NH12_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+    case(f"{wl.name} full size")
+    out = cas.trimul_causal(to_device(qkv, "f32").view(B, T, 3 * NH * HS), NH)
+    torch.cuda.synchronize()
+    assert_scores(out.cpu().numpy(), ref, bound, "f32", wl.name)
 
 
 def test_workload_trimul_f32_B8_T1024(orc):
