@@ -38,6 +38,7 @@ class Oracle:
         lib.oracle_trimul_causal_rows.argtypes = [_vp, _vp, _vp] + [_i64] * 8 + [ctypes.c_int]
         lib.oracle_tiled_matmul_count.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [_vp]
         lib.oracle_decode.argtypes = [_vp, ctypes.c_int, _i64, _vp]
+        lib.oracle_round16.argtypes = [_vp, _vp, _i64, ctypes.c_int]
         lib.oracle_trimul_scale.argtypes = [_i64]
         lib.oracle_trimul_scale.restype = ctypes.c_float
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -72,6 +73,15 @@ class Oracle:
         if rc:
             raise ValueError("oracle_decode rejected its arguments")
         return out.reshape(raw.shape)
+
+    def round16(self, a: np.ndarray, dtype: str) -> np.ndarray:
+        """binary32 -> bfloat16 / binary16 bit patterns (uint16), nearest even."""
+        src = np.ascontiguousarray(a, dtype=np.float32)
+        out = np.empty(src.shape, dtype=np.uint16)
+        rc = self.lib.oracle_round16(self._p(src), self._p(out), src.size, DTYPE_CODE[dtype])
+        if rc:
+            raise ValueError("oracle_round16 rejected its arguments")
+        return out
 
     def trimul_scale(self, hs: int) -> np.float32:
         return np.float32(self.lib.oracle_trimul_scale(hs))

@@ -121,6 +121,59 @@ float oracle_trimul_scale(int64_t HS)
 
 static const uint32_t QNAN_BITS = 0x7FC00000u;
 
+/* A 16-bit score output is the binary32 score rounded once more, to the
+ * nearest representable value of the 16-bit format (ties to even).
+ *
+ * bfloat16 keeps binary32's sign and 8-bit exponent and the top 7 fraction
+ * bits, so rounding works on the bit pattern: add half a unit of the 16th
+ * bit (minus one when the kept last bit is even, so ties go to even) and
+ * truncate. This carries into the exponent exactly when the value rounds up
+ * across a binade, and into infinity above the largest finite bfloat16.
+ *
+ * binary16 has a 5-bit exponent (bias 15, normals from 2^-14) and 10
+ * fraction bits. Every binary32 value is exact in double, and so is its
+ * quotient by a power of two, so the rounding is one rint() (the default
+ * round-to-nearest-even mode) of the value measured in units of the last
+ * place: 2^-24 for subnormals, 2^(e-10) in binade [2^e, 2^(e+1)). */
+static uint16_t round_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u; /* NaN */
+    const uint32_t even = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + even) >> 16);
+}
+
+static uint16_t round_f16(float f)
+{
+    const double x = (double)f;
+    if (isnan(x)) return 0x7E00u;
+    const uint16_t sign = signbit(x) ? 0x8000u : 0;
+    const double a = fabs(x);
+    if (a >= 65520.0) return sign | 0x7C00u; /* at or past the midpoint above 65504: infinity */
+    if (a < ldexp(1.0, -14)) {               /* subnormal range: units of 2^-24 */
+        const double q = rint(ldexp(a, 24)); /* may reach 1024 = the smallest normal */
+        return sign | (uint16_t)q;
+    }
+    int e;
+    (void)frexp(a, &e);                      /* a = m * 2^e, m in [0.5, 1): binade [2^(e-1), 2^e) */
+    e -= 1;
+    double q = rint(ldexp(a, 10 - e));       /* significand in units of the last place: [1024, 2048] */
+    if (q >= 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return sign | 0x7C00u;
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0);
+}
+
+int oracle_round16(const float *in, uint16_t *out, int64_t n, int dtype)
+{
+    if (!in || !out || n < 0 || (dtype != 1 && dtype != 2)) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = dtype == 1 ? round_bf16(in[i]) : round_f16(in[i]);
+    return 0;
+}
+
 /* llm.c trimat_forward.cu, trimul_cpu (the "Referee" of Chapter I):
  * inp is (B, T, 3, NH, HS); query row t of head nh starts at
  * b*T*3C + t*3C + nh*HS, the key row t2 at the same place plus C; for

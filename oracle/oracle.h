@@ -37,6 +37,12 @@ int oracle_gemm_nt(const void *X, const void *W, float *Y, double *bound,
 int oracle_trimul_causal(const void *qkv, float *out, double *bound,
                          int64_t B, int64_t T, int64_t C, int64_t NH, int dtype);
 
+/* Storage rounding of a 16-bit score output: n binary32 values to
+ * bfloat16 (dtype 1) or IEEE binary16 (dtype 2) bit patterns, to nearest
+ * with ties to even, overflow to infinity, subnormals kept; every NaN
+ * becomes the quiet NaN 0x7FC0 (bfloat16) or 0x7E00 (binary16). */
+int oracle_round16(const float *in, uint16_t *out, int64_t n, int dtype);
+
 /* Rows t in [t0, t1) of plane (b, nh) only; out/bound are (t1-t0) x T. */
 int oracle_trimul_causal_rows(const void *qkv, float *out, double *bound,
                               int64_t B, int64_t T, int64_t C, int64_t NH,

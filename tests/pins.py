@@ -152,6 +152,53 @@ def pin_batch_matmul_bruteforce(orc):
                     assert Fraction(float(bound[i, m, n])) == Se[m][n], (dtype, i, m, n)
 
 
+def pin_round16_against_libraries(orc):
+    """16-bit storage rounding against numpy's binary16 conversion and
+    torch's bfloat16 conversion (both round to nearest even), over random
+    values of every magnitude, every binary16 tie, and the edges."""
+    import torch
+    g = np.random.default_rng(5)
+    mags = np.exp2(g.uniform(-30, 20, 200000)).astype(np.float32)
+    vals = mags * np.where(g.random(mags.size) < 0.5, -1, 1).astype(np.float32)
+    bits32 = g.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    rand_bits = bits32.view(np.float32)
+    rand_bits = rand_bits[~np.isnan(rand_bits)]
+    # binary16 ties: halfway between neighbours (exact in binary32)
+    h = np.arange(0, 0x7BFF, dtype=np.uint16).view(np.float16).astype(np.float64)
+    hn = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    ties = ((h + hn) / 2).astype(np.float32)
+    edges = np.array([0.0, -0.0, 65504.0, 65519.996, 65520.0, 65536.0, 1e30, -1e30, np.inf, -np.inf,
+                      2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+                      3.3895314e38, 3.4028235e38, 1.1754944e-38, 1e-45], dtype=np.float32)
+    for x in (vals, rand_bits, ties, edges):
+        f16 = orc.round16(x, "f16")
+        with np.errstate(over="ignore"):  # values past the binary16 range become infinity
+            ref16 = x.astype(np.float16).view(np.uint16)
+        assert np.array_equal(f16, ref16), "binary16 rounding"
+        b16 = orc.round16(x, "bf16")
+        ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(b16, ref), "bfloat16 rounding"
+    nan = np.array([np.nan, -np.nan], dtype=np.float32)
+    assert np.all(orc.round16(nan, "bf16") == 0x7FC0) and np.all(orc.round16(nan, "f16") == 0x7E00)
+
+
+def pin_round16_worked_values(orc):
+    """Hand-derived cases: binary16 keeps 11 significant bits, so 1 + 2^-11
+    is a tie between 1 and 1 + 2^-10 and goes to the even 1, while
+    1 + 3*2^-11, a tie between 1 + 2^-10 and 1 + 2^-9, goes to the even
+    1 + 2^-9; bfloat16 keeps 8 significant bits (ties at 2^-8 likewise)."""
+    cases16 = [(1.0 + 2.0 ** -11, 0x3C00),           # tie below: even 1.0
+               (1.0 + 3 * 2.0 ** -11, 0x3C02),       # tie between 0x3C01 and 0x3C02: even 0x3C02
+               (65519.0, 0x7BFF), (65520.0, 0x7C00),  # the overflow midpoint goes to infinity
+               (2.0 ** -25, 0x0000), (3 * 2.0 ** -25, 0x0002), (2.0 ** -24, 0x0001)]
+    for v, b in cases16:
+        assert int(orc.round16(np.array([v], np.float32), "f16")[0]) == b, (v, hex(b))
+    cases_bf = [(1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82), (-2.0, 0xC000),
+                (3.3961775e38, 0x7F80)]                 # above the largest finite bfloat16: infinity
+    for v, b in cases_bf:
+        assert int(orc.round16(np.array([v], np.float32), "bf16")[0]) == b, (v, hex(b))
+
+
 def pin_gemm_strided(orc):
     """Row pitches larger than K: only the first K entries of a row count."""
     M, N, K, ldx, ldw, ldy = 5, 4, 3, 7, 6, 9

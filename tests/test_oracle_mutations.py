@@ -29,6 +29,10 @@ MUTATIONS = {
     "tile_b_count": ("loads += (ek - sk) * (en - sn);   /* tile of B */",
                      "loads += (ek - sk) * (em - sm);   /* tile of B */"),
     "output_perturbed": ("Y[m * ldy + n] = (float)acc;", "Y[m * ldy + n] = (float)(acc * (1.0 + 0x1p-20));"),
+    "bf16_ties_away": ("return (uint16_t)((u + 0x7FFFu + even) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    "f16_overflow_early": ("if (a >= 65520.0) return", "if (a > 65504.0) return"),
+    "f16_subnormal_unit": ("const double q = rint(ldexp(a, 24));", "const double q = rint(ldexp(a, 23));"),
+    "f16_truncates": ("double q = rint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
 }
 
 
