@@ -92,12 +92,13 @@ def read_traffic(kernel: str):
 class Part:
     """One entry point on one workload, with device buffers ready."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, out_dtype: str = "f32"):
         import torch
 
         import causal_attention_score_amd as cas
         self.wl = wl
         self.cas = cas
+        self.out_dtype = out_dtype
         if wl.kind in ("gemm_nt", "batch_matmul_nt"):
             X, W = wl.inputs()
             self.x, self.w = device_tensor(X, wl.dtype), device_tensor(W, wl.dtype)
@@ -108,7 +109,8 @@ class Part:
             B, T, NH, _ = wl.dims
             self.qkv = device_tensor(qkv, wl.dtype)
             self.NH = NH
-            self.out = torch.empty((B, NH, T, T), dtype=torch.float32, device="cuda")
+            tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
+            self.out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
 
     def __call__(self):
         if self.wl.kind == "gemm_nt":
@@ -146,20 +148,20 @@ def time_parts(parts, steps: int, warmup: int):
     return total / steps, per, wall / steps
 
 
-def roofline_of(wl, ms: float, traffic_bytes):
+def roofline_of(wl, ms: float, traffic_bytes, out_bytes: int = 4):
     """Roofline entry of one kernel from its average launch time. `traffic` is
     the measured HBM bytes per launch (rocprofv3 counters, committed under
     profiles/) over the same launch time, in the unit of `achieved` when the
     bound is HBM; null when no counters match the current kernel sources."""
     t = ms * 1e-3
     if wl.kind == "trimul_causal":
-        achieved = wl.algorithmic_bytes() / t / 1e9
+        achieved = wl.algorithmic_bytes(out_bytes) / t / 1e9
         traffic = round(traffic_bytes / t / 1e9, 1) if traffic_bytes else None
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "traffic_bytes_per_launch": traffic_bytes,
                 "kernel": f"trimul_causal {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
-                "algorithmic_bytes": wl.algorithmic_bytes()}
+                "algorithmic_bytes": wl.algorithmic_bytes(out_bytes)}
     achieved = wl.useful_flops() / t / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
@@ -312,14 +314,19 @@ def main():
     bf16 = None
     if not args.no_bf16:
         bf16 = {}
-        for name in ("dense_bf16_4096", "trimul_bf16_B4_T4096_NH25_HS64"):
+        # The two large shapes with 16-bit inputs; the scores also with 16-bit
+        # outputs (the fp32 scores rounded once more: half the bytes written).
+        for name, out in (("dense_bf16_4096", "f32"), ("trimul_bf16_B4_T4096_NH25_HS64", "f32"),
+                          ("trimul_bf16_B4_T4096_NH25_HS64", "bf16"), ("dense_f16_4096", "f32"),
+                          ("trimul_f16_B4_T4096_NH25_HS64", "f32"), ("trimul_f16_B4_T4096_NH25_HS64", "f16")):
             wl = synth.WORKLOADS[name]
-            log(f"timing {name}")
-            p = Part(wl)
+            key = name if out == "f32" else f"{name}_out_{out}"
+            log(f"timing {key}")
+            p = Part(wl, out)
             _, (ms,), _ = time_parts([p], max(5, args.steps // 5), 2)
-            bf16[name] = {"avg_launch_us": round(ms * 1e3, 2),
-                          "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
-                          "roofline": roofline_of(wl, ms, None)}
+            bf16[key] = {"avg_launch_us": round(ms * 1e3, 2), "out_dtype": out,
+                         "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
+                         "roofline": roofline_of(wl, ms, None, 4 if out == "f32" else 2)}
             del p
             torch.cuda.empty_cache()
 

@@ -145,12 +145,14 @@ def batch_matmul_nt(x, w, out=None):
     return out
 
 
-def trimul_causal(qkv, NH: int, out=None):
+def trimul_causal(qkv, NH: int, out=None, out_dtype=None):
     """Causal attention scores from packed QKV.
 
     qkv: contiguous (B, T, 3*C) or (B, T, 3, NH, HS) tensor (float32,
-    bfloat16 or float16); returns out (B, NH, T, T) float32 with
-    scale * Q.K on and below the diagonal and NaN above it."""
+    bfloat16 or float16); returns out (B, NH, T, T) with scale * Q.K on and
+    below the diagonal and NaN above it. out_dtype (or out's dtype): float32
+    (default), or bfloat16 / float16 for the fp32 scores rounded to that
+    format (half the output bytes)."""
     import torch
     if not qkv.is_contiguous():
         raise ValueError("qkv must be contiguous")
@@ -167,11 +169,13 @@ def trimul_causal(qkv, NH: int, out=None):
     else:
         raise ValueError("qkv must be (B, T, 3C) or (B, T, 3, NH, HS)")
     if out is None:
-        out = torch.empty((B, NH, T, T), dtype=torch.float32, device=qkv.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (B, NH, T, T) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 (B, NH, T, T) tensor")
+        out = torch.empty((B, NH, T, T), dtype=out_dtype or torch.float32, device=qkv.device)
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise TypeError("out does not have out_dtype")
+    if tuple(out.shape) != (B, NH, T, T) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, NH, T, T) tensor")
     _require_device(qkv, out)
     st = lib().cas_trimul_causal(qkv.data_ptr(), out.data_ptr(), B, T, C, NH,
-                                 _dtype_code(qkv), CAS_F32, _stream_ptr(qkv.device))
+                                 _dtype_code(qkv), _dtype_code(out), _stream_ptr(qkv.device))
     _check("cas_trimul_causal", st)
     return out

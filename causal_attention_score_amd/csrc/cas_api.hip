@@ -28,9 +28,15 @@ bool add_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_add_overflow(a
 
 int elem_size(cas_dtype d) { return d == CAS_F32 ? 4 : 2; }
 
-bool dtype_pair_ok(cas_dtype in, cas_dtype out)
+bool dtype_in_ok(cas_dtype in) { return in == CAS_F32 || in == CAS_BF16 || in == CAS_F16; }
+
+// Dense products: fp32 output.
+bool dtype_pair_ok(cas_dtype in, cas_dtype out) { return dtype_in_ok(in) && out == CAS_F32; }
+
+// Causal scores: fp32, bfloat16 or binary16 output.
+bool score_dtype_pair_ok(cas_dtype in, cas_dtype out)
 {
-    return (in == CAS_F32 || in == CAS_BF16 || in == CAS_F16) && out == CAS_F32;
+    return dtype_in_ok(in) && (out == CAS_F32 || out == CAS_BF16 || out == CAS_F16);
 }
 
 // Byte extent of `rows` rows of `cols` elements at pitch `ld`: ((rows-1)*ld + cols)*es.
@@ -189,16 +195,16 @@ CAS_EXPORT int cas_batch_matmul_nt(const void *X, const void *W, void *Y, int64_
 CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t T, int64_t C, int64_t NH,
                                  cas_dtype in_dtype, cas_dtype out_dtype, void *stream)
 {
-    if (!dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (!score_dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
     if (B < 0 || T < 0 || C < 0 || NH < 0) return CAS_ERR_SHAPE;
     if (B == 0 || T == 0 || NH == 0) return CAS_OK;
     if (C == 0 || C % NH != 0) return CAS_ERR_SHAPE;
     if (!qkv || !out) return CAS_ERR_NULL;
-    const int es = elem_size(in_dtype);
+    const int es = elem_size(in_dtype), ob = elem_size(out_dtype);
     int64_t in_elems, out_elems, t, c3, inb, outb;
     if (!mul_ok(3, C, &c3) || !mul_ok(B, T, &t) || !mul_ok(t, c3, &in_elems) || !mul_ok(in_elems, es, &inb))
         return CAS_ERR_SHAPE;
-    if (!mul_ok(B, NH, &t) || !mul_ok(t, T, &t) || !mul_ok(t, T, &out_elems) || !mul_ok(out_elems, 4, &outb))
+    if (!mul_ok(B, NH, &t) || !mul_ok(t, T, &t) || !mul_ok(t, T, &out_elems) || !mul_ok(out_elems, ob, &outb))
         return CAS_ERR_SHAPE;
     if (inb >= (INT64_C(1) << 62) || outb >= (INT64_C(1) << 62)) return CAS_ERR_SHAPE;
     // The kernels address a 64-row tile with 31-bit buffer offsets.
@@ -211,14 +217,15 @@ CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t 
     const int64_t HS = C / NH;
     cas::TrimulArgs a{};
     a.qkv = qkv;
-    a.out = (float *)out;
+    a.out = out;
     a.B = B;
     a.T = T;
     a.C = C;
     a.NH = NH;
     a.HS = HS;
     a.scale = (float)(1.0 / std::sqrt((double)HS)); // nearest fp32 to 1/sqrt(HS)
-    a.vec_store = (T % 4 == 0) && ((uintptr_t)out % 16 == 0);
+    a.vec_store = ((T * ob) % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    a.out_kind = (int)out_dtype;
     const int64_t lens[2] = {HS, C};
     const void *ptrs[1] = {qkv};
     const int vec = pick_vec(es, lens, 2, ptrs, 1);

@@ -20,10 +20,11 @@ struct GemmArgs {
 
 struct TrimulArgs {
     const void *qkv;
-    float *out;
+    void *out;
     int64_t B, T, C, NH, HS;
     float scale;
-    bool vec_store; // T % 4 == 0 and out is 16-byte aligned
+    bool vec_store; // output rows 16-byte aligned: T * out_bytes % 16 == 0 and out 16-byte aligned
+    int out_kind;   // 0 fp32, 1 bfloat16, 2 binary16 (the cas_dtype codes)
 };
 
 // Tile shapes the dense launcher can pick (exposed for tests and tuning).

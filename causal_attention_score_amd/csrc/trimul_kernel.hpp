@@ -46,6 +46,28 @@ constexpr int NTHREADS = 2 * NCOMP * 64;
 constexpr int TILE_BYTES = TB * TB * 4;
 constexpr unsigned QNAN_BITS = 0x7FC00000u;
 
+// Output element kinds of the scores: fp32, or the fp32 score rounded once
+// more to bfloat16 / binary16 (nearest even). The mask above the diagonal is
+// that format's quiet NaN. NAN_DW: the mask pattern filling one dword.
+struct OF32 {
+    static constexpr int OB = 4;
+    static constexpr uint32_t NAN_DW = QNAN_BITS;
+};
+struct OBF16 {
+    static constexpr int OB = 2;
+    static constexpr uint32_t NAN16 = 0x7FC0u, NAN_DW = 0x7FC07FC0u;
+};
+struct OF16 {
+    static constexpr int OB = 2;
+    static constexpr uint32_t NAN16 = 0x7E00u, NAN_DW = 0x7E007E00u;
+};
+__device__ __forceinline__ uint32_t round16(OBF16, float y) { return __builtin_bit_cast(unsigned short, (__bf16)y); }
+__device__ __forceinline__ uint32_t round16(OF16, float y) { return __builtin_bit_cast(unsigned short, (_Float16)y); }
+__device__ __forceinline__ void st_nt16(char *p, uint32_t v)
+{
+    __builtin_nontemporal_store((unsigned short)v, reinterpret_cast<unsigned short *>(p));
+}
+
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void st_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
@@ -89,7 +111,7 @@ struct Tile {
 };
 
 __device__ __forceinline__ Tile make_tile(const char *qkv, float *out, int64_t id, int64_t L, int64_t T, int64_t C,
-                                          int64_t NH, int64_t HS, int es)
+                                          int64_t NH, int64_t HS, int es, int ob = 4)
 {
     Tile tl;
     const int64_t plane = id / L;
@@ -105,7 +127,7 @@ __device__ __forceinline__ Tile make_tile(const char *qkv, float *out, int64_t i
     tl.s0 = j * TB;
     tl.q = qkv + ((b * T + tl.t0) * C3 + nh * HS) * es;
     tl.k = qkv + ((b * T + tl.s0) * C3 + C + nh * HS) * es;
-    tl.o = reinterpret_cast<char *>(out + plane * T * T);
+    tl.o = reinterpret_cast<char *>(out) + plane * T * T * ob;
     tl.rl = (int)((T - tl.t0) < TB ? (T - tl.t0) : TB);
     tl.cl = (int)((T - tl.s0) < TB ? (T - tl.s0) : TB);
     tl.diag = i == j;
@@ -261,6 +283,27 @@ __device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane
     }
 }
 
+// 16-bit output from the tile kernel's fp32 LDS tile (row-major, TB floats
+// per row): one element per lane and row, rounded on the way out, the fp32
+// mask pattern turned into the format's quiet NaN. (This kernel serves the
+// unaligned and wide-head shapes; the super-tile kernel has the fast path.)
+template <class O>
+__device__ __forceinline__ void lds_to_out16(const char *lds, const Tile &tl, int64_t T, int lane)
+{
+    for (int s = 0; s < TB; ++s) {
+        const float v = *reinterpret_cast<const float *>(lds + (s * TB + lane) * 4);
+        const uint32_t h = __float_as_uint(v) == QNAN_BITS ? O::NAN16 : round16(O{}, v);
+        if (s < tl.rl && lane < tl.cl) st_nt16(tl.o + ((tl.t0 + s) * T + tl.s0 + lane) * 2, h);
+    }
+}
+
+template <class O>
+__device__ __forceinline__ void nan_mirror16(const Tile &tl, int64_t T, int lane)
+{
+    for (int s = 0; s < TB; ++s)
+        if (s < tl.cl && lane < tl.rl) st_nt16(tl.o + ((tl.s0 + s) * T + tl.t0 + lane) * 2, O::NAN16);
+}
+
 // One step of a compute wave: the P register passes of tile `tl` (operands of
 // pass 0 already in ops[SB]), prefetching each next pass -- and after the last
 // pass the first pass of `nx` when has_next -- into the other buffer, then the
@@ -302,7 +345,7 @@ __device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile
 template <class E, int U, bool VEC16, int P>
 __global__ void __launch_bounds__(NTHREADS)
 trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, int64_t C, int64_t NH, int64_t HS,
-              int64_t L, int64_t items, float scale, int vec_store)
+              int64_t L, int64_t items, float scale, int vec_store, int out_kind)
 {
     constexpr int ES = E::ES;
     __shared__ __attribute__((aligned(16))) char lds[NCOMP * 2 * TILE_BYTES];
@@ -363,7 +406,17 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
         for (int64_t n = 0; n <= steps; ++n) {
             if (n >= 1) {
                 const int64_t pid = first + (n - 1) * stride + slot;
-                if (pid < hi) {
+                if (pid < hi && out_kind != 0) { // 16-bit output (out_kind is uniform)
+                    const Tile tl = make_tile(qkv, out, pid, L, T, C, NH, HS, ES, 2);
+                    const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
+                    if (out_kind == 1) {
+                        lds_to_out16<OBF16>(buf, tl, T, lane);
+                        if (!tl.diag) nan_mirror16<OBF16>(tl, T, lane);
+                    } else {
+                        lds_to_out16<OF16>(buf, tl, T, lane);
+                        if (!tl.diag) nan_mirror16<OF16>(tl, T, lane);
+                    }
+                } else if (pid < hi) {
                     const Tile tl = make_tile(qkv, out, pid, L, T, C, NH, HS, ES);
                     const uint32_t t4 = opaque_s(T4);
                     const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
@@ -417,8 +470,8 @@ constexpr int ST = 2 * TB;                    // super-tile edge
 constexpr int OP_ROWS = 2 * ST;               // 128 Q rows + 128 K rows
 constexpr int NCOMP_THREADS = NCOMP * 64;   // lanes of one role
 constexpr int SUPER_THREADS = 3 * NCOMP_THREADS;
-constexpr int OUT_PITCH = TB * 4 + 16;        // bytes per LDS output row (+16: bank skew)
-constexpr int OUT_BYTES = TB * OUT_PITCH;
+// LDS output rows: TB elements of the output type plus 16 bytes of bank skew.
+template <class O> constexpr int out_pitch() { return TB * O::OB + 16; }
 
 struct Super {
     uint32_t plane, T0, S0;
@@ -560,50 +613,100 @@ __device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, in
     }
 }
 
-// Scaled sub-tile -> LDS rows of OUT_PITCH bytes. Lane l holds output row
-// 32qb + l%32 and columns 32kb + 8g + 4(l/32) + 0..3 of acc[kb][qb][4g..].
-// DIAG: a sub-tile on the diagonal, whose entries right of it become NaN.
-template <bool DIAG>
+// Scaled sub-tile -> LDS rows of out_pitch<O>() bytes, already in the output
+// type. Lane l holds output row 32qb + l%32 and columns 32kb + 8g + 4(l/32)
+// + 0..3 of acc[kb][qb][4g..]: one 16-byte (fp32) or 8-byte (16-bit) write.
+// DIAG: a sub-tile on the diagonal, whose entries right of it are masked.
+template <bool DIAG, class O>
 __device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, int lane)
 {
+    constexpr int PITCH = out_pitch<O>();
     const int r32 = lane & 31, h4 = 4 * (lane >> 5);
-    const float qnan = __uint_as_float(QNAN_BITS);
-    const uint32_t lo = opaque((uint32_t)(r32 * OUT_PITCH + h4 * 4));
+    const uint32_t lo = opaque((uint32_t)(r32 * PITCH + h4 * O::OB));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4v v;
+                char *dst = lds + lo + (uint32_t)(32 * qb * PITCH + (32 * kb + 8 * g) * O::OB);
+                if constexpr (O::OB == 4) {
+                    const float qnan = __uint_as_float(QNAN_BITS);
+                    f32x4v v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float y = acc[kb][qb][4 * g + e] * scale;
-                    v[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? qnan : y;
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = acc[kb][qb][4 * g + e] * scale;
+                        v[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? qnan : y;
+                    }
+                    *reinterpret_cast<f32x4v *>(dst) = v;
+                } else {
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // The fp32 score first, then the 16-bit rounding: kept
+                        // apart so the multiply and the conversion do not fuse
+                        // into one rounding (a mixed-precision FMA would).
+                        float y32 = acc[kb][qb][4 * g + e] * scale;
+                        asm volatile("" : "+v"(y32));
+                        const uint32_t y = round16(O{}, y32);
+                        hv[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? O::NAN16 : y;
+                    }
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
                 }
-                *reinterpret_cast<f32x4v *>(lds + lo + (uint32_t)(32 * qb * OUT_PITCH + (32 * kb + 8 * g) * 4)) = v;
             }
 }
 
-// Rows [32H, 32H + 32) of the NaN mirror of a whole 64 x 64 tile, with
-// buffer stores whose row offset is a scalar: no vector ALU work per store.
-template <int H>
-__device__ __forceinline__ void nan_mirror_full(const Tile &tl, uint32_t T4, int lane)
+// Store geometry of a 64 x 64 output tile in 16-byte pieces: LPR lanes per
+// row, RPI rows per store instruction, NI instructions per tile, EPC
+// elements per piece.
+template <class O> struct Pieces {
+    static constexpr int LPR = TB * O::OB / 16, RPI = 64 / LPR, NI = TB / RPI, EPC = 16 / O::OB;
+};
+
+// Store one element (index e of a 16-byte piece) of the output type.
+template <class O> __device__ __forceinline__ void st_elem(char *p, const u32x4 &v, int e)
 {
-    constexpr int S0 = H * TB / 8, S1 = S0 + TB / 8; // groups of four rows
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tl.o + ((uint64_t)tl.s0 * (T4 / 4) + (uint64_t)tl.t0) * 4);
-    const uint32_t go = opaque((uint32_t)(lane >> 4) * T4 + (uint32_t)(lane & 15) * 16);
-    const u32x4 n4 = {QNAN_BITS, QNAN_BITS, QNAN_BITS, QNAN_BITS};
-#pragma unroll
-    for (int s = S0; s < S1; ++s) __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * 4) * T4), ST_NT);
+    if constexpr (O::OB == 4) st_nt(reinterpret_cast<float *>(p), __uint_as_float(v[e]));
+    else st_nt16(p, v[e >> 1] >> (16 * (e & 1)));
 }
 
-template <class E, int NCH>
+// Rows [32H, 32H + 32) of the NaN mirror of tile `tl` (rows s0.. of the
+// plane, columns t0..): whole tiles with buffer stores whose row offset is a
+// scalar (no vector ALU work per store); else masked to the plane, 16 bytes
+// at a time when rows are 16-byte aligned (vec), one element otherwise.
+template <int H, class O, bool FULL>
+__device__ __forceinline__ void nan_mirror_o(const Tile &tl, uint32_t T, uint32_t tby, int lane, bool vec)
+{
+    using PC = Pieces<O>;
+    char *base = tl.o + ((uint64_t)tl.s0 * T + (uint64_t)tl.t0) * O::OB;
+    const u32x4 n4 = {O::NAN_DW, O::NAN_DW, O::NAN_DW, O::NAN_DW};
+    const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC;
+    constexpr int S0 = H * PC::NI / 2, S1 = S0 + PC::NI / 2;
+    if (FULL) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc_at(base);
+        const uint32_t go = opaque((uint32_t)rr * tby + (uint32_t)(cc * O::OB));
+#pragma unroll
+        for (int s = S0; s < S1; ++s)
+            __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby), ST_NT);
+    } else if (vec) {
+        const uint32_t go = opaque((uint32_t)rr * tby + (uint32_t)(cc * O::OB));
+#pragma unroll
+        for (int s = S0; s < S1; ++s)
+            if (cc < tl.rl && s * PC::RPI + rr < tl.cl)
+                *reinterpret_cast<u32x4 *>(base + ((uint32_t)(s * PC::RPI) * tby + go)) = n4;
+    } else {
+        for (int s = H * TB / 2; s < H * TB / 2 + TB / 2; ++s)
+            if (s < tl.cl && lane < tl.rl) st_elem<O>(base + ((uint32_t)s * tby + (uint32_t)(lane * O::OB)), n4, 0);
+    }
+}
+
+template <class E, int NCH, class O>
 __global__ void __launch_bounds__(SUPER_THREADS)
-trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
+trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store)
 {
     constexpr int RB = NCH * 16;
+    constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
     __shared__ __attribute__((aligned(16))) char opb[OP_ROWS * RB];
     __shared__ __attribute__((aligned(16))) char outb[NCOMP * OUT_BYTES];
 
@@ -624,9 +727,9 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
     const uint32_t first = lo + blockIdx.x / 8;
     const uint32_t steps = first < hi ? (hi - first + wg_on_x - 1) / wg_on_x : 0;
 
-    const uint32_t T4 = T * 4u;
+    const uint32_t TBY = T * (uint32_t)O::OB; // bytes per output row
     const uint32_t ldb = 3u * C * (uint32_t)E::ES;
-    const bool vec4 = vec_store != 0;
+    const bool vec = vec_store != 0;          // rows 16-byte aligned
     Walker cur;
     cur.init(first < hi ? first : 0, wg_on_x, L, (T + ST - 1) / ST);
 
@@ -665,16 +768,17 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
             if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
             lds_barrier(); // X: operand rows consumed, previous tile read back
             if (live) {
-                if (sp.diag && sa == sb) subtile_to_lds<true>(acc, my_out, scale, lane);
-                else subtile_to_lds<false>(acc, my_out, scale, lane);
+                if (sp.diag && sa == sb) subtile_to_lds<true, O>(acc, my_out, scale, lane);
+                else subtile_to_lds<false, O>(acc, my_out, scale, lane);
             }
             lds_barrier(); // Y: tile n in LDS
         }
     } else {
         lds_barrier();
-        const int r4 = lane >> 4, c = (lane & 15) * 4;
-        const uint32_t li = (uint32_t)(r4 * OUT_PITCH + c * 4);
-        const float qnan = __uint_as_float(QNAN_BITS);
+        using PC = Pieces<O>;
+        const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC; // row in a group, first column
+        const uint32_t li = (uint32_t)(rr * PITCH + cc * O::OB);
+        const u32x4 n4 = {O::NAN_DW, O::NAN_DW, O::NAN_DW, O::NAN_DW};
         Tile pm;              // mirror of the previous step, second half pending
         bool pm_live = false, pm_full = false;
         for (uint32_t n = 0; n < steps; ++n) {
@@ -683,80 +787,78 @@ trimul_super_kernel(const char *__restrict__ qkv, float *__restrict__ out, uint3
             Tile tl;
             tl.t0 = sp.T0 + sa * TB;
             tl.s0 = sp.S0 + sb * TB;
-            tl.o = reinterpret_cast<char *>(out + (uint64_t)sp.plane * T * T);
+            tl.o = out + (uint64_t)sp.plane * T * T * O::OB;
             tl.rl = (int)((int64_t)T - tl.t0 < TB ? (int64_t)T - tl.t0 : TB);
             tl.cl = (int)((int64_t)T - tl.s0 < TB ? (int64_t)T - tl.s0 : TB);
             tl.diag = sp.diag;
             const bool inside = tl.rl > 0 && tl.cl > 0; // else the sub-tile lies past the plane edge
-            const uint32_t t4 = opaque_s(T4);
+            const uint32_t tby = opaque_s(TBY);
             const bool full = tl.rl == TB && tl.cl == TB;
             lds_barrier(); // X
             if (pm_live) { // second half of the previous step's mirror: needs nothing from LDS
-                if (pm_full) nan_mirror_full<1>(pm, t4, lane);
-                else nan_mirror<false, 1>(pm, t4, lane, vec4);
+                if (pm_full) nan_mirror_o<1, O, true>(pm, T, tby, lane, vec);
+                else nan_mirror_o<1, O, false>(pm, T, tby, lane, vec);
             }
             pm_live = false;
             lds_barrier(); // Y: tile n in LDS
             if (!inside) continue;
             const bool all_nan = sp.diag && sa == 0 && sb == 1; // wholly above the diagonal
-            char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * 4;
-            if (full && vec4) {
-                // Whole tile: one LDS read and one buffer store per four rows,
+            char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * O::OB;
+            const uint32_t go = opaque((uint32_t)rr * tby + (uint32_t)(cc * O::OB));
+            if (full && vec) {
+                // Whole tile: one LDS read and one buffer store per RPI rows,
                 // the row offset a scalar, so no vector ALU work: the SIMD's
                 // vector issue belongs to the compute wave's MFMAs.
                 const __amdgpu_buffer_rsrc_t rs = rsrc_at(dst);
-                const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
                 if (all_nan) {
-                    const u32x4 n4 = {QNAN_BITS, QNAN_BITS, QNAN_BITS, QNAN_BITS};
 #pragma unroll
-                    for (int s = 0; s < TB / 4; ++s)
-                        __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * 4) * t4), ST_NT);
+                    for (int s = 0; s < PC::NI; ++s)
+                        __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby),
+                                                               ST_NT);
                 } else {
 #pragma unroll
-                    for (int s = 0; s < TB / 4; ++s) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(my_out + li + s * 4 * OUT_PITCH);
-                        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)go, (int)((uint32_t)(s * 4) * t4), ST_NT);
+                    for (int s = 0; s < PC::NI; ++s) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby),
+                                                               ST_NT);
                     }
                 }
             } else {
-                const uint32_t go = opaque((uint32_t)r4 * t4 + (uint32_t)c * 4);
 #pragma unroll
-                for (int s = 0; s < TB / 4; ++s) {
-                    f32x4v v;
-                    if (all_nan) v = f32x4v{qnan, qnan, qnan, qnan};
-                    else v = *reinterpret_cast<const f32x4v *>(my_out + li + s * 4 * OUT_PITCH);
-                    const int row = s * 4 + r4;
-                    if (vec4) {
-                        if (c < tl.cl && row < tl.rl)
-                            st_nt4(reinterpret_cast<float *>(dst + ((uint32_t)(s * 4) * t4 + go)), v);
+                for (int s = 0; s < PC::NI; ++s) {
+                    const u32x4 v = all_nan ? n4 : *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
+                    const int row = s * PC::RPI + rr;
+                    if (vec) {
+                        if (cc < tl.cl && row < tl.rl)
+                            *reinterpret_cast<u32x4 *>(dst + ((uint32_t)(s * PC::RPI) * tby + go)) = v;
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (row < tl.rl && c + e < tl.cl)
-                                st_nt(reinterpret_cast<float *>(dst + ((uint32_t)row * t4 + (uint32_t)(c + e) * 4)), v[e]);
+                        for (int e = 0; e < PC::EPC; ++e)
+                            if (row < tl.rl && cc + e < tl.cl)
+                                st_elem<O>(dst + ((uint32_t)row * tby + (uint32_t)((cc + e) * O::OB)), v, e);
                     }
                 }
             }
             if (!tl.diag) { // first half of the mirror now, the second after the next X
                 pm = tl;
                 pm_live = true;
-                pm_full = full && vec4;
-                if (pm_full) nan_mirror_full<0>(tl, t4, lane);
-                else nan_mirror<false, 0>(tl, t4, lane, vec4);
+                pm_full = full && vec;
+                if (pm_full) nan_mirror_o<0, O, true>(tl, T, tby, lane, vec);
+                else nan_mirror_o<0, O, false>(tl, T, tby, lane, vec);
             }
         }
         if (pm_live) {
-            const uint32_t t4 = opaque_s(T4);
-            if (pm_full) nan_mirror_full<1>(pm, t4, lane);
-            else nan_mirror<false, 1>(pm, t4, lane, vec4);
+            const uint32_t tby = opaque_s(TBY);
+            if (pm_full) nan_mirror_o<1, O, true>(pm, T, tby, lane, vec);
+            else nan_mirror_o<1, O, false>(pm, T, tby, lane, vec);
         }
     }
 }
 
-template <class E, int NCH>
+template <class E, int NCH, class O>
 hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_super_kernel<E, NCH>;
+    auto kern = trimul_super_kernel<E, NCH, O>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -775,7 +877,8 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, a.out, (uint32_t)a.T,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
+                       (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
                        (int)a.vec_store);
     return hipGetLastError();
@@ -821,8 +924,8 @@ hipError_t launch_cfg(const TrimulArgs &a, hipStream_t s)
     int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
     if (grid > want) grid = want;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, a.out, a.T, a.C, a.NH,
-                       a.HS, L, items, a.scale, (int)a.vec_store);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, (float *)a.out, a.T, a.C,
+                       a.NH, a.HS, L, items, a.scale, (int)a.vec_store, a.out_kind);
     return hipGetLastError();
 }
 
@@ -872,8 +975,12 @@ hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
     // The super-tile kernel's buffer offsets within a 64-row tile reach 256 T
     // bytes, under the 2^31 range of its buffer resources for T < 2^22.
     const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 256 && a.T < (int64_t(1) << 22);
-    if (super_ok && !force_tile)
-        return a.HS * E::ES <= 128 ? launch_super<E, 8>(a, s) : launch_super<E, 16>(a, s);
+    if (super_ok && !force_tile) {
+        const bool narrow = a.HS * E::ES <= 128;
+        if (a.out_kind == 1) return narrow ? launch_super<E, 8, OBF16>(a, s) : launch_super<E, 16, OBF16>(a, s);
+        if (a.out_kind == 2) return narrow ? launch_super<E, 8, OF16>(a, s) : launch_super<E, 16, OF16>(a, s);
+        return narrow ? launch_super<E, 8, OF32>(a, s) : launch_super<E, 16, OF32>(a, s);
+    }
     // 16-byte chunks need base, pitch and head offsets 16-byte aligned and
     // HS*ES a multiple of 16 (vec = elements that divide all of them).
     if (vec * E::ES >= 16) return launch_u<E, true>(a, s);

@@ -137,9 +137,10 @@ class Workload:
         B, T, NH, HS = self.dims
         return 2 * HS * B * NH * T * (T + 1) // 2
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, out_bytes: int = 4) -> int:
         """Each operand read once and the full output written once (for the
-        scores: Q and K read, V never read, the whole (T, T) plane written)."""
+        scores: Q and K read, V never read, the whole (T, T) plane written in
+        elements of out_bytes)."""
         es = 4 if self.dtype == "f32" else 2
         if self.kind == "gemm_nt":
             M, N, K = self.dims
@@ -148,7 +149,7 @@ class Workload:
             Bt, M, N, K = self.dims
             return Bt * (es * (M * K + N * K) + 4 * M * N)
         B, T, NH, HS = self.dims
-        return es * 2 * B * T * NH * HS + 4 * B * NH * T * T
+        return es * 2 * B * T * NH * HS + out_bytes * B * NH * T * T
 
 
 WORKLOADS = {
@@ -169,6 +170,11 @@ WORKLOADS = {
                                           (192, 120, 120, 64)),
     "trimul_f32_B16_T120_NH12_HS64": Workload("trimul_f32_B16_T120_NH12_HS64", "trimul_causal", "f32", 8,
                                               (16, 120, 12, 64)),
+    # binary16 inputs at the two large shapes (the scores are also timed with
+    # 16-bit outputs).
+    "dense_f16_4096": Workload("dense_f16_4096", "gemm_nt", "f16", 9, (4096, 4096, 4096)),
+    "trimul_f16_B4_T4096_NH25_HS64": Workload("trimul_f16_B4_T4096_NH25_HS64", "trimul_causal", "f16", 10,
+                                              (4, 4096, 25, 64)),
     "trimul_bf16_B4_T4096_NH25_HS64": Workload("trimul_bf16_B4_T4096_NH25_HS64", "trimul_causal",
                                                "bf16", 5, (4, 4096, 25, 64)),
 }

@@ -21,7 +21,8 @@
  *     CAS_ERR_HIP and cas_last_hip_error() gives the hipError_t (per thread).
  *     Faults inside a kernel surface at the caller's next synchronisation.
  *   - Accepted (in_dtype, out_dtype) pairs: (F32, F32), (BF16, F32),
- *     (F16, F32). 16-bit inputs are raw bfloat16 / IEEE binary16 patterns.
+ *     (F16, F32); cas_trimul_causal also takes out_dtype BF16 or F16 with any
+ *     input type. 16-bit inputs are raw bfloat16 / IEEE binary16 patterns.
  *   - The output byte range may not overlap an input byte range.
  *   - Any alignment is accepted; 16-byte aligned bases and pitches select
  *     wider loads and stores, with the same results.
@@ -94,9 +95,13 @@ int cas_batch_matmul_nt(const void *X, const void *W, void *Y, int64_t batch,
  *   qkv  (B, T, 3, NH, HS) contiguous, C = NH*HS; Q row t of head nh starts at
  *        element b*T*3C + t*3C + nh*HS, K row t2 at the same place + C; the V
  *        third is never read.
- *   out  (B, NH, T, T) contiguous fp32:
+ *   out  (B, NH, T, T) contiguous, of out_dtype:
  *        out[b,nh,t,t2] = fp32(Q.K) * s  for t2 <= t, s = fp32 nearest 1/sqrt(HS)
  *        out[b,nh,t,t2] = quiet NaN, bits 0x7FC00000, for t2 > t
+ *        With out_dtype CAS_BF16 / CAS_F16 each score is that fp32 value
+ *        rounded to bfloat16 / binary16 (to nearest, ties to even; past the
+ *        range: infinity), and the mask is 0x7FC0 / 0x7E00. Half the bytes of
+ *        the fp32 output, which bounds this operation's time.
  *
  * Only tiles on or below the diagonal are computed; the tiles above it are
  * filled with the NaN pattern by the same launch. Any T >= 1 is accepted.

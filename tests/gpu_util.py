@@ -5,6 +5,11 @@ oracle at the tolerances of the contract:
   fp32 inputs:        |gpu - oracle| <= 1e-4 * sum|a_i b_i| + 1e-6
   bf16 / f16 inputs:  |gpu - oracle| <= 4e-3 * sum|a_i b_i|
   NaN mask:           bit-exact 0x7FC00000 above the diagonal
+
+16-bit score outputs are the fp32 score rounded once more (nearest even), so
+they get the fp32 allowance plus one rounding of that format: half an ulp,
+2^-8 (bfloat16) or 2^-11 (binary16) of the magnitude, and for binary16 half
+its smallest subnormal, 2^-25. Their mask is 0x7FC0 / 0x7E00, bit-exact.
 """
 from __future__ import annotations
 
@@ -18,6 +23,10 @@ CANARY = 0x7F800001           # guard-band fill around every output
 GUARD = 1024                  # elements of guard band on each side
 
 TOL = {"f32": (1e-4, 1e-6), "bf16": (4e-3, 0.0), "f16": (4e-3, 0.0)}
+NAN16 = {"bf16": 0x7FC0, "f16": 0x7E00}
+ROUND16 = {"bf16": (2.0 ** -8, 0.0), "f16": (2.0 ** -11, 2.0 ** -25)}
+SENTINEL16 = -1               # 0xFFFF
+CANARY16 = 0x7C01             # guard-band fill of 16-bit outputs
 
 
 def case(msg: str) -> None:
@@ -43,10 +52,22 @@ def guarded_output(n: int):
     return buf, buf[GUARD:GUARD + n].view(torch.float32)
 
 
+def guarded_output16(n: int, out_dtype: str):
+    """n 16-bit outputs between guard bands, starting as the sentinel; returns
+    (buffer, the n-element view as the output dtype)."""
+    import torch
+    buf = torch.full((n + 2 * GUARD,), CANARY16, dtype=torch.int16, device="cuda")
+    buf[GUARD:GUARD + n] = SENTINEL16
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
+    return buf, buf[GUARD:GUARD + n].view(tdt)
+
+
 def check_guards(buf, n: int) -> None:
+    import torch
     h = buf.cpu().numpy()
-    assert np.all(h[:GUARD] == CANARY), "write before the output buffer"
-    assert np.all(h[GUARD + n:] == CANARY), "write past the output buffer"
+    canary = CANARY16 if buf.dtype == torch.int16 else CANARY
+    assert np.all(h[:GUARD] == canary), "write before the output buffer"
+    assert np.all(h[GUARD + n:] == canary), "write past the output buffer"
 
 
 def bits(a) -> np.ndarray:
@@ -67,6 +88,50 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, dtype: str
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(lim > 0, err / np.where(lim > 0, lim, 1), 0.0)
     return float(r.max()) if r.size else 0.0
+
+
+def decode16(h: np.ndarray, out_dtype: str) -> np.ndarray:
+    h = np.asarray(h).view(np.uint16)
+    if out_dtype == "f16":
+        return h.view(np.float16).astype(np.float64)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_scores16(gpu16: np.ndarray, ref: np.ndarray, bound: np.ndarray, in_dtype: str, out_dtype: str,
+                    what: str, exact16: np.ndarray | None = None) -> float:
+    """16-bit scores (raw uint16 patterns) against the oracle's fp32 scores:
+    the mask bit-exact, the rest within the fp32 allowance plus one rounding to
+    the 16-bit format -- or bit-exact to `exact16` (the oracle's rounding of
+    exact fp32 scores) where given."""
+    g = np.asarray(gpu16).view(np.uint16)
+    mask = bits(ref) == QNAN
+    if not np.all(g[mask] == NAN16[out_dtype]):
+        raise AssertionError(f"{what}: {int(np.sum(g[mask] != NAN16[out_dtype]))} masked elements are not "
+                             f"the {out_dtype} NaN pattern {NAN16[out_dtype]:#06x}")
+    low = ~mask
+    if exact16 is not None:
+        if not np.array_equal(g[low], np.asarray(exact16)[low]):
+            idx = tuple(int(i) for i in np.argwhere((g != exact16) & low)[0])
+            raise AssertionError(f"{what}: not bit-exact; first {idx}: gpu={g[idx]:#06x} "
+                                 f"oracle={int(exact16[idx]):#06x}")
+        return 0.0
+    dec = decode16(g[low], out_dtype)
+    if not np.all(np.isfinite(dec)):
+        raise AssertionError(f"{what}: non-finite value on or below the diagonal")
+    rel, ab = TOL[in_dtype]
+    r16, a16 = ROUND16[out_dtype]
+    r = ref[low].astype(np.float64)
+    fp32_allow = rel * bound[low] + ab
+    lim = fp32_allow + r16 * (np.abs(r) + fp32_allow) + a16
+    err = np.abs(dec - r)
+    bad = ~(err <= lim)
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; first: "
+                             f"gpu={dec[i]!r} oracle={r[i]!r} allowed={lim[i]!r}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(lim > 0, err / np.where(lim > 0, lim, 1), 0.0)
+    return float(q.max()) if q.size else 0.0
 
 
 def assert_exact(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:

@@ -120,7 +120,7 @@ def test_batch_matmul_empty_and_broadcast_reach_the_device_check(L):
 
 def test_trimul_rejections(L):
     assert t(L, ind=3) == EDTYPE
-    assert t(L, outd=F16) == EDTYPE
+    assert t(L, outd=7) == EDTYPE
     assert t(L, B=-1) == ESHAPE
     assert t(L, C=10, NH=3) == ESHAPE       # C % NH != 0
     assert t(L, C=0) == ESHAPE
@@ -130,6 +130,19 @@ def test_trimul_rejections(L):
     assert t(L, B=2**40, T=2**20) == ESHAPE
     assert t(L, B=1, T=2**24, C=12, NH=3) == ESHAPE   # T at the 32-bit offset limit
     assert t(L, B=1, T=4, C=2**22, NH=2) == ESHAPE    # QKV row of 3 * 2^24 fp32 bytes
+
+
+def test_trimul_16bit_outputs(L):
+    import torch
+    # (B, NH, T, T) = (2, 3, 5, 5) outputs of 2 bytes span 300 bytes: qkv
+    # starting 298 bytes past the output overlaps it, 300 bytes past does not
+    # (with fp32 outputs, 600 bytes, it would).
+    assert t(L, qkv=PY + 298, outd=BF16) == EALIAS
+    assert t(L, qkv=PY + 300, outd=F32) == EALIAS
+    if not torch.cuda.is_available():
+        assert t(L, outd=BF16) == EDEV
+        assert t(L, outd=F16, ind=BF16) == EDEV
+        assert t(L, qkv=PY + 300, outd=F16) == EDEV
 
 
 def test_trimul_empty_is_ok(L):

@@ -11,8 +11,8 @@ import torch
 
 import causal_attention_score_amd as cas
 from causal_attention_score_amd import synth
-from gpu_util import (QNAN, SENTINEL, assert_close, assert_exact, assert_scores, bits, case, check_guards,
-                      guarded_output, to_device)
+from gpu_util import (NAN16, QNAN, SENTINEL, assert_close, assert_exact, assert_scores, assert_scores16, bits,
+                      case, check_guards, guarded_output, guarded_output16, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -293,6 +293,21 @@ def run_trimul(qkv, dtype, B, T, NH, HS, label):
     return flat.view(B, NH, T, T).cpu().numpy()
 
 
+def run_trimul16(qkv, dtype, out_dtype, B, T, NH, HS, label, offset=0):
+    """16-bit score output; offset (elements) shifts the output off 16-byte
+    alignment to take the per-element store path."""
+    n = B * NH * T * T
+    buf, flat = guarded_output16(n + offset, out_dtype)
+    out = flat[offset:offset + n].view(B, NH, T, T)
+    case(f"{label} trimul_causal {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS} offset={offset}")
+    cas.trimul_causal(to_device(qkv, dtype).view(B, T, 3 * NH * HS), NH, out=out)
+    torch.cuda.synchronize()
+    check_guards(buf, n + offset)
+    h = flat.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.all(h[:offset] == 0xFFFF), "wrote before the (shifted) output"
+    return h[offset:].reshape(B, NH, T, T)
+
+
 TRI_T = [1, 2, 7, 63, 64, 65, 127, 128, 129, 300]
 TRI_HS = [1, 8, 40, 64, 80, 128]
 
@@ -335,6 +350,47 @@ def test_trimul_exact_small_integers(orc, monkeypatch, dtype, kernel):
         out = run_trimul(qkv, dtype, B, T, NH, HS, "exact")
         # HS = 64 scales by 1/8 exactly; HS = 40 rounds once, like the oracle
         assert_scores(out, ref, bound, dtype, f"trimul exact {dtype}", exact=(HS == 64))
+
+
+@pytest.mark.parametrize("kernel", ["super", "tile"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("HS", [40, 64])
+@pytest.mark.parametrize("T", [1, 65, 128, 200, 256])
+def test_trimul_out16(orc, monkeypatch, T, HS, dtype, out_dtype, kernel):
+    """16-bit score output: whole and ragged tiles, rows 16-byte aligned
+    (T % 8 == 0) or not, both kernels."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 29 + HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul16(qkv, dtype, out_dtype, B, T, NH, HS, "out16")
+    assert_scores16(out, ref, bound, dtype, out_dtype, f"trimul {dtype}->{out_dtype} T={T} HS={HS}")
+
+
+@pytest.mark.parametrize("kernel", ["super", "tile"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_trimul_out16_exact(orc, monkeypatch, dtype, out_dtype, kernel):
+    """Integer inputs and HS = 64 (scale 1/8): the fp32 scores are exact, so
+    the 16-bit outputs must equal the oracle's rounding of them bit for bit."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
+    B, T, NH, HS = 2, 257, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 1, dist="int")
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul16(qkv, dtype, out_dtype, B, T, NH, HS, "out16 exact")
+    assert_scores16(out, ref, bound, dtype, out_dtype, f"trimul exact {dtype}->{out_dtype}",
+                    exact16=orc.round16(ref, out_dtype))
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_trimul_out16_unaligned(orc, out_dtype):
+    """Output one element past a 16-byte boundary: the per-element stores."""
+    B, T, NH, HS = 2, 136, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=77)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "bf16")
+    out = run_trimul16(qkv, "bf16", out_dtype, B, T, NH, HS, "out16 unaligned", offset=1)
+    assert_scores16(out, ref, bound, "bf16", out_dtype, f"trimul unaligned ->{out_dtype}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -473,6 +529,59 @@ def test_workload_dense_bf16_4096(orc):
     r = assert_close(got, ref, bound, "bf16", wl.name)
     assert bool(torch.isfinite(y).all())
     print(f"{wl.name}: sampled rows max err/tol {r:.3g}")
+
+
+def test_workload_dense_f16_4096(orc):
+    wl = synth.WORKLOADS["dense_f16_4096"]
+    X, W = wl.inputs()
+    case(f"{wl.name} gemm_nt full size")
+    y = cas.gemm_nt(to_device(X, "f16"), to_device(W, "f16"))
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 1023, 2048, 3333, 4095]
+    ref, bound = orc.gemm_nt(np.ascontiguousarray(X[rows]), W, "f16")
+    r = assert_close(y[rows].cpu().numpy(), ref, bound, "f16", wl.name)
+    assert bool(torch.isfinite(y).all())
+    print(f"{wl.name}: sampled rows max err/tol {r:.3g}")
+
+
+@pytest.mark.parametrize("name,out_dtype", [("trimul_bf16_B4_T4096_NH25_HS64", "bf16"),
+                                            ("trimul_f16_B4_T4096_NH25_HS64", "f16"),
+                                            ("trimul_f16_B4_T4096_NH25_HS64", "f32")])
+def test_workload_trimul_B4_T4096_out(orc, name, out_dtype):
+    """The large score shape with 16-bit inputs and 16-bit (or fp32) outputs:
+    whole-output mask counts, three whole planes, rows of every seventh."""
+    wl = synth.WORKLOADS[name]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    d = to_device(qkv, wl.dtype)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
+    out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
+    case(f"{wl.name} -> {out_dtype} trimul_causal full size")
+    cas.trimul_causal(d, NH, out=out)
+    torch.cuda.synchronize()
+    if out_dtype == "f32":
+        n_nan = int((out.view(torch.int32) == QNAN).sum())
+    else:
+        n_nan = int((out.view(torch.int16) == NAN16[out_dtype]).sum())
+    n_fin = int(torch.isfinite(out).sum())
+    assert n_nan == B * NH * T * (T - 1) // 2
+    assert n_fin == B * NH * T * (T + 1) // 2
+
+    def check(got, ref, bound, what):
+        if out_dtype == "f32":
+            return assert_scores(got.cpu().numpy(), ref, bound, wl.dtype, what)
+        return assert_scores16(got.view(torch.int16).cpu().numpy().view(np.uint16), ref, bound, wl.dtype,
+                               out_dtype, what)
+    worst = 0.0
+    for (b, h) in [(0, 0), (2, 11), (3, 24)]:
+        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, wl.dtype)
+        worst = max(worst, check(out[b, h], ref, bound, f"{wl.name} plane ({b},{h})"))
+    for p in range(0, B * NH, 7):
+        b, h = divmod(p, NH)
+        t0 = (p * 389) % (T - 8)
+        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, wl.dtype)
+        worst = max(worst, check(out[b, h, t0:t0 + 8], ref, bound, f"{wl.name} rows {t0}.. plane ({b},{h})"))
+    print(f"{wl.name} -> {out_dtype}: sampled max err/tol {worst:.3g}")
 
 
 def test_workload_trimul_bf16_B4_T4096(orc):
