@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 code with the HIP path; the product never imports it.
 
 Inputs are numpy arrays: float32 for fp32, uint16 bit patterns for bfloat16,
-float16 (or uint16 bit patterns) for binary16. Outputs are float32 scores and
-float64 error bounds (sum of |products|, scaled like the output).
+float16 (or uint16 bit patterns) for binary16. Outputs are float32 scores (the
+softmax: float64) and float64 error bounds (sum of |products|, scaled like the
+output).
 """
 from __future__ import annotations
 
@@ -36,6 +37,8 @@ class Oracle:
         lib.oracle_gemm_nt.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 6 + [ctypes.c_int]
         lib.oracle_trimul_causal.argtypes = [_vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int]
         lib.oracle_trimul_causal_rows.argtypes = [_vp, _vp, _vp] + [_i64] * 8 + [ctypes.c_int]
+        lib.oracle_causal_softmax_rows.argtypes = [_vp] * 5 + [_i64] * 8 + [ctypes.c_int] * 2
+        lib.oracle_causal_softmax.argtypes = [_vp] * 5 + [_i64] * 4 + [ctypes.c_int] * 2
         lib.oracle_tiled_matmul_count.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [_vp]
         lib.oracle_decode.argtypes = [_vp, ctypes.c_int, _i64, _vp]
         lib.oracle_round16.argtypes = [_vp, _vp, _i64, ctypes.c_int]
@@ -143,6 +146,42 @@ class Oracle:
         if rc:
             raise ValueError("oracle_trimul_causal_rows rejected its arguments")
         return out, bound
+
+    SOFTMAX_MODE = {"log": 0, "prob": 1}
+
+    def causal_softmax(self, qkv: np.ndarray, B: int, T: int, C: int, NH: int, dtype: str = "f32",
+                       mode: str = "prob", with_out: bool = True, with_bound: bool = True):
+        """Causal softmax of the scores (smallem "Kernels GPU", the softmax in
+        two launches, over the trimul_cpu score rows). Returns (out (B,NH,T,T)
+        or None, row_max (B,NH,T), row_logsum (B,NH,T), bound or None), all
+        float64."""
+        raw = self._raw(qkv, dtype)
+        out = np.empty((B, NH, T, T), dtype=np.float64) if with_out else None
+        mx = np.empty((B, NH, T), dtype=np.float64)
+        ls = np.empty((B, NH, T), dtype=np.float64)
+        bound = np.empty((B, NH, T, T), dtype=np.float64) if with_bound else None
+        rc = self.lib.oracle_causal_softmax(self._p(raw), self._p(out), self._p(mx), self._p(ls), self._p(bound),
+                                            B, T, C, NH, DTYPE_CODE[dtype], self.SOFTMAX_MODE[mode])
+        if rc:
+            raise ValueError("oracle_causal_softmax rejected its arguments")
+        return out, mx, ls, bound
+
+    def causal_softmax_rows(self, qkv: np.ndarray, B: int, T: int, C: int, NH: int, b: int, nh: int,
+                            t0: int, t1: int, dtype: str = "f32", mode: str = "prob",
+                            with_out: bool = True, with_bound: bool = True):
+        """Rows [t0, t1) of plane (b, nh) of causal_softmax."""
+        raw = self._raw(qkv, dtype)
+        n = t1 - t0
+        out = np.empty((n, T), dtype=np.float64) if with_out else None
+        mx = np.empty(n, dtype=np.float64)
+        ls = np.empty(n, dtype=np.float64)
+        bound = np.empty((n, T), dtype=np.float64) if with_bound else None
+        rc = self.lib.oracle_causal_softmax_rows(self._p(raw), self._p(out), self._p(mx), self._p(ls),
+                                                 self._p(bound), B, T, C, NH, b, nh, t0, t1,
+                                                 DTYPE_CODE[dtype], self.SOFTMAX_MODE[mode])
+        if rc:
+            raise ValueError("oracle_causal_softmax_rows rejected its arguments")
+        return out, mx, ls, bound
 
     def tiled_matmul_count(self, A: np.ndarray, Bm: np.ndarray, bm: int, bn: int, bk: int):
         """Returns (A@B, loads, writes, padded_loads, padded_writes)."""

@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, obviously correct CPU oracle for the tiled-matmul
- * hot path (dense NT product and causal triangular attention scores).
+ * hot path (dense NT product, causal triangular attention scores and their
+ * causal softmax).
  *
  * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this file's library. It shares no
@@ -16,7 +17,9 @@
  * Parity pins (all in the CPU test suite): exact-rational brute force on tiny
  * shapes, the ramp closed form, identity and zero products, the worked tiling
  * example (864 loads, 135 writes), the triangle-versus-dense invariant, the
- * NaN count, and thread-count independence.
+ * NaN count, and thread-count independence. The softmax is pinned by the
+ * closed form of geometric score rows, a max-free formula on exact scores,
+ * rows summing to one, and saturated rows.
  */
 #include "oracle.h"
 
@@ -231,6 +234,96 @@ int oracle_trimul_causal(const void *qkv, float *out, double *bound,
             const int64_t plane = (b * NH + nh) * T * T;   /* out[b][nh][:][:] */
             int rc = oracle_trimul_causal_rows(qkv, out + plane, bound ? bound + plane : 0,
                                                B, T, C, NH, b, nh, 0, T, dtype);
+            if (rc) return rc;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ causal softmax */
+
+/* smallem "Kernels GPU" page, section on the softmax in two launches: a
+ * first launch (row_stats) reduces every row to two numbers, its maximum and
+ * ln(sum exp(x - max)); a second (softmax_rows) gives each element
+ * (x - max) - logsum, or the exponential of that for probabilities. The two
+ * reductions stay separate numbers, as the page recommends. Here the rows are
+ * the causal score rows of trimul_cpu (llm.c trimat_forward.cu, the Referee
+ * of Chapter I, whose first pass also notes the row maximum): entries
+ * t2 <= t take part, and t2 > t is the causal mask, which that file says could
+ * as well be -inf: log-probability -inf, probability 0. Everything is double;
+ * the scores are the exact products times the fp32 scale, not rounded. */
+int oracle_causal_softmax_rows(const void *qkv, double *out, double *row_max, double *row_logsum,
+                               double *bound, int64_t B, int64_t T, int64_t C, int64_t NH,
+                               int64_t b, int64_t nh, int64_t t0, int64_t t1, int dtype, int mode)
+{
+    if (!dtype_ok(dtype) || (mode != 0 && mode != 1)) return -1;
+    if (B < 0 || T < 0 || NH <= 0 || C <= 0 || C % NH != 0) return -1;
+    if (b < 0 || b >= B || nh < 0 || nh >= NH || t0 < 0 || t1 > T || t0 > t1) return -1;
+    if (t1 == t0) return 0;
+    if (!qkv) return -1;
+
+    const int64_t HS = C / NH;
+    const int64_t C3 = 3 * C;
+    const double scale = (double)oracle_trimul_scale(HS);
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = t0; t < t1; t++) {
+        double *s = (double *)malloc((size_t)(t + 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const int64_t q0 = b * T * C3 + t * C3 + nh * HS;              /* Q[b][nh][t][:] */
+        for (int64_t t2 = 0; t2 <= t; t2++) {
+            const int64_t k0 = b * T * C3 + t2 * C3 + nh * HS + C;     /* K[b][nh][t2][:] */
+            double acc = 0.0, asum = 0.0;
+            for (int64_t i = 0; i < HS; i++) {
+                double p = elem(qkv, dtype, q0 + i) * elem(qkv, dtype, k0 + i);
+                acc += p;
+                asum += fabs(p);
+            }
+            s[t2] = acc * scale;
+            if (bound) bound[(t - t0) * T + t2] = scale * asum;
+        }
+        /* row_stats: the maximum, then the log of the shifted sum */
+        double mx = s[0];
+        for (int64_t t2 = 1; t2 <= t; t2++)
+            if (s[t2] > mx) mx = s[t2];
+        double sum = 0.0;
+        for (int64_t t2 = 0; t2 <= t; t2++) sum += exp(s[t2] - mx);
+        const double lse = log(sum);
+        if (row_max) row_max[t - t0] = mx;
+        if (row_logsum) row_logsum[t - t0] = lse;
+        /* softmax_rows */
+        if (out) {
+            double *orow = out + (t - t0) * T;
+            for (int64_t t2 = 0; t2 <= t; t2++) {
+                const double lp = (s[t2] - mx) - lse;
+                orow[t2] = mode == 0 ? lp : exp(lp);
+            }
+            for (int64_t t2 = t + 1; t2 < T; t2++) orow[t2] = mode == 0 ? -INFINITY : 0.0;
+        }
+        if (bound)
+            for (int64_t t2 = t + 1; t2 < T; t2++) bound[(t - t0) * T + t2] = 0.0;
+        free(s);
+    }
+    return failed ? -1 : 0;
+}
+
+int oracle_causal_softmax(const void *qkv, double *out, double *row_max, double *row_logsum,
+                          double *bound, int64_t B, int64_t T, int64_t C, int64_t NH, int dtype, int mode)
+{
+    if (!dtype_ok(dtype) || (mode != 0 && mode != 1) || B < 0 || T < 0 || NH < 0) return -1;
+    if (B == 0 || T == 0 || NH == 0) return 0;
+    if (C <= 0 || C % NH != 0) return -1;
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t nh = 0; nh < NH; nh++) {
+            const int64_t row = (b * NH + nh) * T;                 /* row (b, nh, 0) */
+            int rc = oracle_causal_softmax_rows(qkv, out ? out + row * T : 0, row_max ? row_max + row : 0,
+                                                row_logsum ? row_logsum + row : 0, bound ? bound + row * T : 0,
+                                                B, T, C, NH, b, nh, 0, T, dtype, mode);
             if (rc) return rc;
         }
     }

@@ -6,7 +6,8 @@
  * includes or calls it, and it includes nothing from the product.
  *
  * Every routine is the plain definition: one double accumulator per output,
- * summed in ascending contraction order, rounded once to fp32.
+ * summed in ascending contraction order, rounded once to fp32 (the softmax
+ * keeps double outputs).
  *
  * Element codes (dtype): 0 = fp32, 1 = bfloat16 (raw 16-bit patterns),
  * 2 = IEEE binary16 (raw 16-bit patterns). Outputs are always fp32.
@@ -48,6 +49,22 @@ int oracle_trimul_causal_rows(const void *qkv, float *out, double *bound,
                               int64_t B, int64_t T, int64_t C, int64_t NH,
                               int64_t b, int64_t nh, int64_t t0, int64_t t1,
                               int dtype);
+
+/* Causal softmax of the scores, in double throughout (scores not rounded
+ * to fp32). For each row t of plane (b, nh), over t2 <= t:
+ *   row_max[t] = max s[t][t2],  row_logsum[t] = ln sum exp(s[t][t2] - row_max[t]),
+ *   mode 0: out = (s - row_max) - row_logsum   (log-probabilities)
+ *   mode 1: out = exp of that                   (probabilities)
+ * and for t2 > t out = -inf (mode 0) or 0 (mode 1). out (nullable) and bound
+ * (nullable, the scores' error scale as in trimul) are (t1-t0) x T; row_max
+ * and row_logsum (nullable) hold t1-t0 values. */
+int oracle_causal_softmax_rows(const void *qkv, double *out, double *row_max, double *row_logsum,
+                               double *bound, int64_t B, int64_t T, int64_t C, int64_t NH,
+                               int64_t b, int64_t nh, int64_t t0, int64_t t1, int dtype, int mode);
+
+/* The same over every plane: out is (B,NH,T,T), row_max/row_logsum (B,NH,T). */
+int oracle_causal_softmax(const void *qkv, double *out, double *row_max, double *row_logsum,
+                          double *bound, int64_t B, int64_t T, int64_t C, int64_t NH, int dtype, int mode);
 
 /* The scale factor applied to every score: fp32 nearest to 1/sqrt(HS). */
 float oracle_trimul_scale(int64_t HS);

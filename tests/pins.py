@@ -15,7 +15,10 @@ AssertionError when the oracle disagrees with:
   * invariants of the causal scores (lower triangle = scaled dense product,
     NaN count, non-negative diagonal when Q = K) and thread-count
     independence;
-  * library conversions of bfloat16 / binary16 (torch, numpy).
+  * library conversions of bfloat16 / binary16 (torch, numpy);
+  * for the causal softmax: the closed form of geometric score rows, the
+    max-free formula 1 / sum exp(s_k - s) on exact scores, rows summing to
+    one, saturated rows, and the pinned score oracle's row maxima.
 
 The same functions run against mutated copies of the oracle in
 test_oracle_mutations.py, which checks that every planted mistake is caught.
@@ -364,6 +367,121 @@ def pin_thread_independence(orc):
         orc.set_threads(n0)
 
 
+# ------------------------------------------------------------ softmax pins
+
+def geometric_row(slope: float, t: int):
+    """Closed form of the softmax of the row (slope * k for k = 0..t):
+    returns (max, ln sum exp(x - max)). The shifted terms are the geometric
+    series e^(-|slope| j), j = 0..t, whose sum is (1 - r^(t+1)) / (1 - r)."""
+    n = t + 1
+    if slope == 0:
+        return 0.0, math.log(n)
+    a = abs(slope)
+    mx = slope * t if slope > 0 else 0.0
+    return mx, math.log(-math.expm1(-a * n)) - math.log(-math.expm1(-a))
+
+
+def pin_softmax_geometric_closed_form(orc):
+    """Score rows that are exact ramps slope * t2 (HS = 64, scale = 1/8):
+    row max, log-sum, every log-probability and probability against the
+    closed form of a truncated geometric series."""
+    B, T, NH, HS = 2, 40, 3, 64
+    slopes = [0.25, -0.5, 0.0]
+    for dtype in ("f32", "bf16", "f16"):
+        qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in slopes], dtype)
+        C = NH * HS
+        lp, mx, ls, _ = orc.causal_softmax(qkv, B, T, C, NH, dtype, "log", with_bound=False)
+        pr, mx2, ls2, _ = orc.causal_softmax(qkv, B, T, C, NH, dtype, "prob", with_bound=False)
+        assert np.array_equal(mx, mx2) and np.array_equal(ls, ls2)
+        for b in range(B):
+            for h, a in enumerate(slopes):
+                for t in range(T):
+                    m_ref, l_ref = geometric_row(a, t)
+                    assert abs(mx[b, h, t] - m_ref) <= 1e-13, (dtype, h, t, mx[b, h, t], m_ref)
+                    assert abs(ls[b, h, t] - l_ref) <= 1e-13, (dtype, h, t, ls[b, h, t], l_ref)
+                    ref = np.array([a * k - m_ref - l_ref for k in range(t + 1)])
+                    assert np.max(np.abs(lp[b, h, t, :t + 1] - ref)) <= 1e-12, (dtype, h, t)
+                    assert np.max(np.abs(pr[b, h, t, :t + 1] - np.exp(ref))) <= 1e-13, (dtype, h, t)
+
+
+def pin_softmax_maxfree_formula(orc):
+    """Small-integer inputs, exact rational scores: every probability equals
+    1 / sum_k exp(s_k - s_t2) (no maximum, no logarithm of the sum), evaluated
+    with math.fsum, and the row maximum is the largest exact score."""
+    for (B, T, NH, HS, seed, dtype) in [(2, 6, 2, 4, 31, "f32"), (1, 7, 3, 8, 32, "bf16"), (1, 5, 2, 3, 33, "f16")]:
+        C = NH * HS
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed, "int")
+        pr, mx, ls, _ = orc.causal_softmax(qkv, B, T, C, NH, dtype, "prob", with_bound=False)
+        lp, _, _, _ = orc.causal_softmax(qkv, B, T, C, NH, dtype, "log", with_bound=False)
+        Q, Kt = qk_views(qkv, B, T, NH, HS, dtype)
+        sc = Fraction(float(orc.trimul_scale(HS)))
+        for b in range(B):
+            for h in range(NH):
+                for t in range(T):
+                    s = [float(sc * sum((Fraction(float(Q[b, h, t, i])) * Fraction(float(Kt[b, h, k, i]))
+                                         for i in range(HS)), Fraction(0))) for k in range(t + 1)]
+                    assert mx[b, h, t] == max(s), (dtype, b, h, t)
+                    for t2 in range(T):
+                        if t2 > t:
+                            assert pr[b, h, t, t2] == 0.0 and lp[b, h, t, t2] == -np.inf
+                            continue
+                        z = math.fsum(math.exp(sk - s[t2]) for sk in s)
+                        assert abs(pr[b, h, t, t2] - 1.0 / z) <= 1e-14 * (1.0 / z) + 1e-300, (dtype, b, h, t, t2)
+                        assert abs(lp[b, h, t, t2] + math.log(z)) <= 1e-13, (dtype, b, h, t, t2)
+
+
+def pin_softmax_rows_sum_to_one(orc):
+    """Every causal row of probabilities sums to one; masked entries are
+    exactly 0 (probabilities) and -inf (log-probabilities); exp of the
+    log-probabilities gives the probabilities; the largest log-probability of
+    a row is -logsum, and 0 <= logsum <= ln(t + 1)."""
+    B, T, NH, HS = 2, 33, 2, 16
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 34)
+    pr, mx, ls, _ = orc.causal_softmax(qkv, B, T, NH * HS, NH, "f32", "prob", with_bound=False)
+    lp, _, _, _ = orc.causal_softmax(qkv, B, T, NH * HS, NH, "f32", "log", with_bound=False)
+    up = np.triu(np.ones((T, T), dtype=bool), 1)
+    assert np.all(pr[..., up] == 0.0) and np.all(lp[..., up] == -np.inf)
+    assert np.all(np.isfinite(lp[..., ~up]))
+    for b in range(B):
+        for h in range(NH):
+            for t in range(T):
+                assert abs(math.fsum(pr[b, h, t]) - 1.0) <= 1e-13, (b, h, t)
+                assert abs(np.max(lp[b, h, t]) + ls[b, h, t]) <= 1e-15
+                assert -1e-15 <= ls[b, h, t] <= math.log(t + 1) + 1e-13
+    low = ~up
+    assert np.allclose(np.exp(lp[..., low]), pr[..., low], rtol=1e-13, atol=0)
+
+
+def pin_softmax_saturated(orc):
+    """Scores of order 1e3-1e4 (exp of a raw score overflows double): the
+    outputs stay finite, rows sum to one, and the row maximum is the largest
+    score of the pinned score oracle up to its fp32 rounding."""
+    B, T, NH, HS = 1, 24, 2, 16
+    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", 35) * np.float32(64.0)).astype(np.float32)
+    pr, mx, ls, _ = orc.causal_softmax(qkv, B, T, NH * HS, NH, "f32", "prob", with_bound=False)
+    sc, _ = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32", with_bound=False)
+    assert np.max(np.abs(mx)) > 800.0
+    assert np.all(np.isfinite(ls))
+    for b in range(B):
+        for h in range(NH):
+            for t in range(T):
+                assert abs(math.fsum(pr[b, h, t]) - 1.0) <= 1e-13
+                smax = float(np.max(sc[b, h, t, :t + 1]))
+                assert abs(mx[b, h, t] - smax) <= ulp32(smax), (b, h, t, mx[b, h, t], smax)
+
+
+def pin_softmax_rows_match_full(orc):
+    B, T, NH, HS = 2, 21, 3, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f16", 36)
+    for mode in ("log", "prob"):
+        full, mx, ls, bd = orc.causal_softmax(qkv, B, T, NH * HS, NH, "f16", mode)
+        part, pmx, pls, pbd = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, 1, 2, 5, 17, "f16", mode)
+        assert np.array_equal(part, full[1, 2, 5:17]) and np.array_equal(pbd, bd[1, 2, 5:17])
+        assert np.array_equal(pmx, mx[1, 2, 5:17]) and np.array_equal(pls, ls[1, 2, 5:17])
+    _, tb = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f16")
+    assert np.array_equal(bd, tb)  # the same error scale as the scores
+
+
 # ------------------------------------------------------- tiled-count pins
 
 def read_golden_counts():
@@ -427,6 +545,8 @@ def pin_rejects_bad_arguments(orc):
     assert lib.oracle_trimul_causal(p, p, None, 1, 2, 12, 3, 7) == -1   # bad dtype
     assert lib.oracle_gemm_nt(p, p, p, None, 2, 2, 3, 2, 3, 2, 0) == -1  # ldx < K
     assert lib.oracle_trimul_causal(p, p, None, 0, 5, 12, 3, 0) == 0    # empty batch
+    assert lib.oracle_causal_softmax(p, None, p, p, None, 1, 2, 12, 3, 0, 2) == -1  # bad mode
+    assert lib.oracle_causal_softmax(p, None, p, p, None, 1, 2, 10, 3, 0, 1) == -1  # C % NH != 0
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

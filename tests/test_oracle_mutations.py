@@ -22,7 +22,11 @@ MUTATIONS = {
                                 "for (int64_t k = 1; k < K; k++) {\n                double p = elem(X"),
     "gemm_wrong_sign": ("                acc += p;\n                asum += fabs(p);\n            }\n            Y[",
                         "                acc -= p;\n                asum += fabs(p);\n            }\n            Y["),
-    "trimul_last_term_dropped": ("for (int64_t i = 0; i < HS; i++) {", "for (int64_t i = 0; i + 1 < HS; i++) {"),
+    "trimul_last_term_dropped": ("double acc = 0.0, asum = 0.0;\n                for (int64_t i = 0; i < HS; i++) {",
+                                 "double acc = 0.0, asum = 0.0;\n                for (int64_t i = 0; i + 1 < HS; i++) {"),
+    "softmax_last_term_dropped": ("double acc = 0.0, asum = 0.0;\n            for (int64_t i = 0; i < HS; i++) {",
+                                  "double acc = 0.0, asum = 0.0;\n            for (int64_t i = 0; i + 1 < HS; i++) {"),
+    "softmax_key_row_of_query": ("t2 * C3 + nh * HS + C;     /* K[b][nh][t2][:] */", "t * C3 + nh * HS + C;     /* K[b][nh][t2][:] */"),
     "bf16_decode_shift": ("(uint32_t)h << 16;", "(uint32_t)h << 15;"),
     "f16_decode_bias": ("expo - 25); /* (1 + frac/2^10) 2^(e-15) */", "expo - 24); /* (1 + frac/2^10) 2^(e-15) */"),
     "nan_bits": ("0x7FC00000u;", "0x7FC00001u;"),
@@ -32,6 +36,13 @@ MUTATIONS = {
     "bf16_ties_away": ("return (uint16_t)((u + 0x7FFFu + even) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
     "f16_overflow_early": ("if (a >= 65520.0) return", "if (a > 65504.0) return"),
     "f16_subnormal_unit": ("const double q = rint(ldexp(a, 24));", "const double q = rint(ldexp(a, 23));"),
+    "softmax_max_not_subtracted": ("t2 <= t; t2++) sum += exp(s[t2] - mx);", "t2 <= t; t2++) sum += exp(s[t2]);"),
+    "softmax_max_is_min": ("if (s[t2] > mx) mx = s[t2];", "if (s[t2] < mx) mx = s[t2];"),
+    "softmax_diagonal_excluded": ("t2 <= t; t2++) sum += exp(s[t2] - mx);", "t2 < t; t2++) sum += exp(s[t2] - mx);"),
+    "softmax_log_mask_zero": ("orow[t2] = mode == 0 ? -INFINITY : 0.0;", "orow[t2] = 0.0;"),
+    "softmax_scale_dropped": ("s[t2] = acc * scale;", "s[t2] = acc;"),
+    "softmax_log2_sum": ("const double lse = log(sum);", "const double lse = log2(sum);"),
+    "softmax_logsum_added": ("const double lp = (s[t2] - mx) - lse;", "const double lp = (s[t2] - mx) + lse;"),
     "f16_truncates": ("double q = rint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
 }
 
