@@ -1,5 +1,6 @@
-"""MI355X-native tiled-matmul hot path: dense Y = X W^T and causal attention
-scores, as hand-written gfx950 HIP kernels behind a C ABI (``include/cas.h``).
+"""MI355X-native tiled-matmul hot path: dense Y = X W^T, causal attention
+scores and their causal softmax, as hand-written gfx950 HIP kernels behind a C
+ABI (``include/cas.h``).
 
 This module is the thin binding: it marshals torch tensors (device memory and
 the current HIP stream) into the C ABI of ``libcas.so`` and raises on a
@@ -16,9 +17,11 @@ LIB_PATH = os.path.join(HERE, "libcas.so")
 
 CAS_F32, CAS_BF16, CAS_F16 = 0, 1, 2
 STATUS = {0: "CAS_OK", -1: "CAS_ERR_NULL", -2: "CAS_ERR_SHAPE", -3: "CAS_ERR_DTYPE",
-          -4: "CAS_ERR_ALIAS", -5: "CAS_ERR_DEVICE", -6: "CAS_ERR_HIP"}
-EXPORTS = ("cas_gemm_nt", "cas_batch_matmul_nt", "cas_trimul_causal", "cas_status_string", "cas_last_hip_error",
-           "cas_version")
+          -4: "CAS_ERR_ALIAS", -5: "CAS_ERR_DEVICE", -6: "CAS_ERR_HIP", -7: "CAS_ERR_UNSUPPORTED",
+          -8: "CAS_ERR_MODE"}
+SOFTMAX_MODE = {"log": 0, "prob": 1}
+EXPORTS = ("cas_gemm_nt", "cas_batch_matmul_nt", "cas_trimul_causal", "cas_causal_row_stats", "cas_causal_softmax",
+           "cas_status_string", "cas_last_hip_error", "cas_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -45,6 +48,10 @@ def lib() -> ctypes.CDLL:
         L.cas_batch_matmul_nt.restype = ctypes.c_int
         L.cas_trimul_causal.argtypes = [_vp, _vp] + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
         L.cas_trimul_causal.restype = ctypes.c_int
+        L.cas_causal_row_stats.argtypes = [_vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int, _vp]
+        L.cas_causal_row_stats.restype = ctypes.c_int
+        L.cas_causal_softmax.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int] * 3 + [_vp]
+        L.cas_causal_softmax.restype = ctypes.c_int
         L.cas_status_string.argtypes = [ctypes.c_int]
         L.cas_status_string.restype = ctypes.c_char_p
         L.cas_last_hip_error.restype = ctypes.c_int
@@ -145,6 +152,74 @@ def batch_matmul_nt(x, w, out=None):
     return out
 
 
+def _qkv_dims(qkv, NH: int):
+    """(B, T, C) of a contiguous packed QKV tensor, (B, T, 3C) or (B, T, 3, NH, HS)."""
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous")
+    if qkv.dim() == 5:
+        B, T, three, nh, HS = qkv.shape
+        if three != 3 or nh != NH:
+            raise ValueError("qkv must be (B, T, 3, NH, HS)")
+        return B, T, NH * HS
+    if qkv.dim() == 3:
+        B, T, C3 = qkv.shape
+        if C3 % 3:
+            raise ValueError("last dim of qkv must be 3*C")
+        return B, T, C3 // 3
+    raise ValueError("qkv must be (B, T, 3C) or (B, T, 3, NH, HS)")
+
+
+def causal_row_stats(qkv, NH: int, row_max=None, row_logsum=None):
+    """Per-row statistics of the causal scores (the row_stats launch of the
+    two-launch softmax): row_max[b, nh, t] = max over t2 <= t of the fp32
+    score, row_logsum = ln sum exp(score - row_max), both float32 (B, NH, T).
+    The scores are recomputed from qkv and never written."""
+    import torch
+    B, T, C = _qkv_dims(qkv, NH)
+    shape = (B, NH, T)
+    if row_max is None:
+        row_max = torch.empty(shape, dtype=torch.float32, device=qkv.device)
+    if row_logsum is None:
+        row_logsum = torch.empty(shape, dtype=torch.float32, device=qkv.device)
+    for t in (row_max, row_logsum):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("row_max / row_logsum must be contiguous float32 (B, NH, T) tensors")
+    _require_device(qkv, row_max, row_logsum)
+    st = lib().cas_causal_row_stats(qkv.data_ptr(), row_max.data_ptr(), row_logsum.data_ptr(), B, T, C, NH,
+                                    _dtype_code(qkv), _stream_ptr(qkv.device))
+    _check("cas_causal_row_stats", st)
+    return row_max, row_logsum
+
+
+def causal_softmax(qkv, NH: int, mode: str = "prob", out=None, out_dtype=None, stats=None):
+    """Causal softmax of the scores: both launches (row statistics, then the
+    softmax rows). mode "prob": probabilities, 0 above the diagonal; "log":
+    log-probabilities (x - row_max) - row_logsum, -inf above it. out_dtype
+    (or out's dtype): float32 (default), bfloat16 or float16. stats: an
+    optional (row_max, row_logsum) pair to use instead of computing it.
+    Returns (out, row_max, row_logsum)."""
+    import torch
+    if mode not in SOFTMAX_MODE:
+        raise ValueError("mode must be 'prob' or 'log'")
+    B, T, C = _qkv_dims(qkv, NH)
+    row_max, row_logsum = stats if stats is not None else causal_row_stats(qkv, NH)
+    if out is None:
+        out = torch.empty((B, NH, T, T), dtype=out_dtype or torch.float32, device=qkv.device)
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise TypeError("out does not have out_dtype")
+    if tuple(out.shape) != (B, NH, T, T) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, NH, T, T) tensor")
+    for t in (row_max, row_logsum):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, NH, T) or not t.is_contiguous():
+            raise ValueError("row_max / row_logsum must be contiguous float32 (B, NH, T) tensors")
+    _require_device(qkv, out, row_max, row_logsum)
+    st = lib().cas_causal_softmax(qkv.data_ptr(), row_max.data_ptr(), row_logsum.data_ptr(), out.data_ptr(),
+                                  B, T, C, NH, SOFTMAX_MODE[mode], _dtype_code(qkv), _dtype_code(out),
+                                  _stream_ptr(qkv.device))
+    _check("cas_causal_softmax", st)
+    return out, row_max, row_logsum
+
+
 def trimul_causal(qkv, NH: int, out=None, out_dtype=None):
     """Causal attention scores from packed QKV.
 
@@ -154,20 +229,7 @@ def trimul_causal(qkv, NH: int, out=None, out_dtype=None):
     (default), or bfloat16 / float16 for the fp32 scores rounded to that
     format (half the output bytes)."""
     import torch
-    if not qkv.is_contiguous():
-        raise ValueError("qkv must be contiguous")
-    if qkv.dim() == 5:
-        B, T, three, nh, HS = qkv.shape
-        if three != 3 or nh != NH:
-            raise ValueError("qkv must be (B, T, 3, NH, HS)")
-        C = NH * HS
-    elif qkv.dim() == 3:
-        B, T, C3 = qkv.shape
-        if C3 % 3:
-            raise ValueError("last dim of qkv must be 3*C")
-        C = C3 // 3
-    else:
-        raise ValueError("qkv must be (B, T, 3C) or (B, T, 3, NH, HS)")
+    B, T, C = _qkv_dims(qkv, NH)
     if out is None:
         out = torch.empty((B, NH, T, T), dtype=out_dtype or torch.float32, device=qkv.device)
     if out_dtype is not None and out.dtype != out_dtype:

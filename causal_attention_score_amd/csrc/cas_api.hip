@@ -232,6 +232,102 @@ CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t 
     return launch_status(cas::launch_trimul(a, in_dtype, vec, (hipStream_t)stream));
 }
 
+namespace {
+
+// Shared checks of the two causal-softmax entry points: shapes, byte extents
+// of qkv (inb), of one statistics array (stb) and of the output (outb, for
+// out_bytes per element), the fused kernels' domain, and the 16-byte piece
+// width of the QKV rows (vec).
+int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH, cas_dtype in_dtype, int out_bytes,
+                   int64_t *inb, int64_t *stb, int64_t *outb, int *vec)
+{
+    if (B < 0 || T < 0 || C < 0 || NH < 0) return CAS_ERR_SHAPE;
+    if (B == 0 || T == 0 || NH == 0) return 1; // nothing to do
+    if (C == 0 || C % NH != 0) return CAS_ERR_SHAPE;
+    const int es = elem_size(in_dtype);
+    int64_t in_elems, rows, t, c3;
+    if (!mul_ok(3, C, &c3) || !mul_ok(B, T, &t) || !mul_ok(t, c3, &in_elems) || !mul_ok(in_elems, es, inb))
+        return CAS_ERR_SHAPE;
+    if (!mul_ok(B, NH, &t) || !mul_ok(t, T, &rows) || !mul_ok(rows, 4, stb) || !mul_ok(rows, T, &t) ||
+        !mul_ok(t, out_bytes, outb))
+        return CAS_ERR_SHAPE;
+    if (*inb >= (INT64_C(1) << 62) || *outb >= (INT64_C(1) << 62)) return CAS_ERR_SHAPE;
+    if (c3 * es >= (INT64_C(1) << 24) || T >= (INT64_C(1) << 24)) return CAS_ERR_SHAPE;
+    const int64_t HS = C / NH;
+    const int64_t lens[2] = {HS, C};
+    const void *ptrs[1] = {qkv};
+    *vec = qkv ? pick_vec(es, lens, 2, ptrs, 1) : 1;
+    if (!cas::softmax_fits(T, HS, es, *vec)) return CAS_ERR_UNSUPPORTED;
+    const int64_t nts = (T + 127) / 128;
+    if (B * NH * (nts * (nts + 1) / 2) > INT32_MAX || cas::row_stats_workgroups(B, T, NH) > INT32_MAX)
+        return CAS_ERR_SHAPE;
+    return CAS_OK;
+}
+
+cas::TrimulArgs softmax_args(const void *qkv, void *out, const float *row_max, const float *row_logsum, int64_t B,
+                             int64_t T, int64_t C, int64_t NH, int out_bytes, int out_kind)
+{
+    cas::TrimulArgs a{};
+    a.qkv = qkv;
+    a.out = out;
+    a.B = B;
+    a.T = T;
+    a.C = C;
+    a.NH = NH;
+    a.HS = C / NH;
+    a.scale = (float)(1.0 / std::sqrt((double)a.HS)); // nearest fp32 to 1/sqrt(HS)
+    a.vec_store = out && ((T * out_bytes) % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    a.out_kind = out_kind;
+    a.row_max = row_max;
+    a.row_logsum = row_logsum;
+    return a;
+}
+
+} // namespace
+
+CAS_EXPORT int cas_causal_row_stats(const void *qkv, float *row_max, float *row_logsum, int64_t B, int64_t T,
+                                    int64_t C, int64_t NH, cas_dtype in_dtype, void *stream)
+{
+    if (!dtype_in_ok(in_dtype)) return CAS_ERR_DTYPE;
+    int64_t inb, stb, outb;
+    int vec = 1;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    if (rc == 1) return CAS_OK;
+    if (rc == CAS_ERR_SHAPE) return rc;
+    if (!qkv || !row_max || !row_logsum) return CAS_ERR_NULL;
+    if (rc != CAS_OK) return rc;
+    if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0) return CAS_ERR_UNSUPPORTED;
+    if (overlap(row_max, stb, qkv, inb) || overlap(row_logsum, stb, qkv, inb) || overlap(row_max, stb, row_logsum, stb))
+        return CAS_ERR_ALIAS;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+    const cas::TrimulArgs a = softmax_args(qkv, nullptr, row_max, row_logsum, B, T, C, NH, 4, 0);
+    return launch_status(cas::launch_row_stats(a, in_dtype, (hipStream_t)stream));
+}
+
+CAS_EXPORT int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_logsum, void *out,
+                                  int64_t B, int64_t T, int64_t C, int64_t NH, int mode, cas_dtype in_dtype,
+                                  cas_dtype out_dtype, void *stream)
+{
+    if (!score_dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (mode != CAS_SOFTMAX_LOG && mode != CAS_SOFTMAX_PROB) return CAS_ERR_MODE;
+    const int ob = elem_size(out_dtype);
+    int64_t inb, stb, outb;
+    int vec = 1;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec);
+    if (rc == 1) return CAS_OK;
+    if (rc == CAS_ERR_SHAPE) return rc;
+    if (!qkv || !row_max || !row_logsum || !out) return CAS_ERR_NULL;
+    if (rc != CAS_OK) return rc;
+    if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0) return CAS_ERR_UNSUPPORTED;
+    if (overlap(out, outb, qkv, inb) || overlap(out, outb, row_max, stb) || overlap(out, outb, row_logsum, stb))
+        return CAS_ERR_ALIAS;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+    const cas::TrimulArgs a = softmax_args(qkv, out, row_max, row_logsum, B, T, C, NH, ob, (int)out_dtype);
+    return launch_status(cas::launch_softmax(a, in_dtype, mode, (hipStream_t)stream));
+}
+
 CAS_EXPORT const char *cas_status_string(int status)
 {
     switch (status) {
@@ -242,10 +338,14 @@ CAS_EXPORT const char *cas_status_string(int status)
     case CAS_ERR_ALIAS: return "output bytes overlap input bytes";
     case CAS_ERR_DEVICE: return "the current HIP device is not a gfx950 (MI355X) GPU or is unavailable";
     case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
+    case CAS_ERR_UNSUPPORTED:
+        return "valid arguments outside the kernels' domain (QKV rows not in 16-byte pieces, head over 256 bytes, "
+               "T >= 2^22, or misaligned statistics)";
+    case CAS_ERR_MODE: return "unknown softmax mode";
     default: return "unknown status";
     }
 }
 
 CAS_EXPORT int cas_last_hip_error(void) { return g_last_hip; }
 
-CAS_EXPORT int cas_version(void) { return 100; }
+CAS_EXPORT int cas_version(void) { return 200; }

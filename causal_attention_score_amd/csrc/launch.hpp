@@ -25,6 +25,8 @@ struct TrimulArgs {
     float scale;
     bool vec_store; // output rows 16-byte aligned: T * out_bytes % 16 == 0 and out 16-byte aligned
     int out_kind;   // 0 fp32, 1 bfloat16, 2 binary16 (the cas_dtype codes)
+    const float *row_max = nullptr;    // causal softmax: per-row statistics (B, NH, T)
+    const float *row_logsum = nullptr;
 };
 
 // Tile shapes the dense launcher can pick (exposed for tests and tuning).
@@ -43,5 +45,13 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s);
 
 hipError_t launch_trimul(const TrimulArgs &a, int elem, int vec, hipStream_t s);
 int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);
+
+// Causal softmax (softmax.hip): row statistics into a.row_max / a.row_logsum,
+// then the softmax rows (mode 0 log-probabilities, 1 probabilities) into
+// a.out. Both need softmax_fits(); vec as for launch_trimul.
+bool softmax_fits(int64_t T, int64_t HS, int es, int vec);
+int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH);
+hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
+hipError_t launch_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s);
 
 } // namespace cas

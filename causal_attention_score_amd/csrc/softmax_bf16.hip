@@ -1,0 +1,15 @@
+// softmax_bf16.hip -- bf16 inputs of the causal softmax kernels (row statistics
+// and softmax rows; their own translation unit so the variants compile in
+// parallel).
+#include "softmax_kernel.hpp"
+
+namespace cas {
+
+hipError_t launch_row_stats_bf16(const TrimulArgs &a, hipStream_t s) { return sm::launch_row_stats_impl<KBF16>(a, s); }
+
+hipError_t launch_softmax_bf16(const TrimulArgs &a, int mode, hipStream_t s)
+{
+    return sm::launch_softmax_impl<KBF16>(a, mode, s);
+}
+
+} // namespace cas

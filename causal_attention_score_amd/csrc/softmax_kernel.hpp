@@ -1,0 +1,289 @@
+// softmax_kernel.hpp -- causal softmax straight from packed QKV on gfx950.
+//
+// Semantics: the softmax in two launches of the smallem page "Kernels GPU"
+// (row_stats, then softmax_rows), over the causal score rows of llm.c
+// trimat_forward.cu's trimul_cpu (the Referee of Chapter I):
+//   row_stats    row_max[t]    = max_{t2 <= t} x[t][t2]
+//                row_logsum[t] = ln sum_{t2 <= t} exp(x[t][t2] - row_max[t])
+//   softmax_rows log-probability (x - row_max) - row_logsum, or its exponential
+// with x the fp32 score of the score kernel. The two reductions stay two
+// numbers, as the page recommends: folding the small log-sum into a large
+// maximum loses its digits.
+//
+// Neither launch reads or writes the (T, T) scores: both recompute Q K^T from
+// the packed rows. The row-stats kernel below writes 8 bytes per row; the
+// softmax rows are the three-role score kernel (trimul_kernel.hpp) with the
+// EpLog / EpProb epilogue, whose loader waves stage the statistics of the
+// rows they fetch.
+//
+// Row-stats kernel design:
+//  * A workgroup owns a pair of 128-row query blocks of one (b, nh) plane,
+//    I and nt-1-I, so every workgroup walks nt + 1 key tiles whatever I is
+//    (block I needs key tiles 0..I). One workgroup per pair: the hardware
+//    dispatcher balances them; ids are grouped per XCD so that a plane's K
+//    rows stay in one L2.
+//  * Four waves, wave w owns query rows 32w..32w+31 of the block. Its Q
+//    fragments stay in registers for the whole block; the 128 K rows of each
+//    step are fetched by all four waves (coalesced 16-byte loads, issued a
+//    step ahead) into a double-buffered LDS tile.
+//  * D = K Q^T per 32-row key block, so a lane holds 16 scores of ONE query
+//    row (column lane%32) and the two lane halves split the keys. Each lane
+//    keeps a running maximum and a running sum for its row; the halves merge
+//    once at the end.
+//  * The running sum is kept in base 2 against the rounded offset
+//    ms = fl(m * c), c = scale * log2(e): terms are exp2(fma(a, c, -ms)) from
+//    the raw dot product a, earlier sums are rescaled by exp2(ms_old - ms),
+//    and the final log-sum subtracts the exact residual m * c - ms (one fma).
+//    The log-sum then carries no error of order ulp(m * c), which for
+//    saturated rows (|m| in the hundreds) would otherwise dominate.
+#pragma once
+
+#include "trimul_kernel.hpp"
+
+namespace cas {
+namespace sm {
+
+using tri::OOB;
+using tri::rsrc_at;
+using tri::ST;
+
+constexpr int SW = 4; // waves per row-stats workgroup
+constexpr int STATS_THREADS = SW * 64;
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float LN2 = 0.693147180559945309417f;
+
+// Position (bytes) of 16-byte chunk c of row r inside its LDS row of NCH
+// chunks. ds_read_b128 serves 16 lanes at a time from 256 bytes of banks;
+// the MFMA operand read takes one chunk of 16 consecutive rows, and the
+// staging write takes whole rows. XOR-ing the chunk with (row / rows per 256
+// bytes) makes both touch 16 distinct 16-byte bank groups.
+template <int NCH> __device__ __forceinline__ uint32_t kswz(uint32_t r, uint32_t c)
+{
+    constexpr uint32_t SH = NCH == 8 ? 1 : 0;
+    return (c ^ ((r >> SH) & (NCH - 1))) << 4;
+}
+
+// The 128 K rows of key tile J (rows J*128.. of the plane), NCH/2 chunks per
+// lane: lane tid takes chunk tid % NCH of rows q*RPJ + tid / NCH. Rows past T
+// and chunks past the head read zero.
+template <int NCH> struct KStage {
+    u32x4 v[NCH / 2];
+};
+
+template <int NCH>
+__device__ __forceinline__ void k_fetch(KStage<NCH> &st, const char *kb0, uint32_t J, uint32_t T, uint32_t ldb,
+                                        uint32_t head_bytes, int tid)
+{
+    constexpr int RPJ = STATS_THREADS / NCH;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_at(kb0 + (uint64_t)J * ST * ldb);
+    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+    const uint32_t lim = c * 16 < head_bytes ? T : 0u; // a chunk past the head reads zero
+#pragma unroll
+    for (int q = 0; q < NCH / 2; ++q) {
+        const uint32_t r = (uint32_t)(q * RPJ) + r0;
+        const uint32_t ok = 0u - (uint32_t)(J * ST + r < lim);
+        const uint32_t vo = ((r * ldb + c * 16) & ok) | (OOB & ~ok);
+        st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)vo, 0, 0);
+    }
+}
+
+template <int NCH> __device__ __forceinline__ void k_store(const KStage<NCH> &st, char *kb, int tid)
+{
+    constexpr int RPJ = STATS_THREADS / NCH;
+    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+#pragma unroll
+    for (int q = 0; q < NCH / 2; ++q) {
+        const uint32_t r = (uint32_t)(q * RPJ) + r0;
+        *reinterpret_cast<u32x4 *>(kb + r * (NCH * 16) + kswz<NCH>(r, c)) = st.v[q];
+    }
+}
+
+// acc[kb] += K rows 32kb.. of the LDS tile times this wave's Q rows: lane
+// (r32, h) supplies chunk 2u + h of K row 32kb + r32 and of its Q row (the
+// same chunk permutation on both operands, so each product appears once).
+template <class E, int NCH>
+__device__ __forceinline__ void k_mma(f32x16 (&acc)[4], const char *kb, const u32x4 (&qf)[NCH / 2], int lane)
+{
+    constexpr int RB = NCH * 16;
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+#pragma unroll
+    for (int u = 0; u < NCH / 2; ++u) {
+        u32x4 kf[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t row = 32u * b + r32;
+            kf[b] = *reinterpret_cast<const u32x4 *>(kb + row * RB + kswz<NCH>(row, 2u * u + h));
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) mfma_chunk<E>(acc[b], kf[b], qf[u]);
+    }
+}
+
+// A rounded fp32 value the compiler may not look through: the offsets
+// ms = fl(m * c) must stay the rounded products the terms were built
+// against, not be fused (fp-contract) into a later subtraction.
+__device__ __forceinline__ float pinned(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Running statistics of one lane's query row over the keys it has seen:
+// m the largest raw dot product (-inf before any), ms = fl(m * c) (0 while
+// m = -inf), l = sum exp2(a * c - ms).
+struct RowRun {
+    float m, ms, l;
+};
+
+// Fold one step's 64 accumulators into the lane's running statistics.
+// DIAG: the step's keys overlap the block's own rows; keys after the lane's
+// row (t2 > t) are left out.
+template <bool DIAG>
+__device__ __forceinline__ void stats_update(const f32x16 (&acc)[4], RowRun &rr, float c, int w, int lane)
+{
+    const int r32 = lane & 31, h4 = 4 * (lane >> 5);
+    // Accumulator (b, r) is key 32b + 8(r/4) + 4h + r%4 of the step against
+    // query row 32w + lane%32: masked in the diagonal step when the key is
+    // later. Two passes over the accumulators (maximum, then the sum), so no
+    // copy of them is kept.
+    auto masked = [&](int b, int r) { return DIAG && 32 * b + 8 * (r >> 2) + h4 + (r & 3) > 32 * w + r32; };
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = masked(b, r) ? mx : fmaxf(mx, acc[b][r]);
+    const float mn = fmaxf(rr.m, mx);
+    const float msn = mn == -__builtin_inff() ? 0.f : pinned(mn * c);
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(acc[b][r], c, -msn));
+            s += masked(b, r) ? 0.f : e;
+        }
+    const float alpha = rr.m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(rr.ms - msn);
+    rr.l = rr.l * alpha + s;
+    rr.m = mn;
+    rr.ms = msn;
+}
+
+template <class E, int NCH>
+__global__ void __launch_bounds__(STATS_THREADS)
+row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, float *__restrict__ row_logsum,
+                 uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items,
+                 float scale)
+{
+    constexpr int RB = NCH * 16, NU = NCH / 2;
+    __shared__ __attribute__((aligned(16))) char kbuf[2 * ST * RB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+
+    const uint32_t id = (uint32_t)xcd_remap(blockIdx.x, items);
+    const uint32_t plane = id / npair, p = id - plane * npair;
+    const uint32_t b = plane / NH, nh = plane - b * NH;
+    const uint32_t ldb = 3u * C * (uint32_t)E::ES;
+    const uint32_t head_bytes = HS * (uint32_t)E::ES;
+    const char *qb0 = qkv + ((uint64_t)b * T * (3u * C) + (uint64_t)nh * HS) * E::ES; // Q row 0 of the plane
+    const char *kb0 = qb0 + (uint64_t)C * E::ES;                                     // K row 0
+    const float c = scale * LOG2E;
+
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t I = half == 0 ? p : nt - 1 - p;
+        if (half == 1 && I == p) break; // the middle block of an odd count has no partner
+        const uint32_t t0 = I * ST;
+
+        // Q fragments of rows t0 + 32w + r32: chunk 2u + h.
+        u32x4 qf[NU];
+        {
+            const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb0 + (uint64_t)t0 * ldb);
+            const uint32_t row = 32u * w + r32;
+            const bool row_ok = t0 + row < T;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const uint32_t ch = 2u * u + h;
+                const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
+                qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
+            }
+        }
+
+        RowRun rr{-__builtin_inff(), 0.f, 0.f};
+        KStage<NCH> st;
+        k_fetch<NCH>(st, kb0, 0, T, ldb, head_bytes, tid);
+        k_store<NCH>(st, kbuf, tid);
+        tri::lds_barrier();
+        for (uint32_t J = 0; J <= I; ++J) {
+            const bool more = J < I;
+            if (more) k_fetch<NCH>(st, kb0, J + 1, T, ldb, head_bytes, tid);
+            f32x16 acc[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
+            k_mma<E, NCH>(acc, kbuf + (J & 1) * (ST * RB), qf, lane);
+            if (more) {
+                stats_update<false>(acc, rr, c, w, lane);
+                k_store<NCH>(st, kbuf + ((J + 1) & 1) * (ST * RB), tid);
+            } else {
+                stats_update<true>(acc, rr, c, w, lane);
+            }
+            tri::lds_barrier(); // tile J + 1 written; tile J's reads done before it is rewritten
+        }
+
+        // Merge the two lane halves (the same row, disjoint keys) and write.
+        const float m2 = __shfl_xor(rr.m, 32), ms2 = __shfl_xor(rr.ms, 32), l2 = __shfl_xor(rr.l, 32);
+        const float mm = fmaxf(rr.m, m2);
+        const float msm = pinned(mm * c); // row 0 always holds key 0, so mm is finite
+        const float la = rr.m == -__builtin_inff() ? 0.f : rr.l * __builtin_amdgcn_exp2f(rr.ms - msm);
+        const float lb = m2 == -__builtin_inff() ? 0.f : l2 * __builtin_amdgcn_exp2f(ms2 - msm);
+        const float resid = fmaf(mm, c, -msm); // m * c - fl(m * c), exact
+        const uint32_t t = t0 + 32u * w + r32;
+        if (h == 0 && t < T) {
+            const uint64_t o = (uint64_t)plane * T + t;
+            row_max[o] = mm * scale;
+            row_logsum[o] = (__builtin_amdgcn_logf(la + lb) - resid) * LN2;
+        }
+    }
+}
+
+template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a, hipStream_t s)
+{
+    const int64_t nt = (a.T + ST - 1) / ST;
+    const int64_t npair = (nt + 1) / 2;
+    const int64_t items = a.B * a.NH * npair;
+    hipLaunchKernelGGL((row_stats_kernel<E, NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
+                       (const char *)a.qkv, const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum),
+                       (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)npair,
+                       (uint32_t)items, a.scale);
+    return hipGetLastError();
+}
+
+// Row statistics (row_max and row_logsum written through a.row_max /
+// a.row_logsum). The caller has checked that the fused path applies.
+template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStream_t s)
+{
+    if (a.HS * E::ES <= 128) return launch_row_stats_nch<E, 8>(a, s);
+    return launch_row_stats_nch<E, 16>(a, s);
+}
+
+// Softmax rows: the three-role score kernel with the softmax epilogue.
+// mode 0: log-probabilities, 1: probabilities.
+template <class E, class EP> hipError_t launch_softmax_ep(const TrimulArgs &a, hipStream_t s)
+{
+    const bool narrow = a.HS * E::ES <= 128;
+    if (a.out_kind == 1)
+        return narrow ? tri::launch_super<E, 8, tri::OBF16, EP>(a, s) : tri::launch_super<E, 16, tri::OBF16, EP>(a, s);
+    if (a.out_kind == 2)
+        return narrow ? tri::launch_super<E, 8, tri::OF16, EP>(a, s) : tri::launch_super<E, 16, tri::OF16, EP>(a, s);
+    return narrow ? tri::launch_super<E, 8, tri::OF32, EP>(a, s) : tri::launch_super<E, 16, tri::OF32, EP>(a, s);
+}
+
+template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode, hipStream_t s)
+{
+    if (mode == 0) return launch_softmax_ep<E, tri::EpLog>(a, s);
+    return launch_softmax_ep<E, tri::EpProb>(a, s);
+}
+
+} // namespace sm
+} // namespace cas

@@ -36,6 +36,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 namespace cas {
 namespace tri {
@@ -66,6 +67,33 @@ __device__ __forceinline__ uint32_t round16(OF16, float y) { return __builtin_bi
 __device__ __forceinline__ void st_nt16(char *p, uint32_t v)
 {
     __builtin_nontemporal_store((unsigned short)v, reinterpret_cast<unsigned short *>(p));
+}
+
+// What the score kernel writes per element (the epilogue):
+//   EpScore  the scaled score, NaN above the diagonal (llm.c trimul_cpu);
+//   EpLog    the log-probability (x - max) - logsum of the causal softmax,
+//            -inf above the diagonal;
+//   EpProb   its exponential, the probability, 0 above the diagonal.
+// The softmax takes each row's max and logsum from the row-stats kernel
+// (smallem "Kernels GPU", the softmax in two launches: row_stats, then
+// softmax_rows), recomputing the scores instead of reading them back.
+struct EpScore { static constexpr int KIND = 0; };
+struct EpLog { static constexpr int KIND = 1; };
+struct EpProb { static constexpr int KIND = 2; };
+
+// Fill of the masked entries, as one element's bits (fill32 for fp32 output,
+// fill16 for the 16-bit types) and as a dword of them.
+template <class EP> constexpr uint32_t fill32() { return EP::KIND == 0 ? QNAN_BITS : EP::KIND == 1 ? 0xFF800000u : 0u; }
+template <class O, class EP> constexpr uint32_t fill16()
+{
+    if constexpr (EP::KIND == 0) return O::NAN16;
+    else if constexpr (EP::KIND == 1) return std::is_same<O, OBF16>::value ? 0xFF80u : 0xFC00u; // -inf
+    else return 0u;
+}
+template <class O, class EP> constexpr uint32_t fill_dw()
+{
+    if constexpr (O::OB == 4) return fill32<EP>();
+    else return fill16<O, EP>() | (fill16<O, EP>() << 16);
 }
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -613,12 +641,31 @@ __device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, in
     }
 }
 
-// Scaled sub-tile -> LDS rows of out_pitch<O>() bytes, already in the output
-// type. Lane l holds output row 32qb + l%32 and columns 32kb + 8g + 4(l/32)
-// + 0..3 of acc[kb][qb][4g..]: one 16-byte (fp32) or 8-byte (16-bit) write.
+// The element written for accumulator value a: the fp32 score a * scale,
+// then for the softmax (x - max) - logsum of its row and, for
+// probabilities, the exponential of that (v_exp_f32 of the value times
+// log2(e)). The empty asm keeps the score a separate fp32 value: the compiler
+// may not fuse its rounding into the subtraction.
+template <class EP>
+__device__ __forceinline__ float epilogue(float a, float scale, float mx, float ls)
+{
+    float y = a * scale;
+    if constexpr (EP::KIND != 0) {
+        asm volatile("" : "+v"(y));
+        const float lp = (y - mx) - ls;
+        y = EP::KIND == 1 ? lp : __builtin_amdgcn_exp2f(lp * 1.44269504088896340736f);
+    }
+    return y;
+}
+
+// Sub-tile -> LDS rows of out_pitch<O>() bytes, already in the output type.
+// Lane l holds output row 32qb + l%32 and columns 32kb + 8g + 4(l/32) + 0..3
+// of acc[kb][qb][4g..]: one 16-byte (fp32) or 8-byte (16-bit) write.
 // DIAG: a sub-tile on the diagonal, whose entries right of it are masked.
-template <bool DIAG, class O>
-__device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, int lane)
+// mx / ls: the softmax statistics of the lane's two rows (qb = 0, 1).
+template <bool DIAG, class O, class EP = EpScore>
+__device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, int lane,
+                                               const float (&mx)[2], const float (&ls)[2])
 {
     constexpr int PITCH = out_pitch<O>();
     const int r32 = lane & 31, h4 = 4 * (lane >> 5);
@@ -631,25 +678,25 @@ __device__ __forceinline__ void subtile_to_lds(const f32x16 (&acc)[2][2], char *
             for (int g = 0; g < 4; ++g) {
                 char *dst = lds + lo + (uint32_t)(32 * qb * PITCH + (32 * kb + 8 * g) * O::OB);
                 if constexpr (O::OB == 4) {
-                    const float qnan = __uint_as_float(QNAN_BITS);
+                    const float fill = __uint_as_float(fill32<EP>());
                     f32x4v v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float y = acc[kb][qb][4 * g + e] * scale;
-                        v[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? qnan : y;
+                        const float y = epilogue<EP>(acc[kb][qb][4 * g + e], scale, mx[qb], ls[qb]);
+                        v[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? fill : y;
                     }
                     *reinterpret_cast<f32x4v *>(dst) = v;
                 } else {
                     uint32_t hv[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        // The fp32 score first, then the 16-bit rounding: kept
-                        // apart so the multiply and the conversion do not fuse
-                        // into one rounding (a mixed-precision FMA would).
-                        float y32 = acc[kb][qb][4 * g + e] * scale;
+                        // The fp32 value first, then the 16-bit rounding: kept
+                        // apart so the arithmetic and the conversion do not
+                        // fuse into one rounding (a mixed-precision FMA would).
+                        float y32 = epilogue<EP>(acc[kb][qb][4 * g + e], scale, mx[qb], ls[qb]);
                         asm volatile("" : "+v"(y32));
                         const uint32_t y = round16(O{}, y32);
-                        hv[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? O::NAN16 : y;
+                        hv[e] = (DIAG && 32 * kb + 8 * g + h4 + e > 32 * qb + r32) ? fill16<O, EP>() : y;
                     }
                     *reinterpret_cast<u32x2 *>(dst) = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
                 }
@@ -670,16 +717,17 @@ template <class O> __device__ __forceinline__ void st_elem(char *p, const u32x4 
     else st_nt16(p, v[e >> 1] >> (16 * (e & 1)));
 }
 
-// Rows [32H, 32H + 32) of the NaN mirror of tile `tl` (rows s0.. of the
-// plane, columns t0..): whole tiles with buffer stores whose row offset is a
+// Rows [32H, 32H + 32) of the mirror of tile `tl` (rows s0.. of the plane,
+// columns t0..), all masked (NaN for scores, EP's fill for the softmax): whole tiles with buffer stores whose row offset is a
 // scalar (no vector ALU work per store); else masked to the plane, 16 bytes
 // at a time when rows are 16-byte aligned (vec), one element otherwise.
-template <int H, class O, bool FULL>
+template <int H, class O, bool FULL, class EP = EpScore>
 __device__ __forceinline__ void nan_mirror_o(const Tile &tl, uint32_t T, uint32_t tby, int lane, bool vec)
 {
     using PC = Pieces<O>;
     char *base = tl.o + ((uint64_t)tl.s0 * T + (uint64_t)tl.t0) * O::OB;
-    const u32x4 n4 = {O::NAN_DW, O::NAN_DW, O::NAN_DW, O::NAN_DW};
+    constexpr uint32_t F = fill_dw<O, EP>();
+    const u32x4 n4 = {F, F, F, F};
     const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC;
     constexpr int S0 = H * PC::NI / 2, S1 = S0 + PC::NI / 2;
     if (FULL) {
@@ -700,15 +748,31 @@ __device__ __forceinline__ void nan_mirror_o(const Tile &tl, uint32_t T, uint32_
     }
 }
 
-template <class E, int NCH, class O>
+// Softmax statistics of the 128 query rows of super-tile `sp`, one value
+// per loader lane: lanes 0..127 (loader waves 0, 1) the row maxima, lanes
+// 128..255 the log-sums; rows past T read zero.
+__device__ __forceinline__ float stat_fetch(const float *row_max, const float *row_logsum, const Super &sp,
+                                            uint32_t T, int cl)
+{
+    const float *src = (cl < ST ? row_max : row_logsum) + (uint64_t)sp.plane * T; // uniform per wave
+    const uint32_t r = sp.T0 + (uint32_t)(cl & (ST - 1));
+    const uint32_t vo = r < T ? r * 4u : OOB;
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_at(reinterpret_cast<const char *>(src)),
+                                                                (int)vo, 0, 0));
+}
+
+template <class E, int NCH, class O, class EP = EpScore>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
-                    uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store)
+                    uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store,
+                    const float *__restrict__ row_max, const float *__restrict__ row_logsum)
 {
     constexpr int RB = NCH * 16;
     constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
+    constexpr bool SM = EP::KIND != 0; // softmax: per-row statistics ride along with the operand rows
     __shared__ __attribute__((aligned(16))) char opb[OP_ROWS * RB];
     __shared__ __attribute__((aligned(16))) char outb[NCOMP * OUT_BYTES];
+    __shared__ float stb[SM ? 2 * ST : 1]; // [0, 128): row max, [128, 256): row logsum
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -738,9 +802,12 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
     if (role == 2) {
         const int cl = slot * 64 + lane;
         Staged<NCH> st;
+        float sv = 0.f;
         if (steps > 0) {
             stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+            if constexpr (SM) sv = stat_fetch(row_max, row_logsum, cur.item(), T, cl);
             stage_store<NCH>(st, opb, cl);
+            if constexpr (SM) stb[cl] = sv;
         }
         lds_barrier(); // operand rows of step 0 in LDS
         for (uint32_t n = 0; n < steps; ++n) {
@@ -748,9 +815,13 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             if (more) {
                 cur.advance();
                 stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+                if constexpr (SM) sv = stat_fetch(row_max, row_logsum, cur.item(), T, cl);
             }
             lds_barrier(); // X: operand rows of step n consumed
-            if (more) stage_store<NCH>(st, opb, cl);
+            if (more) {
+                stage_store<NCH>(st, opb, cl);
+                if constexpr (SM) stb[cl] = sv;
+            }
             lds_barrier(); // Y: operand rows of step n + 1 in LDS
         }
     } else if (role == 0) {
@@ -760,6 +831,14 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             cur.advance();
             // Diagonal sub-tile (0, 1) is all NaN: its store wave writes it directly.
             const bool live = !(sp.diag && sa == 0 && sb == 1);
+            float mx[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f}; // statistics of rows 64sa + 32qb + lane%32
+            if constexpr (SM) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    mx[qb] = stb[64 * sa + 32 * qb + (lane & 31)];
+                    ls[qb] = stb[ST + 64 * sa + 32 * qb + (lane & 31)];
+                }
+            }
             f32x16 acc[2][2];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -768,8 +847,8 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
             lds_barrier(); // X: operand rows consumed, previous tile read back
             if (live) {
-                if (sp.diag && sa == sb) subtile_to_lds<true, O>(acc, my_out, scale, lane);
-                else subtile_to_lds<false, O>(acc, my_out, scale, lane);
+                if (sp.diag && sa == sb) subtile_to_lds<true, O, EP>(acc, my_out, scale, lane, mx, ls);
+                else subtile_to_lds<false, O, EP>(acc, my_out, scale, lane, mx, ls);
             }
             lds_barrier(); // Y: tile n in LDS
         }
@@ -778,7 +857,8 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         using PC = Pieces<O>;
         const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC; // row in a group, first column
         const uint32_t li = (uint32_t)(rr * PITCH + cc * O::OB);
-        const u32x4 n4 = {O::NAN_DW, O::NAN_DW, O::NAN_DW, O::NAN_DW};
+        constexpr uint32_t F = fill_dw<O, EP>();
+        const u32x4 n4 = {F, F, F, F}; // the masked pattern
         Tile pm;              // mirror of the previous step, second half pending
         bool pm_live = false, pm_full = false;
         for (uint32_t n = 0; n < steps; ++n) {
@@ -796,8 +876,8 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             const bool full = tl.rl == TB && tl.cl == TB;
             lds_barrier(); // X
             if (pm_live) { // second half of the previous step's mirror: needs nothing from LDS
-                if (pm_full) nan_mirror_o<1, O, true>(pm, T, tby, lane, vec);
-                else nan_mirror_o<1, O, false>(pm, T, tby, lane, vec);
+                if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+                else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
             }
             pm_live = false;
             lds_barrier(); // Y: tile n in LDS
@@ -843,22 +923,22 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
                 pm = tl;
                 pm_live = true;
                 pm_full = full && vec;
-                if (pm_full) nan_mirror_o<0, O, true>(tl, T, tby, lane, vec);
-                else nan_mirror_o<0, O, false>(tl, T, tby, lane, vec);
+                if (pm_full) nan_mirror_o<0, O, true, EP>(tl, T, tby, lane, vec);
+                else nan_mirror_o<0, O, false, EP>(tl, T, tby, lane, vec);
             }
         }
         if (pm_live) {
             const uint32_t tby = opaque_s(TBY);
-            if (pm_full) nan_mirror_o<1, O, true>(pm, T, tby, lane, vec);
-            else nan_mirror_o<1, O, false>(pm, T, tby, lane, vec);
+            if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+            else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
         }
     }
 }
 
-template <class E, int NCH, class O>
+template <class E, int NCH, class O, class EP = EpScore>
 hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_super_kernel<E, NCH, O>;
+    auto kern = trimul_super_kernel<E, NCH, O, EP>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -880,7 +960,7 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
                        (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
-                       (int)a.vec_store);
+                       (int)a.vec_store, a.row_max, a.row_logsum);
     return hipGetLastError();
 }
 

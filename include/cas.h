@@ -6,10 +6,12 @@
  *   cas_gemm_nt          dense Y = X W^T over ragged shapes
  *   cas_batch_matmul_nt  the same over a batch of independent products
  *   cas_trimul_causal    causal attention scores read straight from packed QKV
+ *   cas_causal_row_stats per-row max and log-sum of the causal scores
+ *   cas_causal_softmax   causal softmax (log-probabilities or probabilities)
  *
  * Conventions shared by every entry point
- *   - Pointers X, W, Y, qkv, out are DEVICE pointers (hipMalloc or any
- *     allocator of device memory). The caller owns every buffer; the library
+ *   - Pointers X, W, Y, qkv, out, row_max, row_logsum are DEVICE pointers
+ *     (hipMalloc or any allocator of device memory). The caller owns every buffer; the library
  *     allocates nothing, keeps no pointer after returning and never
  *     synchronises. Buffers must stay alive until the stream reaches the
  *     kernel.
@@ -21,11 +23,12 @@
  *     CAS_ERR_HIP and cas_last_hip_error() gives the hipError_t (per thread).
  *     Faults inside a kernel surface at the caller's next synchronisation.
  *   - Accepted (in_dtype, out_dtype) pairs: (F32, F32), (BF16, F32),
- *     (F16, F32); cas_trimul_causal also takes out_dtype BF16 or F16 with any
- *     input type. 16-bit inputs are raw bfloat16 / IEEE binary16 patterns.
+ *     (F16, F32); cas_trimul_causal and cas_causal_softmax also take out_dtype
+ *     BF16 or F16 with any input type. 16-bit inputs are raw bfloat16 / IEEE
+ *     binary16 patterns.
  *   - The output byte range may not overlap an input byte range.
- *   - Any alignment is accepted; 16-byte aligned bases and pitches select
- *     wider loads and stores, with the same results.
+ *   - Any alignment is accepted (the softmax: see its domain); 16-byte aligned
+ *     bases and pitches select wider loads and stores, with the same results.
  */
 #ifndef CAS_H
 #define CAS_H
@@ -45,8 +48,13 @@ typedef enum {
     CAS_ERR_DTYPE = -3,  /* unsupported (in_dtype, out_dtype) pair           */
     CAS_ERR_ALIAS = -4,  /* output bytes overlap input bytes                 */
     CAS_ERR_DEVICE = -5, /* current device is not gfx950, or no device       */
-    CAS_ERR_HIP = -6     /* the HIP launch failed; see cas_last_hip_error()  */
+    CAS_ERR_HIP = -6,    /* the HIP launch failed; see cas_last_hip_error()  */
+    CAS_ERR_UNSUPPORTED = -7, /* valid, but outside the kernels' domain       */
+    CAS_ERR_MODE = -8    /* unknown softmax mode                             */
 } cas_status;
+
+/* Output of cas_causal_softmax. */
+enum { CAS_SOFTMAX_LOG = 0, CAS_SOFTMAX_PROB = 1 };
 
 /*
  * Dense NT product (DietCode tests/codegen/test_1_local_padding.py,
@@ -112,6 +120,51 @@ int cas_batch_matmul_nt(const void *X, const void *W, void *Y, int64_t batch,
 int cas_trimul_causal(const void *qkv, void *out,
                       int64_t B, int64_t T, int64_t C, int64_t NH,
                       cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * Causal softmax of the scores, in the two launches of the smallem page
+ * "Kernels GPU" (its softmax section: row_stats computes each row's maximum
+ * and ln(sum exp(x - max)), kept as two numbers; softmax_rows then forms
+ * (x - max) - logsum per element, or the exponential of that), applied to
+ * the causal score rows of cas_trimul_causal. Neither call reads or writes
+ * the (T, T) scores: both recompute them from qkv, so the scores never
+ * travel to HBM.
+ *
+ * cas_causal_row_stats
+ *   qkv         as for cas_trimul_causal, of in_dtype.
+ *   row_max     (B, NH, T) fp32, written: max over t2 <= t of the fp32
+ *               score x[b,nh,t,t2] of cas_trimul_causal.
+ *   row_logsum  (B, NH, T) fp32, written: ln sum_{t2 <= t} exp(x - row_max).
+ *
+ * cas_causal_softmax
+ *   row_max, row_logsum   read: the statistics of cas_causal_row_stats on the
+ *               same qkv (the caller may pass others; they are used as given).
+ *   out         (B, NH, T, T) of out_dtype (fp32, bfloat16 or binary16):
+ *               mode CAS_SOFTMAX_LOG:  (x - row_max) - row_logsum for t2 <= t,
+ *                                      -inf for t2 > t;
+ *               mode CAS_SOFTMAX_PROB: exp of that for t2 <= t, 0 for t2 > t
+ *               (the softmax of the scores masked to -inf above the
+ *               diagonal, the mask llm.c's trimul_cpu names as an
+ *               alternative to its NaN). 16-bit outputs are the fp32 value
+ *               rounded once more (to nearest even).
+ *
+ * Both: fp32 arithmetic; the scores are bit-identical to cas_trimul_causal's
+ * (same products in the same order). Domain (else CAS_ERR_UNSUPPORTED, with
+ * nothing written): QKV rows in 16-byte pieces (qkv 16-byte aligned, HS and
+ * C times the element size multiples of 16), HS times the element size at
+ * most 256 bytes, T < 2^22, and 4-byte aligned statistics. Other limits,
+ * empty shapes and the no-overlap rule as for cas_trimul_causal: the
+ * statistics written by cas_causal_row_stats may overlap neither qkv nor each
+ * other, and out may overlap neither qkv nor the statistics it reads.
+ * Unknown mode: CAS_ERR_MODE.
+ */
+int cas_causal_row_stats(const void *qkv, float *row_max, float *row_logsum,
+                         int64_t B, int64_t T, int64_t C, int64_t NH,
+                         cas_dtype in_dtype, void *stream);
+
+int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_logsum, void *out,
+                       int64_t B, int64_t T, int64_t C, int64_t NH, int mode,
+                       cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *cas_status_string(int status);

@@ -156,3 +156,95 @@ def assert_scores(gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, dtype: st
         assert_exact(gpu[low], ref[low], what)
         return 0.0
     return assert_close(gpu[low], ref[low], bound[low], dtype, what)
+
+
+# ------------------------------------------------------------------ softmax
+#
+# Tolerance of the causal softmax, derived from the score tolerance above.
+# Let d_j be the allowance of score j of a row (the contract's, plus half an
+# fp32 ulp of the score since the oracle's softmax uses unrounded scores;
+# 0 where the scores are exact) and D = max_{j <= t} d_j. The row maximum and
+# log-sum-exp are 1-Lipschitz in the largest score error, so
+#   |row_max - m|           <= D
+#   |(x_j - m^) - L^ - lp_j| <= d_j + D + S + R (1 + |lp_j| + |L|)
+#   |row_logsum - L|        <= 2 D + S + R (1 + |L|)
+# with S = (n + 64) 2^-24 the fp32 summation of n = t + 1 terms (exp2 and
+# rescaling included) and R = 2^-21 the roundings of log2, ln 2 and the two
+# subtractions. A probability p = exp(lp) is then within p expm1(that + R(1 +
+# |lp|)), and at least 2^-126 (results below fp32's normal range may flush
+# to zero). 16-bit outputs add one rounding of the format, as for the scores.
+
+FILL = {("f32", "log"): 0xFF800000, ("f32", "prob"): 0x00000000,
+        ("bf16", "log"): 0xFF80, ("f16", "log"): 0xFC00, ("bf16", "prob"): 0x0000, ("f16", "prob"): 0x0000}
+SM_R = 2.0 ** -21
+
+
+def softmax_allowance(bound: np.ndarray, t_idx: np.ndarray, in_dtype: str, exact_scores: bool = False):
+    """(d (R, T), D (R,), S (R,), valid (R, T)) for rows of index t_idx."""
+    rel, ab = TOL[in_dtype]
+    T = bound.shape[-1]
+    valid = np.arange(T)[None, :] <= np.asarray(t_idx)[:, None]
+    if exact_scores:
+        d = np.zeros(bound.shape)
+    else:
+        d = np.where(valid, rel * bound + ab + 2.0 ** -24 * bound, 0.0)
+    return d, d.max(axis=1), (np.asarray(t_idx) + 65) * 2.0 ** -24, valid
+
+
+def _ratio(err, lim):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(lim > 0, err / np.where(lim > 0, lim, 1), np.where(err > 0, np.inf, 0.0))
+    return float(q.max()) if q.size else 0.0
+
+
+def assert_softmax_stats(mx, ls, mx_ref, ls_ref, bound, t_idx, in_dtype, what, exact_scores=False) -> float:
+    """GPU row statistics (R,) against the oracle's."""
+    _, D, S, _ = softmax_allowance(bound, t_idx, in_dtype, exact_scores)
+    mx, ls = np.asarray(mx, np.float64), np.asarray(ls, np.float64)
+    em, lm = np.abs(mx - mx_ref), D
+    el, ll = np.abs(ls - ls_ref), 2 * D + S + SM_R * (1 + np.abs(ls_ref))
+    for name, e, lim, g, r in (("row_max", em, lm, mx, mx_ref), ("row_logsum", el, ll, ls, ls_ref)):
+        bad = ~(e <= lim)
+        if bad.any():
+            i = int(np.argwhere(bad)[0][0])
+            raise AssertionError(f"{what}: {name} {int(bad.sum())} of {bad.size} out of tolerance; first row "
+                                 f"{i} (t={int(t_idx[i])}): gpu={g[i]!r} oracle={r[i]!r} allowed={lim[i]!r}")
+    return max(_ratio(em, lm), _ratio(el, ll))
+
+
+def assert_softmax(got, ref, ls_ref, bound, t_idx, in_dtype, mode, out_dtype, what, exact_scores=False) -> float:
+    """GPU softmax rows (R, T) against the oracle's (float64): float32 values
+    for fp32 output, raw uint16 patterns for 16-bit output. The masked part
+    (t2 > t) must be the fill pattern bit for bit."""
+    d, D, S, valid = softmax_allowance(bound, t_idx, in_dtype, exact_scores)
+    if out_dtype == "f32":
+        gb = np.asarray(got, np.float32).view(np.uint32)
+        vals = np.asarray(got, np.float32).astype(np.float64)
+    else:
+        gb = np.asarray(got).view(np.uint16)
+        vals = decode16(gb, out_dtype)
+    fill = FILL[(out_dtype, mode)]
+    if not np.all(gb[~valid] == fill):
+        n = int(np.sum(gb[~valid] != fill))
+        raise AssertionError(f"{what}: {n} masked elements are not the fill pattern {fill:#x}")
+    lsr = np.broadcast_to(np.abs(np.asarray(ls_ref))[:, None], ref.shape)
+    if mode == "log":
+        lim = d + D[:, None] + S[:, None] + SM_R * (1 + np.abs(ref) + lsr)
+    else:
+        lp = np.log(np.maximum(ref, 1e-300))
+        tl = d + D[:, None] + S[:, None] + SM_R * (1 + np.abs(lp) + lsr)
+        lim = ref * np.expm1(tl + SM_R * (1 + np.abs(lp))) + 2.0 ** -126
+    if out_dtype != "f32":
+        r16, a16 = ROUND16[out_dtype]
+        lim = lim + r16 * (np.abs(ref) + lim) + a16
+    v, r, lm = vals[valid], ref[valid], lim[valid]
+    if not np.all(np.isfinite(v)):
+        raise AssertionError(f"{what}: non-finite value on or below the diagonal")
+    err = np.abs(v - r)
+    bad = ~(err <= lm)
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        rows, cols = np.nonzero(valid)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; first (row {rows[i]}, "
+                             f"t2 {cols[i]}): gpu={v[i]!r} oracle={r[i]!r} allowed={lm[i]!r}")
+    return _ratio(err, lm)

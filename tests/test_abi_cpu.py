@@ -12,9 +12,10 @@ HEADER = os.path.join(ROOT, "include", "cas.h")
 
 F32, BF16, F16 = cas.CAS_F32, cas.CAS_BF16, cas.CAS_F16
 OK, ENULL, ESHAPE, EDTYPE, EALIAS, EDEV = 0, -1, -2, -3, -4, -5
+EUNSUP, EMODE = -7, -8
 
 # Fake, distinct, aligned addresses: validation never dereferences them.
-PX, PW, PY = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+PX, PW, PY, PZ = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000, 0x40_0000_0000
 
 
 @pytest.fixture(scope="module")
@@ -63,6 +64,14 @@ def bm(L, X=PX, W=PW, Y=PY, batch=3, M=4, N=5, K=6, ldx=None, ldw=None, ldy=None
 
 def t(L, qkv=PX, out=PY, B=2, T=5, C=12, NH=3, ind=F32, outd=F32):
     return L.cas_trimul_causal(qkv, out, B, T, C, NH, ind, outd, None)
+
+
+def rs(L, qkv=PX, mx=PY, ls=PW, B=2, T=5, C=12, NH=3, ind=F32):
+    return L.cas_causal_row_stats(qkv, mx, ls, B, T, C, NH, ind, None)
+
+
+def sm(L, qkv=PX, mx=PY, ls=PW, out=PZ, B=2, T=5, C=12, NH=3, mode=1, ind=F32, outd=F32):
+    return L.cas_causal_softmax(qkv, mx, ls, out, B, T, C, NH, mode, ind, outd, None)
 
 
 def test_gemm_rejections(L):
@@ -151,6 +160,48 @@ def test_trimul_empty_is_ok(L):
     assert t(L, NH=0, C=0) == OK
 
 
+def test_softmax_rejections(L):
+    for f in (rs, sm):
+        assert f(L, ind=5) == EDTYPE
+        assert f(L, B=-1) == ESHAPE
+        assert f(L, C=10, NH=3) == ESHAPE
+        assert f(L, qkv=None) == ENULL
+        assert f(L, mx=None) == ENULL
+        assert f(L, ls=None) == ENULL
+        assert f(L, B=2**40, T=2**20) == ESHAPE
+        assert f(L, B=1, T=4, C=2**22, NH=2) == ESHAPE
+        # outside the fused kernels' domain (valid arguments otherwise)
+        assert f(L, qkv=PX + 4) == EUNSUP                 # QKV rows not in 16-byte pieces
+        assert f(L, C=15, NH=3) == EUNSUP                  # HS = 5 fp32: 20-byte heads
+        assert f(L, C=3 * 65, NH=3, ind=F32) == EUNSUP     # HS = 65 fp32: 260-byte heads
+        assert f(L, C=3 * 136, NH=3, ind=BF16) == EUNSUP   # HS = 136 bf16: 272-byte heads
+        assert f(L, B=1, T=2**22, C=12, NH=3) == EUNSUP
+        assert f(L, mx=PY + 2) == EUNSUP                   # misaligned statistics
+        assert f(L, B=0) == OK and f(L, T=0) == OK and f(L, NH=0, C=0) == OK
+        assert f(L, qkv=None, mx=None, ls=None, B=0) == OK
+    assert sm(L, out=None) == ENULL
+    assert sm(L, mode=2) == EMODE and sm(L, mode=-1) == EMODE
+    assert sm(L, outd=9) == EDTYPE
+    # (B, NH, T) statistics of 4 bytes span 120 bytes.
+    assert rs(L, mx=PX + 16) == EALIAS                      # statistics inside qkv
+    assert rs(L, ls=PY + 116) == EALIAS                     # row_logsum over row_max's last value
+    assert sm(L, out=PY + 64) == EALIAS                     # output over the statistics it reads
+    assert sm(L, out=PX + 64) == EALIAS                     # output over qkv
+    assert sm(L, qkv=PZ + 288, outd=BF16) == EALIAS      # 16-bit output spans 300 bytes
+
+
+def test_softmax_valid_calls_reach_the_device_check(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert rs(L) == EDEV
+    assert rs(L, ind=BF16, C=3 * 128, NH=3) == EDEV        # 256-byte heads: the largest accepted
+    assert sm(L) == EDEV
+    assert sm(L, mode=0, outd=BF16, ind=F16, C=24) == EDEV  # HS = 8: 16-byte heads
+    assert sm(L, qkv=PZ + 304, outd=F16) == EDEV           # qkv (aligned) after the 300-byte output
+    assert sm(L, mx=PX + 16) == EDEV                       # statistics may overlap qkv when read
+
+
 def test_valid_calls_reach_the_device_check(L):
     # On a machine with no GPU a valid call fails at the device check only.
     import torch
@@ -169,3 +220,7 @@ def test_binding_validates_shapes():
         cas.gemm_nt(x, torch.zeros(5, 4, dtype=torch.float16))
     with pytest.raises(ValueError):
         cas.trimul_causal(torch.zeros(2, 3, 10), 2)
+    with pytest.raises(ValueError):
+        cas.causal_softmax(torch.zeros(2, 3, 12), 3, mode="softmax")
+    with pytest.raises(ValueError):
+        cas.causal_row_stats(torch.zeros(2, 3, 10), 2)

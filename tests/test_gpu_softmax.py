@@ -1,0 +1,243 @@
+"""GPU parity of the causal softmax (cas_causal_row_stats, cas_causal_softmax)
+against the CPU oracle, through the C ABI.
+
+The tolerance is derived from the score tolerance (see gpu_util): max and
+log-sum-exp are 1-Lipschitz in the largest score error, plus fp32 summation
+and rounding terms. Inputs whose scores are exact in fp32 (the ramp rows)
+leave only the latter, a tight check of the GPU's exp / log / sum arithmetic.
+Masked entries must be the fill pattern bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import causal_attention_score_amd as cas
+from causal_attention_score_amd import synth
+from gpu_util import (FILL, GUARD, assert_softmax, assert_softmax_stats, case, check_guards, guarded_output,
+                      guarded_output16, to_device)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "bf16", "f16"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0):
+    """Both launches into guarded buffers; returns (out rows (B*NH*T, T) as
+    float32 or raw uint16, row_max (B*NH*T,), row_logsum (B*NH*T,))."""
+    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    ns = B * NH * T
+    bm, mx = guarded_output(ns)
+    bl, ls = guarded_output(ns)
+    case(f"{label} causal_row_stats {dtype} B={B} T={T} NH={NH} HS={HS}")
+    cas.causal_row_stats(d, NH, row_max=mx.view(B, NH, T), row_logsum=ls.view(B, NH, T))
+    torch.cuda.synchronize()
+    check_guards(bm, ns)
+    check_guards(bl, ns)
+    n = B * NH * T * T
+    if out_dtype == "f32":
+        buf, flat = guarded_output(n + offset)
+    else:
+        buf, flat = guarded_output16(n + offset, out_dtype)
+    out = flat[offset:offset + n].view(B, NH, T, T)
+    case(f"{label} causal_softmax {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS} offset={offset}")
+    cas.causal_softmax(d, NH, mode, out=out, stats=(mx.view(B, NH, T), ls.view(B, NH, T)))
+    torch.cuda.synchronize()
+    check_guards(buf, n + offset)
+    if out_dtype == "f32":
+        h = flat.cpu().numpy()
+        assert np.all(h[:offset].view(np.uint32) == 0xFFFFFFFF), "wrote before the (shifted) output"
+    else:
+        h = flat.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.all(h[:offset] == 0xFFFF), "wrote before the (shifted) output"
+    return h[offset:].reshape(ns, T), mx.cpu().numpy().astype(np.float64), ls.cpu().numpy().astype(np.float64)
+
+
+def oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode):
+    out, mx, ls, bound = orc.causal_softmax(qkv, B, T, NH * HS, NH, dtype, mode)
+    ns = B * NH * T
+    return out.reshape(ns, T), mx.reshape(ns), ls.reshape(ns), bound.reshape(ns, T)
+
+
+def check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, exact_scores=False):
+    got, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, label, offset)
+    ref, mref, lref, bound = oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode)
+    t_idx = np.tile(np.arange(T), B * NH)
+    what = f"{label} {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS}"
+    q1 = assert_softmax_stats(mx, ls, mref, lref, bound, t_idx, dtype, what, exact_scores)
+    q2 = assert_softmax(got, ref, lref, bound, t_idx, dtype, mode, out_dtype, what, exact_scores)
+    return max(q1, q2)
+
+
+SM_T = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("HS", [8, 16, 40, 64])
+@pytest.mark.parametrize("T", SM_T)
+def test_softmax_ragged_f32(orc, T, HS, mode):
+    for (B, NH) in [(1, 1), (2, 3)]:
+        qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 7 + HS)
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="sweep")
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("HS", [8, 64, 128])
+@pytest.mark.parametrize("T", [1, 65, 128, 129, 300])
+def test_softmax_ragged_16bit(orc, T, HS, dtype, mode):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 11 + HS)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="sweep16")
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_softmax_ramp_rows_exact_scores(orc, dtype, mode):
+    """Ramp score rows slope * t2 (exact in fp32 for every input type): only
+    the fp32 exp / log / sum error is allowed. Slopes 0.25, -0.5, 0 and 64
+    (saturated: row maxima up to 64 * 299)."""
+    B, T, NH, HS = 2, 300, 4, 64
+    slopes = [0.25, -0.5, 0.0, 64.0]
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in slopes], dtype)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="ramp", exact_scores=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_softmax_stats_match_the_score_kernel(orc, dtype):
+    """The recomputed scores are the score kernel's, bit for bit: row_max is
+    the largest fp32 score of cas_trimul_causal's row, and the largest
+    log-probability of a row is exactly -row_logsum."""
+    B, T, NH, HS = 2, 333, 3, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=91)
+    d = to_device(qkv, dtype).view(B, T, -1)
+    case(f"stats vs scores {dtype}")
+    sc = cas.trimul_causal(d, NH)
+    lp, mx, ls = cas.causal_softmax(d, NH, "log")
+    torch.cuda.synchronize()
+    low = torch.tril(torch.ones(T, T, dtype=torch.bool, device="cuda"))
+    smax = torch.where(low, sc, torch.full_like(sc, -float("inf"))).amax(dim=-1)
+    assert torch.equal(smax.view(torch.int32), mx.view(torch.int32))
+    assert torch.equal(lp.amax(dim=-1).view(torch.int32), (-ls).view(torch.int32))
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [65, 128, 200, 256])
+def test_softmax_out16(orc, T, dtype, out_dtype, mode):
+    B, NH, HS = 2, 3, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 3 + 5)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="out16")
+
+
+@pytest.mark.parametrize("out_dtype,offset", [("f32", 1), ("bf16", 1), ("f16", 3)])
+def test_softmax_unaligned_output(orc, out_dtype, offset):
+    """Output off a 16-byte boundary: the per-element store path."""
+    B, T, NH, HS = 2, 136, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=17)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, "bf16", B, T, NH, HS, mode, out_dtype, label="unaligned", offset=offset)
+
+
+def test_softmax_saturated(orc):
+    """Inputs scaled by 64: scores of order 1e3-1e4 (exp of a score overflows
+    fp32). The two statistics stay separate numbers, so nothing overflows."""
+    B, T, NH, HS = 1, 257, 2, 64
+    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=5) * np.float32(64.0)).astype(np.float32)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="saturated")
+
+
+def test_softmax_rejections():
+    qkv = torch.zeros(2, 8, 3 * 2 * 5, device="cuda")        # HS = 5 fp32: 20-byte heads
+    for call in (lambda: cas.causal_softmax(qkv, 2), lambda: cas.causal_row_stats(qkv, 2)):
+        with pytest.raises(cas.CasError) as e:
+            call()
+        assert e.value.status == -7
+    with pytest.raises(ValueError):
+        cas.causal_softmax(torch.zeros(2, 8, 3 * 2 * 8, device="cuda"), 2, mode="softmax")
+
+
+def test_softmax_output_over_statistics_rejected():
+    qkv = torch.zeros(1, 8, 3 * 2 * 8, device="cuda")
+    buf = torch.zeros(4096, device="cuda")
+    mx, ls = buf[:16].view(1, 2, 8), buf[16:32].view(1, 2, 8)
+    cas.causal_row_stats(qkv, 2, row_max=mx, row_logsum=ls)
+    with pytest.raises(cas.CasError) as e:
+        cas.causal_softmax(qkv, 2, out=buf[:128].view(1, 2, 8, 8), stats=(mx, ls))
+    assert e.value.status == -4
+
+
+def test_softmax_empty_and_side_stream(orc):
+    assert cas.causal_softmax(torch.zeros(0, 5, 3 * 8, device="cuda"), 1)[0].numel() == 0
+    B, T, NH, HS = 1, 200, 4, 32
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=8)
+    d = to_device(qkv, "bf16").view(B, T, 3, NH, HS)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        case("softmax 5-d input on a side stream")
+        out, mx, ls = cas.causal_softmax(d, NH, "prob")
+    s.synchronize()
+    ref, mref, lref, bound = oracle_rows(orc, qkv, "bf16", B, T, NH, HS, "prob")
+    t_idx = np.tile(np.arange(T), B * NH)
+    assert_softmax(out.cpu().numpy().reshape(-1, T), ref, lref, bound, t_idx, "bf16", "prob", "f32", "side stream")
+
+
+@pytest.mark.parametrize("name,mode,out_dtype", [("trimul_f32_B8_T1024_NH12_HS64", "prob", "f32"),
+                                                 ("trimul_f32_B8_T1024_NH12_HS64", "log", "f32"),
+                                                 ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "bf16"),
+                                                 ("trimul_f16_B4_T4096_NH25_HS64", "log", "f16")])
+def test_workload_softmax_full_size(orc, name, mode, out_dtype):
+    """The benchmark's score shapes, in the launch configuration the benchmark
+    times: every statistic of three planes and the fill of the whole output
+    checked; whole planes and rows of every seventh plane compared."""
+    wl = synth.WORKLOADS[name]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    d = to_device(qkv, wl.dtype)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
+    out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
+    case(f"{wl.name} causal_softmax {mode} -> {out_dtype} full size")
+    _, mx, ls = cas.causal_softmax(d, NH, mode, out=out)
+    torch.cuda.synchronize()
+    fill = FILL[(out_dtype, mode)]
+    iv = out.view(torch.int32) if out_dtype == "f32" else out.view(torch.int16)
+    fv = fill if out_dtype == "f32" or fill < 0x8000 else fill - 0x10000
+    if out_dtype == "f32" and fill >= 0x80000000:
+        fv = fill - 0x100000000
+    up = torch.triu(torch.ones(T, T, dtype=torch.bool, device="cuda"), 1)
+    n_fill_up = int((iv[..., up] == fv).sum())
+    assert n_fill_up == B * NH * T * (T - 1) // 2, "fill above the diagonal"
+    assert bool(torch.isfinite(out[..., ~up]).all()), "non-finite value on or below the diagonal"
+    del up
+    worst = 0.0
+    planes = [(0, 0), (B - 1, NH - 1), (B // 2, NH // 3)]
+    for (b, h) in planes:
+        ref, mref, lref, bound = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, wl.dtype, mode)
+        t_idx = np.arange(T)
+        what = f"{wl.name} {mode} plane ({b},{h})"
+        worst = max(worst, assert_softmax_stats(mx[b, h].cpu().numpy(), ls[b, h].cpu().numpy(), mref, lref,
+                                                bound, t_idx, wl.dtype, what))
+        got = out[b, h].cpu().numpy() if out_dtype == "f32" else out[b, h].view(torch.int16).cpu().numpy()
+        worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
+    for p in range(0, B * NH, 7):
+        b, h = divmod(p, NH)
+        t0 = (p * 389) % (T - 8)
+        ref, mref, lref, bound = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, wl.dtype,
+                                                         mode)
+        t_idx = np.arange(t0, t0 + 8)
+        what = f"{wl.name} {mode} rows {t0}.. plane ({b},{h})"
+        worst = max(worst, assert_softmax_stats(mx[b, h, t0:t0 + 8].cpu().numpy(),
+                                                ls[b, h, t0:t0 + 8].cpu().numpy(), mref, lref, bound, t_idx,
+                                                wl.dtype, what))
+        blk = out[b, h, t0:t0 + 8]
+        got = blk.cpu().numpy() if out_dtype == "f32" else blk.view(torch.int16).cpu().numpy()
+        worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
+    print(f"{wl.name} softmax {mode} -> {out_dtype}: sampled max err/tol {worst:.3g}")
