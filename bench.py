@@ -170,6 +170,73 @@ def roofline_of(wl, ms: float, traffic_bytes, out_bytes: int = 4):
             "useful_flops": wl.useful_flops()}
 
 
+class SoftmaxParts:
+    """The two launches of the causal softmax (row statistics, softmax rows)
+    on one score workload, with device buffers ready."""
+
+    def __init__(self, wl, mode: str, out_dtype: str):
+        import torch
+
+        import causal_attention_score_amd as cas
+        (qkv,) = wl.inputs()
+        B, T, NH, _ = wl.dims
+        self.cas, self.NH, self.mode = cas, NH, mode
+        self.qkv = device_tensor(qkv, wl.dtype)
+        self.mx = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+        self.ls = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
+        self.out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
+
+    def stats(self):
+        self.cas.causal_row_stats(self.qkv, self.NH, row_max=self.mx, row_logsum=self.ls)
+
+    def rows(self):
+        self.cas.causal_softmax(self.qkv, self.NH, self.mode, out=self.out, stats=(self.mx, self.ls))
+
+
+def softmax_timings(steps: int):
+    """The causal softmax fused on the scores (both launches recompute Q K^T
+    from packed QKV; the (T, T) scores never reach HBM) on the two score
+    shapes. Row statistics: bounded by the MFMA work (fp32) or by the one
+    exp2 per score (16-bit inputs); softmax rows: HBM-bound like the scores
+    (Q and K read, statistics read, every output written once)."""
+    import torch
+
+    from causal_attention_score_amd import synth
+    out = {}
+    for name, mode, od in (("trimul_f32_B8_T1024_NH12_HS64", "prob", "f32"),
+                           ("trimul_f32_B8_T1024_NH12_HS64", "log", "f32"),
+                           ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "bf16"),
+                           ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "f32")):
+        wl = synth.WORKLOADS[name]
+        B, T, NH, HS = wl.dims
+        key = f"{name}_{mode}_out_{od}"
+        log(f"softmax timing {key}")
+        sp = SoftmaxParts(wl, mode, od)
+        n = max(5, steps // (10 if T > 2048 else 2))
+        ms_step, (ms_st, ms_rows), _ = time_parts([sp.stats, sp.rows], n, 2)
+        ob = 4 if od == "f32" else 2
+        rows_bytes = wl.algorithmic_bytes(ob) + 8 * B * NH * T
+        st_bytes = wl.algorithmic_bytes(0) + 8 * B * NH * T
+        scores = B * NH * T * (T + 1) // 2
+        out[key] = {
+            "step_us": round(ms_step * 1e3, 2),
+            "row_stats": {"avg_launch_us": round(ms_st * 1e3, 2),
+                          "useful_tflops": round(wl.useful_flops() / (ms_st * 1e-3) / 1e12, 2),
+                          "mfma_frac": round(wl.useful_flops() / (ms_st * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
+                          "exp_per_ns": round(scores / (ms_st * 1e6), 1),
+                          "hbm_gbs": round(st_bytes / (ms_st * 1e-3) / 1e9, 1)},
+            "softmax_rows": {"avg_launch_us": round(ms_rows * 1e3, 2),
+                             "roofline": {"bound": "hbm", "achieved": round(rows_bytes / (ms_rows * 1e-3) / 1e9, 1),
+                                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                          "frac": round(rows_bytes / (ms_rows * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                          "algorithmic_bytes": rows_bytes}},
+        }
+        del sp
+        torch.cuda.empty_cache()
+    return out
+
+
 def local_padding_ab(steps: int):
     """The dense fp32 layer with local padding (predicates only at fetch and
     writeback) against the same kernel with the bounds checks kept inside the
@@ -277,6 +344,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-ab", action="store_true", help="skip the local-padding A/B")
+    ap.add_argument("--no-softmax", action="store_true", help="skip the causal-softmax timings")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the kernels for the rocprofv3 HBM-traffic counter runs")
     args = ap.parse_args()
@@ -330,6 +398,10 @@ def main():
             del p
             torch.cuda.empty_cache()
 
+    smx = None
+    if not args.no_softmax:
+        smx = softmax_timings(args.steps)
+
     ab = None
     if not args.no_ab:
         ab = local_padding_ab(max(10, args.steps // 2))
@@ -351,6 +423,7 @@ def main():
         "cpu_baseline": cpu,
         "parts": parts_report,
         "bf16_workloads": bf16,
+        "causal_softmax": smx,
         "local_padding_ab": ab,
         "wall_ms_per_step": round(wall_ms, 5),
         "device": torch.cuda.get_device_name(0),

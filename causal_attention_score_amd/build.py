@@ -27,9 +27,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hi
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file extra flags. The softmax kernels keep their MFMA accumulators in
+# ordinary VGPRs: the row-statistics kernel reads every accumulator with
+# vector-ALU instructions, which would otherwise first copy each one out of
+# the accumulation registers (64 extra VALU instructions per step).
+EXTRA = {"softmax_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "softmax_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "softmax_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -135,33 +135,42 @@ struct RowRun {
     float m, ms, l;
 };
 
-// Fold one step's 64 accumulators into the lane's running statistics.
-// DIAG: the step's keys overlap the block's own rows; keys after the lane's
-// row (t2 > t) are left out.
-template <bool DIAG>
-__device__ __forceinline__ void stats_update(const f32x16 (&acc)[4], RowRun &rr, float c, int w, int lane)
+// Fold a step's accumulators into the lane's running statistics. Blocks
+// b < NB take part whole; block NB (if NB < 4) with the keys after the lane's
+// row masked: accumulator (b, r) is key 32b + 8(r/4) + 4h + r%4 of the step,
+// against query row 32w + lane%32. NB = 4: an off-diagonal step, nothing
+// masked. The diagonal step of wave w is NB = w: its blocks after w hold only
+// later keys and are skipped. Two passes over the accumulators (maximum,
+// then the sum), so no copy of them is kept.
+template <int NB>
+__device__ __forceinline__ void stats_update(const f32x16 (&acc)[4], RowRun &rr, float c, int lane)
 {
     const int r32 = lane & 31, h4 = 4 * (lane >> 5);
-    // Accumulator (b, r) is key 32b + 8(r/4) + 4h + r%4 of the step against
-    // query row 32w + lane%32: masked in the diagonal step when the key is
-    // later. Two passes over the accumulators (maximum, then the sum), so no
-    // copy of them is kept.
-    auto masked = [&](int b, int r) { return DIAG && 32 * b + 8 * (r >> 2) + h4 + (r & 3) > 32 * w + r32; };
+    float v[16]; // block NB, masked
+    if constexpr (NB < 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = 8 * (r >> 2) + h4 + (r & 3) > r32 ? -__builtin_inff() : acc[NB][r];
+    }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB && b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = masked(b, r) ? mx : fmaxf(mx, acc[b][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[b][r]);
+    if constexpr (NB < 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, v[r]);
+    }
     const float mn = fmaxf(rr.m, mx);
     const float msn = mn == -__builtin_inff() ? 0.f : pinned(mn * c);
     float s = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB && b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(acc[b][r], c, -msn));
-            s += masked(b, r) ? 0.f : e;
-        }
+        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[b][r], c, -msn));
+    if constexpr (NB < 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(fmaf(v[r], c, -msn)); // exp2(-inf) = 0
+    }
     const float alpha = rr.m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(rr.ms - msn);
     rr.l = rr.l * alpha + s;
     rr.m = mn;
@@ -214,21 +223,32 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
         KStage<NCH> st;
         k_fetch<NCH>(st, kb0, 0, T, ldb, head_bytes, tid);
         k_store<NCH>(st, kbuf, tid);
+        // Every load so far (Q fragments included) has landed: the loop's
+        // waits then only ever concern the key tile fetched a step ahead.
+        __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0)
         tri::lds_barrier();
-        for (uint32_t J = 0; J <= I; ++J) {
-            const bool more = J < I;
-            if (more) k_fetch<NCH>(st, kb0, J + 1, T, ldb, head_bytes, tid);
+        for (uint32_t J = 0; J < I; ++J) { // key tiles left of the diagonal: nothing masked
+            k_fetch<NCH>(st, kb0, J + 1, T, ldb, head_bytes, tid);
             f32x16 acc[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
             k_mma<E, NCH>(acc, kbuf + (J & 1) * (ST * RB), qf, lane);
-            if (more) {
-                stats_update<false>(acc, rr, c, w, lane);
-                k_store<NCH>(st, kbuf + ((J + 1) & 1) * (ST * RB), tid);
-            } else {
-                stats_update<true>(acc, rr, c, w, lane);
-            }
+            stats_update<4>(acc, rr, c, lane);
+            k_store<NCH>(st, kbuf + ((J + 1) & 1) * (ST * RB), tid);
             tri::lds_barrier(); // tile J + 1 written; tile J's reads done before it is rewritten
+        }
+        {   // the diagonal tile J = I
+            f32x16 acc[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
+            k_mma<E, NCH>(acc, kbuf + (I & 1) * (ST * RB), qf, lane);
+            switch (w) {
+            case 0: stats_update<0>(acc, rr, c, lane); break;
+            case 1: stats_update<1>(acc, rr, c, lane); break;
+            case 2: stats_update<2>(acc, rr, c, lane); break;
+            default: stats_update<3>(acc, rr, c, lane); break;
+            }
+            tri::lds_barrier(); // tile I's reads done before the next block's tile 0 is written
         }
 
         // Merge the two lane halves (the same row, disjoint keys) and write.
