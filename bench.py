@@ -181,6 +181,7 @@ class SoftmaxParts:
         (qkv,) = wl.inputs()
         B, T, NH, _ = wl.dims
         self.cas, self.NH, self.mode = cas, NH, mode
+        self.dims = (B, T, NH * wl.dims[3], NH)
         self.qkv = device_tensor(qkv, wl.dtype)
         self.mx = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
         self.ls = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
@@ -192,6 +193,14 @@ class SoftmaxParts:
 
     def rows(self):
         self.cas.causal_softmax(self.qkv, self.NH, self.mode, out=self.out, stats=(self.mx, self.ls))
+
+    def fused(self):
+        L = self.cas.lib()
+        st = L.cas_causal_softmax_fused(self.qkv.data_ptr(), self.out.data_ptr(), self.mx.data_ptr(),
+                                        self.ls.data_ptr(), *self.dims, self.cas.SOFTMAX_MODE[self.mode],
+                                        self.cas._dtype_code(self.qkv), self.cas._dtype_code(self.out),
+                                        self.cas._stream_ptr(self.qkv.device))
+        self.cas._check("cas_causal_softmax_fused", st)
 
 
 def softmax_timings(steps: int):
@@ -215,12 +224,18 @@ def softmax_timings(steps: int):
         sp = SoftmaxParts(wl, mode, od)
         n = max(5, steps // (10 if T > 2048 else 2))
         ms_step, (ms_st, ms_rows), _ = time_parts([sp.stats, sp.rows], n, 2)
+        _, (ms_fused,), _ = time_parts([sp.fused], n, 2)
         ob = 4 if od == "f32" else 2
         rows_bytes = wl.algorithmic_bytes(ob) + 8 * B * NH * T
         st_bytes = wl.algorithmic_bytes(0) + 8 * B * NH * T
         scores = B * NH * T * (T + 1) // 2
         out[key] = {
             "step_us": round(ms_step * 1e3, 2),
+            "fused": {"avg_launch_us": round(ms_fused * 1e3, 2),
+                      "roofline": {"bound": "hbm", "achieved": round(rows_bytes / (ms_fused * 1e-3) / 1e9, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(rows_bytes / (ms_fused * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes": rows_bytes}},
             "row_stats": {"avg_launch_us": round(ms_st * 1e3, 2),
                           "useful_tflops": round(wl.useful_flops() / (ms_st * 1e-3) / 1e12, 2),
                           "mfma_frac": round(wl.useful_flops() / (ms_st * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),

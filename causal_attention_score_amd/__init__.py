@@ -21,7 +21,7 @@ STATUS = {0: "CAS_OK", -1: "CAS_ERR_NULL", -2: "CAS_ERR_SHAPE", -3: "CAS_ERR_DTY
           -8: "CAS_ERR_MODE"}
 SOFTMAX_MODE = {"log": 0, "prob": 1}
 EXPORTS = ("cas_gemm_nt", "cas_batch_matmul_nt", "cas_trimul_causal", "cas_causal_row_stats", "cas_causal_softmax",
-           "cas_status_string", "cas_last_hip_error", "cas_version")
+           "cas_causal_softmax_fused", "cas_status_string", "cas_last_hip_error", "cas_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.cas_causal_row_stats.restype = ctypes.c_int
         L.cas_causal_softmax.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int] * 3 + [_vp]
         L.cas_causal_softmax.restype = ctypes.c_int
+        L.cas_causal_softmax_fused.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int] * 3 + [_vp]
+        L.cas_causal_softmax_fused.restype = ctypes.c_int
         L.cas_status_string.argtypes = [ctypes.c_int]
         L.cas_status_string.restype = ctypes.c_char_p
         L.cas_last_hip_error.restype = ctypes.c_int
@@ -191,17 +193,33 @@ def causal_row_stats(qkv, NH: int, row_max=None, row_logsum=None):
     return row_max, row_logsum
 
 
-def causal_softmax(qkv, NH: int, mode: str = "prob", out=None, out_dtype=None, stats=None):
-    """Causal softmax of the scores: both launches (row statistics, then the
-    softmax rows). mode "prob": probabilities, 0 above the diagonal; "log":
-    log-probabilities (x - row_max) - row_logsum, -inf above it. out_dtype
-    (or out's dtype): float32 (default), bfloat16 or float16. stats: an
-    optional (row_max, row_logsum) pair to use instead of computing it.
-    Returns (out, row_max, row_logsum)."""
+def causal_softmax(qkv, NH: int, mode: str = "prob", out=None, out_dtype=None, stats=None, fused: bool = True):
+    """Causal softmax of the scores. mode "prob": probabilities, 0 above the
+    diagonal; "log": log-probabilities (x - row_max) - row_logsum, -inf above
+    it. out_dtype (or out's dtype): float32 (default), bfloat16 or float16.
+    stats: an optional (row_max, row_logsum) pair to use as given (the
+    softmax-rows launch alone). Without stats, fused=True computes statistics
+    and rows in one launch, fused=False in the two launches of row statistics
+    then softmax rows. Returns (out, row_max, row_logsum)."""
     import torch
     if mode not in SOFTMAX_MODE:
         raise ValueError("mode must be 'prob' or 'log'")
     B, T, C = _qkv_dims(qkv, NH)
+    if stats is None and fused:
+        if out is None:
+            out = torch.empty((B, NH, T, T), dtype=out_dtype or torch.float32, device=qkv.device)
+        if out_dtype is not None and out.dtype != out_dtype:
+            raise TypeError("out does not have out_dtype")
+        if tuple(out.shape) != (B, NH, T, T) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous (B, NH, T, T) tensor")
+        row_max = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
+        row_logsum = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
+        _require_device(qkv, out)
+        st = lib().cas_causal_softmax_fused(qkv.data_ptr(), out.data_ptr(), row_max.data_ptr(),
+                                            row_logsum.data_ptr(), B, T, C, NH, SOFTMAX_MODE[mode],
+                                            _dtype_code(qkv), _dtype_code(out), _stream_ptr(qkv.device))
+        _check("cas_causal_softmax_fused", st)
+        return out, row_max, row_logsum
     row_max, row_logsum = stats if stats is not None else causal_row_stats(qkv, NH)
     if out is None:
         out = torch.empty((B, NH, T, T), dtype=out_dtype or torch.float32, device=qkv.device)

@@ -328,6 +328,32 @@ CAS_EXPORT int cas_causal_softmax(const void *qkv, const float *row_max, const f
     return launch_status(cas::launch_softmax(a, in_dtype, mode, (hipStream_t)stream));
 }
 
+CAS_EXPORT int cas_causal_softmax_fused(const void *qkv, void *out, float *row_max, float *row_logsum, int64_t B,
+                                        int64_t T, int64_t C, int64_t NH, int mode, cas_dtype in_dtype,
+                                        cas_dtype out_dtype, void *stream)
+{
+    if (!score_dtype_pair_ok(in_dtype, out_dtype)) return CAS_ERR_DTYPE;
+    if (mode != CAS_SOFTMAX_LOG && mode != CAS_SOFTMAX_PROB) return CAS_ERR_MODE;
+    const int ob = elem_size(out_dtype);
+    int64_t inb, stb, outb;
+    int vec = 1;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec);
+    if (rc == 1) return CAS_OK;
+    if (rc == CAS_ERR_SHAPE) return rc;
+    if (!qkv || !out || !row_max || !row_logsum) return CAS_ERR_NULL;
+    if (rc != CAS_OK) return rc;
+    if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0) return CAS_ERR_UNSUPPORTED;
+    // Three outputs: none may overlap qkv or another output.
+    if (overlap(out, outb, qkv, inb) || overlap(row_max, stb, qkv, inb) || overlap(row_logsum, stb, qkv, inb) ||
+        overlap(out, outb, row_max, stb) || overlap(out, outb, row_logsum, stb) ||
+        overlap(row_max, stb, row_logsum, stb))
+        return CAS_ERR_ALIAS;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+    const cas::TrimulArgs a = softmax_args(qkv, out, row_max, row_logsum, B, T, C, NH, ob, (int)out_dtype);
+    return launch_status(cas::launch_softmax_fused(a, in_dtype, mode, (hipStream_t)stream));
+}
+
 CAS_EXPORT const char *cas_status_string(int status)
 {
     switch (status) {

@@ -53,5 +53,7 @@ bool softmax_fits(int64_t T, int64_t HS, int es, int vec);
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH);
 hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
 hipError_t launch_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s);
+// Both in one launch: statistics written through a.row_max / a.row_logsum.
+hipError_t launch_softmax_fused(const TrimulArgs &a, int elem, int mode, hipStream_t s);
 
 } // namespace cas

@@ -10,6 +10,9 @@ hipError_t launch_row_stats_f16(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_softmax_f32(const TrimulArgs &a, int mode, hipStream_t s);
 hipError_t launch_softmax_bf16(const TrimulArgs &a, int mode, hipStream_t s);
 hipError_t launch_softmax_f16(const TrimulArgs &a, int mode, hipStream_t s);
+hipError_t launch_softmax_fused_f32(const TrimulArgs &a, int mode, hipStream_t s);
+hipError_t launch_softmax_fused_bf16(const TrimulArgs &a, int mode, hipStream_t s);
+hipError_t launch_softmax_fused_f16(const TrimulArgs &a, int mode, hipStream_t s);
 
 bool softmax_fits(int64_t T, int64_t HS, int es, int vec)
 {
@@ -39,6 +42,15 @@ hipError_t launch_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s
     case E_F32: return launch_softmax_f32(a, mode, s);
     case E_BF16: return launch_softmax_bf16(a, mode, s);
     default: return launch_softmax_f16(a, mode, s);
+    }
+}
+
+hipError_t launch_softmax_fused(const TrimulArgs &a, int elem, int mode, hipStream_t s)
+{
+    switch (elem) {
+    case E_F32: return launch_softmax_fused_f32(a, mode, s);
+    case E_BF16: return launch_softmax_fused_bf16(a, mode, s);
+    default: return launch_softmax_fused_f16(a, mode, s);
     }
 }
 

@@ -1,5 +1,5 @@
-// softmax_bf16.hip -- bf16 inputs of the causal softmax kernels (row statistics
-// and softmax rows; their own translation unit so the variants compile in
+// softmax_bf16.hip -- bf16 inputs of the causal softmax kernels (row statistics,
+// softmax rows and both fused; their own translation unit so the variants compile in
 // parallel).
 #include "softmax_kernel.hpp"
 
@@ -10,6 +10,11 @@ hipError_t launch_row_stats_bf16(const TrimulArgs &a, hipStream_t s) { return sm
 hipError_t launch_softmax_bf16(const TrimulArgs &a, int mode, hipStream_t s)
 {
     return sm::launch_softmax_impl<KBF16>(a, mode, s);
+}
+
+hipError_t launch_softmax_fused_bf16(const TrimulArgs &a, int mode, hipStream_t s)
+{
+    return sm::launch_softmax_fused_impl<KBF16>(a, mode, s);
 }
 
 } // namespace cas

@@ -267,6 +267,344 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused kernel: both launches in one. The three roles of the score kernel
+// (loader, compute, store waves; trimul_kernel.hpp) walk whole 128-row query
+// blocks. A block I takes 2 (I + 1) steps over key tiles 0..I: first the
+// statistics phase, where the compute waves fold their sub-tile's scores into
+// running statistics and nothing is stored, then the output phase, where they
+// write (x - max) - logsum (or its exponential) and the store waves stream it
+// with the mirror tiles, as for the scores. The statistics phase is vector-ALU
+// work with no HBM traffic of its own, so it runs while other workgroups'
+// store streams keep HBM busy, instead of being a launch of its own.
+//
+// Compute wave (sa, sb) holds query rows 64sa + 32qb + lane%32 (qb = 0, 1)
+// against keys 64sb.. of each super-tile. Per row, its two lane halves, then
+// the two waves sb = 0, 1 (through LDS), merge at the end of the statistics
+// phase; both waves of a pair then hold the final statistics in registers.
+// The store waves write them to row_max / row_logsum.
+//
+// Row blocks are dealt per XCD: XCD x owns planes [P x / 8, P (x+1) / 8) and
+// its nw workgroups take that range's blocks sorted longest first (position k
+// is block nt - 1 - k / P_x of plane base + k % P_x), in snake order: round r
+// gives workgroup w position r nw + w (r even) or r nw + nw - 1 - w (r odd).
+// Blocks differ in length (I + 1 tiles), and the snake keeps every
+// workgroup's total close to the mean. Each workgroup walks its rounds
+// starting from a different one (see FWalk::decode).
+// ---------------------------------------------------------------------------
+struct FWalk {
+    uint32_t nw, w, px, pbase, nt, nblk, rounds; // fixed per workgroup
+    uint32_t i, plane, I, J;
+    bool out_phase, valid;
+
+    // Round i of this workgroup's walk is round (i + w) % rounds of the deal:
+    // the workgroup still takes the same blocks, but neighbours start on
+    // blocks of different lengths, so their statistics phases (no stores)
+    // drift apart instead of all workgroups pausing their stores together.
+    __device__ __forceinline__ void decode()
+    {
+        valid = i < rounds;
+        const uint32_t r = valid ? (i + w) % rounds : 0;
+        const uint32_t k = r * nw + ((r & 1) ? nw - 1 - w : w);
+        if (valid) {
+            const uint32_t rank = k / px;
+            I = nt - 1 - rank;
+            plane = pbase + (k - rank * px);
+        }
+        J = 0;
+        out_phase = false;
+    }
+    __device__ __forceinline__ void init(uint32_t P, uint32_t nt_)
+    {
+        const uint32_t nwg = gridDim.x, x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
+        nw = q8 + (x < r8 ? 1u : 0u);
+        w = blockIdx.x / 8;
+        pbase = (uint32_t)((uint64_t)P * x / 8);
+        px = (uint32_t)((uint64_t)P * (x + 1) / 8) - pbase;
+        nt = nt_;
+        nblk = px * nt;
+        // rounds whose position exists for this workgroup: the full ones, and
+        // the last partial one if its position falls inside
+        const uint32_t full = nblk / nw, rem = nblk - full * nw;
+        rounds = full + (((full & 1) ? nw - 1 - w : w) < rem ? 1u : 0u);
+        i = 0;
+        decode();
+    }
+    __device__ __forceinline__ void advance()
+    {
+        if (J < I) {
+            ++J;
+        } else if (!out_phase) {
+            out_phase = true;
+            J = 0;
+        } else {
+            ++i;
+            decode();
+        }
+    }
+    __device__ __forceinline__ tri::Super item() const
+    {
+        tri::Super sp;
+        sp.plane = plane;
+        sp.T0 = I * ST;
+        sp.S0 = J * ST;
+        sp.diag = J == I;
+        return sp;
+    }
+};
+
+// Running statistics of a compute lane's two query rows (qb = 0, 1).
+struct Run2 {
+    float m[2], ms[2], l[2];
+};
+
+// Fold sub-tile scores acc[kb][qb] (keys 32kb + 8(r/4) + 4h + r%4, query
+// 32qb + lane%32, both within the sub-tile) into the running statistics.
+// DIAG: a sub-tile on the diagonal, whose keys after the query are left out.
+template <bool DIAG>
+__device__ __forceinline__ void sub_stats_update(const f32x16 (&acc)[2][2], Run2 &rn, float c, int lane)
+{
+    const int r32 = lane & 31, h4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        auto masked = [&](int kb, int r) { return DIAG && 32 * kb + 8 * (r >> 2) + h4 + (r & 3) > 32 * qb + r32; };
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = masked(kb, r) ? mx : fmaxf(mx, acc[kb][qb][r]);
+        const float mn = fmaxf(rn.m[qb], mx);
+        const float msn = mn == -__builtin_inff() ? 0.f : pinned(mn * c);
+        float s = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(acc[kb][qb][r], c, -msn));
+                s += masked(kb, r) ? 0.f : e;
+            }
+        const float alpha = rn.m[qb] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(rn.ms[qb] - msn);
+        rn.l[qb] = rn.l[qb] * alpha + s;
+        rn.m[qb] = mn;
+        rn.ms[qb] = msn;
+    }
+}
+
+// Merge statistics (m2, ms2, l2) into (m, ms, l): the larger maximum wins and
+// both sums are rescaled to its rounded offset.
+__device__ __forceinline__ void stats_merge(float &m, float &ms, float &l, float m2, float ms2, float l2, float c)
+{
+    const float mm = fmaxf(m, m2);
+    const float msm = mm == -__builtin_inff() ? 0.f : pinned(mm * c);
+    const float la = m == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(ms - msm);
+    const float lb = m2 == -__builtin_inff() ? 0.f : l2 * __builtin_amdgcn_exp2f(ms2 - msm);
+    m = mm;
+    ms = msm;
+    l = la + lb;
+}
+
+template <class E, int NCH, class O, class EP>
+__global__ void __launch_bounds__(tri::SUPER_THREADS)
+softmax_fused_kernel(const char *__restrict__ qkv, char *__restrict__ out, float *__restrict__ row_max,
+                     float *__restrict__ row_logsum, uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t P,
+                     uint32_t nt, float scale, int vec_store)
+{
+    using namespace tri;
+    constexpr int RB = NCH * 16;
+    constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
+    __shared__ __attribute__((aligned(16))) char opb[OP_ROWS * RB];
+    __shared__ __attribute__((aligned(16))) char outb[NCOMP * OUT_BYTES];
+    __shared__ float part[NCOMP][3][64]; // per compute wave: m, ms, l of its 64 rows (lane-merged)
+    __shared__ float stb[2 * ST];        // final statistics of the block: [0, 128) max, [128, 256) logsum
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int role = wave / NCOMP; // 0 compute, 1 store, 2 loader
+    const int slot = wave % NCOMP;
+    const int sa = slot >> 1, sb = slot & 1;
+    char *my_out = outb + slot * OUT_BYTES;
+    const uint32_t TBY = T * (uint32_t)O::OB;
+    const uint32_t ldb = 3u * C * (uint32_t)E::ES;
+    const bool vec = vec_store != 0;
+    const float c = scale * LOG2E;
+
+    FWalk cur;
+    cur.init(P, nt);
+
+    // Every wave passes the same barriers: one after the prologue, then X and
+    // Y once per step, for as many steps as the walk has.
+    if (role == 2) {
+        const int cl = slot * 64 + lane;
+        Staged<NCH> st;
+        if (cur.valid) {
+            stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+            stage_store<NCH>(st, opb, cl);
+        }
+        lds_barrier();
+        while (cur.valid) {
+            cur.advance();
+            const bool more = cur.valid;
+            if (more) stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+            lds_barrier(); // X: operand rows of this step consumed
+            if (more) stage_store<NCH>(st, opb, cl);
+            lds_barrier(); // Y: operand rows of the next step in LDS
+        }
+    } else if (role == 0) {
+        const int r32 = lane & 31;
+        Run2 rn;
+        float mx[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
+        lds_barrier();
+        while (cur.valid) {
+            const Super sp = cur.item();
+            const bool out_phase = cur.out_phase, first_out = out_phase && cur.J == 0;
+            const bool last_stats = !out_phase && cur.J == cur.I;
+            cur.advance();
+            if (!out_phase && sp.S0 == 0) { // a new block: statistics start empty
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    rn.m[qb] = -__builtin_inff();
+                    rn.ms[qb] = 0.f;
+                    rn.l[qb] = 0.f;
+                }
+            }
+            if (first_out) { // the partner wave's statistics (written before the last Y) complete the rows
+                const int ps = sa * 2 + (1 - sb);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const int row = 32 * qb + r32;
+                    stats_merge(rn.m[qb], rn.ms[qb], rn.l[qb], part[ps][0][row], part[ps][1][row], part[ps][2][row], c);
+                    mx[qb] = rn.m[qb] * scale;
+                    ls[qb] = (__builtin_amdgcn_logf(rn.l[qb]) - fmaf(rn.m[qb], c, -rn.ms[qb])) * LN2;
+                    if (sb == 0 && lane < 32) {
+                        stb[64 * sa + row] = mx[qb];
+                        stb[ST + 64 * sa + row] = ls[qb];
+                    }
+                }
+            }
+            // Diagonal sub-tile (0, 1) lies wholly above the diagonal: no work.
+            const bool live = !(sp.diag && sa == 0 && sb == 1);
+            f32x16 acc[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+            if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
+            lds_barrier(); // X: operand rows consumed, previous tile read back
+            if (out_phase) {
+                if (live) {
+                    if (sp.diag && sa == sb) subtile_to_lds<true, O, EP>(acc, my_out, scale, lane, mx, ls);
+                    else subtile_to_lds<false, O, EP>(acc, my_out, scale, lane, mx, ls);
+                }
+            } else {
+                if (live) {
+                    if (sp.diag && sa == sb) sub_stats_update<true>(acc, rn, c, lane);
+                    else sub_stats_update<false>(acc, rn, c, lane);
+                }
+                if (last_stats) { // merge the lane halves, publish for the partner wave
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        stats_merge(rn.m[qb], rn.ms[qb], rn.l[qb], __shfl_xor(rn.m[qb], 32),
+                                    __shfl_xor(rn.ms[qb], 32), __shfl_xor(rn.l[qb], 32), c);
+                        if (lane < 32) {
+                            part[slot][0][32 * qb + r32] = rn.m[qb];
+                            part[slot][1][32 * qb + r32] = rn.ms[qb];
+                            part[slot][2][32 * qb + r32] = rn.l[qb];
+                        }
+                    }
+                }
+            }
+            lds_barrier(); // Y: tile in LDS / partial statistics in LDS
+        }
+    } else {
+        lds_barrier();
+        Tile pm; // mirror of the previous output step, second half pending
+        bool pm_live = false, pm_full = false;
+        while (cur.valid) {
+            const Super sp = cur.item();
+            const bool out_phase = cur.out_phase, first_out = out_phase && cur.J == 0;
+            cur.advance();
+            const Tile tl = sub_tile<O>(sp, sa, sb, out, T);
+            const bool inside = tl.rl > 0 && tl.cl > 0;
+            const uint32_t tby = opaque_s(TBY);
+            const bool full = tl.rl == TB && tl.cl == TB;
+            lds_barrier(); // X
+            if (pm_live) {
+                if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+                else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
+            }
+            pm_live = false;
+            if (first_out) { // the block's statistics, written by the compute waves before X
+                const int cl = slot * 64 + lane;
+                const uint32_t row = sp.T0 + (uint32_t)(cl & (ST - 1));
+                if (row < T) (cl < ST ? row_max : row_logsum)[(uint64_t)sp.plane * T + row] = stb[cl];
+            }
+            lds_barrier(); // Y: tile in LDS
+            if (!out_phase || !inside) continue;
+            stream_subtile<O, EP>(tl, sp.diag && sa == 0 && sb == 1, full, vec, my_out, T, tby, lane);
+            if (!tl.diag) { // first half of the mirror now, the second after the next X
+                pm = tl;
+                pm_live = true;
+                pm_full = full && vec;
+                if (pm_full) nan_mirror_o<0, O, true, EP>(tl, T, tby, lane, vec);
+                else nan_mirror_o<0, O, false, EP>(tl, T, tby, lane, vec);
+            }
+        }
+        if (pm_live) {
+            const uint32_t tby = opaque_s(TBY);
+            if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+            else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
+        }
+    }
+}
+
+template <class E, int NCH, class O, class EP> hipError_t launch_fused(const TrimulArgs &a, hipStream_t s)
+{
+    auto kern = softmax_fused_kernel<E, NCH, O, EP>;
+    const int64_t nt = (a.T + ST - 1) / ST;
+    const int64_t P = a.B * a.NH;
+    static int resident_per_cu[64] = {0};
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (resident_per_cu[dev] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, tri::SUPER_THREADS, 0) != hipSuccess || n < 1)
+            n = 1;
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
+        cus[dev] = cu;
+        resident_per_cu[dev] = n;
+    }
+    // Persistent grid; no more workgroups than row blocks (each XCD's share).
+    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    const int64_t blocks = P * nt;
+    if (grid > 8 * ((blocks + 7) / 8)) grid = 8 * ((blocks + 7) / 8);
+    if (grid < 8) grid = 8;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(tri::SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
+                       const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (uint32_t)a.T,
+                       (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)P, (uint32_t)nt, a.scale,
+                       (int)a.vec_store);
+    return hipGetLastError();
+}
+
+template <class E, class EP> hipError_t launch_fused_ep(const TrimulArgs &a, hipStream_t s)
+{
+    const bool narrow = a.HS * E::ES <= 128;
+    if (a.out_kind == 1)
+        return narrow ? launch_fused<E, 8, tri::OBF16, EP>(a, s) : launch_fused<E, 16, tri::OBF16, EP>(a, s);
+    if (a.out_kind == 2)
+        return narrow ? launch_fused<E, 8, tri::OF16, EP>(a, s) : launch_fused<E, 16, tri::OF16, EP>(a, s);
+    return narrow ? launch_fused<E, 8, tri::OF32, EP>(a, s) : launch_fused<E, 16, tri::OF32, EP>(a, s);
+}
+
+// Both launches in one (softmax_fused_kernel); statistics written through
+// a.row_max / a.row_logsum, the rows through a.out.
+template <class E> hipError_t launch_softmax_fused_impl(const TrimulArgs &a, int mode, hipStream_t s)
+{
+    if (mode == 0) return launch_fused_ep<E, tri::EpLog>(a, s);
+    return launch_fused_ep<E, tri::EpProb>(a, s);
+}
+
 template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a, hipStream_t s)
 {
     const int64_t nt = (a.T + ST - 1) / ST;

@@ -761,6 +761,69 @@ __device__ __forceinline__ float stat_fetch(const float *row_max, const float *r
                                                                 (int)vo, 0, 0));
 }
 
+// Sub-tile (sa, sb) of super-tile `sp` as an output tile of the (T, T) plane.
+template <class O>
+__device__ __forceinline__ Tile sub_tile(const Super &sp, int sa, int sb, char *out, uint32_t T)
+{
+    Tile tl;
+    tl.t0 = sp.T0 + sa * TB;
+    tl.s0 = sp.S0 + sb * TB;
+    tl.o = out + (uint64_t)sp.plane * T * T * O::OB;
+    tl.rl = (int)((int64_t)T - tl.t0 < TB ? (int64_t)T - tl.t0 : TB);
+    tl.cl = (int)((int64_t)T - tl.s0 < TB ? (int64_t)T - tl.s0 : TB);
+    tl.diag = sp.diag;
+    return tl;
+}
+
+// A store wave streams its sub-tile from LDS (rows of out_pitch<O>() bytes)
+// to HBM, or the masked pattern when the sub-tile lies wholly above the
+// diagonal (all_masked). Whole tiles with 16-byte aligned rows (full && vec)
+// take one LDS read and one buffer store per RPI rows, the row offset a
+// scalar, so no vector ALU work: the SIMD's vector issue belongs to the
+// compute wave's MFMAs. Otherwise masked to the plane, 16 bytes at a time
+// where rows are aligned, one element otherwise.
+template <class O, class EP>
+__device__ __forceinline__ void stream_subtile(const Tile &tl, bool all_masked, bool full, bool vec,
+                                               const char *my_out, uint32_t T, uint32_t tby, int lane)
+{
+    using PC = Pieces<O>;
+    constexpr int PITCH = out_pitch<O>();
+    const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC; // row in a group, first column
+    const uint32_t li = (uint32_t)(rr * PITCH + cc * O::OB);
+    constexpr uint32_t F = fill_dw<O, EP>();
+    const u32x4 n4 = {F, F, F, F}; // the masked pattern
+    char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * O::OB;
+    const uint32_t go = opaque((uint32_t)rr * tby + (uint32_t)(cc * O::OB));
+    if (full && vec) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc_at(dst);
+        if (all_masked) {
+#pragma unroll
+            for (int s = 0; s < PC::NI; ++s)
+                __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby), ST_NT);
+        } else {
+#pragma unroll
+            for (int s = 0; s < PC::NI; ++s) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby), ST_NT);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < PC::NI; ++s) {
+            const u32x4 v = all_masked ? n4 : *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
+            const int row = s * PC::RPI + rr;
+            if (vec) {
+                if (cc < tl.cl && row < tl.rl) *reinterpret_cast<u32x4 *>(dst + ((uint32_t)(s * PC::RPI) * tby + go)) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < PC::EPC; ++e)
+                    if (row < tl.rl && cc + e < tl.cl)
+                        st_elem<O>(dst + ((uint32_t)row * tby + (uint32_t)((cc + e) * O::OB)), v, e);
+            }
+        }
+    }
+}
+
 template <class E, int NCH, class O, class EP = EpScore>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
@@ -854,23 +917,12 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         }
     } else {
         lds_barrier();
-        using PC = Pieces<O>;
-        const int rr = lane / PC::LPR, cc = (lane % PC::LPR) * PC::EPC; // row in a group, first column
-        const uint32_t li = (uint32_t)(rr * PITCH + cc * O::OB);
-        constexpr uint32_t F = fill_dw<O, EP>();
-        const u32x4 n4 = {F, F, F, F}; // the masked pattern
         Tile pm;              // mirror of the previous step, second half pending
         bool pm_live = false, pm_full = false;
         for (uint32_t n = 0; n < steps; ++n) {
             const Super sp = cur.item();
             cur.advance();
-            Tile tl;
-            tl.t0 = sp.T0 + sa * TB;
-            tl.s0 = sp.S0 + sb * TB;
-            tl.o = out + (uint64_t)sp.plane * T * T * O::OB;
-            tl.rl = (int)((int64_t)T - tl.t0 < TB ? (int64_t)T - tl.t0 : TB);
-            tl.cl = (int)((int64_t)T - tl.s0 < TB ? (int64_t)T - tl.s0 : TB);
-            tl.diag = sp.diag;
+            const Tile tl = sub_tile<O>(sp, sa, sb, out, T);
             const bool inside = tl.rl > 0 && tl.cl > 0; // else the sub-tile lies past the plane edge
             const uint32_t tby = opaque_s(TBY);
             const bool full = tl.rl == TB && tl.cl == TB;
@@ -882,43 +934,8 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             pm_live = false;
             lds_barrier(); // Y: tile n in LDS
             if (!inside) continue;
-            const bool all_nan = sp.diag && sa == 0 && sb == 1; // wholly above the diagonal
-            char *dst = tl.o + ((uint64_t)tl.t0 * T + (uint64_t)tl.s0) * O::OB;
-            const uint32_t go = opaque((uint32_t)rr * tby + (uint32_t)(cc * O::OB));
-            if (full && vec) {
-                // Whole tile: one LDS read and one buffer store per RPI rows,
-                // the row offset a scalar, so no vector ALU work: the SIMD's
-                // vector issue belongs to the compute wave's MFMAs.
-                const __amdgpu_buffer_rsrc_t rs = rsrc_at(dst);
-                if (all_nan) {
-#pragma unroll
-                    for (int s = 0; s < PC::NI; ++s)
-                        __builtin_amdgcn_raw_buffer_store_b128(n4, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby),
-                                                               ST_NT);
-                } else {
-#pragma unroll
-                    for (int s = 0; s < PC::NI; ++s) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
-                        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)go, (int)((uint32_t)(s * PC::RPI) * tby),
-                                                               ST_NT);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < PC::NI; ++s) {
-                    const u32x4 v = all_nan ? n4 : *reinterpret_cast<const u32x4 *>(my_out + li + s * PC::RPI * PITCH);
-                    const int row = s * PC::RPI + rr;
-                    if (vec) {
-                        if (cc < tl.cl && row < tl.rl)
-                            *reinterpret_cast<u32x4 *>(dst + ((uint32_t)(s * PC::RPI) * tby + go)) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < PC::EPC; ++e)
-                            if (row < tl.rl && cc + e < tl.cl)
-                                st_elem<O>(dst + ((uint32_t)row * tby + (uint32_t)((cc + e) * O::OB)), v, e);
-                    }
-                }
-            }
+            // Sub-tile (0, 1) of a diagonal super-tile lies wholly above the diagonal.
+            stream_subtile<O, EP>(tl, sp.diag && sa == 0 && sb == 1, full, vec, my_out, T, tby, lane);
             if (!tl.diag) { // first half of the mirror now, the second after the next X
                 pm = tl;
                 pm_live = true;

@@ -8,6 +8,7 @@
  *   cas_trimul_causal    causal attention scores read straight from packed QKV
  *   cas_causal_row_stats per-row max and log-sum of the causal scores
  *   cas_causal_softmax   causal softmax (log-probabilities or probabilities)
+ *   cas_causal_softmax_fused  both softmax launches in one
  *
  * Conventions shared by every entry point
  *   - Pointers X, W, Y, qkv, out, row_max, row_logsum are DEVICE pointers
@@ -165,6 +166,22 @@ int cas_causal_row_stats(const void *qkv, float *row_max, float *row_logsum,
 int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_logsum, void *out,
                        int64_t B, int64_t T, int64_t C, int64_t NH, int mode,
                        cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * Both softmax launches in one (the same outputs, statistics included):
+ * each 128-row block of queries has its statistics computed and then its
+ * rows written by the same workgroup, so the statistics work overlaps other
+ * blocks' output stores instead of taking a launch of its own. Arguments,
+ * modes, output types, domain and errors as for cas_causal_softmax, with
+ * row_max / row_logsum written (as by cas_causal_row_stats) instead of read;
+ * out, row_max and row_logsum may overlap neither qkv nor one another.
+ * row_max equals cas_causal_row_stats' bit for bit; row_logsum may differ from
+ * it in the last bits (another summation order), and out uses this call's
+ * own row_logsum.
+ */
+int cas_causal_softmax_fused(const void *qkv, void *out, float *row_max, float *row_logsum,
+                             int64_t B, int64_t T, int64_t C, int64_t NH, int mode,
+                             cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *cas_status_string(int status);

@@ -160,8 +160,12 @@ def test_trimul_empty_is_ok(L):
     assert t(L, NH=0, C=0) == OK
 
 
+def fu(L, qkv=PX, mx=PY, ls=PW, out=PZ, B=2, T=5, C=12, NH=3, mode=1, ind=F32, outd=F32):
+    return L.cas_causal_softmax_fused(qkv, out, mx, ls, B, T, C, NH, mode, ind, outd, None)
+
+
 def test_softmax_rejections(L):
-    for f in (rs, sm):
+    for f in (rs, sm, fu):
         assert f(L, ind=5) == EDTYPE
         assert f(L, B=-1) == ESHAPE
         assert f(L, C=10, NH=3) == ESHAPE
@@ -179,9 +183,15 @@ def test_softmax_rejections(L):
         assert f(L, mx=PY + 2) == EUNSUP                   # misaligned statistics
         assert f(L, B=0) == OK and f(L, T=0) == OK and f(L, NH=0, C=0) == OK
         assert f(L, qkv=None, mx=None, ls=None, B=0) == OK
-    assert sm(L, out=None) == ENULL
-    assert sm(L, mode=2) == EMODE and sm(L, mode=-1) == EMODE
-    assert sm(L, outd=9) == EDTYPE
+    for f in (sm, fu):
+        assert f(L, out=None) == ENULL
+        assert f(L, mode=2) == EMODE and f(L, mode=-1) == EMODE
+        assert f(L, outd=9) == EDTYPE
+    # the fused call writes all three: no overlap among them or with qkv
+    assert fu(L, mx=PX + 16) == EALIAS
+    assert fu(L, ls=PY + 116) == EALIAS
+    assert fu(L, out=PY) == EALIAS
+    assert fu(L, mx=PZ + 64) == EALIAS
     # (B, NH, T) statistics of 4 bytes span 120 bytes.
     assert rs(L, mx=PX + 16) == EALIAS                      # statistics inside qkv
     assert rs(L, ls=PY + 116) == EALIAS                     # row_logsum over row_max's last value
@@ -200,6 +210,8 @@ def test_softmax_valid_calls_reach_the_device_check(L):
     assert sm(L, mode=0, outd=BF16, ind=F16, C=24) == EDEV  # HS = 8: 16-byte heads
     assert sm(L, qkv=PZ + 304, outd=F16) == EDEV           # qkv (aligned) after the 300-byte output
     assert sm(L, mx=PX + 16) == EDEV                       # statistics may overlap qkv when read
+    assert fu(L) == EDEV
+    assert fu(L, mode=0, outd=F16, ind=BF16, C=24) == EDEV
 
 
 def test_valid_calls_reach_the_device_check(L):

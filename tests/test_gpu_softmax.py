@@ -27,27 +27,38 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0):
-    """Both launches into guarded buffers; returns (out rows (B*NH*T, T) as
-    float32 or raw uint16, row_max (B*NH*T,), row_logsum (B*NH*T,))."""
+LAUNCHES = ["two", "fused"]
+
+
+def run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, launch="two"):
+    """The softmax into guarded buffers, as two launches (row statistics, then
+    softmax rows) or the fused one; returns (out rows (B*NH*T, T) as float32
+    or raw uint16, row_max (B*NH*T,), row_logsum (B*NH*T,))."""
     d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
     ns = B * NH * T
     bm, mx = guarded_output(ns)
     bl, ls = guarded_output(ns)
-    case(f"{label} causal_row_stats {dtype} B={B} T={T} NH={NH} HS={HS}")
-    cas.causal_row_stats(d, NH, row_max=mx.view(B, NH, T), row_logsum=ls.view(B, NH, T))
-    torch.cuda.synchronize()
-    check_guards(bm, ns)
-    check_guards(bl, ns)
     n = B * NH * T * T
     if out_dtype == "f32":
         buf, flat = guarded_output(n + offset)
     else:
         buf, flat = guarded_output16(n + offset, out_dtype)
     out = flat[offset:offset + n].view(B, NH, T, T)
-    case(f"{label} causal_softmax {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS} offset={offset}")
-    cas.causal_softmax(d, NH, mode, out=out, stats=(mx.view(B, NH, T), ls.view(B, NH, T)))
+    if launch == "fused":
+        case(f"{label} causal_softmax_fused {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS} offset={offset}")
+        st = cas.lib().cas_causal_softmax_fused(d.data_ptr(), out.data_ptr(), mx.data_ptr(), ls.data_ptr(), B, T,
+                                                NH * HS, NH, cas.SOFTMAX_MODE[mode], cas._dtype_code(d),
+                                                cas._dtype_code(out), cas._stream_ptr(d.device))
+        assert st == 0, cas.status_string(st)
+    else:
+        case(f"{label} causal_row_stats {dtype} B={B} T={T} NH={NH} HS={HS}")
+        cas.causal_row_stats(d, NH, row_max=mx.view(B, NH, T), row_logsum=ls.view(B, NH, T))
+        torch.cuda.synchronize()
+        case(f"{label} causal_softmax {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS} offset={offset}")
+        cas.causal_softmax(d, NH, mode, out=out, stats=(mx.view(B, NH, T), ls.view(B, NH, T)))
     torch.cuda.synchronize()
+    check_guards(bm, ns)
+    check_guards(bl, ns)
     check_guards(buf, n + offset)
     if out_dtype == "f32":
         h = flat.cpu().numpy()
@@ -64,8 +75,9 @@ def oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode):
     return out.reshape(ns, T), mx.reshape(ns), ls.reshape(ns), bound.reshape(ns, T)
 
 
-def check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, exact_scores=False):
-    got, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, label, offset)
+def check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, exact_scores=False,
+               launch="two"):
+    got, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, f"{label} {launch}", offset, launch)
     ref, mref, lref, bound = oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode)
     t_idx = np.tile(np.arange(T), B * NH)
     what = f"{label} {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS}"
@@ -80,32 +92,35 @@ SM_T = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("HS", [8, 16, 40, 64])
 @pytest.mark.parametrize("T", SM_T)
-def test_softmax_ragged_f32(orc, T, HS, mode):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_ragged_f32(orc, launch, T, HS, mode):
     for (B, NH) in [(1, 1), (2, 3)]:
         qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 7 + HS)
-        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="sweep")
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="sweep", launch=launch)
 
 
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("HS", [8, 64, 128])
 @pytest.mark.parametrize("T", [1, 65, 128, 129, 300])
-def test_softmax_ragged_16bit(orc, T, HS, dtype, mode):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_ragged_16bit(orc, launch, T, HS, dtype, mode):
     B, NH = 2, 3
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 11 + HS)
-    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="sweep16")
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="sweep16", launch=launch)
 
 
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_softmax_ramp_rows_exact_scores(orc, dtype, mode):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_ramp_rows_exact_scores(orc, launch, dtype, mode):
     """Ramp score rows slope * t2 (exact in fp32 for every input type): only
     the fp32 exp / log / sum error is allowed. Slopes 0.25, -0.5, 0 and 64
     (saturated: row maxima up to 64 * 299)."""
     B, T, NH, HS = 2, 300, 4, 64
     slopes = [0.25, -0.5, 0.0, 64.0]
     qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in slopes], dtype)
-    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="ramp", exact_scores=True)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="ramp", exact_scores=True, launch=launch)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -118,40 +133,50 @@ def test_softmax_stats_match_the_score_kernel(orc, dtype):
     d = to_device(qkv, dtype).view(B, T, -1)
     case(f"stats vs scores {dtype}")
     sc = cas.trimul_causal(d, NH)
-    lp, mx, ls = cas.causal_softmax(d, NH, "log")
-    torch.cuda.synchronize()
     low = torch.tril(torch.ones(T, T, dtype=torch.bool, device="cuda"))
     smax = torch.where(low, sc, torch.full_like(sc, -float("inf"))).amax(dim=-1)
-    assert torch.equal(smax.view(torch.int32), mx.view(torch.int32))
-    assert torch.equal(lp.amax(dim=-1).view(torch.int32), (-ls).view(torch.int32))
+    res = {}
+    for fused in (False, True):
+        lp, mx, ls = cas.causal_softmax(d, NH, "log", fused=fused)
+        torch.cuda.synchronize()
+        assert torch.equal(smax.view(torch.int32), mx.view(torch.int32)), f"row_max (fused={fused})"
+        assert torch.equal(lp.amax(dim=-1).view(torch.int32), (-ls).view(torch.int32)), f"max lp (fused={fused})"
+        res[fused] = ls
+    # the two launches and the fused one sum in different orders: logsums agree to fp32 summation error
+    n = torch.arange(1, T + 1, device="cuda", dtype=torch.float32)
+    assert bool(((res[False] - res[True]).abs() <= (2 * n + 128) * 2.0 ** -24 + 2.0 ** -20).all())
 
 
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T", [65, 128, 200, 256])
-def test_softmax_out16(orc, T, dtype, out_dtype, mode):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_out16(orc, launch, T, dtype, out_dtype, mode):
     B, NH, HS = 2, 3, 64
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 3 + 5)
-    check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="out16")
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="out16", launch=launch)
 
 
 @pytest.mark.parametrize("out_dtype,offset", [("f32", 1), ("bf16", 1), ("f16", 3)])
-def test_softmax_unaligned_output(orc, out_dtype, offset):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_unaligned_output(orc, launch, out_dtype, offset):
     """Output off a 16-byte boundary: the per-element store path."""
     B, T, NH, HS = 2, 136, 2, 64
     qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=17)
     for mode in ("prob", "log"):
-        check_case(orc, qkv, "bf16", B, T, NH, HS, mode, out_dtype, label="unaligned", offset=offset)
+        check_case(orc, qkv, "bf16", B, T, NH, HS, mode, out_dtype, label="unaligned", offset=offset,
+                   launch=launch)
 
 
-def test_softmax_saturated(orc):
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_saturated(orc, launch):
     """Inputs scaled by 64: scores of order 1e3-1e4 (exp of a score overflows
     fp32). The two statistics stay separate numbers, so nothing overflows."""
     B, T, NH, HS = 1, 257, 2, 64
     qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=5) * np.float32(64.0)).astype(np.float32)
     for mode in ("prob", "log"):
-        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="saturated")
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="saturated", launch=launch)
 
 
 def test_softmax_rejections():
@@ -190,11 +215,12 @@ def test_softmax_empty_and_side_stream(orc):
     assert_softmax(out.cpu().numpy().reshape(-1, T), ref, lref, bound, t_idx, "bf16", "prob", "f32", "side stream")
 
 
-@pytest.mark.parametrize("name,mode,out_dtype", [("trimul_f32_B8_T1024_NH12_HS64", "prob", "f32"),
-                                                 ("trimul_f32_B8_T1024_NH12_HS64", "log", "f32"),
-                                                 ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "bf16"),
-                                                 ("trimul_f16_B4_T4096_NH25_HS64", "log", "f16")])
-def test_workload_softmax_full_size(orc, name, mode, out_dtype):
+@pytest.mark.parametrize("name,mode,out_dtype,fused", [("trimul_f32_B8_T1024_NH12_HS64", "prob", "f32", True),
+                                                       ("trimul_f32_B8_T1024_NH12_HS64", "log", "f32", False),
+                                                       ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "bf16", True),
+                                                       ("trimul_bf16_B4_T4096_NH25_HS64", "prob", "bf16", False),
+                                                       ("trimul_f16_B4_T4096_NH25_HS64", "log", "f16", True)])
+def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
     """The benchmark's score shapes, in the launch configuration the benchmark
     times: every statistic of three planes and the fill of the whole output
     checked; whole planes and rows of every seventh plane compared."""
@@ -204,8 +230,8 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype):
     d = to_device(qkv, wl.dtype)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
     out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
-    case(f"{wl.name} causal_softmax {mode} -> {out_dtype} full size")
-    _, mx, ls = cas.causal_softmax(d, NH, mode, out=out)
+    case(f"{wl.name} causal_softmax {mode} -> {out_dtype} full size, fused={fused}")
+    _, mx, ls = cas.causal_softmax(d, NH, mode, out=out, fused=fused)
     torch.cuda.synchronize()
     fill = FILL[(out_dtype, mode)]
     iv = out.view(torch.int32) if out_dtype == "f32" else out.view(torch.int16)
@@ -240,4 +266,4 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype):
         blk = out[b, h, t0:t0 + 8]
         got = blk.cpu().numpy() if out_dtype == "f32" else blk.view(torch.int16).cpu().numpy()
         worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
-    print(f"{wl.name} softmax {mode} -> {out_dtype}: sampled max err/tol {worst:.3g}")
+    print(f"{wl.name} softmax {mode} -> {out_dtype} fused={fused}: sampled max err/tol {worst:.3g}")
