@@ -39,6 +39,7 @@ class Oracle:
         lib.oracle_trimul_causal_rows.argtypes = [_vp, _vp, _vp] + [_i64] * 8 + [ctypes.c_int]
         lib.oracle_causal_softmax_rows.argtypes = [_vp] * 5 + [_i64] * 8 + [ctypes.c_int] * 2
         lib.oracle_causal_softmax.argtypes = [_vp] * 5 + [_i64] * 4 + [ctypes.c_int] * 2
+        lib.oracle_causal_attention_rows.argtypes = [_vp] * 3 + [_i64] * 7 + [ctypes.c_int]
         lib.oracle_tiled_matmul_count.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [_vp]
         lib.oracle_decode.argtypes = [_vp, ctypes.c_int, _i64, _vp]
         lib.oracle_round16.argtypes = [_vp, _vp, _i64, ctypes.c_int]
@@ -182,6 +183,23 @@ class Oracle:
         if rc:
             raise ValueError("oracle_causal_softmax_rows rejected its arguments")
         return out, mx, ls, bound
+
+    def causal_attention(self, qkv: np.ndarray, B: int, T: int, C: int, NH: int, dtype: str = "f32",
+                         with_abs: bool = True, b_range=None, t_range=None):
+        """Attention output y (B, T, C) (or batches b_range, rows t_range) of
+        the causal softmax times the value rows, float64; with the error
+        scale sum p |V| of each output."""
+        raw = self._raw(qkv, dtype)
+        bs = range(B) if b_range is None else b_range
+        t0, t1 = (0, T) if t_range is None else t_range
+        y = np.empty((len(bs), t1 - t0, C), dtype=np.float64)
+        aw = np.empty((len(bs), t1 - t0, C), dtype=np.float64) if with_abs else None
+        for n, b in enumerate(bs):
+            rc = self.lib.oracle_causal_attention_rows(self._p(raw), self._p(y[n]), self._p(None if aw is None else aw[n]),
+                                                       B, T, C, NH, b, t0, t1, DTYPE_CODE[dtype])
+            if rc:
+                raise ValueError("oracle_causal_attention_rows rejected its arguments")
+        return y, aw
 
     def tiled_matmul_count(self, A: np.ndarray, Bm: np.ndarray, bm: int, bn: int, bk: int):
         """Returns (A@B, loads, writes, padded_loads, padded_writes)."""

@@ -1,7 +1,7 @@
 /*
  * oracle.c -- plain, slow, obviously correct CPU oracle for the tiled-matmul
- * hot path (dense NT product, causal triangular attention scores and their
- * causal softmax).
+ * hot path (dense NT product, causal triangular attention scores, their
+ * causal softmax and the attention output).
  *
  * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this file's library. It shares no
@@ -328,6 +328,69 @@ int oracle_causal_softmax(const void *qkv, double *out, double *row_max, double 
         }
     }
     return 0;
+}
+
+/* -------------------------------------------------- attention output */
+
+/* The step after the softmax (the page's row_stats / softmax_rows feed it):
+ * the attention output of query row t of head nh is the probability-weighted
+ * sum of the value rows, y[b][t][nh][:] = sum_{t2 <= t} p[t][t2] V[b][nh][t2][:],
+ * V[b][nh][t2][:] = inp[b][t2][2][nh][:] (the third slot of the packed row,
+ * after Q and K). p is the causal softmax above, recomputed here in double.
+ * y is (rows t0..t1-1 of batch b) x C, head nh at columns nh*HS..; absw
+ * (nullable, same shape) gets sum_t2 p |V|, the error scale of each output. */
+int oracle_causal_attention_rows(const void *qkv, double *y, double *absw, int64_t B, int64_t T, int64_t C,
+                                 int64_t NH, int64_t b, int64_t t0, int64_t t1, int dtype)
+{
+    if (!dtype_ok(dtype) || B < 0 || T < 0 || NH <= 0 || C <= 0 || C % NH != 0) return -1;
+    if (b < 0 || b >= B || t0 < 0 || t1 > T || t0 > t1) return -1;
+    if (t1 == t0) return 0;
+    if (!qkv || !y) return -1;
+
+    const int64_t HS = C / NH;
+    const int64_t C3 = 3 * C;
+    const double scale = (double)oracle_trimul_scale(HS);
+    int failed = 0;
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t t = t0; t < t1; t++) {
+        for (int64_t nh = 0; nh < NH; nh++) {
+            double *s = (double *)malloc((size_t)(t + 1) * sizeof(double));
+            if (!s) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            const int64_t q0 = b * T * C3 + t * C3 + nh * HS;           /* Q[b][nh][t][:] */
+            for (int64_t t2 = 0; t2 <= t; t2++) {
+                const int64_t k0 = b * T * C3 + t2 * C3 + C + nh * HS;  /* K[b][nh][t2][:] */
+                double acc = 0.0;
+                for (int64_t i = 0; i < HS; i++) acc += elem(qkv, dtype, q0 + i) * elem(qkv, dtype, k0 + i);
+                s[t2] = scale * acc;                                     /* the score of (t, t2) */
+            }
+            /* the softmax of row t: its maximum, then its log-sum */
+            double rmax = s[0];
+            for (int64_t t2 = 1; t2 <= t; t2++) rmax = s[t2] > rmax ? s[t2] : rmax;
+            double rsum = 0.0;
+            for (int64_t t2 = 0; t2 <= t; t2++) rsum += exp(s[t2] - rmax);
+            const double rlog = log(rsum);
+            double *yrow = y + (t - t0) * C + nh * HS;
+            double *arow = absw ? absw + (t - t0) * C + nh * HS : 0;
+            for (int64_t i = 0; i < HS; i++) {
+                double acc = 0.0, aacc = 0.0;
+                for (int64_t t2 = 0; t2 <= t; t2++) {
+                    const double p = exp((s[t2] - rmax) - rlog);
+                    const double v = elem(qkv, dtype, b * T * C3 + t2 * C3 + 2 * C + nh * HS + i); /* V[b][nh][t2][i] */
+                    acc += p * v;
+                    aacc += p * fabs(v);
+                }
+                yrow[i] = acc;
+                if (arow) arow[i] = aacc;
+            }
+            free(s);
+        }
+    }
+    return failed ? -1 : 0;
 }
 
 /* ------------------------------------------- tiled count (kernl tutorial) */

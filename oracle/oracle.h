@@ -66,6 +66,13 @@ int oracle_causal_softmax_rows(const void *qkv, double *out, double *row_max, do
 int oracle_causal_softmax(const void *qkv, double *out, double *row_max, double *row_logsum,
                           double *bound, int64_t B, int64_t T, int64_t C, int64_t NH, int dtype, int mode);
 
+/* Attention output of rows t in [t0, t1) of batch b, every head:
+ * y[t][nh*HS + i] = sum_{t2 <= t} p[t][t2] V[b][nh][t2][i] with p the causal
+ * softmax (double throughout); y and absw (nullable: sum p |V|) are
+ * (t1-t0) x C doubles. */
+int oracle_causal_attention_rows(const void *qkv, double *y, double *absw, int64_t B, int64_t T, int64_t C,
+                                 int64_t NH, int64_t b, int64_t t0, int64_t t1, int dtype);
+
 /* The scale factor applied to every score: fp32 nearest to 1/sqrt(HS). */
 float oracle_trimul_scale(int64_t HS);
 

@@ -18,7 +18,10 @@ AssertionError when the oracle disagrees with:
   * library conversions of bfloat16 / binary16 (torch, numpy);
   * for the causal softmax: the closed form of geometric score rows, the
     max-free formula 1 / sum exp(s_k - s) on exact scores, rows summing to
-    one, saturated rows, and the pinned score oracle's row maxima.
+    one, saturated rows, and the pinned score oracle's row maxima;
+  * for the attention output: row 0 equals V's row 0, all-ones V gives ones,
+    uniform scores give running means, ramp scores give the expectation of
+    a truncated geometric law, and a max-free formula on exact scores.
 
 The same functions run against mutated copies of the oracle in
 test_oracle_mutations.py, which checks that every planted mistake is caught.
@@ -480,6 +483,102 @@ def pin_softmax_rows_match_full(orc):
         assert np.array_equal(pmx, mx[1, 2, 5:17]) and np.array_equal(pls, ls[1, 2, 5:17])
     _, tb = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f16")
     assert np.array_equal(bd, tb)  # the same error scale as the scores
+
+
+# ---------------------------------------------------- attention-output pins
+
+def v_views(qkv, B, T, NH, HS, dtype):
+    """V as (B, NH, T, HS), sliced from the packed layout by numpy reshapes."""
+    d = lib_decode(qkv, dtype).reshape(B, T, 3, NH, HS)
+    return d[:, :, 2].transpose(0, 2, 1, 3)
+
+
+def pin_attention_first_row_and_ones(orc):
+    """Row 0 attends only to itself (p = 1): y equals V's row 0 exactly. With
+    V all ones, every output is 1 (the probabilities sum to one)."""
+    B, T, NH, HS = 2, 17, 3, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", 41)
+    y, _ = orc.causal_attention(qkv, B, T, NH * HS, NH, "f32")
+    V = v_views(qkv, B, T, NH, HS, "f32")
+    assert np.array_equal(y[:, 0, :].reshape(B, NH, HS), V[:, :, 0, :])
+    ones = qkv.reshape(B, T, 3, NH * HS).copy()
+    ones[:, :, 2] = 1.0
+    y1, _ = orc.causal_attention(ones.reshape(B, T, -1), B, T, NH * HS, NH, "f32")
+    assert np.max(np.abs(y1 - 1.0)) <= 1e-13
+
+
+def pin_attention_uniform_is_running_mean(orc):
+    """Q = 0 makes every score 0, so p = 1/(t+1) and y[t] is the mean of V's
+    rows 0..t (numpy cumulative sums)."""
+    B, T, NH, HS = 1, 30, 2, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", 42)
+    d = qkv.reshape(B, T, 3, NH * HS).copy()
+    d[:, :, 0] = 0
+    d = d.reshape(B, T, -1)
+    y, _ = orc.causal_attention(d, B, T, NH * HS, NH, "bf16")
+    V = lib_decode(d, "bf16").reshape(B, T, 3, NH * HS)[:, :, 2]
+    mean = np.cumsum(V, axis=1) / np.arange(1, T + 1)[None, :, None]
+    assert np.max(np.abs(y - mean)) <= 1e-12
+
+
+def pin_attention_ramp_expectation(orc):
+    """Ramp scores a * t2 with V entry 0 = t2: y[t][0] is the expectation of
+    k under p_k proportional to exp(a k), k = 0..t (direct sums with
+    math.fsum, no maximum taken); the other entries are 0."""
+    B, T, NH, HS = 1, 40, 3, 64
+    slopes = [0.25, -0.5, 0.0]
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in slopes], "f32", v_ramp=True)
+    y, _ = orc.causal_attention(qkv, B, T, NH * HS, NH, "f32")
+    y = y.reshape(B, T, NH, HS)
+    for h, a in enumerate(slopes):
+        for t in range(T):
+            w = [math.exp(a * k) for k in range(t + 1)]
+            ref = math.fsum(k * wk for k, wk in enumerate(w)) / math.fsum(w)
+            assert abs(y[0, t, h, 0] - ref) <= 1e-12 * max(1.0, ref), (h, t, y[0, t, h, 0], ref)
+            assert np.all(y[0, t, h, 1:] == 0.0)
+
+
+def pin_attention_maxfree_bruteforce(orc):
+    """Small-integer inputs, exact rational scores: y_t = sum_j v_j / sum_k
+    exp(s_k - s_j) (no maximum, no logarithm), via math.fsum."""
+    for (B, T, NH, HS, seed, dtype) in [(2, 6, 2, 4, 43, "f32"), (1, 5, 2, 8, 44, "f16")]:
+        C = NH * HS
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed, "int")
+        y, aw = orc.causal_attention(qkv, B, T, C, NH, dtype)
+        Q, Kt = qk_views(qkv, B, T, NH, HS, dtype)
+        V = v_views(qkv, B, T, NH, HS, dtype)
+        sc = Fraction(float(orc.trimul_scale(HS)))
+        for b in range(B):
+            for h in range(NH):
+                for t in range(T):
+                    s = [float(sc * sum((Fraction(float(Q[b, h, t, i])) * Fraction(float(Kt[b, h, k, i]))
+                                         for i in range(HS)), Fraction(0))) for k in range(t + 1)]
+                    p = [1.0 / math.fsum(math.exp(sk - sj) for sk in s) for sj in s]
+                    for i in range(HS):
+                        ref = math.fsum(p[j] * float(V[b, h, j, i]) for j in range(t + 1))
+                        aref = math.fsum(p[j] * abs(float(V[b, h, j, i])) for j in range(t + 1))
+                        assert abs(y[b, t, h * HS + i] - ref) <= 1e-13 * max(1.0, aref), (dtype, b, h, t, i)
+                        assert abs(aw[b, t, h * HS + i] - aref) <= 1e-13 * max(1.0, aref)
+
+
+def pin_attention_saturated(orc):
+    """Scores of order 1e3-1e4 with V all ones: every output is 1 and finite
+    (exp of an unshifted score overflows; the row maximum keeps it in range)."""
+    B, T, NH, HS = 1, 24, 2, 16
+    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", 46) * np.float32(64.0)).astype(np.float32)
+    d = qkv.reshape(B, T, 3, NH * HS).copy()
+    d[:, :, 2] = 1.0
+    y, aw = orc.causal_attention(d.reshape(B, T, -1), B, T, NH * HS, NH, "f32")
+    assert np.all(np.isfinite(y)) and np.max(np.abs(y - 1.0)) <= 1e-12
+    assert np.max(np.abs(aw - 1.0)) <= 1e-12
+
+
+def pin_attention_rows_match_full(orc):
+    B, T, NH, HS = 2, 21, 3, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", 45)
+    full, fa = orc.causal_attention(qkv, B, T, NH * HS, NH, "bf16")
+    part, pa = orc.causal_attention(qkv, B, T, NH * HS, NH, "bf16", b_range=[1], t_range=(5, 17))
+    assert np.array_equal(part[0], full[1, 5:17]) and np.array_equal(pa[0], fa[1, 5:17])
 
 
 # ------------------------------------------------------- tiled-count pins

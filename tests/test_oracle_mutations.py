@@ -43,6 +43,16 @@ MUTATIONS = {
     "softmax_scale_dropped": ("s[t2] = acc * scale;", "s[t2] = acc;"),
     "softmax_log2_sum": ("const double lse = log(sum);", "const double lse = log2(sum);"),
     "softmax_logsum_added": ("const double lp = (s[t2] - mx) - lse;", "const double lp = (s[t2] - mx) + lse;"),
+    "attention_value_from_key_slot": ("t2 * C3 + 2 * C + nh * HS + i); /* V[b][nh][t2][i] */",
+                                      "t2 * C3 + C + nh * HS + i); /* V[b][nh][t2][i] */"),
+    "attention_diagonal_value_dropped": ("for (int64_t t2 = 0; t2 <= t; t2++) {\n                    const double p",
+                                         "for (int64_t t2 = 0; t2 < t; t2++) {\n                    const double p"),
+    "attention_logsum_dropped": ("const double p = exp((s[t2] - rmax) - rlog);", "const double p = exp(s[t2] - rmax);"),
+    "attention_scale_dropped": ("s[t2] = scale * acc;", "s[t2] = acc;"),
+    "attention_max_is_min": ("rmax = s[t2] > rmax ? s[t2] : rmax;", "rmax = s[t2] < rmax ? s[t2] : rmax;"),
+    "attention_diagonal_out_of_sum": ("t2 <= t; t2++) rsum += exp(s[t2] - rmax);", "t2 < t; t2++) rsum += exp(s[t2] - rmax);"),
+    "attention_key_row_of_query": ("t2 * C3 + C + nh * HS;  /* K[b][nh][t2][:] */",
+                                   "t * C3 + C + nh * HS;  /* K[b][nh][t2][:] */"),
     "f16_truncates": ("double q = rint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
 }
 
