@@ -182,6 +182,7 @@ class SoftmaxParts:
         B, T, NH, _ = wl.dims
         self.cas, self.NH, self.mode = cas, NH, mode
         self.dims = (B, T, NH * wl.dims[3], NH)
+        self.y = None
         self.qkv = device_tensor(qkv, wl.dtype)
         self.mx = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
         self.ls = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
@@ -193,6 +194,13 @@ class SoftmaxParts:
 
     def rows(self):
         self.cas.causal_softmax(self.qkv, self.NH, self.mode, out=self.out, stats=(self.mx, self.ls))
+
+    def attention(self):
+        if self.y is None:
+            import torch
+            B, T, C, _ = self.dims
+            self.y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+        self.cas.causal_attention(self.qkv, self.NH, y=self.y, stats=(self.mx, self.ls))
 
     def fused(self):
         L = self.cas.lib()
@@ -247,6 +255,17 @@ def softmax_timings(steps: int):
                                           "frac": round(rows_bytes / (ms_rows * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": rows_bytes}},
         }
+        if wl.dtype == "f32" and mode == "prob":
+            # the attention output: softmax probabilities times V (statistics from the launch above)
+            _, (ms_att,), _ = time_parts([sp.attention], n, 2)
+            flops = 2 * wl.useful_flops()  # Q K^T and P V over the causal triangle
+            out[key]["attention"] = {
+                "avg_launch_us": round(ms_att * 1e3, 2),
+                "with_row_stats_us": round((ms_att + ms_st) * 1e3, 2),
+                "roofline": {"bound": "mfma", "achieved": round(flops / (ms_att * 1e-3) / 1e12, 2),
+                             "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                             "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
+                             "useful_flops": flops}}
         del sp
         torch.cuda.empty_cache()
     return out

@@ -354,6 +354,31 @@ CAS_EXPORT int cas_causal_softmax_fused(const void *qkv, void *out, float *row_m
     return launch_status(cas::launch_softmax_fused(a, in_dtype, mode, (hipStream_t)stream));
 }
 
+CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const float *row_logsum, void *y,
+                                    int64_t B, int64_t T, int64_t C, int64_t NH, cas_dtype in_dtype,
+                                    cas_dtype out_dtype, void *stream)
+{
+    if (!dtype_in_ok(in_dtype) || out_dtype != CAS_F32) return CAS_ERR_DTYPE;
+    int64_t inb, stb, outb;
+    int vec = 1;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    if (rc == 1) return CAS_OK;
+    if (rc == CAS_ERR_SHAPE) return rc;
+    if (!qkv || !row_max || !row_logsum || !y) return CAS_ERR_NULL;
+    if (rc != CAS_OK) return rc;
+    if (in_dtype != CAS_F32) return CAS_ERR_UNSUPPORTED; // fp32 inputs only, for now
+    if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0 || (uintptr_t)y % 4 != 0)
+        return CAS_ERR_UNSUPPORTED;
+    int64_t yb = 0;
+    if (!mul_ok(inb / 3, 1, &yb)) return CAS_ERR_SHAPE; // (B, T, C) fp32: a third of the fp32 qkv bytes
+    if (overlap(y, yb, qkv, inb) || overlap(y, yb, row_max, stb) || overlap(y, yb, row_logsum, stb))
+        return CAS_ERR_ALIAS;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+    cas::TrimulArgs a = softmax_args(qkv, y, row_max, row_logsum, B, T, C, NH, 4, 0);
+    return launch_status(cas::launch_attention_f32(a, (hipStream_t)stream));
+}
+
 CAS_EXPORT const char *cas_status_string(int status)
 {
     switch (status) {

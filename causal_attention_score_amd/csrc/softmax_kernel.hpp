@@ -643,5 +643,210 @@ template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode,
     return launch_softmax_ep<E, tri::EpProb>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Attention output (the step after the softmax): y[b, t, nh, :] =
+// sum_{t2 <= t} p[t][t2] V[b, t2, nh, :], with p the probabilities of the
+// softmax-rows kernel, formed from the row statistics exactly as that kernel
+// forms them, and V the third slot of the packed rows. Neither the scores nor
+// the probabilities reach HBM: per key tile the scores are recomputed, turned
+// into p in registers and multiplied into the output on the MFMAs.
+//
+// fp32 inputs (v_mfma_f32_32x32x2_f32). A workgroup owns a pair of 128-row
+// query blocks (as the row-statistics kernel), four waves of 32 query rows,
+// each wave's Q fragments in registers; per step 64 keys: their K rows (for
+// D = K Q^T) and V rows are fetched a step ahead into double-buffered LDS.
+//  * Lane (r32, h) of the score MFMAs holds p for query r32 and keys
+//    8g + 4h + e of each 32-key block (accumulator r = 4g + e). The product
+//    P V contracts over keys, and its MFMA j takes key 8(j/4) + 4h + j%4 in
+//    k-slot h: exactly accumulator j, so P feeds the A operand from the
+//    registers it was computed in; the B operand is V[that key][d] from LDS.
+//  * V rows sit 288 bytes apart in LDS, so the two keys an MFMA reads (4
+//    apart) fall in different bank halves.
+// ---------------------------------------------------------------------------
+constexpr int AKT = 64;            // keys per attention step
+constexpr int AV_PITCH = 256 + 32; // LDS bytes per V row (HS * 4 <= 256)
+
+template <int NCH> struct AStage {
+    u32x4 k[NCH / 4], v[NCH / 4];
+};
+
+// The 64 K rows and 64 V rows of key tile J (rows J*64.. of the plane), NCH
+// 16-byte chunks per row; lane tid takes chunk tid % NCH of rows
+// q * (256 / NCH) + tid / NCH. Rows past T and chunks past the head read zero.
+template <int NCH>
+__device__ __forceinline__ void a_fetch(AStage<NCH> &st, const char *kb0, const char *vb0, uint32_t J, uint32_t T,
+                                        uint32_t ldb, uint32_t head_bytes, int tid)
+{
+    constexpr int RPJ = STATS_THREADS / NCH;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_at(kb0 + (uint64_t)J * AKT * ldb);
+    const __amdgpu_buffer_rsrc_t rv = rsrc_at(vb0 + (uint64_t)J * AKT * ldb);
+    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+    const uint32_t lim = c * 16 < head_bytes ? T : 0u;
+#pragma unroll
+    for (int q = 0; q < NCH / 4; ++q) {
+        const uint32_t r = (uint32_t)(q * RPJ) + r0;
+        const uint32_t ok = 0u - (uint32_t)(J * AKT + r < lim);
+        const uint32_t vo = ((r * ldb + c * 16) & ok) | (OOB & ~ok);
+        st.k[q] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)vo, 0, 0);
+        st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)vo, 0, 0);
+    }
+}
+
+template <int NCH> __device__ __forceinline__ void a_store(const AStage<NCH> &st, char *kbuf, char *vbuf, int tid)
+{
+    constexpr int RPJ = STATS_THREADS / NCH;
+    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+#pragma unroll
+    for (int q = 0; q < NCH / 4; ++q) {
+        const uint32_t r = (uint32_t)(q * RPJ) + r0;
+        *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.k[q];
+        *reinterpret_cast<u32x4 *>(vbuf + r * AV_PITCH + c * 16) = st.v[q];
+    }
+}
+
+// One step: scores of this wave's 32 queries against the tile's 64 keys,
+// p from the row statistics (mx: the row's max score, ls: its logsum), then
+// y[nb] += P V for the NBV 32-column blocks of the head. DIAG: keys after the
+// query (absolute index kabs0 + key > qabs) get p = 0.
+template <int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
+                                       const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
+                                       uint32_t kabs0, uint32_t qabs)
+{
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    constexpr int RB = NCH * 16;
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+#pragma unroll
+    for (int u = 0; u < NCH / 2; ++u) {
+        u32x4 kf[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t row = 32u * b + r32;
+            kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) mfma_chunk<KF32>(s[b], kf[b], qf[u]);
+    }
+    // p, in place, as the softmax-rows kernel forms it
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = tri::epilogue<tri::EpProb>(s[b][r], scale, mx, ls);
+            if (DIAG && kabs0 + 32u * b + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3) > qabs) p = 0.f;
+            s[b][r] = p;
+        }
+    // y += P V: MFMA j of key block b takes key 32b + 8(j/4) + 4h + j%4 in
+    // k-slot h: A = s[b][j] (this lane's p), B = V[key][32 nb + lane%32].
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
+                yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[b][j], v, yacc[nb], 0, 0, 0);
+            }
+        }
+}
+
+template <int NCH>
+__global__ void __launch_bounds__(STATS_THREADS)
+attention_f32_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
+                     const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
+                     uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items, float scale)
+{
+    constexpr int RB = NCH * 16, NU = NCH / 2;
+    constexpr int NBV = NCH * 16 / 4 / 32; // 32-column blocks of the head (HS * 4 <= RB bytes)
+    __shared__ __attribute__((aligned(16))) char kbuf[2 * AKT * RB];
+    __shared__ __attribute__((aligned(16))) char vbuf[2 * AKT * AV_PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+
+    const uint32_t id = (uint32_t)xcd_remap(blockIdx.x, items);
+    const uint32_t plane = id / npair, p = id - plane * npair;
+    const uint32_t b = plane / NH, nh = plane - b * NH;
+    const uint32_t ldb = 3u * C * 4u;
+    const uint32_t head_bytes = HS * 4u;
+    const char *qb0 = qkv + ((uint64_t)b * T * (3u * C) + (uint64_t)nh * HS) * 4; // Q row 0 of the plane
+    const char *kb0 = qb0 + (uint64_t)C * 4;                                    // K row 0
+    const char *vb0 = qb0 + (uint64_t)2 * C * 4;                                // V row 0
+
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t I = half == 0 ? p : nt - 1 - p;
+        if (half == 1 && I == p) break;
+        const uint32_t t0 = I * ST;
+        const uint32_t qabs = t0 + 32u * w + r32; // this lane's query row (score side)
+
+        u32x4 qf[NU];
+        {
+            const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb0 + (uint64_t)t0 * ldb);
+            const uint32_t row = 32u * w + r32;
+            const bool row_ok = t0 + row < T;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const uint32_t ch = 2u * u + h;
+                const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
+                qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
+            }
+        }
+        // the row statistics of this lane's query row (rows past T: unused)
+        const uint64_t so = (uint64_t)plane * T + (qabs < T ? qabs : T - 1);
+        const float mx = row_max[so], ls = row_logsum[so];
+
+        f32x16 yacc[NBV];
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) yacc[nb] = f32x16{};
+        const uint32_t nst = 2 * I + 2; // 64-key tiles 0 .. 2I + 1
+        AStage<NCH> st;
+        a_fetch<NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
+        a_store<NCH>(st, kbuf, vbuf, tid);
+        __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
+        tri::lds_barrier();
+        for (uint32_t J = 0; J < nst; ++J) {
+            const bool more = J + 1 < nst;
+            if (more) a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+            const char *kc = kbuf + (J & 1) * (AKT * RB), *vc = vbuf + (J & 1) * (AKT * AV_PITCH);
+            if (J + 2 < nst) a_step<NCH, NBV, false>(yacc, kc, vc, qf, scale, mx, ls, lane, J * AKT, qabs);
+            else a_step<NCH, NBV, true>(yacc, kc, vc, qf, scale, mx, ls, lane, J * AKT, qabs);
+            if (more) a_store<NCH>(st, kbuf + ((J + 1) & 1) * (AKT * RB), vbuf + ((J + 1) & 1) * (AKT * AV_PITCH), tid);
+            tri::lds_barrier();
+        }
+        // y rows: lane holds query 32w + 8(r/4) + 4h + r%4 and column 32nb + lane%32
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t t = t0 + 32u * w + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3);
+                const uint32_t d = 32u * nb + r32;
+                if (t < T && d < HS) y[((uint64_t)b * T + t) * C + (uint64_t)nh * HS + d] = yacc[nb][r];
+            }
+    }
+}
+
+template <int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
+{
+    const int64_t nt = (a.T + ST - 1) / ST;
+    const int64_t npair = (nt + 1) / 2;
+    const int64_t items = a.B * a.NH * npair;
+    hipLaunchKernelGGL((attention_f32_kernel<NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
+                       (const char *)a.qkv, a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
+                       (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)npair, (uint32_t)items, a.scale);
+    return hipGetLastError();
+}
+
+// Attention output into a.out ((B, T, C) fp32) from a.row_max / a.row_logsum.
+inline hipError_t launch_attention_f32_impl(const TrimulArgs &a, hipStream_t s)
+{
+    if (a.HS * 4 <= 128) return launch_attention_nch<8>(a, s);
+    return launch_attention_nch<16>(a, s);
+}
+
 } // namespace sm
 } // namespace cas

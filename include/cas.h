@@ -9,6 +9,7 @@
  *   cas_causal_row_stats per-row max and log-sum of the causal scores
  *   cas_causal_softmax   causal softmax (log-probabilities or probabilities)
  *   cas_causal_softmax_fused  both softmax launches in one
+ *   cas_causal_attention the attention output: softmax probabilities times V
  *
  * Conventions shared by every entry point
  *   - Pointers X, W, Y, qkv, out, row_max, row_logsum are DEVICE pointers
@@ -182,6 +183,23 @@ int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_l
 int cas_causal_softmax_fused(const void *qkv, void *out, float *row_max, float *row_logsum,
                              int64_t B, int64_t T, int64_t C, int64_t NH, int mode,
                              cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * Attention output, the step after the softmax:
+ *   y[b, t, nh*HS + i] = sum_{t2 <= t} p[b,nh,t,t2] * V[b,t2,nh,i]
+ * with V the third slot of the packed rows (element b*T*3C + t2*3C + 2C +
+ * nh*HS + i) and p the probabilities cas_causal_softmax (CAS_SOFTMAX_PROB)
+ * forms from the given row statistics (those of cas_causal_row_stats on the
+ * same qkv), bit for bit. Neither the scores nor p reach HBM: both are
+ * recomputed per key tile and multiplied into y on the MFMAs.
+ *   y   (B, T, C) fp32 (out_dtype must be CAS_F32), written whole.
+ * fp32 inputs only (16-bit inputs: CAS_ERR_UNSUPPORTED). Domain, limits and
+ * empty shapes as for cas_causal_softmax; y (and the 4-byte aligned
+ * statistics) may not overlap qkv, and y may not overlap the statistics.
+ */
+int cas_causal_attention(const void *qkv, const float *row_max, const float *row_logsum, void *y,
+                         int64_t B, int64_t T, int64_t C, int64_t NH,
+                         cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *cas_status_string(int status);

@@ -212,6 +212,36 @@ def assert_softmax_stats(mx, ls, mx_ref, ls_ref, bound, t_idx, in_dtype, what, e
     return max(_ratio(em, lm), _ratio(el, ll))
 
 
+def prob_limits(ref, ls_ref, bound, t_idx, in_dtype, exact_scores=False):
+    """Allowed |p_gpu - p| per element (rows (R, T) of fp32 probabilities),
+    and the mask of entries t2 <= t."""
+    d, D, S, valid = softmax_allowance(bound, t_idx, in_dtype, exact_scores)
+    lsr = np.broadcast_to(np.abs(np.asarray(ls_ref))[:, None], ref.shape)
+    lp = np.log(np.maximum(ref, 1e-300))
+    tl = d + D[:, None] + S[:, None] + SM_R * (1 + np.abs(lp) + lsr)
+    return np.where(valid, ref * np.expm1(tl + SM_R * (1 + np.abs(lp))) + 2.0 ** -126, 0.0), valid
+
+
+def assert_attention(got, ref, absw, p_ref, ls_ref, bound, t_idx, v_abs, in_dtype, what, exact_scores=False) -> float:
+    """Attention output rows (R, HS) of one head against the oracle's. Each
+    output is sum_j p_j v_j: with |p_gpu - p| <= lim_j (prob_limits) and an
+    fp32 sum of n products, |y_gpu - y| <= sum_j lim_j |v_j| + S sum_j p_j |v_j|
+    (S as for the softmax); v_abs is |V| (T, HS) of the head."""
+    lim_p, _ = prob_limits(p_ref, ls_ref, bound, t_idx, in_dtype, exact_scores)
+    S = (np.asarray(t_idx) + 65) * 2.0 ** -24
+    lim = lim_p @ v_abs + S[:, None] * absw
+    g = np.asarray(got, np.float64)
+    if not np.all(np.isfinite(g)):
+        raise AssertionError(f"{what}: non-finite output")
+    err = np.abs(g - ref)
+    bad = ~(err <= lim)
+    if bad.any():
+        i, j = (int(x) for x in np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; first (row {i}, col {j}): "
+                             f"gpu={g[i, j]!r} oracle={ref[i, j]!r} allowed={lim[i, j]!r}")
+    return _ratio(err, lim)
+
+
 def assert_softmax(got, ref, ls_ref, bound, t_idx, in_dtype, mode, out_dtype, what, exact_scores=False) -> float:
     """GPU softmax rows (R, T) against the oracle's (float64): float32 values
     for fp32 output, raw uint16 patterns for 16-bit output. The masked part

@@ -164,6 +164,27 @@ def fu(L, qkv=PX, mx=PY, ls=PW, out=PZ, B=2, T=5, C=12, NH=3, mode=1, ind=F32, o
     return L.cas_causal_softmax_fused(qkv, out, mx, ls, B, T, C, NH, mode, ind, outd, None)
 
 
+def at(L, qkv=PX, mx=PY, ls=PW, y=PZ, B=2, T=5, C=12, NH=3, ind=F32, outd=F32):
+    return L.cas_causal_attention(qkv, mx, ls, y, B, T, C, NH, ind, outd, None)
+
+
+def test_attention_rejections(L):
+    import torch
+    assert at(L, ind=5) == EDTYPE
+    assert at(L, outd=BF16) == EDTYPE
+    assert at(L, B=-1) == ESHAPE
+    assert at(L, C=10, NH=3) == ESHAPE
+    assert at(L, y=None) == ENULL and at(L, qkv=None) == ENULL and at(L, mx=None) == ENULL
+    assert at(L, ind=BF16, C=24) == EUNSUP                  # 16-bit inputs: not yet
+    assert at(L, C=15, NH=3) == EUNSUP                      # 20-byte heads
+    assert at(L, y=PX + 16) == EALIAS                       # y inside qkv
+    assert at(L, y=PY + 64) == EALIAS                       # y over the statistics
+    assert at(L, B=0) == OK and at(L, T=0) == OK
+    if not torch.cuda.is_available():
+        assert at(L) == EDEV
+        assert at(L, mx=PX + 16, ls=PX + 32) == EDEV        # the statistics are only read
+
+
 def test_softmax_rejections(L):
     for f in (rs, sm, fu):
         assert f(L, ind=5) == EDTYPE

@@ -12,8 +12,8 @@ import torch
 
 import causal_attention_score_amd as cas
 from causal_attention_score_amd import synth
-from gpu_util import (FILL, GUARD, assert_softmax, assert_softmax_stats, case, check_guards, guarded_output,
-                      guarded_output16, to_device)
+from gpu_util import (FILL, GUARD, assert_attention, assert_softmax, assert_softmax_stats, case, check_guards,
+                      guarded_output, guarded_output16, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,3 +267,85 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
         got = blk.cpu().numpy() if out_dtype == "f32" else blk.view(torch.int16).cpu().numpy()
         worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
     print(f"{wl.name} softmax {mode} -> {out_dtype} fused={fused}: sampled max err/tol {worst:.3g}")
+
+
+# ------------------------------------------------------------ attention output
+
+def run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats=False):
+    """Row statistics (two-launch or fused softmax), then the attention output
+    into a guarded buffer; returns y (B, T, C)."""
+    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    C = NH * HS
+    if fused_stats:
+        _, mx, ls = cas.causal_softmax(d, NH, "prob", fused=True)
+    else:
+        mx, ls = cas.causal_row_stats(d, NH)
+    n = B * T * C
+    buf, flat = guarded_output(n)
+    case(f"{label} causal_attention {dtype} B={B} T={T} NH={NH} HS={HS}")
+    cas.causal_attention(d, NH, y=flat.view(B, T, C), stats=(mx, ls))
+    torch.cuda.synchronize()
+    check_guards(buf, n)
+    return flat.view(B, T, C).cpu().numpy()
+
+
+def check_attention(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, fused_stats=False, b_t=None):
+    """GPU attention output against the oracle's, head by head. b_t: optional
+    list of (b, t0, t1) row ranges to compare (default: everything)."""
+    C = NH * HS
+    y = run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats)
+    V = np.abs(orc.decode(qkv, dtype).reshape(B, T, 3, NH, HS)[:, :, 2]) if dtype != "f32" else \
+        np.abs(qkv.reshape(B, T, 3, NH, HS)[:, :, 2].astype(np.float64))
+    worst = 0.0
+    for (b, t0, t1) in (b_t or [(b, 0, T) for b in range(B)]):
+        yr, aw = orc.causal_attention(qkv, B, T, C, NH, dtype, b_range=[b], t_range=(t0, t1))
+        for h in range(NH):
+            p, _, lr, bd = orc.causal_softmax_rows(qkv, B, T, C, NH, b, h, t0, t1, dtype, "prob")
+            cols = slice(h * HS, (h + 1) * HS)
+            worst = max(worst, assert_attention(y[b, t0:t1, cols], yr[0, :, cols], aw[0, :, cols], p, lr, bd,
+                                                np.arange(t0, t1), V[b, :, h], dtype,
+                                                f"{label} attention b={b} h={h} rows {t0}..", exact_scores))
+    return worst
+
+
+@pytest.mark.parametrize("HS", [8, 16, 40, 64])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 300])
+def test_attention_ragged_f32(orc, T, HS):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 13 + HS)
+    check_attention(orc, qkv, "f32", B, T, NH, HS, "sweep")
+
+
+def test_attention_ramp_rows_exact_scores(orc):
+    """Ramp scores (exact in fp32) and V entry 0 = key index: y[t][0] is the
+    expected key under the row's probabilities (slopes 0.25, -0.5, 0, 64);
+    only the fp32 exp / sum error is allowed."""
+    B, T, NH, HS = 2, 300, 4, 64
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in (0.25, -0.5, 0.0, 64.0)], "f32", v_ramp=True)
+    check_attention(orc, qkv, "f32", B, T, NH, HS, "ramp", exact_scores=True)
+
+
+def test_attention_saturated_and_fused_stats(orc):
+    """Scores of order 1e3-1e4, statistics from the fused softmax launch."""
+    B, T, NH, HS = 1, 257, 2, 64
+    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(64.0)).astype(np.float32)
+    check_attention(orc, qkv, "f32", B, T, NH, HS, "saturated", fused_stats=True)
+
+
+def test_attention_rejections():
+    qkv = torch.zeros(2, 8, 3 * 2 * 8, device="cuda", dtype=torch.bfloat16)
+    mx = torch.zeros(2, 2, 8, device="cuda")
+    with pytest.raises(cas.CasError) as e:
+        cas.causal_attention(qkv, 2, stats=(mx, mx))
+    assert e.value.status == -7
+
+
+def test_workload_attention_full_size(orc):
+    """The fp32 score shape B=8 T=1024 NH=12 HS=64: three whole batches' rows
+    of every head compared at sampled ranges."""
+    wl = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    worst = check_attention(orc, qkv, "f32", B, T, NH, HS, wl.name,
+                            b_t=[(0, 0, 64), (3, 500, 540), (7, 960, 1024)])
+    print(f"{wl.name} attention: sampled max err/tol {worst:.3g}")
