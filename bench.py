@@ -255,7 +255,7 @@ def softmax_timings(steps: int):
                                           "frac": round(rows_bytes / (ms_rows * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": rows_bytes}},
         }
-        if wl.dtype == "f32" and mode == "prob":
+        if mode == "prob" and od == "f32":
             # the attention output: softmax probabilities times V (statistics from the launch above)
             _, (ms_att,), _ = time_parts([sp.attention], n, 2)
             flops = 2 * wl.useful_flops()  # Q K^T and P V over the causal triangle
@@ -263,8 +263,8 @@ def softmax_timings(steps: int):
                 "avg_launch_us": round(ms_att * 1e3, 2),
                 "with_row_stats_us": round((ms_att + ms_st) * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(flops / (ms_att * 1e-3) / 1e12, 2),
-                             "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                             "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
+                             "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
+                             "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
                              "useful_flops": flops}}
         del sp
         torch.cuda.empty_cache()

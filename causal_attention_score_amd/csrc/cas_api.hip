@@ -366,17 +366,20 @@ CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum || !y) return CAS_ERR_NULL;
     if (rc != CAS_OK) return rc;
-    if (in_dtype != CAS_F32) return CAS_ERR_UNSUPPORTED; // fp32 inputs only, for now
     if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0 || (uintptr_t)y % 4 != 0)
         return CAS_ERR_UNSUPPORTED;
-    int64_t yb = 0;
-    if (!mul_ok(inb / 3, 1, &yb)) return CAS_ERR_SHAPE; // (B, T, C) fp32: a third of the fp32 qkv bytes
+    const int64_t yb = inb / 3 / elem_size(in_dtype) * 4; // (B, T, C) fp32
     if (overlap(y, yb, qkv, inb) || overlap(y, yb, row_max, stb) || overlap(y, yb, row_logsum, stb))
         return CAS_ERR_ALIAS;
     const int dc = device_check();
     if (dc != CAS_OK) return dc;
     cas::TrimulArgs a = softmax_args(qkv, y, row_max, row_logsum, B, T, C, NH, 4, 0);
-    return launch_status(cas::launch_attention_f32(a, (hipStream_t)stream));
+    const hipStream_t st = (hipStream_t)stream;
+    switch (in_dtype) {
+    case CAS_F32: return launch_status(cas::launch_attention_f32(a, st));
+    case CAS_BF16: return launch_status(cas::launch_attention_bf16(a, st));
+    default: return launch_status(cas::launch_attention_f16(a, st));
+    }
 }
 
 CAS_EXPORT const char *cas_status_string(int status)

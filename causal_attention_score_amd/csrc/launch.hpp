@@ -55,8 +55,10 @@ hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
 hipError_t launch_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s);
 // Both in one launch: statistics written through a.row_max / a.row_logsum.
 hipError_t launch_softmax_fused(const TrimulArgs &a, int elem, int mode, hipStream_t s);
-// Attention output (B, T, C) fp32 into a.out from a.row_max / a.row_logsum
-// (softmax_f32.hip; fp32 inputs).
+// Attention output (B, T, C) fp32 into a.out from a.row_max / a.row_logsum,
+// by input type (softmax_{f32,bf16,f16}.hip).
 hipError_t launch_attention_f32(const TrimulArgs &a, hipStream_t s);
+hipError_t launch_attention_bf16(const TrimulArgs &a, hipStream_t s);
+hipError_t launch_attention_f16(const TrimulArgs &a, hipStream_t s);
 
 } // namespace cas

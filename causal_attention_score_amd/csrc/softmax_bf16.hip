@@ -17,4 +17,9 @@ hipError_t launch_softmax_fused_bf16(const TrimulArgs &a, int mode, hipStream_t 
     return sm::launch_softmax_fused_impl<KBF16>(a, mode, s);
 }
 
+hipError_t launch_attention_bf16(const TrimulArgs &a, hipStream_t s)
+{
+    return sm::launch_attention_impl<KBF16>(a, s);
+}
+
 } // namespace cas

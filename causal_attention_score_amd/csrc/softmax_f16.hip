@@ -17,4 +17,9 @@ hipError_t launch_softmax_fused_f16(const TrimulArgs &a, int mode, hipStream_t s
     return sm::launch_softmax_fused_impl<KF16>(a, mode, s);
 }
 
+hipError_t launch_attention_f16(const TrimulArgs &a, hipStream_t s)
+{
+    return sm::launch_attention_impl<KF16>(a, s);
+}
+
 } // namespace cas

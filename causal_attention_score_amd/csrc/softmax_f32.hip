@@ -17,6 +17,6 @@ hipError_t launch_softmax_fused_f32(const TrimulArgs &a, int mode, hipStream_t s
     return sm::launch_softmax_fused_impl<KF32>(a, mode, s);
 }
 
-hipError_t launch_attention_f32(const TrimulArgs &a, hipStream_t s) { return sm::launch_attention_f32_impl(a, s); }
+hipError_t launch_attention_f32(const TrimulArgs &a, hipStream_t s) { return sm::launch_attention_impl<KF32>(a, s); }
 
 } // namespace cas

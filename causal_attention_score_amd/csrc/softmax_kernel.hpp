@@ -714,8 +714,6 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
                                        uint32_t kabs0, uint32_t qabs)
 {
     f32x16 s[2];
-    s[0] = f32x16{};
-    s[1] = f32x16{};
     constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 #pragma unroll
@@ -727,7 +725,10 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
             kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
         }
 #pragma unroll
-        for (int b = 0; b < 2; ++b) mfma_chunk<KF32>(s[b], kf[b], qf[u]);
+        for (int b = 0; b < 2; ++b) {
+            if (u == 0) s[b] = mfma_first<KF32>(kf[b], qf[u]);
+            else mfma_chunk<KF32>(s[b], kf[b], qf[u]);
+        }
     }
     // p, in place, as the softmax-rows kernel forms it
 #pragma unroll
@@ -753,16 +754,134 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
         }
 }
 
-template <int NCH>
-__global__ void __launch_bounds__(STATS_THREADS)
-attention_f32_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
-                     const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
-                     uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items, float scale)
+// ---------------------------------------------------------------------------
+// 16-bit inputs (v_mfma_f32_32x32x16_{bf16,f16}). The same walk and p; P is
+// rounded to the input type (nearest even) for the P V MFMAs. Their lane
+// half h supplies 8 consecutive k-slots: MFMA j (of two per 32-key block)
+// takes, for k-slots 8h .. 8h + 7, keys 8(2j + i/4) + 4h + i%4 (i = 0..7),
+// which are score accumulators 8j .. 8j + 7 of that lane, so P again stays
+// in place. Those keys come in two runs of four, so V is staged transposed
+// (V^T[d][key], rows of AVT_PITCH bytes) and each operand is two 8-byte LDS
+// reads. The pitch 136 (34 dwords) puts the 32 d-rows an MFMA reads on 32
+// distinct bank pairs.
+// ---------------------------------------------------------------------------
+constexpr int AVT_PITCH = AKT * 2 + 8;
+
+// Two fp32 values rounded (nearest even) to the input format, a in the low
+// half: one packed conversion.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+template <class E> __device__ __forceinline__ uint32_t pack16(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack16<KBF16>(float a, float b)
 {
-    constexpr int RB = NCH * 16, NU = NCH / 2;
-    constexpr int NBV = NCH * 16 / 4 / 32; // 32-column blocks of the head (HS * 4 <= RB bytes)
-    __shared__ __attribute__((aligned(16))) char kbuf[2 * AKT * RB];
-    __shared__ __attribute__((aligned(16))) char vbuf[2 * AKT * AV_PITCH];
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
+template <> __device__ __forceinline__ uint32_t pack16<KF16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, f16x2v));
+}
+
+// Stage: the tile's 64 K rows as for the fp32 kernel, and its 64 V rows
+// written transposed, 2-byte elements.
+template <int NCH> __device__ __forceinline__ void a_store16(const AStage<NCH> &st, char *kbuf, char *vtbuf, int tid)
+{
+    constexpr int RPJ = STATS_THREADS / NCH;
+    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+#pragma unroll
+    for (int q = 0; q < NCH / 4; ++q) {
+        const uint32_t r = (uint32_t)(q * RPJ) + r0; // key
+        *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.k[q];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { // V[key r][8c + i] -> V^T[8c + i][r]
+            const unsigned short e = (unsigned short)(st.v[q][i >> 1] >> (16 * (i & 1)));
+            *reinterpret_cast<unsigned short *>(vtbuf + (8u * c + (uint32_t)i) * AVT_PITCH + r * 2u) = e;
+        }
+    }
+}
+
+template <class E, int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, const char *vtbuf,
+                                         const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
+                                         uint32_t kabs0, uint32_t qabs)
+{
+    f32x16 s[2];
+    constexpr int RB = NCH * 16;
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+#pragma unroll
+    for (int u = 0; u < NCH / 2; ++u) {
+        u32x4 kf[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t row = 32u * b + r32;
+            kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (u == 0) s[b] = mfma_first<E>(kf[b], qf[u]);
+            else mfma_chunk<E>(s[b], kf[b], qf[u]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = tri::epilogue<tri::EpProb>(s[b][r], scale, mx, ls);
+            if (DIAG && kabs0 + 32u * b + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3) > qabs) p = 0.f;
+            s[b][r] = p;
+        }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 pa = {pack16<E>(s[b][8 * j + 0], s[b][8 * j + 1]), pack16<E>(s[b][8 * j + 2], s[b][8 * j + 3]),
+                              pack16<E>(s[b][8 * j + 4], s[b][8 * j + 5]), pack16<E>(s[b][8 * j + 6], s[b][8 * j + 7])};
+            const uint32_t k0 = 32u * b + 16u * j + 4u * h; // keys k0 .. k0+3 and k0+8 .. k0+11
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const char *vr = vtbuf + (32u * nb + r32) * AVT_PITCH;
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + k0 * 2u);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + (k0 + 8u) * 2u);
+                mfma_chunk<E>(yacc[nb], pa, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+        }
+}
+
+// One kernel for the three input types: the staging and the step differ
+// (fp32: V rows as read, 16-bit: V transposed, P rounded to the format).
+template <class E, int NCH> struct AttnCfg {
+    static constexpr bool F32 = std::is_same<E, KF32>::value;
+    static constexpr int ES = F32 ? 4 : 2;
+    static constexpr int NBV = NCH * 16 / ES / 32; // 32-column blocks of the head (HS * ES <= NCH * 16 bytes)
+    static constexpr int VBYTES = F32 ? AKT * AV_PITCH : NBV * 32 * AVT_PITCH; // one V stage in LDS
+};
+
+template <class E, int NCH>
+__device__ __forceinline__ void attn_stage(const AStage<NCH> &st, char *kbuf, char *vbuf, int tid)
+{
+    if constexpr (AttnCfg<E, NCH>::F32) a_store<NCH>(st, kbuf, vbuf, tid);
+    else a_store16<NCH>(st, kbuf, vbuf, tid);
+}
+
+template <class E, int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void attn_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
+                                          const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
+                                          uint32_t kabs0, uint32_t qabs)
+{
+    if constexpr (AttnCfg<E, NCH>::F32) a_step<NCH, NBV, DIAG>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, kabs0, qabs);
+    else a_step16<E, NCH, NBV, DIAG>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, kabs0, qabs);
+}
+
+template <class E, int NCH>
+__global__ void __launch_bounds__(STATS_THREADS)
+attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
+                 const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
+                 uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items, float scale)
+{
+    using Cfg = AttnCfg<E, NCH>;
+    constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB, VBYTES = Cfg::VBYTES;
+    __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
+    __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -772,11 +891,11 @@ attention_f32_kernel(const char *__restrict__ qkv, const float *__restrict__ row
     const uint32_t id = (uint32_t)xcd_remap(blockIdx.x, items);
     const uint32_t plane = id / npair, p = id - plane * npair;
     const uint32_t b = plane / NH, nh = plane - b * NH;
-    const uint32_t ldb = 3u * C * 4u;
-    const uint32_t head_bytes = HS * 4u;
-    const char *qb0 = qkv + ((uint64_t)b * T * (3u * C) + (uint64_t)nh * HS) * 4; // Q row 0 of the plane
-    const char *kb0 = qb0 + (uint64_t)C * 4;                                    // K row 0
-    const char *vb0 = qb0 + (uint64_t)2 * C * 4;                                // V row 0
+    const uint32_t ldb = 3u * C * (uint32_t)Cfg::ES;
+    const uint32_t head_bytes = HS * (uint32_t)Cfg::ES;
+    const char *qb0 = qkv + ((uint64_t)b * T * (3u * C) + (uint64_t)nh * HS) * Cfg::ES; // Q row 0 of the plane
+    const char *kb0 = qb0 + (uint64_t)C * Cfg::ES;                                      // K row 0
+    const char *vb0 = qb0 + (uint64_t)2 * C * Cfg::ES;                                  // V row 0
 
     for (int half = 0; half < 2; ++half) {
         const uint32_t I = half == 0 ? p : nt - 1 - p;
@@ -803,21 +922,29 @@ attention_f32_kernel(const char *__restrict__ qkv, const float *__restrict__ row
         f32x16 yacc[NBV];
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) yacc[nb] = f32x16{};
-        const uint32_t nst = 2 * I + 2; // 64-key tiles 0 .. 2I + 1
+        // 64-key tiles 0 .. 2I + 1: tiles below 2I lie wholly before the
+        // block's first query; the last two hold the diagonal.
+        const uint32_t nst = 2 * I + 2;
         AStage<NCH> st;
         a_fetch<NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
-        a_store<NCH>(st, kbuf, vbuf, tid);
+        attn_stage<E, NCH>(st, kbuf, vbuf, tid);
         __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
         tri::lds_barrier();
-        for (uint32_t J = 0; J < nst; ++J) {
-            const bool more = J + 1 < nst;
-            if (more) a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-            const char *kc = kbuf + (J & 1) * (AKT * RB), *vc = vbuf + (J & 1) * (AKT * AV_PITCH);
-            if (J + 2 < nst) a_step<NCH, NBV, false>(yacc, kc, vc, qf, scale, mx, ls, lane, J * AKT, qabs);
-            else a_step<NCH, NBV, true>(yacc, kc, vc, qf, scale, mx, ls, lane, J * AKT, qabs);
-            if (more) a_store<NCH>(st, kbuf + ((J + 1) & 1) * (AKT * RB), vbuf + ((J + 1) & 1) * (AKT * AV_PITCH), tid);
+        uint32_t J = 0;
+        for (; J + 2 < nst; ++J) {
+            a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+            attn_step<E, NCH, NBV, false>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls, lane,
+                                     J * AKT, qabs);
+            attn_stage<E, NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
             tri::lds_barrier();
         }
+        // the diagonal pair: J = nst - 2 (even, buffer 0), then nst - 1
+        a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+        attn_step<E, NCH, NBV, true>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
+        attn_stage<E, NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
+        tri::lds_barrier();
+        attn_step<E, NCH, NBV, true>(yacc, kbuf + KBYTES, vbuf + VBYTES, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+        tri::lds_barrier();
         // y rows: lane holds query 32w + 8(r/4) + 4h + r%4 and column 32nb + lane%32
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb)
@@ -830,22 +957,22 @@ attention_f32_kernel(const char *__restrict__ qkv, const float *__restrict__ row
     }
 }
 
-template <int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
+template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
 {
     const int64_t nt = (a.T + ST - 1) / ST;
-    const int64_t npair = (nt + 1) / 2;
+    const int64_t npair = (nt + 1) / 2; // pairs of 128-row query blocks per plane
     const int64_t items = a.B * a.NH * npair;
-    hipLaunchKernelGGL((attention_f32_kernel<NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
+    hipLaunchKernelGGL((attention_kernel<E, NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
                        (const char *)a.qkv, a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
                        (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)npair, (uint32_t)items, a.scale);
     return hipGetLastError();
 }
 
 // Attention output into a.out ((B, T, C) fp32) from a.row_max / a.row_logsum.
-inline hipError_t launch_attention_f32_impl(const TrimulArgs &a, hipStream_t s)
+template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStream_t s)
 {
-    if (a.HS * 4 <= 128) return launch_attention_nch<8>(a, s);
-    return launch_attention_nch<16>(a, s);
+    if (a.HS * AttnCfg<E, 8>::ES <= 128) return launch_attention_nch<E, 8>(a, s);
+    return launch_attention_nch<E, 16>(a, s);
 }
 
 } // namespace sm

@@ -62,6 +62,27 @@ template <> __device__ __forceinline__ void mfma_chunk<KF16>(f32x16 &acc, u32x4 
                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
+// The first chunk of a tile: the product alone, with a zero accumulator
+// the MFMA takes as an inline constant (no register clearing).
+template <class E> __device__ __forceinline__ f32x16 mfma_first(u32x4 a, u32x4 b);
+template <> __device__ __forceinline__ f32x16 mfma_first<KF32>(u32x4 a, u32x4 b)
+{
+    f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), f32x16{}, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma_first<KBF16>(u32x4 a, u32x4 b)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   f32x16{}, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma_first<KF16>(u32x4 a, u32x4 b)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  f32x16{}, 0, 0, 0);
+}
+
 // Global-load vector types by byte width.
 template <int BYTES> struct VecT;
 template <> struct VecT<16> { using T = u32x4; };

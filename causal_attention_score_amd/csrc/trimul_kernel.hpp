@@ -641,19 +641,27 @@ __device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, in
     }
 }
 
-// The element written for accumulator value a: the fp32 score a * scale,
-// then for the softmax (x - max) - logsum of its row and, for
-// probabilities, the exponential of that (v_exp_f32 of the value times
-// log2(e)). The empty asm keeps the score a separate fp32 value: the compiler
-// may not fuse its rounding into the subtraction.
+// The element written for accumulator value a: the fp32 score a * scale;
+// for log-probabilities (x - max) - logsum of its row, where the empty asm
+// keeps the score a separate fp32 value (the compiler may not fuse its
+// rounding into the subtraction); for probabilities the exponential of the
+// log-probability, formed in base 2 (v_exp_f32).
 template <class EP>
 __device__ __forceinline__ float epilogue(float a, float scale, float mx, float ls)
 {
+    constexpr float LOG2E = 1.44269504088896340736f;
+    if constexpr (EP::KIND == 2) {
+        // p = 2^((a scale - mx) log2 e - ls log2 e): two fused multiply-adds,
+        // each one rounding, and ls log2 e once per row. Every rounding is
+        // relative to lp or to ls <= |lp| (x <= mx and ls >= 0), never to
+        // the size of the scores themselves.
+        const float t = __builtin_fmaf(a, scale, -mx);
+        return __builtin_amdgcn_exp2f(__builtin_fmaf(t, LOG2E, -(ls * LOG2E)));
+    }
     float y = a * scale;
-    if constexpr (EP::KIND != 0) {
+    if constexpr (EP::KIND == 1) {
         asm volatile("" : "+v"(y));
-        const float lp = (y - mx) - ls;
-        y = EP::KIND == 1 ? lp : __builtin_amdgcn_exp2f(lp * 1.44269504088896340736f);
+        y = (y - mx) - ls;
     }
     return y;
 }

@@ -147,8 +147,11 @@ int cas_trimul_causal(const void *qkv, void *out,
  *               mode CAS_SOFTMAX_PROB: exp of that for t2 <= t, 0 for t2 > t
  *               (the softmax of the scores masked to -inf above the
  *               diagonal, the mask llm.c's trimul_cpu names as an
- *               alternative to its NaN). 16-bit outputs are the fp32 value
- *               rounded once more (to nearest even).
+ *               alternative to its NaN), formed in base 2 from the
+ *               accumulated product a as 2^((a scale - row_max) log2 e -
+ *               row_logsum log2 e) with two fused multiply-adds. 16-bit
+ *               outputs are the fp32 value rounded once more (to nearest
+ *               even).
  *
  * Both: fp32 arithmetic; the scores are bit-identical to cas_trimul_causal's
  * (same products in the same order). Domain (else CAS_ERR_UNSUPPORTED, with
@@ -190,11 +193,12 @@ int cas_causal_softmax_fused(const void *qkv, void *out, float *row_max, float *
  * with V the third slot of the packed rows (element b*T*3C + t2*3C + 2C +
  * nh*HS + i) and p the probabilities cas_causal_softmax (CAS_SOFTMAX_PROB)
  * forms from the given row statistics (those of cas_causal_row_stats on the
- * same qkv), bit for bit. Neither the scores nor p reach HBM: both are
- * recomputed per key tile and multiplied into y on the MFMAs.
+ * same qkv), bit for bit; for 16-bit inputs p is then rounded to the input
+ * format (nearest even) and multiplied by V in that format, with fp32
+ * accumulation. Neither the scores nor p reach HBM: both are recomputed per
+ * key tile and multiplied into y on the MFMAs.
  *   y   (B, T, C) fp32 (out_dtype must be CAS_F32), written whole.
- * fp32 inputs only (16-bit inputs: CAS_ERR_UNSUPPORTED). Domain, limits and
- * empty shapes as for cas_causal_softmax; y (and the 4-byte aligned
+ * Domain, limits and empty shapes as for cas_causal_softmax; y (and the 4-byte aligned
  * statistics) may not overlap qkv, and y may not overlap the statistics.
  */
 int cas_causal_attention(const void *qkv, const float *row_max, const float *row_logsum, void *y,

@@ -172,7 +172,11 @@ def assert_scores(gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, dtype: st
 # rescaling included) and R = 2^-21 the roundings of log2, ln 2 and the two
 # subtractions. A probability p = exp(lp) is then within p expm1(that + R(1 +
 # |lp|)), and at least 2^-126 (results below fp32's normal range may flush
-# to zero). 16-bit outputs add one rounding of the format, as for the scores.
+# to zero). The kernels form p as exp2(fma(fma(a, scale, -max), log2 e,
+# -logsum log2 e)): its roundings, and exp2's own, come to at most
+# 2^-24 (2 + 5 |lp|) in ln p (logsum <= |lp| since x <= max and logsum >= 0),
+# inside the R (1 + 2 |lp|) left for that step. 16-bit outputs add one
+# rounding of the format, as for the scores.
 
 FILL = {("f32", "log"): 0xFF800000, ("f32", "prob"): 0x00000000,
         ("bf16", "log"): 0xFF80, ("f16", "log"): 0xFC00, ("bf16", "prob"): 0x0000, ("f16", "prob"): 0x0000}
@@ -226,8 +230,13 @@ def assert_attention(got, ref, absw, p_ref, ls_ref, bound, t_idx, v_abs, in_dtyp
     """Attention output rows (R, HS) of one head against the oracle's. Each
     output is sum_j p_j v_j: with |p_gpu - p| <= lim_j (prob_limits) and an
     fp32 sum of n products, |y_gpu - y| <= sum_j lim_j |v_j| + S sum_j p_j |v_j|
-    (S as for the softmax); v_abs is |V| (T, HS) of the head."""
-    lim_p, _ = prob_limits(p_ref, ls_ref, bound, t_idx, in_dtype, exact_scores)
+    (S as for the softmax); v_abs is |V| (T, HS) of the head. For 16-bit
+    inputs p is rounded to the input format before the products: one more
+    relative rounding of that format on p_gpu, and 2^-126 for a flushed one."""
+    lim_p, valid = prob_limits(p_ref, ls_ref, bound, t_idx, in_dtype, exact_scores)
+    if in_dtype != "f32":
+        r16, a16 = ROUND16[in_dtype]
+        lim_p = lim_p + np.where(valid, r16 * (p_ref + lim_p) + max(a16, 2.0 ** -126), 0.0)
     S = (np.asarray(t_idx) + 65) * 2.0 ** -24
     lim = lim_p @ v_abs + S[:, None] * absw
     g = np.asarray(got, np.float64)

@@ -175,7 +175,7 @@ def test_attention_rejections(L):
     assert at(L, B=-1) == ESHAPE
     assert at(L, C=10, NH=3) == ESHAPE
     assert at(L, y=None) == ENULL and at(L, qkv=None) == ENULL and at(L, mx=None) == ENULL
-    assert at(L, ind=BF16, C=24) == EUNSUP                  # 16-bit inputs: not yet
+    assert at(L, ind=F16, C=12) == EUNSUP                   # 8-byte heads of a 16-bit type
     assert at(L, C=15, NH=3) == EUNSUP                      # 20-byte heads
     assert at(L, y=PX + 16) == EALIAS                       # y inside qkv
     assert at(L, y=PY + 64) == EALIAS                       # y over the statistics
@@ -183,6 +183,7 @@ def test_attention_rejections(L):
     if not torch.cuda.is_available():
         assert at(L) == EDEV
         assert at(L, mx=PX + 16, ls=PX + 32) == EDEV        # the statistics are only read
+        assert at(L, ind=BF16, C=24) == EDEV                # 16-byte heads of a 16-bit type
 
 
 def test_softmax_rejections(L):

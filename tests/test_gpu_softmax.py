@@ -332,8 +332,26 @@ def test_attention_saturated_and_fused_stats(orc):
     check_attention(orc, qkv, "f32", B, T, NH, HS, "saturated", fused_stats=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("HS", [8, 40, 64, 128])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 128, 129, 300])
+def test_attention_ragged_16bit(orc, T, HS, dtype):
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 7 + HS)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "sweep")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attention_saturated_16bit_fused_stats(orc, dtype):
+    """Scores of order 1e2-1e3 (one dominant key per row, tiny p elsewhere:
+    f16's subnormal range), statistics from the fused softmax launch."""
+    B, T, NH, HS = 1, 200, 2, 64
+    qkv = synth.to_storage(synth.trimul_inputs(B, T, NH, HS, "f32", seed=9) * np.float32(16.0), dtype)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "saturated", fused_stats=True)
+
+
 def test_attention_rejections():
-    qkv = torch.zeros(2, 8, 3 * 2 * 8, device="cuda", dtype=torch.bfloat16)
+    qkv = torch.zeros(2, 8, 3 * 2 * 4, device="cuda", dtype=torch.float16)
     mx = torch.zeros(2, 2, 8, device="cuda")
     with pytest.raises(cas.CasError) as e:
         cas.causal_attention(qkv, 2, stats=(mx, mx))
@@ -348,4 +366,14 @@ def test_workload_attention_full_size(orc):
     (qkv,) = wl.inputs()
     worst = check_attention(orc, qkv, "f32", B, T, NH, HS, wl.name,
                             b_t=[(0, 0, 64), (3, 500, 540), (7, 960, 1024)])
+    print(f"{wl.name} attention: sampled max err/tol {worst:.3g}")
+
+
+def test_workload_attention_bf16_full_size(orc):
+    """The bf16 score shape B=4 T=4096: sampled row ranges of every head."""
+    wl = synth.WORKLOADS["trimul_bf16_B4_T4096_NH25_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    worst = check_attention(orc, qkv, wl.dtype, B, T, NH, HS, wl.name,
+                            b_t=[(0, 0, 32), (2, 2040, 2060), (3, 4070, 4096)])
     print(f"{wl.name} attention: sampled max err/tol {worst:.3g}")
