@@ -257,10 +257,13 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     const int64_t lens[2] = {HS, C};
     const void *ptrs[1] = {qkv};
     *vec = qkv ? pick_vec(es, lens, 2, ptrs, 1) : 1;
-    if (!cas::softmax_fits(T, HS, es, *vec)) return CAS_ERR_UNSUPPORTED;
     const int64_t nts = (T + 127) / 128;
     if (B * NH * (nts * (nts + 1) / 2) > INT32_MAX || cas::row_stats_workgroups(B, T, NH) > INT32_MAX)
         return CAS_ERR_SHAPE;
+    if (!cas::softmax_fits(T, HS, es, *vec)) return CAS_ERR_UNSUPPORTED;
+    // one launch's grid is below 2^32 work-items (256 per workgroup)
+    if (cas::row_stats_workgroups(B, T, NH) >= (INT64_C(1) << 24) || B * NH >= (INT64_C(1) << 23))
+        return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
 }
 
@@ -394,7 +397,8 @@ CAS_EXPORT const char *cas_status_string(int status)
     case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
     case CAS_ERR_UNSUPPORTED:
         return "valid arguments outside the kernels' domain (QKV rows not in 16-byte pieces, head over 256 bytes, "
-               "T >= 2^22, or misaligned statistics)";
+               "T >= 2^22, B * NH >= 2^23 or B * NH * ceil(ceil(T / 128) / 2) >= 2^24 for the softmax, or misaligned "
+               "statistics)";
     case CAS_ERR_MODE: return "unknown softmax mode";
     default: return "unknown status";
     }

@@ -876,7 +876,7 @@ template <class E, int NCH>
 __global__ void __launch_bounds__(STATS_THREADS)
 attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
                  const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
-                 uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items, float scale)
+                 uint32_t HS, uint32_t nt, uint32_t planes, uint32_t rank0, float scale)
 {
     using Cfg = AttnCfg<E, NCH>;
     constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB, VBYTES = Cfg::VBYTES;
@@ -888,8 +888,12 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 
-    const uint32_t id = (uint32_t)xcd_remap(blockIdx.x, items);
-    const uint32_t plane = id / npair, p = id - plane * npair;
+    // One 128-row query block per workgroup, the longest first: block I
+    // takes 2I + 2 key tiles, and workgroups are dispatched in index order,
+    // so the short blocks fill in behind the long ones.
+    const uint32_t q = blockIdx.x / planes, plane = blockIdx.x - q * planes;
+    const uint32_t rank = rank0 + q;
+    const uint32_t I = nt - 1 - rank;
     const uint32_t b = plane / NH, nh = plane - b * NH;
     const uint32_t ldb = 3u * C * (uint32_t)Cfg::ES;
     const uint32_t head_bytes = HS * (uint32_t)Cfg::ES;
@@ -897,9 +901,7 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
     const char *kb0 = qb0 + (uint64_t)C * Cfg::ES;                                      // K row 0
     const char *vb0 = qb0 + (uint64_t)2 * C * Cfg::ES;                                  // V row 0
 
-    for (int half = 0; half < 2; ++half) {
-        const uint32_t I = half == 0 ? p : nt - 1 - p;
-        if (half == 1 && I == p) break;
+    {
         const uint32_t t0 = I * ST;
         const uint32_t qabs = t0 + 32u * w + r32; // this lane's query row (score side)
 
@@ -960,12 +962,20 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
 template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
 {
     const int64_t nt = (a.T + ST - 1) / ST;
-    const int64_t npair = (nt + 1) / 2; // pairs of 128-row query blocks per plane
-    const int64_t items = a.B * a.NH * npair;
-    hipLaunchKernelGGL((attention_kernel<E, NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
-                       (const char *)a.qkv, a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
-                       (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)npair, (uint32_t)items, a.scale);
-    return hipGetLastError();
+    const int64_t planes = a.B * a.NH;
+    // ranks (query blocks of every plane) per launch, so that a grid stays
+    // below 2^32 work-items
+    const int64_t per = std::max<int64_t>(1, ((int64_t)1 << 23) / planes);
+    for (int64_t r0 = 0; r0 < nt; r0 += per) {
+        const int64_t n = std::min(per, nt - r0);
+        hipLaunchKernelGGL((attention_kernel<E, NCH>), dim3((unsigned)(planes * n)), dim3(STATS_THREADS), 0, s,
+                           (const char *)a.qkv, a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T,
+                           (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)planes,
+                           (uint32_t)r0, a.scale);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Attention output into a.out ((B, T, C) fp32) from a.row_max / a.row_logsum.

@@ -177,6 +177,7 @@ def test_attention_rejections(L):
     assert at(L, y=None) == ENULL and at(L, qkv=None) == ENULL and at(L, mx=None) == ENULL
     assert at(L, ind=F16, C=12) == EUNSUP                   # 8-byte heads of a 16-bit type
     assert at(L, C=15, NH=3) == EUNSUP                      # 20-byte heads
+    assert at(L, B=2**23, T=1, C=4, NH=1) == EUNSUP         # the grid limits of the softmax
     assert at(L, y=PX + 16) == EALIAS                       # y inside qkv
     assert at(L, y=PY + 64) == EALIAS                       # y over the statistics
     assert at(L, B=0) == OK and at(L, T=0) == OK
@@ -202,6 +203,9 @@ def test_softmax_rejections(L):
         assert f(L, C=3 * 65, NH=3, ind=F32) == EUNSUP     # HS = 65 fp32: 260-byte heads
         assert f(L, C=3 * 136, NH=3, ind=BF16) == EUNSUP   # HS = 136 bf16: 272-byte heads
         assert f(L, B=1, T=2**22, C=12, NH=3) == EUNSUP
+        assert f(L, B=2**23, T=1, C=4, NH=1) == EUNSUP     # B * NH planes: 2^23 workgroups of 256
+        assert f(L, B=2**22, T=1024, C=4, NH=1) == EUNSUP  # row-stats grid of 2^24 workgroups
+        assert f(L, B=2**22 - 1, T=1024, C=4, NH=1) != EUNSUP
         assert f(L, mx=PY + 2) == EUNSUP                   # misaligned statistics
         assert f(L, B=0) == OK and f(L, T=0) == OK and f(L, NH=0, C=0) == OK
         assert f(L, qkv=None, mx=None, ls=None, B=0) == OK
