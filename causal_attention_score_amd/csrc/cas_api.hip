@@ -261,9 +261,9 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     if (B * NH * (nts * (nts + 1) / 2) > INT32_MAX || cas::row_stats_workgroups(B, T, NH) > INT32_MAX)
         return CAS_ERR_SHAPE;
     if (!cas::softmax_fits(T, HS, es, *vec)) return CAS_ERR_UNSUPPORTED;
-    // one launch's grid is below 2^32 work-items (256 per workgroup)
-    if (cas::row_stats_workgroups(B, T, NH) >= (INT64_C(1) << 24) || B * NH >= (INT64_C(1) << 23))
-        return CAS_ERR_UNSUPPORTED;
+    // launches split by query block keep a grid below 2^32 work-items (256
+    // per workgroup) while the B * NH planes of one block fit in one grid
+    if (B * NH >= (INT64_C(1) << 23)) return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
 }
 
@@ -397,8 +397,7 @@ CAS_EXPORT const char *cas_status_string(int status)
     case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
     case CAS_ERR_UNSUPPORTED:
         return "valid arguments outside the kernels' domain (QKV rows not in 16-byte pieces, head over 256 bytes, "
-               "T >= 2^22, B * NH >= 2^23 or B * NH * ceil(ceil(T / 128) / 2) >= 2^24 for the softmax, or misaligned "
-               "statistics)";
+               "T >= 2^22, B * NH >= 2^23 for the softmax, or misaligned statistics)";
     case CAS_ERR_MODE: return "unknown softmax mode";
     default: return "unknown status";
     }

@@ -23,8 +23,8 @@ bool softmax_fits(int64_t T, int64_t HS, int es, int vec)
 
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH)
 {
-    const int64_t nt = (T + 127) / 128; // 128-row query blocks, paired
-    return B * NH * ((nt + 1) / 2);
+    const int64_t nt = (T + 127) / 128; // 128-row query blocks, one per workgroup
+    return B * NH * nt;
 }
 
 hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s)

@@ -177,10 +177,38 @@ __device__ __forceinline__ void stats_update(const f32x16 (&acc)[4], RowRun &rr,
     rr.ms = msn;
 }
 
+// Query blocks in decreasing length: block I of a plane has I + 1 (or
+// 2I + 2) key tiles, and workgroups are dispatched in index order, so
+// giving the low indices the long blocks lets the short ones fill in behind
+// them (no pairing needed). Workgroup index (rank - rank0) * planes + plane
+// takes block I = nt - 1 - rank of that plane.
+struct BlockIdx { uint32_t plane, I; };
+__device__ __forceinline__ BlockIdx longest_first(uint32_t planes, uint32_t rank0, uint32_t nt)
+{
+    const uint32_t q = blockIdx.x / planes;
+    return BlockIdx{blockIdx.x - q * planes, nt - 1 - (rank0 + q)};
+}
+
+// Launches of planes x ranks workgroups, ranks split so that a grid stays
+// below 2^32 work-items (STATS_THREADS per workgroup; planes < 2^23).
+template <class F> hipError_t launch_longest_first(const TrimulArgs &a, hipStream_t s, F &&launch)
+{
+    const int64_t nt = (a.T + ST - 1) / ST;
+    const int64_t planes = a.B * a.NH;
+    const int64_t per = std::max<int64_t>(1, ((int64_t)1 << 23) / planes);
+    for (int64_t r0 = 0; r0 < nt; r0 += per) {
+        const int64_t n = std::min(per, nt - r0);
+        launch(dim3((unsigned)(planes * n)), (uint32_t)nt, (uint32_t)planes, (uint32_t)r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <class E, int NCH>
 __global__ void __launch_bounds__(STATS_THREADS)
 row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, float *__restrict__ row_logsum,
-                 uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt, uint32_t npair, uint32_t items,
+                 uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt, uint32_t planes, uint32_t rank0,
                  float scale)
 {
     constexpr int RB = NCH * 16, NU = NCH / 2;
@@ -191,8 +219,8 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 
-    const uint32_t id = (uint32_t)xcd_remap(blockIdx.x, items);
-    const uint32_t plane = id / npair, p = id - plane * npair;
+    const BlockIdx bi = longest_first(planes, rank0, nt);
+    const uint32_t plane = bi.plane, I = bi.I;
     const uint32_t b = plane / NH, nh = plane - b * NH;
     const uint32_t ldb = 3u * C * (uint32_t)E::ES;
     const uint32_t head_bytes = HS * (uint32_t)E::ES;
@@ -200,9 +228,7 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
     const char *kb0 = qb0 + (uint64_t)C * E::ES;                                     // K row 0
     const float c = scale * LOG2E;
 
-    for (int half = 0; half < 2; ++half) {
-        const uint32_t I = half == 0 ? p : nt - 1 - p;
-        if (half == 1 && I == p) break; // the middle block of an odd count has no partner
+    {
         const uint32_t t0 = I * ST;
 
         // Q fragments of rows t0 + 32w + r32: chunk 2u + h.
@@ -248,7 +274,6 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
             case 2: stats_update<2>(acc, rr, c, lane); break;
             default: stats_update<3>(acc, rr, c, lane); break;
             }
-            tri::lds_barrier(); // tile I's reads done before the next block's tile 0 is written
         }
 
         // Merge the two lane halves (the same row, disjoint keys) and write.
@@ -607,14 +632,11 @@ template <class E> hipError_t launch_softmax_fused_impl(const TrimulArgs &a, int
 
 template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a, hipStream_t s)
 {
-    const int64_t nt = (a.T + ST - 1) / ST;
-    const int64_t npair = (nt + 1) / 2;
-    const int64_t items = a.B * a.NH * npair;
-    hipLaunchKernelGGL((row_stats_kernel<E, NCH>), dim3((unsigned)items), dim3(STATS_THREADS), 0, s,
-                       (const char *)a.qkv, const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum),
-                       (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)npair,
-                       (uint32_t)items, a.scale);
-    return hipGetLastError();
+    return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
+        hipLaunchKernelGGL((row_stats_kernel<E, NCH>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+                           const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (uint32_t)a.T,
+                           (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale);
+    });
 }
 
 // Row statistics (row_max and row_logsum written through a.row_max /
@@ -888,12 +910,8 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 
-    // One 128-row query block per workgroup, the longest first: block I
-    // takes 2I + 2 key tiles, and workgroups are dispatched in index order,
-    // so the short blocks fill in behind the long ones.
-    const uint32_t q = blockIdx.x / planes, plane = blockIdx.x - q * planes;
-    const uint32_t rank = rank0 + q;
-    const uint32_t I = nt - 1 - rank;
+    const BlockIdx bi = longest_first(planes, rank0, nt);
+    const uint32_t plane = bi.plane, I = bi.I;
     const uint32_t b = plane / NH, nh = plane - b * NH;
     const uint32_t ldb = 3u * C * (uint32_t)Cfg::ES;
     const uint32_t head_bytes = HS * (uint32_t)Cfg::ES;
@@ -961,21 +979,11 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
 
 template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
 {
-    const int64_t nt = (a.T + ST - 1) / ST;
-    const int64_t planes = a.B * a.NH;
-    // ranks (query blocks of every plane) per launch, so that a grid stays
-    // below 2^32 work-items
-    const int64_t per = std::max<int64_t>(1, ((int64_t)1 << 23) / planes);
-    for (int64_t r0 = 0; r0 < nt; r0 += per) {
-        const int64_t n = std::min(per, nt - r0);
-        hipLaunchKernelGGL((attention_kernel<E, NCH>), dim3((unsigned)(planes * n)), dim3(STATS_THREADS), 0, s,
-                           (const char *)a.qkv, a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T,
-                           (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)nt, (uint32_t)planes,
-                           (uint32_t)r0, a.scale);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
+        hipLaunchKernelGGL((attention_kernel<E, NCH>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+                           a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH,
+                           (uint32_t)a.HS, nt, planes, rank0, a.scale);
+    });
 }
 
 // Attention output into a.out ((B, T, C) fp32) from a.row_max / a.row_logsum.

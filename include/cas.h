@@ -157,9 +157,8 @@ int cas_trimul_causal(const void *qkv, void *out,
  * (same products in the same order). Domain (else CAS_ERR_UNSUPPORTED, with
  * nothing written): QKV rows in 16-byte pieces (qkv 16-byte aligned, HS and
  * C times the element size multiples of 16), HS times the element size at
- * most 256 bytes, T < 2^22, B * NH < 2^23 and B * NH * ceil(ceil(T / 128) / 2)
- * < 2^24 (each launch's grid below 2^32 work-items), and 4-byte aligned
- * statistics. Other limits,
+ * most 256 bytes, T < 2^22, B * NH < 2^23 (the planes of one query block in
+ * one grid of under 2^32 work-items), and 4-byte aligned statistics. Other limits,
  * empty shapes and the no-overlap rule as for cas_trimul_causal: the
  * statistics written by cas_causal_row_stats may overlap neither qkv nor each
  * other, and out may overlap neither qkv nor the statistics it reads.
