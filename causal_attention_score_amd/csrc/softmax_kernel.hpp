@@ -804,20 +804,66 @@ template <> __device__ __forceinline__ uint32_t pack16<KF16>(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, f16x2v));
 }
 
-// Stage: the tile's 64 K rows as for the fp32 kernel, and its 64 V rows
-// written transposed, 2-byte elements.
-template <int NCH> __device__ __forceinline__ void a_store16(const AStage<NCH> &st, char *kbuf, char *vtbuf, int tid)
+// 16-bit staging. Waves 0 and 1 fetch the K tile: chunk t % NCH of rows
+// t / NCH + j (128 / NCH), j < NCH / 2 (t = tid % 128). Waves 2 and 3 fetch
+// the V tile as items of four consecutive rows 4g .. 4g + 3 of one chunk
+// (item t + 128 m, m < NCH / 8: chunk c = t % NCH, g = t / NCH + 8 m), so a
+// lane holds four keys of each of its eight head columns and writes them to
+// V^T as one 8-byte store per column: whole 4-key runs, no 2-byte stores.
+// Either way a lane stages NCH / 2 chunks. Rows past T and chunks past the
+// head read zero.
+template <int NCH> struct AStage16 {
+    u32x4 x[NCH / 2];
+};
+
+// Row of load j for this lane: A + B_j (A per lane, B_j a constant of j and
+// of the lane's side).
+template <int NCH> __device__ __forceinline__ uint32_t a16_row(bool kside, uint32_t t, int j)
 {
-    constexpr int RPJ = STATS_THREADS / NCH;
-    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+    const uint32_t kb = (uint32_t)(j * (128 / NCH)), vb = (uint32_t)(32 * (j / 4) + (j % 4));
+    return (kside ? t / NCH : 4u * (t / NCH)) + (kside ? kb : vb);
+}
+
+template <int NCH>
+__device__ __forceinline__ void a_fetch16(AStage16<NCH> &st, const char *kb0, const char *vb0, uint32_t J, uint32_t T,
+                                          uint32_t ldb, uint32_t head_bytes, int tid)
+{
+    const bool kside = tid < 128; // wave-uniform
+    const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at((kside ? kb0 : vb0) + (uint64_t)J * AKT * ldb);
+    const uint32_t lim = c * 16 < head_bytes ? T : 0u;
 #pragma unroll
-    for (int q = 0; q < NCH / 4; ++q) {
-        const uint32_t r = (uint32_t)(q * RPJ) + r0; // key
-        *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.k[q];
+    for (int j = 0; j < NCH / 2; ++j) {
+        const uint32_t r = a16_row<NCH>(kside, t, j);
+        const uint32_t ok = 0u - (uint32_t)(J * AKT + r < lim);
+        const uint32_t vo = ((r * ldb + c * 16) & ok) | (OOB & ~ok);
+        st.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0);
+    }
+}
+
+template <int NCH> __device__ __forceinline__ void a_store16(const AStage16<NCH> &st, char *kbuf, char *vtbuf, int tid)
+{
+    const bool kside = tid < 128;
+    const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
+    if (kside) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { // V[key r][8c + i] -> V^T[8c + i][r]
-            const unsigned short e = (unsigned short)(st.v[q][i >> 1] >> (16 * (i & 1)));
-            *reinterpret_cast<unsigned short *>(vtbuf + (8u * c + (uint32_t)i) * AVT_PITCH + r * 2u) = e;
+        for (int j = 0; j < NCH / 2; ++j) {
+            const uint32_t r = a16_row<NCH>(true, t, j);
+            *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.x[j];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NCH / 8; ++m) {
+            const uint32_t g = t / NCH + 8u * (uint32_t)m; // keys 4g .. 4g + 3
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { // head columns 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
+                const uint32_t x0 = st.x[4 * m][e], x1 = st.x[4 * m + 1][e];
+                const uint32_t x2 = st.x[4 * m + 2][e], x3 = st.x[4 * m + 3][e];
+                char *d0 = vtbuf + (8u * c + 2u * (uint32_t)e) * AVT_PITCH + 8u * g;
+                *reinterpret_cast<u32x2 *>(d0) = u32x2{(x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16)};
+                *reinterpret_cast<u32x2 *>(d0 + AVT_PITCH) =
+                    u32x2{(x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u)};
+            }
         }
     }
 }
@@ -876,10 +922,22 @@ template <class E, int NCH> struct AttnCfg {
     static constexpr int ES = F32 ? 4 : 2;
     static constexpr int NBV = NCH * 16 / ES / 32; // 32-column blocks of the head (HS * ES <= NCH * 16 bytes)
     static constexpr int VBYTES = F32 ? AKT * AV_PITCH : NBV * 32 * AVT_PITCH; // one V stage in LDS
+    static constexpr int MIN_WG = (!F32 && NCH == 8) ? 3 : 1; // workgroups per CU the registers must allow
 };
 
 template <class E, int NCH>
-__device__ __forceinline__ void attn_stage(const AStage<NCH> &st, char *kbuf, char *vbuf, int tid)
+using AttnStage = typename std::conditional<AttnCfg<E, NCH>::F32, AStage<NCH>, AStage16<NCH>>::type;
+
+template <class E, int NCH>
+__device__ __forceinline__ void attn_fetch(AttnStage<E, NCH> &st, const char *kb0, const char *vb0, uint32_t J,
+                                           uint32_t T, uint32_t ldb, uint32_t head_bytes, int tid)
+{
+    if constexpr (AttnCfg<E, NCH>::F32) a_fetch<NCH>(st, kb0, vb0, J, T, ldb, head_bytes, tid);
+    else a_fetch16<NCH>(st, kb0, vb0, J, T, ldb, head_bytes, tid);
+}
+
+template <class E, int NCH>
+__device__ __forceinline__ void attn_stage(const AttnStage<E, NCH> &st, char *kbuf, char *vbuf, int tid)
 {
     if constexpr (AttnCfg<E, NCH>::F32) a_store<NCH>(st, kbuf, vbuf, tid);
     else a_store16<NCH>(st, kbuf, vbuf, tid);
@@ -895,7 +953,7 @@ __device__ __forceinline__ void attn_step(f32x16 (&yacc)[NBV], const char *kbuf,
 }
 
 template <class E, int NCH>
-__global__ void __launch_bounds__(STATS_THREADS)
+__global__ void __launch_bounds__(STATS_THREADS, (AttnCfg<E, NCH>::MIN_WG))
 attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
                  const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
                  uint32_t HS, uint32_t nt, uint32_t planes, uint32_t rank0, float scale)
@@ -945,21 +1003,21 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
         // 64-key tiles 0 .. 2I + 1: tiles below 2I lie wholly before the
         // block's first query; the last two hold the diagonal.
         const uint32_t nst = 2 * I + 2;
-        AStage<NCH> st;
-        a_fetch<NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
+        AttnStage<E, NCH> st;
+        attn_fetch<E, NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
         attn_stage<E, NCH>(st, kbuf, vbuf, tid);
         __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
         tri::lds_barrier();
         uint32_t J = 0;
         for (; J + 2 < nst; ++J) {
-            a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+            attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
             attn_step<E, NCH, NBV, false>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls, lane,
                                      J * AKT, qabs);
             attn_stage<E, NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
             tri::lds_barrier();
         }
         // the diagonal pair: J = nst - 2 (even, buffer 0), then nst - 1
-        a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+        attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
         attn_step<E, NCH, NBV, true>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
         attn_stage<E, NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
         tri::lds_barrier();
