@@ -202,6 +202,13 @@ class SoftmaxParts:
             self.y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
         self.cas.causal_attention(self.qkv, self.NH, y=self.y, stats=(self.mx, self.ls))
 
+    def attention_fused(self):
+        if self.y is None:
+            import torch
+            B, T, C, _ = self.dims
+            self.y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+        self.cas.causal_attention_fused(self.qkv, self.NH, y=self.y, row_max=self.mx, row_logsum=self.ls)
+
     def fused(self):
         L = self.cas.lib()
         st = L.cas_causal_softmax_fused(self.qkv.data_ptr(), self.out.data_ptr(), self.mx.data_ptr(),
@@ -265,6 +272,14 @@ def softmax_timings(steps: int):
                 "roofline": {"bound": "mfma", "achieved": round(flops / (ms_att * 1e-3) / 1e12, 2),
                              "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
                              "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
+                             "useful_flops": flops}}
+            # the same output and the statistics in one pass (running maximum and sum)
+            _, (ms_one,), _ = time_parts([sp.attention_fused], n, 2)
+            out[key]["attention_single_pass"] = {
+                "avg_launch_us": round(ms_one * 1e3, 2),
+                "roofline": {"bound": "mfma", "achieved": round(flops / (ms_one * 1e-3) / 1e12, 2),
+                             "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
+                             "frac": round(flops / (ms_one * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
                              "useful_flops": flops}}
         del sp
         torch.cuda.empty_cache()

@@ -21,8 +21,8 @@ STATUS = {0: "CAS_OK", -1: "CAS_ERR_NULL", -2: "CAS_ERR_SHAPE", -3: "CAS_ERR_DTY
           -8: "CAS_ERR_MODE"}
 SOFTMAX_MODE = {"log": 0, "prob": 1}
 EXPORTS = ("cas_gemm_nt", "cas_batch_matmul_nt", "cas_trimul_causal", "cas_causal_row_stats", "cas_causal_softmax",
-           "cas_causal_softmax_fused", "cas_causal_attention", "cas_status_string", "cas_last_hip_error",
-           "cas_version")
+           "cas_causal_softmax_fused", "cas_causal_attention", "cas_causal_attention_fused", "cas_status_string",
+           "cas_last_hip_error", "cas_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.cas_causal_softmax_fused.restype = ctypes.c_int
         L.cas_causal_attention.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int] * 2 + [_vp]
         L.cas_causal_attention.restype = ctypes.c_int
+        L.cas_causal_attention_fused.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 4 + [ctypes.c_int] * 2 + [_vp]
+        L.cas_causal_attention_fused.restype = ctypes.c_int
         L.cas_status_string.argtypes = [ctypes.c_int]
         L.cas_status_string.restype = ctypes.c_char_p
         L.cas_last_hip_error.restype = ctypes.c_int
@@ -244,19 +246,47 @@ def causal_softmax(qkv, NH: int, mode: str = "prob", out=None, out_dtype=None, s
 def causal_attention(qkv, NH: int, y=None, stats=None):
     """Attention output y (B, T, C) float32: the causal softmax probabilities
     times the value rows, per head. stats: an optional (row_max, row_logsum)
-    pair (else the row statistics are computed first). Returns
-    (y, row_max, row_logsum)."""
+    pair, read as given (cas_causal_attention); without it, y and the
+    statistics come from the single-pass kernel (cas_causal_attention_fused).
+    Returns (y, row_max, row_logsum)."""
     import torch
+    if stats is None:
+        return causal_attention_fused(qkv, NH, y=y)
     B, T, C = _qkv_dims(qkv, NH)
-    row_max, row_logsum = stats if stats is not None else causal_row_stats(qkv, NH)
+    row_max, row_logsum = stats
     if y is None:
         y = torch.empty((B, T, C), dtype=torch.float32, device=qkv.device)
-    if y.dtype != torch.float32 or tuple(y.reshape(B, T, -1).shape) != (B, T, C) or not y.is_contiguous():
+    if y.dtype != torch.float32 or tuple(y.shape) != (B, T, C) or not y.is_contiguous():
         raise ValueError("y must be a contiguous float32 (B, T, C) tensor")
     _require_device(qkv, y, row_max, row_logsum)
     st = lib().cas_causal_attention(qkv.data_ptr(), row_max.data_ptr(), row_logsum.data_ptr(), y.data_ptr(),
                                     B, T, C, NH, _dtype_code(qkv), CAS_F32, _stream_ptr(qkv.device))
     _check("cas_causal_attention", st)
+    return y, row_max, row_logsum
+
+
+def causal_attention_fused(qkv, NH: int, y=None, row_max=None, row_logsum=None):
+    """The attention output y (B, T, C) float32 and the row statistics
+    (B, NH, T) in one pass (running maximum and sum, y rescaled as they move).
+    Returns (y, row_max, row_logsum)."""
+    import torch
+    B, T, C = _qkv_dims(qkv, NH)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32, device=qkv.device)
+    if y.dtype != torch.float32 or tuple(y.shape) != (B, T, C) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous float32 (B, T, C) tensor")
+    shape = (B, NH, T)
+    if row_max is None:
+        row_max = torch.empty(shape, dtype=torch.float32, device=qkv.device)
+    if row_logsum is None:
+        row_logsum = torch.empty(shape, dtype=torch.float32, device=qkv.device)
+    for t in (row_max, row_logsum):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("row_max / row_logsum must be contiguous float32 (B, NH, T) tensors")
+    _require_device(qkv, y, row_max, row_logsum)
+    st = lib().cas_causal_attention_fused(qkv.data_ptr(), y.data_ptr(), row_max.data_ptr(), row_logsum.data_ptr(),
+                                          B, T, C, NH, _dtype_code(qkv), CAS_F32, _stream_ptr(qkv.device))
+    _check("cas_causal_attention_fused", st)
     return y, row_max, row_logsum
 
 

@@ -385,6 +385,37 @@ CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const
     }
 }
 
+CAS_EXPORT int cas_causal_attention_fused(const void *qkv, void *y, float *row_max, float *row_logsum, int64_t B,
+                                          int64_t T, int64_t C, int64_t NH, cas_dtype in_dtype, cas_dtype out_dtype,
+                                          void *stream)
+{
+    if (!dtype_in_ok(in_dtype) || out_dtype != CAS_F32) return CAS_ERR_DTYPE;
+    int64_t inb, stb, outb;
+    int vec = 1;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    if (rc == 1) return CAS_OK;
+    if (rc == CAS_ERR_SHAPE) return rc;
+    if (!qkv || !y || !row_max || !row_logsum) return CAS_ERR_NULL;
+    if (rc != CAS_OK) return rc;
+    if ((uintptr_t)row_max % 4 != 0 || (uintptr_t)row_logsum % 4 != 0 || (uintptr_t)y % 4 != 0)
+        return CAS_ERR_UNSUPPORTED;
+    const int64_t yb = inb / 3 / elem_size(in_dtype) * 4; // (B, T, C) fp32
+    // Three outputs: none may overlap qkv or another output.
+    if (overlap(y, yb, qkv, inb) || overlap(row_max, stb, qkv, inb) || overlap(row_logsum, stb, qkv, inb) ||
+        overlap(y, yb, row_max, stb) || overlap(y, yb, row_logsum, stb) || overlap(row_max, stb, row_logsum, stb))
+        return CAS_ERR_ALIAS;
+    const int dc = device_check();
+    if (dc != CAS_OK) return dc;
+    cas::TrimulArgs a = softmax_args(qkv, y, row_max, row_logsum, B, T, C, NH, 4, 0);
+    a.vec_store = (uintptr_t)y % 16 == 0; // rows and head offsets are whole 16-byte pieces (C, HS multiples of 4)
+    const hipStream_t st = (hipStream_t)stream;
+    switch (in_dtype) {
+    case CAS_F32: return launch_status(cas::launch_attention_online_f32(a, st));
+    case CAS_BF16: return launch_status(cas::launch_attention_online_bf16(a, st));
+    default: return launch_status(cas::launch_attention_online_f16(a, st));
+    }
+}
+
 CAS_EXPORT const char *cas_status_string(int status)
 {
     switch (status) {
@@ -405,4 +436,4 @@ CAS_EXPORT const char *cas_status_string(int status)
 
 CAS_EXPORT int cas_last_hip_error(void) { return g_last_hip; }
 
-CAS_EXPORT int cas_version(void) { return 200; }
+CAS_EXPORT int cas_version(void) { return 210; }

@@ -60,5 +60,10 @@ hipError_t launch_softmax_fused(const TrimulArgs &a, int elem, int mode, hipStre
 hipError_t launch_attention_f32(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_attention_bf16(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_attention_f16(const TrimulArgs &a, hipStream_t s);
+// Single pass: y into a.out (16-byte stores when a.vec_store) and the row
+// statistics written through a.row_max / a.row_logsum.
+hipError_t launch_attention_online_f32(const TrimulArgs &a, hipStream_t s);
+hipError_t launch_attention_online_bf16(const TrimulArgs &a, hipStream_t s);
+hipError_t launch_attention_online_f16(const TrimulArgs &a, hipStream_t s);
 
 } // namespace cas

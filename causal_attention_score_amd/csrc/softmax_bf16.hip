@@ -22,4 +22,9 @@ hipError_t launch_attention_bf16(const TrimulArgs &a, hipStream_t s)
     return sm::launch_attention_impl<KBF16>(a, s);
 }
 
+hipError_t launch_attention_online_bf16(const TrimulArgs &a, hipStream_t s)
+{
+    return sm::launch_attention_online_impl<KBF16>(a, s);
+}
+
 } // namespace cas

@@ -22,4 +22,9 @@ hipError_t launch_attention_f16(const TrimulArgs &a, hipStream_t s)
     return sm::launch_attention_impl<KF16>(a, s);
 }
 
+hipError_t launch_attention_online_f16(const TrimulArgs &a, hipStream_t s)
+{
+    return sm::launch_attention_online_impl<KF16>(a, s);
+}
+
 } // namespace cas

@@ -19,4 +19,9 @@ hipError_t launch_softmax_fused_f32(const TrimulArgs &a, int mode, hipStream_t s
 
 hipError_t launch_attention_f32(const TrimulArgs &a, hipStream_t s) { return sm::launch_attention_impl<KF32>(a, s); }
 
+hipError_t launch_attention_online_f32(const TrimulArgs &a, hipStream_t s)
+{
+    return sm::launch_attention_online_impl<KF32>(a, s);
+}
+
 } // namespace cas

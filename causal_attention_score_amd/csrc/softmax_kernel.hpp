@@ -1051,5 +1051,235 @@ template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStre
     return launch_attention_nch<E, 16>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Single-pass attention: y and the row statistics in one launch, each score
+// and its exponential computed once (the two-launch path computes both in the
+// statistics launch and again in the attention launch).
+//
+// Per row the kernel keeps a running offset ms in base 2 and a running sum
+// l = sum_j exp2(a_j c - ms) (c = scale log2 e), and y accumulates
+// sum_j exp2(a_j c - ms) v_j; when the offset moves, l and y are rescaled by
+// exp2(ms_old - ms_new), and y / l is written at the end. The offset follows
+// the running maximum lazily: it moves only when a tile's largest score
+// exceeds it by more than ONLINE_TAU (in base 2), so after the first steps of
+// a row it rarely moves and the rescale is skipped for the whole wave. The
+// exponentials are then at most 2^ONLINE_TAU, well inside every format used.
+//
+// For the rescale to be one factor per lane, the output is accumulated
+// transposed, Y^T = V^T P^T: the MFMA operands of the P V product are
+// swapped, so a lane's accumulators all belong to its own query row (the
+// column of the score MFMAs), with head columns 32 nb + 8(r/4) + 4h + r%4.
+// ---------------------------------------------------------------------------
+constexpr float ONLINE_TAU = 8.f;
+
+struct OnlineRow {
+    float mt; // largest dot product of the row so far (row_max = mt * scale)
+    float ms; // offset of the exponentials: fl(m c) of an earlier maximum m <= mt
+    float l;  // this lane half's sum of exp2(a c - ms) (the halves see disjoint keys)
+};
+
+template <class E, int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, const char *kbuf,
+                                            const char *vbuf, const u32x4 (&qf)[NCH / 2], float c, int lane,
+                                            uint32_t kabs0, uint32_t qabs)
+{
+    constexpr bool F32 = std::is_same<E, KF32>::value;
+    constexpr int RB = NCH * 16;
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    f32x16 s[2];
+#pragma unroll
+    for (int u = 0; u < NCH / 2; ++u) {
+        u32x4 kf[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t row = 32u * b + r32;
+            kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (u == 0) s[b] = mfma_first<E>(kf[b], qf[u]);
+            else mfma_chunk<E>(s[b], kf[b], qf[u]);
+        }
+    }
+    // Keys after the query become -inf: no part in the maximum, exponential 0.
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (DIAG && kabs0 + 32u * b + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3) > qabs)
+                s[b][r] = -__builtin_inff();
+            tmax = fmaxf(tmax, s[b][r]);
+        }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)); // the row's other lane half: both take the same offset
+    rw.mt = fmaxf(rw.mt, tmax);
+    const bool need = fmaf(tmax, c, -rw.ms) > ONLINE_TAU; // first step: ms = -inf
+    if (__any(need)) {
+        const float msn = need ? pinned(tmax * c) : rw.ms;
+        const float alpha = __builtin_amdgcn_exp2f(rw.ms - msn); // 1 where the offset stays, 0 on the first step
+        rw.ms = msn;
+        rw.l *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yacc[nb][r] *= alpha;
+    }
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -rw.ms));
+            s[b][r] = p;
+            part[r & 3] += p;
+        }
+    rw.l += (part[0] + part[1]) + (part[2] + part[3]);
+    // Y^T += V^T P^T: the A operand is V (as the B operand of the P V form),
+    // the B operand this lane's p, in the same k-slots.
+    if constexpr (F32) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
+                    yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, s[b][j], yacc[nb], 0, 0, 0);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4 pb = {pack16<E>(s[b][8 * j + 0], s[b][8 * j + 1]),
+                                  pack16<E>(s[b][8 * j + 2], s[b][8 * j + 3]),
+                                  pack16<E>(s[b][8 * j + 4], s[b][8 * j + 5]),
+                                  pack16<E>(s[b][8 * j + 6], s[b][8 * j + 7])};
+                const uint32_t k0 = 32u * b + 16u * j + 4u * h; // keys k0 .. k0+3 and k0+8 .. k0+11
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const char *vr = vbuf + (32u * nb + r32) * AVT_PITCH;
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + k0 * 2u);
+                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + (k0 + 8u) * 2u);
+                    mfma_chunk<E>(yacc[nb], u32x4{lo[0], lo[1], hi[0], hi[1]}, pb);
+                }
+            }
+    }
+}
+
+template <class E, int NCH>
+__global__ void __launch_bounds__(STATS_THREADS, (AttnCfg<E, NCH>::MIN_WG))
+attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, float *__restrict__ row_logsum,
+                        float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt,
+                        uint32_t planes, uint32_t rank0, float scale, int vec_y)
+{
+    using Cfg = AttnCfg<E, NCH>;
+    constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB, VBYTES = Cfg::VBYTES;
+    __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
+    __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+
+    const BlockIdx bi = longest_first(planes, rank0, nt);
+    const uint32_t plane = bi.plane, I = bi.I;
+    const uint32_t b = plane / NH, nh = plane - b * NH;
+    const uint32_t ldb = 3u * C * (uint32_t)Cfg::ES;
+    const uint32_t head_bytes = HS * (uint32_t)Cfg::ES;
+    const char *qb0 = qkv + ((uint64_t)b * T * (3u * C) + (uint64_t)nh * HS) * Cfg::ES; // Q row 0 of the plane
+    const char *kb0 = qb0 + (uint64_t)C * Cfg::ES;                                      // K row 0
+    const char *vb0 = qb0 + (uint64_t)2 * C * Cfg::ES;                                  // V row 0
+    const float c = scale * LOG2E;
+
+    const uint32_t t0 = I * ST;
+    const uint32_t qabs = t0 + 32u * w + r32; // this lane's query row
+    u32x4 qf[NU];
+    {
+        const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb0 + (uint64_t)t0 * ldb);
+        const uint32_t row = 32u * w + r32;
+        const bool row_ok = t0 + row < T;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const uint32_t ch = 2u * u + h;
+            const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
+            qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
+        }
+    }
+    OnlineRow rw{-__builtin_inff(), -__builtin_inff(), 0.f};
+    f32x16 yacc[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) yacc[nb] = f32x16{};
+    const uint32_t nst = 2 * I + 2; // 64-key tiles 0 .. 2I + 1; the last two hold the diagonal
+    AttnStage<E, NCH> st;
+    attn_fetch<E, NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
+    attn_stage<E, NCH>(st, kbuf, vbuf, tid);
+    __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q and tile 0 in place
+    tri::lds_barrier();
+    uint32_t J = 0;
+    for (; J + 2 < nst; ++J) {
+        attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+        online_step<E, NCH, NBV, false>(yacc, rw, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, c, lane,
+                                        J * AKT, qabs);
+        attn_stage<E, NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
+        tri::lds_barrier();
+    }
+    attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+    online_step<E, NCH, NBV, true>(yacc, rw, kbuf, vbuf, qf, c, lane, J * AKT, qabs);
+    attn_stage<E, NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
+    tri::lds_barrier();
+    online_step<E, NCH, NBV, true>(yacc, rw, kbuf + KBYTES, vbuf + VBYTES, qf, c, lane, (J + 1) * AKT, qabs);
+
+    // y = Y / l and the statistics; the lane halves hold disjoint keys of one row.
+    const float lt = rw.l + __shfl_xor(rw.l, 32);
+    const float inv = 1.f / lt;
+    if (qabs < T) {
+        float *yr = y + ((uint64_t)b * T + qabs) * C + (uint64_t)nh * HS;
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t d0 = 32u * nb + 8u * g + 4u * h; // head columns d0 .. d0 + 3
+                if (d0 < HS) {
+                    const tri::f32x4v v = {yacc[nb][4 * g] * inv, yacc[nb][4 * g + 1] * inv, yacc[nb][4 * g + 2] * inv,
+                                      yacc[nb][4 * g + 3] * inv};
+                    if (vec_y) {
+                        *reinterpret_cast<tri::f32x4v *>(yr + d0) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) yr[d0 + e] = v[e];
+                    }
+                }
+            }
+        if (h == 0) {
+            const uint64_t o = (uint64_t)plane * T + qabs;
+            row_max[o] = rw.mt * scale;
+            // ln sum exp(x - max) = (log2 l + ms - mt c) ln 2; mt c - ms in [0, ONLINE_TAU], one rounding
+            row_logsum[o] = (__builtin_amdgcn_logf(lt) - fmaf(rw.mt, c, -rw.ms)) * LN2;
+        }
+    }
+}
+
+// Single-pass attention: y into a.out ((B, T, C) fp32, 16-byte stores when
+// a.vec_store), the statistics into a.row_max / a.row_logsum.
+template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, hipStream_t s)
+{
+    return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
+        if (a.HS * AttnCfg<E, 8>::ES <= 128)
+            hipLaunchKernelGGL((attention_online_kernel<E, 8>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+                               const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (float *)a.out,
+                               (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0,
+                               a.scale, (int)a.vec_store);
+        else
+            hipLaunchKernelGGL((attention_online_kernel<E, 16>), grid, dim3(STATS_THREADS), 0, s,
+                               (const char *)a.qkv, const_cast<float *>(a.row_max),
+                               const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
+                               (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+    });
+}
+
 } // namespace sm
 } // namespace cas

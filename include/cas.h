@@ -10,6 +10,7 @@
  *   cas_causal_softmax   causal softmax (log-probabilities or probabilities)
  *   cas_causal_softmax_fused  both softmax launches in one
  *   cas_causal_attention the attention output: softmax probabilities times V
+ *   cas_causal_attention_fused  the attention output and the row statistics in one pass
  *
  * Conventions shared by every entry point
  *   - Pointers X, W, Y, qkv, out, row_max, row_logsum are DEVICE pointers
@@ -205,6 +206,30 @@ int cas_causal_softmax_fused(const void *qkv, void *out, float *row_max, float *
 int cas_causal_attention(const void *qkv, const float *row_max, const float *row_logsum, void *y,
                          int64_t B, int64_t T, int64_t C, int64_t NH,
                          cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
+
+/*
+ * The attention output and the row statistics in one pass:
+ *   y, row_max, row_logsum   written, as cas_causal_attention's y and
+ *                            cas_causal_row_stats' statistics on the same qkv.
+ * Each score and its exponential are computed once. The row max is kept as it
+ * goes, the exponentials are taken against a running offset (a base-2 multiple
+ * of an earlier maximum, moved only when a key tile's largest score exceeds it
+ * by more than 2^8), and y and the sum are rescaled whenever the offset moves,
+ * so y = sum_j p_j V_j is formed as (sum_j w_j V_j) / (sum_j w_j). This is the
+ * softmax of the "Kernels GPU" section (row max, then ln sum exp(x - max),
+ * then the probabilities), taken over a row in one sweep instead of two.
+ * row_max equals cas_causal_row_stats' bit for bit; row_logsum and y agree
+ * with the two-pass results up to rounding (another summation order). For
+ * 16-bit inputs the weights w_j are rounded to the input format for the
+ * products with V; the sum uses them unrounded.
+ *   y   (B, T, C) fp32 (out_dtype must be CAS_F32), written whole, 16-byte
+ *       stores when y is 16-byte aligned.
+ * Domain, limits and empty shapes as for cas_causal_softmax; y and the 4-byte
+ * aligned statistics may overlap neither qkv nor one another.
+ */
+int cas_causal_attention_fused(const void *qkv, void *y, float *row_max, float *row_logsum,
+                               int64_t B, int64_t T, int64_t C, int64_t NH,
+                               cas_dtype in_dtype, cas_dtype out_dtype, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *cas_status_string(int status);

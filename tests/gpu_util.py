@@ -201,12 +201,14 @@ def _ratio(err, lim):
     return float(q.max()) if q.size else 0.0
 
 
-def assert_softmax_stats(mx, ls, mx_ref, ls_ref, bound, t_idx, in_dtype, what, exact_scores=False) -> float:
-    """GPU row statistics (R,) against the oracle's."""
+def assert_softmax_stats(mx, ls, mx_ref, ls_ref, bound, t_idx, in_dtype, what, exact_scores=False,
+                         extra=0.0) -> float:
+    """GPU row statistics (R,) against the oracle's. extra: a further
+    allowance on row_logsum (per row or scalar)."""
     _, D, S, _ = softmax_allowance(bound, t_idx, in_dtype, exact_scores)
     mx, ls = np.asarray(mx, np.float64), np.asarray(ls, np.float64)
     em, lm = np.abs(mx - mx_ref), D
-    el, ll = np.abs(ls - ls_ref), 2 * D + S + SM_R * (1 + np.abs(ls_ref))
+    el, ll = np.abs(ls - ls_ref), 2 * D + S + SM_R * (1 + np.abs(ls_ref)) + extra
     for name, e, lim, g, r in (("row_max", em, lm, mx, mx_ref), ("row_logsum", el, ll, ls, ls_ref)):
         bad = ~(e <= lim)
         if bad.any():
@@ -249,6 +251,64 @@ def assert_attention(got, ref, absw, p_ref, ls_ref, bound, t_idx, v_abs, in_dtyp
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; first (row {i}, col {j}): "
                              f"gpu={g[i, j]!r} oracle={ref[i, j]!r} allowed={lim[i, j]!r}")
     return _ratio(err, lim)
+
+
+# Single-pass attention (cas_causal_attention_fused). The kernel forms
+# y = sum_j w_j v_j / sum_j w_j with w_j = exp2(a_j c - ms) against a running
+# offset ms that lags the running maximum by at most ONLINE_TAU in base 2 and
+# rescales earlier terms by exp2(ms_old - ms_new) when it moves (at most once
+# per 64-key step). An error common to all w_j cancels in the ratio. Per
+# weight, in ln w_j, there remain the score error d_j, the roundings of the
+# exp2 argument and of exp2 itself, 2^-24 (8 + 3 (|lp_j| + |L| + TAU ln 2)),
+# and 2^-22 per rescale. With E_j = expm1(that) and E = max_j E_j the
+# normalised weights are within pi_j (E_j + E) / (1 - E), so
+#   |y_gpu - y| <= sum_j lim_j |v_j| + (u16 + 2 S + 2^-22) (sum_j p_j |v_j| + sum_j lim_j |v_j|) + a16 sum_j |v_j|,
+# where u16 and a16 are the input format's rounding of w_j for the 16-bit
+# MFMA (the sum uses the unrounded w_j), S the fp32 sums, and 2^-22 the final
+# division; weights that flush to zero are below 2^-126 of the sum. Where
+# E >= 1/2 (large score allowances, e.g. saturated 16-bit rows) that bound
+# is void, and the plain one holds instead: both are weighted means of the
+# same value rows, so |y_gpu - y| <= 2 max_j |v_j| (1 + u16) + a16 sum_j |v_j|
+# (plus the fp32 roundings). The row_logsum adds 2^-22 per step and 2^-21 TAU (the offset's distance from the
+# maximum) to the two-pass allowance; row_max is the two-pass value.
+ONLINE_TAU = 8.0
+
+
+def online_steps(t_idx):
+    return np.asarray(t_idx) // 64 + 1
+
+
+def assert_attention_online(got, ref, absw, p_ref, ls_ref, bound, t_idx, v_abs, in_dtype, what,
+                            exact_scores=False) -> float:
+    d, _, S, valid = softmax_allowance(bound, t_idx, in_dtype, exact_scores)
+    lp = np.log(np.maximum(p_ref, 1e-300))
+    L = np.abs(np.asarray(ls_ref, np.float64))[:, None]
+    arg = d + 2.0 ** -24 * (8 + 3 * (np.abs(lp) + L + ONLINE_TAU * np.log(2.0))) + \
+        online_steps(t_idx)[:, None] * 2.0 ** -22
+    E = np.where(valid, np.expm1(arg), 0.0)
+    Em = E.max(axis=1, keepdims=True)
+    lim_p = np.where(valid, p_ref * (E + Em) / (1 - Em) + 2.0 ** -118, 0.0)
+    u16, a16 = ROUND16[in_dtype] if in_dtype != "f32" else (0.0, 0.0)
+    lpv = lim_p @ v_abs
+    vsum = valid.astype(np.float64) @ v_abs
+    lim = lpv + (u16 + 2 * S[:, None] + 2.0 ** -22) * (absw + lpv) + a16 * vsum
+    vmax = np.stack([v_abs[:int(t) + 1].max(axis=0) for t in np.asarray(t_idx)])
+    hull = 2 * vmax * (1 + u16 + 2 * S[:, None] + 2.0 ** -22) + a16 * vsum
+    lim = np.where(Em < 0.5, lim, hull)
+    g = np.asarray(got, np.float64)
+    if not np.all(np.isfinite(g)):
+        raise AssertionError(f"{what}: non-finite output")
+    err = np.abs(g - ref)
+    bad = ~(err <= lim)
+    if bad.any():
+        i, j = (int(x) for x in np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; first (row {i}, col {j}): "
+                             f"gpu={g[i, j]!r} oracle={ref[i, j]!r} allowed={lim[i, j]!r}")
+    return _ratio(err, lim)
+
+
+def online_logsum_extra(t_idx):
+    return online_steps(t_idx) * 2.0 ** -22 + SM_R * ONLINE_TAU
 
 
 def assert_softmax(got, ref, ls_ref, bound, t_idx, in_dtype, mode, out_dtype, what, exact_scores=False) -> float:

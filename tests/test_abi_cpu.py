@@ -187,6 +187,35 @@ def test_attention_rejections(L):
         assert at(L, ind=BF16, C=24) == EDEV                # 16-byte heads of a 16-bit type
 
 
+def af(L, qkv=PX, y=PZ, mx=PY, ls=PW, B=2, T=5, C=12, NH=3, ind=F32, outd=F32):
+    return L.cas_causal_attention_fused(qkv, y, mx, ls, B, T, C, NH, ind, outd, None)
+
+
+def test_attention_fused_rejections(L):
+    import torch
+    assert af(L, ind=5) == EDTYPE
+    assert af(L, outd=BF16) == EDTYPE
+    assert af(L, B=-1) == ESHAPE
+    assert af(L, C=10, NH=3) == ESHAPE
+    assert af(L, y=None) == ENULL and af(L, qkv=None) == ENULL and af(L, mx=None) == ENULL
+    assert af(L, ls=None) == ENULL
+    assert af(L, ind=F16, C=12) == EUNSUP                   # 8-byte heads of a 16-bit type
+    assert af(L, C=15, NH=3) == EUNSUP                      # 20-byte heads
+    assert af(L, mx=PY + 2) == EUNSUP and af(L, y=PZ + 2) == EUNSUP
+    assert af(L, B=2**23, T=1, C=4, NH=1) == EUNSUP
+    # three outputs: none over qkv or over another; (B, T, C) fp32 y spans 480 bytes, statistics 120
+    assert af(L, y=PX + 16) == EALIAS
+    assert af(L, mx=PX + 16) == EALIAS
+    assert af(L, y=PY - 256) == EALIAS                      # y over row_max
+    assert af(L, ls=PY + 116) == EALIAS                     # row_logsum over row_max's last value
+    assert af(L, B=0) == OK and af(L, T=0) == OK
+    assert af(L, qkv=None, y=None, mx=None, ls=None, B=0) == OK
+    if not torch.cuda.is_available():
+        assert af(L) == EDEV
+        assert af(L, y=PZ + 4) == EDEV                      # 4-byte aligned y: scalar stores
+        assert af(L, ind=BF16, C=24) == EDEV
+
+
 def test_softmax_rejections(L):
     for f in (rs, sm, fu):
         assert f(L, ind=5) == EDTYPE

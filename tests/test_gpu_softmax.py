@@ -12,7 +12,8 @@ import torch
 
 import causal_attention_score_amd as cas
 from causal_attention_score_amd import synth
-from gpu_util import (FILL, GUARD, assert_attention, assert_softmax, assert_softmax_stats, case, check_guards,
+from gpu_util import (FILL, GUARD, assert_attention, assert_attention_online, assert_softmax, assert_softmax_stats,
+                      case, check_guards, online_logsum_extra,
                       guarded_output, guarded_output16, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -377,3 +378,125 @@ def test_workload_attention_bf16_full_size(orc):
     worst = check_attention(orc, qkv, wl.dtype, B, T, NH, HS, wl.name,
                             b_t=[(0, 0, 32), (2, 2040, 2060), (3, 4070, 4096)])
     print(f"{wl.name} attention: sampled max err/tol {worst:.3g}")
+
+
+# ------------------------------------------------------- single-pass attention
+
+def run_attention_fused(qkv, dtype, B, T, NH, HS, label, y_offset=0):
+    """The single-pass attention into guarded buffers (y shifted by y_offset
+    elements: 4 gives a y that is only 4-byte aligned); returns y (B, T, C)
+    and the statistics (B, NH, T), as numpy."""
+    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    C = NH * HS
+    n = B * T * C
+    ybuf, yflat = guarded_output(n + y_offset)
+    y = yflat[y_offset:y_offset + n]
+    mbuf, mflat = guarded_output(B * NH * T)
+    lbuf, lflat = guarded_output(B * NH * T)
+    case(f"{label} causal_attention_fused {dtype} B={B} T={T} NH={NH} HS={HS} y_offset={y_offset}")
+    L = cas.lib()
+    st = L.cas_causal_attention_fused(d.data_ptr(), y.data_ptr(), mflat.data_ptr(), lflat.data_ptr(), B, T, C, NH,
+                                      cas._dtype_code(d), cas.CAS_F32, cas._stream_ptr(d.device))
+    cas._check("cas_causal_attention_fused", st)
+    torch.cuda.synchronize()
+    check_guards(ybuf, n + y_offset)
+    check_guards(mbuf, B * NH * T)
+    check_guards(lbuf, B * NH * T)
+    return (y.view(B, T, C).cpu().numpy(), mflat.view(B, NH, T).cpu().numpy(), lflat.view(B, NH, T).cpu().numpy())
+
+
+def check_attention_fused(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, b_t=None, y_offset=0,
+                          two_pass_max=True):
+    """Single-pass y and statistics against the oracle's, head by head; the
+    row maxima also against the two-pass statistics launch, bit for bit."""
+    C = NH * HS
+    y, mx, ls = run_attention_fused(qkv, dtype, B, T, NH, HS, label, y_offset)
+    if two_pass_max:
+        mx2, _ = cas.causal_row_stats(to_device(qkv, dtype).view(B, T, 3 * C), NH)
+        mx2 = mx2.cpu().numpy()
+        if not np.array_equal(mx.view(np.uint32), mx2.view(np.uint32)):
+            raise AssertionError(f"{label}: single-pass row_max differs from the statistics launch")
+    V = np.abs(orc.decode(qkv, dtype).reshape(B, T, 3, NH, HS)[:, :, 2]) if dtype != "f32" else \
+        np.abs(qkv.reshape(B, T, 3, NH, HS)[:, :, 2].astype(np.float64))
+    worst = 0.0
+    for (b, t0, t1) in (b_t or [(b, 0, T) for b in range(B)]):
+        yr, aw = orc.causal_attention(qkv, B, T, C, NH, dtype, b_range=[b], t_range=(t0, t1))
+        for h in range(NH):
+            p, mr, lr, bd = orc.causal_softmax_rows(qkv, B, T, C, NH, b, h, t0, t1, dtype, "prob")
+            cols = slice(h * HS, (h + 1) * HS)
+            rows = np.arange(t0, t1)
+            what = f"{label} fused attention b={b} h={h} rows {t0}.."
+            worst = max(worst, assert_attention_online(y[b, t0:t1, cols], yr[0, :, cols], aw[0, :, cols], p, lr, bd,
+                                                       rows, V[b, :, h], dtype, what, exact_scores))
+            worst = max(worst, assert_softmax_stats(mx[b, h, t0:t1], ls[b, h, t0:t1], mr, lr, bd, rows, dtype,
+                                                    what + " stats", exact_scores, online_logsum_extra(rows)))
+    return worst
+
+
+@pytest.mark.parametrize("HS", [8, 40, 64])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 255, 300])
+def test_attention_fused_ragged_f32(orc, T, HS):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 17 + HS)
+    check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "sweep")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("HS", [8, 64, 128])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 300])
+def test_attention_fused_ragged_16bit(orc, T, HS, dtype):
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 11 + HS)
+    check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "sweep")
+
+
+def test_attention_fused_ramp_rescales(orc):
+    """Ramp scores (exact in fp32) with slopes 0.25, -0.5, 0 and 64 per key:
+    the running maximum grows on every step in the steep rows, so the offset
+    moves and y is rescaled again and again; only exp / sum roundings allowed."""
+    B, T, NH, HS = 2, 300, 4, 64
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in (0.25, -0.5, 0.0, 64.0)], "f32", v_ramp=True)
+    check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "ramp", exact_scores=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_fused_saturated(orc, dtype):
+    B, T, NH, HS = 1, 257, 2, 64
+    qkv = synth.to_storage(synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(16.0), dtype)
+    check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "saturated")
+
+
+def test_attention_fused_unaligned_y(orc):
+    B, T, NH, HS = 2, 70, 3, 16
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=3)
+    check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "y+4B", y_offset=1)
+
+
+def test_attention_fused_empty_and_rejections():
+    qkv = torch.zeros(2, 0, 3 * 2 * 8, device="cuda")
+    y, mx, ls = cas.causal_attention_fused(qkv, 2)
+    assert y.numel() == 0 and mx.numel() == 0
+    y2, _, _ = cas.causal_attention(qkv, 2)
+    assert y2.numel() == 0
+    bad = torch.zeros(2, 8, 3 * 2 * 4, device="cuda", dtype=torch.float16)
+    with pytest.raises(cas.CasError) as e:
+        cas.causal_attention_fused(bad, 2)
+    assert e.value.status == -7
+
+
+def test_workload_attention_fused_full_size(orc):
+    wl = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    worst = check_attention_fused(orc, qkv, "f32", B, T, NH, HS, wl.name,
+                                  b_t=[(0, 0, 64), (3, 500, 540), (7, 960, 1024)])
+    print(f"{wl.name} fused attention: sampled max err/tol {worst:.3g}")
+
+
+def test_workload_attention_fused_bf16_full_size(orc):
+    wl = synth.WORKLOADS["trimul_bf16_B4_T4096_NH25_HS64"]
+    B, T, NH, HS = wl.dims
+    (qkv,) = wl.inputs()
+    worst = check_attention_fused(orc, qkv, wl.dtype, B, T, NH, HS, wl.name,
+                                  b_t=[(0, 0, 32), (2, 2040, 2060), (3, 4070, 4096)])
+    print(f"{wl.name} fused attention: sampled max err/tol {worst:.3g}")
