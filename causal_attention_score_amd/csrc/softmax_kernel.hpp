@@ -17,11 +17,10 @@
 // rows they fetch.
 //
 // Row-stats kernel design:
-//  * A workgroup owns a pair of 128-row query blocks of one (b, nh) plane,
-//    I and nt-1-I, so every workgroup walks nt + 1 key tiles whatever I is
-//    (block I needs key tiles 0..I). One workgroup per pair: the hardware
-//    dispatcher balances them; ids are grouped per XCD so that a plane's K
-//    rows stay in one L2.
+//  * A workgroup owns one 128-row query block I of one (b, nh) plane (key
+//    tiles 0..I). Workgroups are numbered longest block first, and the
+//    dispatcher hands them out in index order, so the short blocks fill the
+//    last round (longest_first below).
 //  * Four waves, wave w owns query rows 32w..32w+31 of the block. Its Q
 //    fragments stay in registers for the whole block; the 128 K rows of each
 //    step are fetched by all four waves (coalesced 16-byte loads, issued a
@@ -673,17 +672,20 @@ template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode,
 // the probabilities reach HBM: per key tile the scores are recomputed, turned
 // into p in registers and multiplied into the output on the MFMAs.
 //
-// fp32 inputs (v_mfma_f32_32x32x2_f32). A workgroup owns a pair of 128-row
-// query blocks (as the row-statistics kernel), four waves of 32 query rows,
-// each wave's Q fragments in registers; per step 64 keys: their K rows (for
-// D = K Q^T) and V rows are fetched a step ahead into double-buffered LDS.
+// A workgroup owns one 128-row query block (longest first, as the
+// row-statistics kernel), four waves of 32 query rows, each wave's Q
+// fragments in registers; per step 64 keys: their K rows (for D = K Q^T) and
+// V rows are fetched a step ahead into double-buffered LDS.
 //  * Lane (r32, h) of the score MFMAs holds p for query r32 and keys
-//    8g + 4h + e of each 32-key block (accumulator r = 4g + e). The product
-//    P V contracts over keys, and its MFMA j takes key 8(j/4) + 4h + j%4 in
-//    k-slot h: exactly accumulator j, so P feeds the A operand from the
-//    registers it was computed in; the B operand is V[that key][d] from LDS.
-//  * V rows sit 288 bytes apart in LDS, so the two keys an MFMA reads (4
-//    apart) fall in different bank halves.
+//    8g + 4h + e of each 32-key block (accumulator r = 4g + e).
+//  * fp32 inputs (v_mfma_f32_32x32x2_f32): the product P V contracts over
+//    keys, and its MFMA j takes key 8(j/4) + 4h + j%4 in k-slot h: exactly
+//    accumulator j, so P feeds the A operand from the registers it was
+//    computed in; the B operand is V[that key][d] from LDS. V rows sit 288
+//    bytes apart, so the two keys an MFMA reads (4 apart) fall in different
+//    bank halves.
+//  * 16-bit inputs (v_mfma_f32_32x32x16): see the 16-bit section below (P
+//    rounded to the format, V staged transposed).
 // ---------------------------------------------------------------------------
 constexpr int AKT = 64;            // keys per attention step
 constexpr int AV_PITCH = 256 + 32; // LDS bytes per V row (HS * 4 <= 256)
