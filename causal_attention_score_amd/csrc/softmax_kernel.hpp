@@ -830,7 +830,10 @@ template <int NCH>
 __device__ __forceinline__ void a_fetch16(AStage16<NCH> &st, const char *kb0, const char *vb0, uint32_t J, uint32_t T,
                                           uint32_t ldb, uint32_t head_bytes, int tid)
 {
-    const bool kside = tid < 128; // wave-uniform
+    // Wave-uniform, and visibly so: from the wave's first lane. A per-lane
+    // test here would make the compiler build the buffer resource in a loop
+    // over the distinct values among the lanes (a waterfall) on every fetch.
+    const bool kside = __builtin_amdgcn_readfirstlane(tid) < 128;
     const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
     const __amdgpu_buffer_rsrc_t rs = rsrc_at((kside ? kb0 : vb0) + (uint64_t)J * AKT * ldb);
     const uint32_t lim = c * 16 < head_bytes ? T : 0u;
@@ -845,7 +848,7 @@ __device__ __forceinline__ void a_fetch16(AStage16<NCH> &st, const char *kb0, co
 
 template <int NCH> __device__ __forceinline__ void a_store16(const AStage16<NCH> &st, char *kbuf, char *vtbuf, int tid)
 {
-    const bool kside = tid < 128;
+    const bool kside = __builtin_amdgcn_readfirstlane(tid) < 128;
     const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
     if (kside) {
 #pragma unroll
