@@ -24,7 +24,13 @@ template <> struct GemmBK<KF32> { static constexpr int v = 32; };
 template <> struct GemmBK<KBF16> { static constexpr int v = 64; };
 template <> struct GemmBK<KF16> { static constexpr int v = 64; };
 
-template <class E, int BM, int BN, int WGM, int WGN, int VEC, bool PRED>
+// Depth of the register ring that fetches ahead on 64x64 tiles (RING > 0).
+// Those tiles serve shapes with about one tile per CU, where the single wave
+// on each SIMD has nothing else to hide a panel's first touch behind; RING = 0
+// fetches one chunk ahead (two LDS stages, no ring).
+constexpr int GEMM_RING = 4;
+
+template <class E, int BM, int BN, int WGM, int WGN, int VEC, bool PRED, int RING>
 __global__ void __launch_bounds__(WGM *WGN * 64)
 gemm_nt_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
                int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
@@ -49,7 +55,10 @@ gemm_nt_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__
     const int64_t tn = (pid % group) / gm;
 
     f32x16 acc[G::MB][G::NB];
-    G::template mainloop<2>(acc, lds, X, ldx, M, tm * BM, W, ldw, N, tn * BN, K, tid);
+    if constexpr (RING > 0)
+        G::template mainloop_ring<RING>(acc, lds, X, ldx, M, tm * BM, W, ldw, N, tn * BN, K, tid);
+    else
+        G::template mainloop<2>(acc, lds, X, ldx, M, tm * BM, W, ldw, N, tn * BN, K, tid);
 
     // Writeback stage: predicated on the true M and N.
     const int lane = tid & 63, wave = tid >> 6;
@@ -78,14 +87,26 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s)
     using C = TileCfg<BM, BN>;
     const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn * a.batch));
-    if (a.predicated)
-        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, true>), grid, dim3(C::WGM * C::WGN * 64),
-                           0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm,
-                           tn, a.batch, a.bsx, a.bsw, a.bsy);
-    else
-        hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, false>), grid,
-                           dim3(C::WGM * C::WGN * 64), 0, s, (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N,
-                           a.K, a.ldx, a.ldw, a.ldy, tm, tn, a.batch, a.bsx, a.bsw, a.bsy);
+    const dim3 block(C::WGM * C::WGN * 64);
+    // The ring's buffer loads address a tile's rows from its first row with
+    // 32-bit offsets below 2^31 - 1.
+    constexpr int64_t BKB = GemmBK<E>::v * E::ES;
+    const int64_t lim = INT64_C(0x7FFFFFFF);
+    const bool ring = BM == 64 && (BM * a.ldx * E::ES + BKB) <= lim && (BN * a.ldw * E::ES + BKB) <= lim;
+#define CAS_GEMM_LAUNCH(PRED, RING)                                                                                    \
+    hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, PRED, RING>), grid, block, 0, s,               \
+                       (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn, a.batch, \
+                       a.bsx, a.bsw, a.bsy)
+    if constexpr (BM == 64) {
+        if (ring) {
+            if (a.predicated) CAS_GEMM_LAUNCH(true, GEMM_RING);
+            else CAS_GEMM_LAUNCH(false, GEMM_RING);
+            return hipGetLastError();
+        }
+    }
+    if (a.predicated) CAS_GEMM_LAUNCH(true, 0);
+    else CAS_GEMM_LAUNCH(false, 0);
+#undef CAS_GEMM_LAUNCH
     return hipGetLastError();
 }
 

@@ -99,6 +99,48 @@ struct TileBounds {
     int64_t ra0, rowsA, rb0, rowsB, K;
 };
 
+// Raw buffer loads by width. With num_records 2^31 - 1, an offset of 2^31
+// lies outside the buffer and reads as zero (no access is made).
+constexpr uint32_t BUF_OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const char *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+template <int VB> struct BufLoad;
+template <> struct BufLoad<16> {
+    __device__ static __forceinline__ u32x4 ld(__amdgpu_buffer_rsrc_t r, uint32_t o)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0);
+    }
+};
+template <> struct BufLoad<8> {
+    __device__ static __forceinline__ u32x2 ld(__amdgpu_buffer_rsrc_t r, uint32_t o)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, (int)o, 0, 0);
+    }
+};
+template <> struct BufLoad<4> {
+    __device__ static __forceinline__ unsigned int ld(__amdgpu_buffer_rsrc_t r, uint32_t o)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
+    }
+};
+template <> struct BufLoad<2> {
+    __device__ static __forceinline__ unsigned short ld(__amdgpu_buffer_rsrc_t r, uint32_t o)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)o, 0, 0);
+    }
+};
+
+// A workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the wave's global loads, which may stay in flight.
+__device__ __forceinline__ void lds_only_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // E: element kind. BM x BN output tile, BK contraction chunk, WGM x WGN waves,
 // VEC elements per global load. PRED: the compute stage re-checks every
 // operand element against the matrix bounds, zeroing those outside -- the
@@ -156,6 +198,36 @@ struct Engine {
             V val = {};
             if (gr < rowsB && gk < K) val = *reinterpret_cast<const V *>(B + (gr * ldb + gk) * ES);
             R.b[it] = val;
+        }
+    }
+
+    // The same fetch with buffer loads and no branch: an element outside the
+    // matrix gets the out-of-range offset and reads zero. Loads under
+    // per-lane branches make the compiler's wait at the stash cover every
+    // load in flight, which a fetch several chunks ahead cannot afford. The
+    // host guarantees BM * lda * ES and BN * ldb * ES below 2^31, so every
+    // in-range offset from the tile's first row fits.
+    __device__ static __forceinline__ void fetch_buf(Regs &R, const char *A, int64_t lda, int64_t rowsA, int64_t ra0,
+                                                     const char *B, int64_t ldb, int64_t rowsB, int64_t rb0,
+                                                     int64_t K, int64_t k0, int tid)
+    {
+        const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A + (ra0 * lda + k0) * ES);
+        const __amdgpu_buffer_rsrc_t rb = buf_rsrc(B + (rb0 * ldb + k0) * ES);
+#pragma unroll
+        for (int it = 0; it < A_IT; ++it) {
+            const int v = it * NT + tid;
+            const int r = v / VPR, c = v % VPR;
+            const bool ok = ra0 + r < rowsA && k0 + (int64_t)c * VEC < K;
+            const uint32_t o = ok ? (uint32_t)(r * lda * ES) + (uint32_t)(c * VB) : BUF_OOB;
+            R.a[it] = BufLoad<VB>::ld(ra, o);
+        }
+#pragma unroll
+        for (int it = 0; it < B_IT; ++it) {
+            const int v = it * NT + tid;
+            const int r = v / VPR, c = v % VPR;
+            const bool ok = rb0 + r < rowsB && k0 + (int64_t)c * VEC < K;
+            const uint32_t o = ok ? (uint32_t)(r * ldb * ES) + (uint32_t)(c * VB) : BUF_OOB;
+            R.b[it] = BufLoad<VB>::ld(rb, o);
         }
     }
 
@@ -218,6 +290,46 @@ struct Engine {
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) mfma_chunk<E>(acc[mb][nb], af[mb], bfr[nb]);
+        }
+    }
+
+    // Full contraction over K with a ring of D register sets: chunk kc + D is
+    // fetched while chunk kc is multiplied, so a fetch has D - 1 chunks of
+    // MFMA work to land before it is stashed (first touches of a panel come
+    // from beyond the L2 and take longer than one chunk). Two LDS stages; the
+    // barriers order LDS only, so the ring's loads stay in flight across them.
+    template <int D>
+    __device__ static __forceinline__ void mainloop_ring(f32x16 (&acc)[MB][NB], char *lds,
+                                                         const char *A, int64_t lda, int64_t rowsA, int64_t ra0,
+                                                         const char *B, int64_t ldb, int64_t rowsB, int64_t rb0,
+                                                         int64_t K, int tid)
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wave_m = wave / WGN, wave_n = wave % WGN;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+
+        const int64_t nk = (K + BK - 1) / BK;
+        Regs R[D]; // chunk c lives in R[c % D] from its fetch to its stash
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (d < nk) fetch_buf(R[d], A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, (int64_t)d * BK, tid);
+        if (nk > 0) stash(R[0], lds, tid);
+        lds_only_barrier();
+        for (int64_t k0 = 0; k0 < nk; k0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int64_t kc = k0 + d;
+                if (kc >= nk) break;
+                // R[d] held chunk kc, stashed at the end of chunk kc - 1: refill it
+                if (kc + D < nk) fetch_buf(R[d], A, lda, rowsA, ra0, B, ldb, rowsB, rb0, K, (kc + D) * BK, tid);
+                compute(acc, lds + (kc & 1) * STAGE, wave_m, wave_n, lane, TileBounds{ra0, rowsA, rb0, rowsB, K},
+                        kc * BK);
+                if (kc + 1 < nk) stash(R[(d + 1) % D], lds + ((kc + 1) & 1) * STAGE, tid);
+                lds_only_barrier(); // stage kc + 1 written, stage kc read by every wave
+            }
         }
     }
 
