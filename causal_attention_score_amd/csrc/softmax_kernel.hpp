@@ -732,12 +732,12 @@ template <int NCH> __device__ __forceinline__ void a_store(const AStage<NCH> &st
 // p from the row statistics (mx: the row's max score, ls: its logsum), then
 // y[nb] += P V for the NBV 32-column blocks of the head. DIAG: keys after the
 // query (absolute index kabs0 + key > qabs) get p = 0.
-template <int NCH, int NBV, bool DIAG>
-__device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
-                                       const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
-                                       uint32_t kabs0, uint32_t qabs)
+// Scores of this wave's 32 queries against the tile's 64 keys: D = K Q^T
+// per 32-key block b, so s[b][r] is the dot product of query lane%32 and key
+// 32b + 8(r/4) + 4(lane/32) + r%4 (unscaled).
+template <class E, int NCH>
+__device__ __forceinline__ void attn_scores(f32x16 (&s)[2], const char *kbuf, const u32x4 (&qf)[NCH / 2], int lane)
 {
-    f32x16 s[2];
     constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 #pragma unroll
@@ -750,10 +750,20 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
         }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            if (u == 0) s[b] = mfma_first<KF32>(kf[b], qf[u]);
-            else mfma_chunk<KF32>(s[b], kf[b], qf[u]);
+            if (u == 0) s[b] = mfma_first<E>(kf[b], qf[u]);
+            else mfma_chunk<E>(s[b], kf[b], qf[u]);
         }
     }
+}
+
+template <int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
+                                       const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
+                                       uint32_t kabs0, uint32_t qabs)
+{
+    f32x16 s[2];
+    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    attn_scores<KF32, NCH>(s, kbuf, qf, lane);
     // p, in place, as the softmax-rows kernel forms it
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -879,22 +889,8 @@ __device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, 
                                          uint32_t kabs0, uint32_t qabs)
 {
     f32x16 s[2];
-    constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-#pragma unroll
-    for (int u = 0; u < NCH / 2; ++u) {
-        u32x4 kf[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t row = 32u * b + r32;
-            kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (u == 0) s[b] = mfma_first<E>(kf[b], qf[u]);
-            else mfma_chunk<E>(s[b], kf[b], qf[u]);
-        }
-    }
+    attn_scores<E, NCH>(s, kbuf, qf, lane);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1089,23 +1085,9 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
                                             uint32_t kabs0, uint32_t qabs)
 {
     constexpr bool F32 = std::is_same<E, KF32>::value;
-    constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
     f32x16 s[2];
-#pragma unroll
-    for (int u = 0; u < NCH / 2; ++u) {
-        u32x4 kf[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t row = 32u * b + r32;
-            kf[b] = *reinterpret_cast<const u32x4 *>(kbuf + row * RB + kswz<NCH>(row, 2u * u + h));
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (u == 0) s[b] = mfma_first<E>(kf[b], qf[u]);
-            else mfma_chunk<E>(s[b], kf[b], qf[u]);
-        }
-    }
+    attn_scores<E, NCH>(s, kbuf, qf, lane);
     // Keys after the query become -inf: no part in the maximum, exponential 0.
     float tmax = -__builtin_inff();
 #pragma unroll
