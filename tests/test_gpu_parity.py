@@ -153,6 +153,26 @@ def test_gemm_strided_misaligned(orc, dtype):
     assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
 
 
+@pytest.mark.parametrize("ldx", [8_000_000, 9_000_000])
+def test_gemm_huge_row_pitch(orc, ldx):
+    """Row pitches near the 31-bit offset range: 64x64 tiles fetch through
+    buffer offsets from a tile's first row while 64 rows of the pitch fit
+    below 2^31 bytes (8M fp32 elements, the register-ring loop) and fall back
+    to the two-stage loop above it (9M); both must match the oracle."""
+    M, N, K = 3, 70, 100
+    g = np.random.default_rng(ldx % 997)
+    Xf = synth.to_storage(g.standard_normal(((M - 1) * ldx + K,)).astype(np.float32), "f32")
+    W = synth.to_storage(g.standard_normal((N, K)).astype(np.float32), "f32")
+    ref, bound = orc.gemm_nt(Xf, W.ravel(), "f32", M=M, N=N, K=K, ldx=ldx, ldw=K, ldy=N)
+    x = to_device(Xf, "f32").as_strided((M, K), (ldx, 1))
+    buf, flat = guarded_output(M * N)
+    case(f"gemm row pitch {ldx}")
+    cas.gemm_nt(x, to_device(W, "f32"), out=flat.view(M, N))
+    torch.cuda.synchronize()
+    check_guards(buf, M * N)
+    assert_close(flat.view(M, N).cpu().numpy(), ref, bound, "f32", f"gemm ldx={ldx}")
+
+
 # ------------------------------------------------------- batch_matmul_nt
 
 BMM_SHAPES = [(192, 120, 120, 64), (3, 65, 33, 127), (5, 1, 257, 129), (7, 200, 72, 3), (2, 128, 128, 128),
