@@ -409,8 +409,8 @@ def main():
                     help="only launch the kernels for the rocprofv3 HBM-traffic counter runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the hot path shards with no communication "
-              "and this build measures one GPU's share; --gpus above 1 is not supported.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the hot path shards with no communication, "
+              "so one GPU's share is what is measured; --gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
