@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace cas {
 
 enum ElemCode { E_F32 = 0, E_BF16 = 1, E_F16 = 2 };
@@ -28,6 +30,30 @@ struct TrimulArgs {
     const float *row_max = nullptr;    // causal softmax: per-row statistics (B, NH, T)
     const float *row_logsum = nullptr;
 };
+
+// Persistent grids: workgroups of one kernel resident on a device at once
+// (occupancy per compute unit times compute units), found once per device.
+// Each launcher keeps one ResidentSlots per kernel instance as a static; the
+// per-device once_flag makes the first fill safe under concurrent host threads.
+struct ResidentSlots {
+    static constexpr int MAX_DEV = 64;
+    std::once_flag once[MAX_DEV];
+    int64_t slots[MAX_DEV] = {};
+};
+
+template <class F> int64_t resident_slots(ResidentSlots &c, F kern, int threads)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ResidentSlots::MAX_DEV) dev = 0;
+    std::call_once(c.once[dev], [&c, kern, threads, dev] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess || n < 1) n = 1;
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
+        c.slots[dev] = (int64_t)n * cu;
+    });
+    return c.slots[dev];
+}
 
 // Tile shapes the dense launcher can pick (exposed for tests and tuning).
 enum GemmTile { GEMM_TILE_AUTO = 0, GEMM_TILE_64 = 1, GEMM_TILE_128 = 2, GEMM_TILE_256 = 3 };

@@ -586,21 +586,9 @@ template <class E, int NCH, class O, class EP> hipError_t launch_fused(const Tri
     auto kern = softmax_fused_kernel<E, NCH, O, EP>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t P = a.B * a.NH;
-    static int resident_per_cu[64] = {0};
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (resident_per_cu[dev] == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, tri::SUPER_THREADS, 0) != hipSuccess || n < 1)
-            n = 1;
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
-        cus[dev] = cu;
-        resident_per_cu[dev] = n;
-    }
+    static ResidentSlots resident;
     // Persistent grid; no more workgroups than row blocks (each XCD's share).
-    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    int64_t grid = resident_slots(resident, kern, tri::SUPER_THREADS);
     const int64_t blocks = P * nt;
     if (grid > 8 * ((blocks + 7) / 8)) grid = 8 * ((blocks + 7) / 8);
     if (grid < 8) grid = 8;

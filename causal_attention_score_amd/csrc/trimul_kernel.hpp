@@ -967,19 +967,8 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
-    static int resident_per_cu[64] = {0};
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (resident_per_cu[dev] == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, SUPER_THREADS, 0) != hipSuccess || n < 1) n = 1;
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
-        cus[dev] = cu;
-        resident_per_cu[dev] = n;
-    }
-    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    static ResidentSlots resident;
+    int64_t grid = resident_slots(resident, kern, SUPER_THREADS);
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
@@ -1013,20 +1002,9 @@ hipError_t launch_cfg(const TrimulArgs &a, hipStream_t s)
     const int64_t items = a.B * a.NH * L;
 
     // Persistent grid: as many workgroups as stay resident on the device.
-    static int resident_per_cu[64] = {0};
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (resident_per_cu[dev] == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NTHREADS, 0) != hipSuccess || n < 1) n = 1;
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1) cu = 256;
-        cus[dev] = cu;
-        resident_per_cu[dev] = n;
-    }
+    static ResidentSlots resident;
     const int64_t want = (items + NCOMP - 1) / NCOMP;
-    int64_t grid = (int64_t)resident_per_cu[dev] * cus[dev];
+    int64_t grid = resident_slots(resident, kern, NTHREADS);
     if (grid > want) grid = want;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, (float *)a.out, a.T, a.C,
