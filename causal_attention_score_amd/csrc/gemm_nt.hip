@@ -24,11 +24,15 @@ template <> struct GemmBK<KF32> { static constexpr int v = 32; };
 template <> struct GemmBK<KBF16> { static constexpr int v = 64; };
 template <> struct GemmBK<KF16> { static constexpr int v = 64; };
 
-// Depth of the register ring that fetches ahead on 64x64 tiles (RING > 0).
-// Those tiles serve shapes with about one tile per CU, where the single wave
-// on each SIMD has nothing else to hide a panel's first touch behind; RING = 0
-// fetches one chunk ahead (two LDS stages, no ring).
-constexpr int GEMM_RING = 4;
+// Depth of the register ring that fetches ahead (RING > 0), by tile edge and
+// bytes per global load. A ring lets a fetch have three chunks of MFMA work to
+// land, which the single wave per SIMD of a one-tile-per-CU launch needs. On
+// 128 x 128 tiles it pays only with 16-byte loads: narrower ones take more
+// registers per chunk, the kernel passes 256 VGPRs, and two workgroups per CU
+// no longer fit (bf16 4096 x 4096 x 4098: 237 us without, 252 with; bf16
+// 2048^3: 34.3 us without, 26.6 with). RING = 0 fetches one chunk ahead (two
+// LDS stages, no ring).
+template <int BM, int VB> constexpr int gemm_ring = (BM == 64 || VB == 16) ? 4 : 0;
 
 template <class E, int BM, int BN, int WGM, int WGN, int VEC, bool PRED, int RING>
 __global__ void __launch_bounds__(WGM *WGN * 64)
@@ -92,15 +96,16 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s)
     // 32-bit offsets below 2^31 - 1.
     constexpr int64_t BKB = GemmBK<E>::v * E::ES;
     const int64_t lim = INT64_C(0x7FFFFFFF);
-    const bool ring = BM == 64 && (BM * a.ldx * E::ES + BKB) <= lim && (BN * a.ldw * E::ES + BKB) <= lim;
+    const bool ring = (BM * a.ldx * E::ES + BKB) <= lim && (BN * a.ldw * E::ES + BKB) <= lim;
 #define CAS_GEMM_LAUNCH(PRED, RING)                                                                                    \
     hipLaunchKernelGGL((gemm_nt_kernel<E, BM, BN, C::WGM, C::WGN, VEC, PRED, RING>), grid, block, 0, s,               \
                        (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn, a.batch, \
                        a.bsx, a.bsw, a.bsy)
-    if constexpr (BM == 64) {
+    constexpr int RING = gemm_ring<BM, VEC * E::ES>;
+    if constexpr (RING > 0) {
         if (ring) {
-            if (a.predicated) CAS_GEMM_LAUNCH(true, GEMM_RING);
-            else CAS_GEMM_LAUNCH(false, GEMM_RING);
+            if (a.predicated) CAS_GEMM_LAUNCH(true, RING);
+            else CAS_GEMM_LAUNCH(false, RING);
             return hipGetLastError();
         }
     }

@@ -153,12 +153,15 @@ def test_gemm_strided_misaligned(orc, dtype):
     assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
 
 
-@pytest.mark.parametrize("ldx", [8_000_000, 9_000_000])
-def test_gemm_huge_row_pitch(orc, ldx):
-    """Row pitches near the 31-bit offset range: 64x64 tiles fetch through
-    buffer offsets from a tile's first row while 64 rows of the pitch fit
-    below 2^31 bytes (8M fp32 elements, the register-ring loop) and fall back
-    to the two-stage loop above it (9M); both must match the oracle."""
+@pytest.mark.parametrize("tile,ldx", [("64", 8_000_000), ("64", 9_000_000), ("128", 4_000_000), ("128", 4_500_000)])
+def test_gemm_huge_row_pitch(orc, monkeypatch, tile, ldx):
+    """Row pitches near the 31-bit offset range: the register-ring loop
+    fetches through buffer offsets from a tile's first row while a tile's rows
+    of the pitch fit below 2^31 bytes (64x64 tiles: 8M fp32 elements; 128x128
+    tiles: 4M), and the two-stage loop takes over above that (9M; 4.5M). K and
+    the pitch are multiples of four, so the loads are 16 bytes wide, the case
+    in which 128x128 tiles take the ring too. Both must match the oracle."""
+    monkeypatch.setenv("CAS_GEMM_TILE", tile)
     M, N, K = 3, 70, 100
     g = np.random.default_rng(ldx % 997)
     Xf = synth.to_storage(g.standard_normal(((M - 1) * ldx + K,)).astype(np.float32), "f32")
@@ -166,11 +169,11 @@ def test_gemm_huge_row_pitch(orc, ldx):
     ref, bound = orc.gemm_nt(Xf, W.ravel(), "f32", M=M, N=N, K=K, ldx=ldx, ldw=K, ldy=N)
     x = to_device(Xf, "f32").as_strided((M, K), (ldx, 1))
     buf, flat = guarded_output(M * N)
-    case(f"gemm row pitch {ldx}")
+    case(f"gemm tile {tile} row pitch {ldx}")
     cas.gemm_nt(x, to_device(W, "f32"), out=flat.view(M, N))
     torch.cuda.synchronize()
     check_guards(buf, M * N)
-    assert_close(flat.view(M, N).cpu().numpy(), ref, bound, "f32", f"gemm ldx={ldx}")
+    assert_close(flat.view(M, N).cpu().numpy(), ref, bound, "f32", f"gemm tile {tile} ldx={ldx}")
 
 
 # ------------------------------------------------------- batch_matmul_nt
