@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -123,7 +124,8 @@ class Part:
 
 def time_parts(parts, steps: int, warmup: int):
     """Warm up, then time `steps` steps; every part is bracketed by HIP events
-    on the stream it is launched on. Returns (ms per step, [avg ms per part])."""
+    on the stream it is launched on. Returns (ms per step, [mean ms per part],
+    wall ms per step, [median ms per part])."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -144,8 +146,10 @@ def time_parts(parts, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     total = start.elapsed_time(stop)
-    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps for i in range(len(parts))]
-    return total / steps, per, wall / steps
+    each = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(len(parts))]
+    per = [sum(e) / steps for e in each]
+    med = [statistics.median(e) for e in each]
+    return total / steps, per, wall / steps, med
 
 
 def roofline_of(wl, ms: float, traffic_bytes, out_bytes: int = 4):
@@ -238,8 +242,8 @@ def softmax_timings(steps: int):
         log(f"softmax timing {key}")
         sp = SoftmaxParts(wl, mode, od)
         n = max(5, steps // (10 if T > 2048 else 2))
-        ms_step, (ms_st, ms_rows), _ = time_parts([sp.stats, sp.rows], n, 2)
-        _, (ms_fused,), _ = time_parts([sp.fused], n, 2)
+        ms_step, (ms_st, ms_rows), _, _ = time_parts([sp.stats, sp.rows], n, 2)
+        _, (ms_fused,), _, _ = time_parts([sp.fused], n, 2)
         ob = 4 if od == "f32" else 2
         rows_bytes = wl.algorithmic_bytes(ob) + 8 * B * NH * T
         st_bytes = wl.algorithmic_bytes(0) + 8 * B * NH * T
@@ -264,7 +268,7 @@ def softmax_timings(steps: int):
         }
         if mode == "prob" and od == "f32":
             # the attention output: softmax probabilities times V (statistics from the launch above)
-            _, (ms_att,), _ = time_parts([sp.attention], n, 2)
+            _, (ms_att,), _, _ = time_parts([sp.attention], n, 2)
             flops = 2 * wl.useful_flops()  # Q K^T and P V over the causal triangle
             out[key]["attention"] = {
                 "avg_launch_us": round(ms_att * 1e3, 2),
@@ -274,7 +278,7 @@ def softmax_timings(steps: int):
                              "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
                              "useful_flops": flops}}
             # the same output and the statistics in one pass (running maximum and sum)
-            _, (ms_one,), _ = time_parts([sp.attention_fused], n, 2)
+            _, (ms_one,), _, _ = time_parts([sp.attention_fused], n, 2)
             out[key]["attention_single_pass"] = {
                 "avg_launch_us": round(ms_one * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(flops / (ms_one * 1e-3) / 1e12, 2),
@@ -307,8 +311,8 @@ def local_padding_ab(steps: int):
                 os.environ["CAS_VARIANT"] = "predicated"
             else:
                 os.environ.pop("CAS_VARIANT", None)
-            _, (ms,), _ = time_parts([p], steps, 3)
-            res[variant] = {"avg_launch_us": round(ms * 1e3, 2),
+            _, (ms,), _, (md,) = time_parts([p], steps, 3)
+            res[variant] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                             "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2)}
         os.environ.pop("CAS_VARIANT", None)
         res["speedup"] = round(res["predicated"]["avg_launch_us"] / res["local_padding"]["avg_launch_us"], 3)
@@ -323,8 +327,8 @@ def local_padding_ab(steps: int):
         torch.cuda.empty_cache()
     wl = synth.WORKLOADS["trimul_f32_B16_T120_NH12_HS64"]
     p = Part(wl)
-    _, (ms,), _ = time_parts([p], steps, 3)
-    out[wl.name] = {"avg_launch_us": round(ms * 1e3, 2),
+    _, (ms,), _, (md,) = time_parts([p], steps, 3)
+    out[wl.name] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                     "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                     "roofline": roofline_of(wl, ms, None)}
     del p
@@ -425,17 +429,17 @@ def main():
     log("preparing inputs")
     parts = [Part(wg), Part(wt)]
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, per, wall_ms = time_parts(parts, args.steps, args.warmup)
+    ms_step, per, wall_ms, med = time_parts(parts, args.steps, args.warmup)
     flops = wg.useful_flops() + wt.useful_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     dom = max(range(2), key=lambda i: per[i])
     dom_wl = [wg, wt][dom]
     kname = "trimul_f32_B8_T1024" if dom_wl.kind == "trimul_causal" else "gemm_nt_f32_960x1024x770"
     roof = roofline_of(dom_wl, per[dom], read_traffic(kname))
-    parts_report = {wl.name: {"avg_launch_us": round(ms * 1e3, 2),
+    parts_report = {wl.name: {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                               "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                               "roofline": roofline_of(wl, ms, None)}
-                    for wl, ms in zip([wg, wt], per)}
+                    for wl, ms, md in zip([wg, wt], per, med)}
     del parts
     torch.cuda.empty_cache()
 
@@ -451,8 +455,8 @@ def main():
             key = name if out == "f32" else f"{name}_out_{out}"
             log(f"timing {key}")
             p = Part(wl, out)
-            _, (ms,), _ = time_parts([p], max(5, args.steps // 5), 2)
-            bf16[key] = {"avg_launch_us": round(ms * 1e3, 2), "out_dtype": out,
+            _, (ms,), _, (md,) = time_parts([p], max(5, args.steps // 5), 2)
+            bf16[key] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2), "out_dtype": out,
                          "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                          "roofline": roofline_of(wl, ms, None, 4 if out == "f32" else 2)}
             del p
