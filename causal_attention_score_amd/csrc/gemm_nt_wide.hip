@@ -165,7 +165,10 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
     // its last k16 step's MFMAs: by then every wave holds that step's
     // fragments in registers, so from the barrier inside chunk c on, the
     // stage of chunk c is free for chunk c + S, and the next chunk's first
-    // fragments are read behind the MFMAs.
+    // fragments are read behind the MFMAs. Each step's reads of the next
+    // step's fragments go one after each MFMA, in the order that step takes
+    // them (bf16 4096^3: 115.7 against 117.7 us with all six reads issued
+    // ahead of the MFMAs).
     // Chunk c's loads: one step's worth (LPS) right after the barrier inside
     // chunk c - S, the rest during steps 0 .. NU - 2 of chunk c - S + 1, one
     // load after every P MFMAs. Chunks past the end are loaded too (as zeros,
@@ -198,6 +201,31 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    // The same step with the fragment reads of the next step (stage `nst`,
+    // k16 step `nu`) issued one after each of the first 4 + NB MFMAs instead
+    // of all before them.
+    auto mma_step_rd = [&](int fi, int c, int q0, auto with_loads, const char *nst, int nu) {
+        const int pos = ((h * G::NU + nu) ^ fr) * 16;
+        const char *xa = nst + (wm * 128 + r32) * BKB + pos;
+        const char *wa = nst + G::OPB + (wn * WN + r32) * BKB + pos;
+#pragma unroll
+        for (int i = 0; i < MPS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_chunk<E>(acc[i / NB][i % NB], fb[fi][i % NB], fa[fi][i / NB]);
+            // In the order the next step takes them (its MFMA j reads A
+            // fragment j / NB and B fragment j % NB): a0, b0 .. b(NB-1), a1 .. a3.
+            if (i == 0) fa[fi ^ 1][0] = *reinterpret_cast<const u32x4 *>(xa);
+            else if (i <= NB) fb[fi ^ 1][i - 1] = *reinterpret_cast<const u32x4 *>(wa + (i - 1) * 32 * BKB);
+            else if (i < 4 + NB) fa[fi ^ 1][i - NB] = *reinterpret_cast<const u32x4 *>(xa + (i - NB) * 32 * BKB);
+            if constexpr (decltype(with_loads)::value) {
+                if ((i + 1) % P == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    fetch_one(c, q0 + (i + 1) / P - 1);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
     using loads = std::true_type;
     using no_loads = std::false_type;
     // The writeback's arguments, read from the kernel arguments now: a
@@ -219,13 +247,11 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
         for (int u = 0; u < G::NU; ++u) {
             const int fi = u & 1;
             if (u + 1 < G::NU) {
-                read_frags(cur, u + 1, fa[fi ^ 1], fb[fi ^ 1]);
-                mma_step(fi, kc - 1 + S, (u + 1) * LPS, loads{});
+                mma_step_rd(fi, kc - 1 + S, (u + 1) * LPS, loads{}, cur, u + 1);
             } else {
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<(S - 2) * G::PC>); // chunk kc + 1 landed
                 plain_barrier(); // ... for every wave; every wave done reading chunk kc
-                read_frags(lds + ((kc + 1) % S) * G::STAGE, 0, fa[fi ^ 1], fb[fi ^ 1]);
-                mma_step(fi, kc + S, 0, loads{});
+                mma_step_rd(fi, kc + S, 0, loads{}, lds + ((kc + 1) % S) * G::STAGE, 0);
             }
         }
     }
