@@ -560,7 +560,7 @@ template <int NCH> struct Staged {
 // chunk (cl % NCH). Rows past T and chunks past the head read zero.
 template <class E, int NCH>
 __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, const Super &sp, uint32_t T, uint32_t C,
-                                            uint32_t NH, uint32_t HS, uint32_t ldb, int cl)
+                                            uint32_t NH, uint32_t HS, uint32_t ldb, int cl, bool with_q = true)
 {
     constexpr int ES = E::ES;
     constexpr int RPJ = NCOMP_THREADS / NCH; // rows per j
@@ -574,6 +574,7 @@ __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, co
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const bool isq = j < NCH / 2; // uniform: rows 0..127 are Q, 128..255 K
+        if (isq && !with_q) continue;   // Q rows already in LDS
         const uint32_t rin = (uint32_t)((isq ? j : j - NCH / 2) * RPJ) + r0;
         const uint32_t ok = 0u - (uint32_t)((isq ? sp.T0 : sp.S0) + rin < lim); // all ones in range
         const uint32_t vo = ((rin * ldb + c * 16) & ok) | (OOB & ~ok);
@@ -582,12 +583,13 @@ __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, co
 }
 
 template <int NCH>
-__device__ __forceinline__ void stage_store(const Staged<NCH> &st, char *opb, int cl)
+__device__ __forceinline__ void stage_store(const Staged<NCH> &st, char *opb, int cl, bool with_q = true)
 {
     constexpr int RPJ = NCOMP_THREADS / NCH;
     const int c = cl % NCH;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
+        if (j < NCH / 2 && !with_q) continue; // Q rows already in LDS
         const int row = j * RPJ + cl / NCH;
         *reinterpret_cast<u32x4 *>(opb + row * (NCH * 16) + ((c ^ (row & 7)) << 4)) = st.v[j];
     }
@@ -836,7 +838,7 @@ template <class E, int NCH, class O, class EP = EpScore>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store,
-                    const float *__restrict__ row_max, const float *__restrict__ row_logsum)
+                    const float *__restrict__ row_max, const float *__restrict__ row_logsum, int runs)
 {
     constexpr int RB = NCH * 16;
     constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
@@ -853,20 +855,34 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
     char *my_out = outb + slot * OUT_BYTES;
 
     // XCD-local contiguous item range; one super-tile per workgroup step.
+    // runs == 0: the workgroups of an XCD take its items in turn, so at any
+    // time they write neighbouring tiles. runs != 0: each takes one
+    // contiguous run of the range, whose consecutive items mostly lie in one
+    // row of a plane's triangle and share their Q rows, which the loaders
+    // then leave in LDS (fewer reads, scattered writes; the host picks).
     const uint32_t nwg = gridDim.x;
     const uint32_t x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
     const uint32_t wg_before = x * q8 + (x < r8 ? x : r8);
     const uint32_t wg_on_x = q8 + (x < r8 ? 1 : 0);
     const uint32_t lo = (uint32_t)((uint64_t)items * wg_before / nwg);
     const uint32_t hi = (uint32_t)((uint64_t)items * (wg_before + wg_on_x) / nwg);
-    const uint32_t first = lo + blockIdx.x / 8;
-    const uint32_t steps = first < hi ? (hi - first + wg_on_x - 1) / wg_on_x : 0;
+    const uint32_t k = blockIdx.x / 8; // this workgroup's index on its XCD, < wg_on_x
+    uint32_t first, steps, stride;
+    if (runs) {
+        first = lo + (uint32_t)((uint64_t)(hi - lo) * k / wg_on_x);
+        steps = lo + (uint32_t)((uint64_t)(hi - lo) * (k + 1) / wg_on_x) - first;
+        stride = 1;
+    } else {
+        first = lo + k;
+        steps = first < hi ? (hi - first + wg_on_x - 1) / wg_on_x : 0;
+        stride = wg_on_x;
+    }
 
     const uint32_t TBY = T * (uint32_t)O::OB; // bytes per output row
     const uint32_t ldb = 3u * C * (uint32_t)E::ES;
     const bool vec = vec_store != 0;          // rows 16-byte aligned
     Walker cur;
-    cur.init(first < hi ? first : 0, wg_on_x, L, (T + ST - 1) / ST);
+    cur.init(steps > 0 ? first : 0, stride, L, (T + ST - 1) / ST);
 
     // Every wave passes the same barriers: one after the prologue, then X and
     // Y once per step.
@@ -883,14 +899,18 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         lds_barrier(); // operand rows of step 0 in LDS
         for (uint32_t n = 0; n < steps; ++n) {
             const bool more = n + 1 < steps;
+            bool with_q = true; // the next item's Q rows differ from this one's
             if (more) {
+                const Super was = cur.item();
                 cur.advance();
-                stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
-                if constexpr (SM) sv = stat_fetch(row_max, row_logsum, cur.item(), T, cl);
+                const Super nx = cur.item();
+                with_q = !(nx.plane == was.plane && nx.T0 == was.T0);
+                stage_fetch<E, NCH>(st, qkv, nx, T, C, NH, HS, ldb, cl, with_q);
+                if constexpr (SM) sv = stat_fetch(row_max, row_logsum, nx, T, cl);
             }
             lds_barrier(); // X: operand rows of step n consumed
             if (more) {
-                stage_store<NCH>(st, opb, cl);
+                stage_store<NCH>(st, opb, cl, with_q);
                 if constexpr (SM) stb[cl] = sv;
             }
             lds_barrier(); // Y: operand rows of step n + 1 in LDS
@@ -971,10 +991,16 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     int64_t grid = resident_slots(resident, kern, SUPER_THREADS);
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
+    // Contiguous runs per workgroup for fp32 inputs with at least eight
+    // super-tile rows: there the saved Q-row reloads outweigh the scattered
+    // writes (fp32 B8 T1024: 85.8 -> 82.8 us; B8 T2048: 321 -> 309 us; B32
+    // T512: 88.6 -> 89.9 us). The store-bound 16-bit inputs lose with them
+    // (bf16 B4 T4096 to bf16: 577 -> 659 us).
+    const int runs = std::is_same<E, KF32>::value && nt >= 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
                        (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
-                       (int)a.vec_store, a.row_max, a.row_logsum);
+                       (int)a.vec_store, a.row_max, a.row_logsum, runs);
     return hipGetLastError();
 }
 
