@@ -350,6 +350,20 @@ def test_trimul_ragged_f32(orc, monkeypatch, T, HS, kernel):
         assert_scores(out, ref, bound, "f32", f"trimul f32 B={B} T={T} NH={NH} HS={HS}")
 
 
+@pytest.mark.parametrize("HS", [40, 64])
+@pytest.mark.parametrize("T", [897, 1153])
+def test_trimul_item_runs_f32(orc, T, HS):
+    """fp32 inputs with eight or more 128-row blocks (T > 896): each workgroup
+    walks one contiguous run of items and keeps the Q rows in LDS across
+    consecutive items of a triangle row. 32 planes give runs of four or five
+    items that start and end mid-row; every element against the oracle."""
+    B, NH = 4, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 17 + HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "f32")
+    out = run_trimul(qkv, "f32", B, T, NH, HS, "item runs")
+    assert_scores(out, ref, bound, "f32", f"trimul item runs f32 B={B} T={T} NH={NH} HS={HS}")
+
+
 @pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("HS", [8, 40, 64, 80, 128, 136, 3])

@@ -101,6 +101,16 @@ def test_softmax_ragged_f32(orc, launch, T, HS, mode):
 
 
 @pytest.mark.parametrize("mode", ["prob", "log"])
+def test_softmax_item_runs_f32(orc, mode):
+    """The two-launch rows on fp32 inputs with eight 128-row blocks, where the
+    rows kernel walks contiguous item runs and keeps Q rows (and their
+    statistics) in LDS across items: 32 planes, every element."""
+    B, T, NH, HS = 4, 1000, 8, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=1000 * 7 + HS)
+    check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="item runs", launch="two")
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("HS", [8, 64, 128])
 @pytest.mark.parametrize("T", [1, 65, 128, 129, 300])
