@@ -75,6 +75,20 @@ def test_gemm_wide_ragged(orc, monkeypatch, shape, dtype):
     assert_close(y, ref, bound, dtype, f"gemm wide {shape} {dtype}")
 
 
+@pytest.mark.parametrize("layout", ["64x4", "128x2", "64x3", "128x2w8", "64x3w8"])
+@pytest.mark.parametrize("shape", [(300, 520, 136), (520, 513, 1032)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_wide_tuning_layouts(orc, monkeypatch, shape, layout):
+    """The wide kernel's other chunk widths, stage counts and wave layouts
+    (CAS_GEMM_WIDE, tuning): four waves of 128 x 128 and eight of 128 x 64."""
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    monkeypatch.setenv("CAS_GEMM_WIDE", layout)
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, "bf16", seed=M + N + K)
+    ref, bound = orc.gemm_nt(X, W, "bf16")
+    y = run_gemm(X, W, "bf16", M, N, K, f"wide {layout}")
+    assert_close(y, ref, bound, "bf16", f"gemm wide {layout} {shape}")
+
+
 def test_gemm_wide_k0_writes_zeros(monkeypatch):
     monkeypatch.setenv("CAS_GEMM_TILE", "256")
     x = torch.empty((300, 0), device="cuda", dtype=torch.bfloat16)
