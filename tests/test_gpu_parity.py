@@ -364,6 +364,22 @@ def test_trimul_ragged_f32(orc, monkeypatch, T, HS, kernel):
         assert_scores(out, ref, bound, "f32", f"trimul f32 B={B} T={T} NH={NH} HS={HS}")
 
 
+@pytest.mark.parametrize("passw", ["1", "2", "4"])
+@pytest.mark.parametrize("dtype,HS", [("f32", 16), ("f32", 64), ("f32", 72), ("bf16", 32), ("bf16", 136), ("f16", 24)])
+def test_trimul_tile_pass_widths(orc, monkeypatch, dtype, HS, passw):
+    """The tile kernel's register pass width (CAS_TRIMUL_PASS, tuning): every
+    width against every head size, one pass or several, including the width
+    the automatic choice takes only for 33..64-byte heads."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+    monkeypatch.setenv("CAS_TRIMUL_PASS", passw)
+    for T in (65, 300):
+        B, NH = 2, 3
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 13 + HS)
+        ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+        out = run_trimul(qkv, dtype, B, T, NH, HS, f"pass {passw}")
+        assert_scores(out, ref, bound, dtype, f"trimul tile pass {passw} {dtype} T={T} HS={HS}")
+
+
 @pytest.mark.parametrize("HS", [40, 64])
 @pytest.mark.parametrize("T", [897, 1153])
 def test_trimul_item_runs_f32(orc, T, HS):
