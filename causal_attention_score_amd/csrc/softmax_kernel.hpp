@@ -466,11 +466,19 @@ softmax_fused_kernel(const char *__restrict__ qkv, char *__restrict__ out, float
         }
         lds_barrier();
         while (cur.valid) {
+            // Every step of a block has the block's 128 Q rows: they stay in
+            // LDS, and only a new block's are fetched.
+            const Super was = cur.item();
             cur.advance();
             const bool more = cur.valid;
-            if (more) stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+            bool with_q = true;
+            if (more) {
+                const Super nx = cur.item();
+                with_q = !(nx.plane == was.plane && nx.T0 == was.T0);
+                stage_fetch<E, NCH>(st, qkv, nx, T, C, NH, HS, ldb, cl, with_q);
+            }
             lds_barrier(); // X: operand rows of this step consumed
-            if (more) stage_store<NCH>(st, opb, cl);
+            if (more) stage_store<NCH>(st, opb, cl, with_q);
             lds_barrier(); // Y: operand rows of the next step in LDS
         }
     } else if (role == 0) {
