@@ -254,6 +254,9 @@ def causal_attention(qkv, NH: int, y=None, stats=None):
         return causal_attention_fused(qkv, NH, y=y)
     B, T, C = _qkv_dims(qkv, NH)
     row_max, row_logsum = stats
+    for t in (row_max, row_logsum):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, NH, T) or not t.is_contiguous():
+            raise ValueError("row_max / row_logsum must be contiguous float32 (B, NH, T) tensors")
     if y is None:
         y = torch.empty((B, T, C), dtype=torch.float32, device=qkv.device)
     if y.dtype != torch.float32 or tuple(y.shape) != (B, T, C) or not y.is_contiguous():

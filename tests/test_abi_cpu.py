@@ -290,3 +290,23 @@ def test_binding_validates_shapes():
         cas.causal_softmax(torch.zeros(2, 3, 12), 3, mode="softmax")
     with pytest.raises(ValueError):
         cas.causal_row_stats(torch.zeros(2, 3, 10), 2)
+
+
+@pytest.mark.parametrize("bad", ["dtype", "shape", "strided"])
+def test_binding_validates_attention_stats(bad):
+    """causal_attention(stats=...) hands the two pointers to a kernel that reads
+    B*NH*T floats from each: a wrong dtype, shape or layout is rejected before
+    any call reaches the library."""
+    import torch
+    B, T, NH, HS = 2, 8, 2, 4
+    qkv = torch.zeros(B, T, 3 * NH * HS)
+    good = torch.zeros(B, NH, T)
+    if bad == "dtype":
+        wrong = torch.zeros(B, NH, T, dtype=torch.float16)
+    elif bad == "shape":
+        wrong = torch.zeros(B, NH, T - 1)
+    else:
+        wrong = torch.zeros(B, NH, 2 * T)[..., ::2]
+    for stats in ((wrong, good), (good, wrong)):
+        with pytest.raises(ValueError, match="row_max / row_logsum"):
+            cas.causal_attention(qkv, NH, stats=stats)
