@@ -3,16 +3,17 @@ element by element on the same seeded inputs.
 
 Sizes span several tiles and ragged tails; the workload tests run the
 full-size configurations in the launch configuration the benchmark times and
-compare every element the oracle can afford (sampled rows / planes at the two
-largest sizes, plus whole-output mask counts)."""
+compare every element of every output with the oracle's, each output starting
+as a sentinel between guard bands."""
 import numpy as np
 import pytest
 import torch
 
 import causal_attention_score_amd as cas
 from causal_attention_score_amd import synth
-from gpu_util import (NAN16, QNAN, SENTINEL, assert_close, assert_exact, assert_scores, assert_scores16, bits,
-                      case, check_guards, guarded_output, guarded_output16, to_device)
+from gpu_util import (SENTINEL, assert_close, assert_exact, assert_plane_scores, assert_plane_scores16,
+                      assert_scores, assert_scores16, case, check_guards, guarded_output, guarded_output16,
+                      to_device, upper_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -582,99 +583,74 @@ def test_workload_trimul_f32_B8_T1024(orc):
     print(f"{wl.name}: max err/tol {worst:.3g}")
 
 
-def test_workload_dense_bf16_4096(orc):
-    wl = synth.WORKLOADS["dense_bf16_4096"]
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["dense_bf16_4096", "dense_f16_4096"])
+def test_workload_dense_4096_whole(orc, name):
+    """M = N = K = 4096 with 16-bit inputs in the launch configuration the
+    benchmark times (256 x 256 tiles, one per CU): the output starts as the
+    sentinel between guard bands, and every one of its 16.8 M elements is
+    compared with the oracle's (all 4096 rows, 256 workgroups)."""
+    wl = synth.WORKLOADS[name]
     M, N, K = wl.dims
     X, W = wl.inputs()
-    x, w = to_device(X, "bf16"), to_device(W, "bf16")
-    case(f"{wl.name} gemm_nt full size")
-    y = cas.gemm_nt(x, w)
-    torch.cuda.synchronize()
-    rows = [0, 1, 127, 128, 255, 256, 1000, 2047, 2048, 3071, 4064, 4095]
-    ref, bound = orc.gemm_nt(np.ascontiguousarray(X[rows]), W, "bf16")
-    got = y[rows].cpu().numpy()
-    r = assert_close(got, ref, bound, "bf16", wl.name)
-    assert bool(torch.isfinite(y).all())
-    print(f"{wl.name}: sampled rows max err/tol {r:.3g}")
+    y = run_gemm(X, W, wl.dtype, M, N, K, f"{wl.name} full size")
+    ref, bound = orc.gemm_nt(X, W, wl.dtype)
+    r = assert_close(y, ref, bound, wl.dtype, wl.name)
+    print(f"{wl.name}: every element, max err/tol {r:.3g}")
 
 
-def test_workload_dense_f16_4096(orc):
-    wl = synth.WORKLOADS["dense_f16_4096"]
-    X, W = wl.inputs()
-    case(f"{wl.name} gemm_nt full size")
-    y = cas.gemm_nt(to_device(X, "f16"), to_device(W, "f16"))
-    torch.cuda.synchronize()
-    rows = [0, 1, 255, 256, 1023, 2048, 3333, 4095]
-    ref, bound = orc.gemm_nt(np.ascontiguousarray(X[rows]), W, "f16")
-    r = assert_close(y[rows].cpu().numpy(), ref, bound, "f16", wl.name)
-    assert bool(torch.isfinite(y).all())
-    print(f"{wl.name}: sampled rows max err/tol {r:.3g}")
+def _plane_oracle(orc, qkv, wl):
+    """Oracle planes (b, nh) in order, each computed on a worker thread while
+    the previous one is compared (the oracle releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, T, NH, HS = wl.dims
+    P = B * NH
+    with ThreadPoolExecutor(1) as ex:
+        fut = ex.submit(orc.trimul_causal_rows, qkv, B, T, NH * HS, NH, 0, 0, 0, T, wl.dtype)
+        for p in range(P):
+            ref, bound = fut.result()
+            if p + 1 < P:
+                b1, h1 = divmod(p + 1, NH)
+                fut = ex.submit(orc.trimul_causal_rows, qkv, B, T, NH * HS, NH, b1, h1, 0, T, wl.dtype)
+            yield divmod(p, NH), ref, bound
 
 
-@pytest.mark.parametrize("name,out_dtype", [("trimul_bf16_B4_T4096_NH25_HS64", "bf16"),
-                                            ("trimul_f16_B4_T4096_NH25_HS64", "f16"),
-                                            ("trimul_f16_B4_T4096_NH25_HS64", "f32")])
-def test_workload_trimul_B4_T4096_out(orc, name, out_dtype):
-    """The large score shape with 16-bit inputs and 16-bit (or fp32) outputs:
-    whole-output mask counts, three whole planes, rows of every seventh."""
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,out16", [("trimul_bf16_B4_T4096_NH25_HS64", "bf16"),
+                                        ("trimul_f16_B4_T4096_NH25_HS64", "f16")])
+def test_workload_trimul_B4_T4096_whole(orc, name, out16):
+    """The large score shape, QKV (4, 4096, 3, 25, 64) with 16-bit inputs,
+    in the launch configuration the benchmark times, into an fp32 output
+    (the bf16 case is the fp32-output workload of the contract) and into a
+    16-bit one. Both outputs start as the sentinel between guard bands; every
+    element of all 100 (T, T) planes of both is compared with the oracle's
+    plane: the NaN pattern exactly above the diagonal, the tolerance on and
+    below it."""
     wl = synth.WORKLOADS[name]
     B, T, NH, HS = wl.dims
     (qkv,) = wl.inputs()
     d = to_device(qkv, wl.dtype)
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
-    out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
-    case(f"{wl.name} -> {out_dtype} trimul_causal full size")
-    cas.trimul_causal(d, NH, out=out)
+    n = B * NH * T * T
+    buf32, flat32 = guarded_output(n)
+    buf16, flat16 = guarded_output16(n, out16)
+    o32, o16 = flat32.view(B, NH, T, T), flat16.view(B, NH, T, T)
+    case(f"{wl.name} -> f32 trimul_causal full size")
+    cas.trimul_causal(d, NH, out=o32)
     torch.cuda.synchronize()
-    if out_dtype == "f32":
-        n_nan = int((out.view(torch.int32) == QNAN).sum())
-    else:
-        n_nan = int((out.view(torch.int16) == NAN16[out_dtype]).sum())
-    n_fin = int(torch.isfinite(out).sum())
-    assert n_nan == B * NH * T * (T - 1) // 2
-    assert n_fin == B * NH * T * (T + 1) // 2
-
-    def check(got, ref, bound, what):
-        if out_dtype == "f32":
-            return assert_scores(got.cpu().numpy(), ref, bound, wl.dtype, what)
-        return assert_scores16(got.view(torch.int16).cpu().numpy().view(np.uint16), ref, bound, wl.dtype,
-                               out_dtype, what)
-    worst = 0.0
-    for (b, h) in [(0, 0), (2, 11), (3, 24)]:
-        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, wl.dtype)
-        worst = max(worst, check(out[b, h], ref, bound, f"{wl.name} plane ({b},{h})"))
-    for p in range(0, B * NH, 7):
-        b, h = divmod(p, NH)
-        t0 = (p * 389) % (T - 8)
-        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, wl.dtype)
-        worst = max(worst, check(out[b, h, t0:t0 + 8], ref, bound, f"{wl.name} rows {t0}.. plane ({b},{h})"))
-    print(f"{wl.name} -> {out_dtype}: sampled max err/tol {worst:.3g}")
-
-
-def test_workload_trimul_bf16_B4_T4096(orc):
-    wl = synth.WORKLOADS["trimul_bf16_B4_T4096_NH25_HS64"]
-    B, T, NH, HS = wl.dims
-    (qkv,) = wl.inputs()
-    d = to_device(qkv, "bf16")
-    out = torch.empty((B, NH, T, T), dtype=torch.float32, device="cuda")
-    out.view(torch.int32).fill_(SENTINEL)
-    case(f"{wl.name} trimul_causal full size")
-    cas.trimul_causal(d, NH, out=out)
+    case(f"{wl.name} -> {out16} trimul_causal full size")
+    cas.trimul_causal(d, NH, out=o16)
     torch.cuda.synchronize()
-    ob = out.view(torch.int32)
-    n_nan = int((ob == QNAN).sum())
-    n_fin = int(torch.isfinite(out).sum())
-    assert n_nan == B * NH * T * (T - 1) // 2
-    assert n_fin == B * NH * T * (T + 1) // 2
-    worst = 0.0
-    for (b, h) in [(0, 0), (1, 13), (3, 24)]:
-        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, "bf16")
-        worst = max(worst, assert_scores(out[b, h].cpu().numpy(), ref, bound, "bf16", f"{wl.name} plane ({b},{h})"))
-    # rows sampled from every other plane
-    for p in range(0, B * NH, 7):
-        b, h = divmod(p, NH)
-        t0 = (p * 613) % (T - 8)
-        ref, bound = orc.trimul_causal_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, "bf16")
-        worst = max(worst, assert_scores(out[b, h, t0:t0 + 8].cpu().numpy(), ref, bound, "bf16",
-                                         f"{wl.name} rows {t0}.. of plane ({b},{h})"))
-    print(f"{wl.name}: sampled max err/tol {worst:.3g}")
+    check_guards(buf32, n)
+    check_guards(buf16, n)
+    up = upper_mask(T)
+    w32 = w16 = 0.0
+    for (b, h), ref, bound in _plane_oracle(orc, qkv, wl):
+        if (b * NH + h) % 10 == 0:
+            case(f"{wl.name}: comparing plane ({b},{h}) of {B * NH}")
+        w32 = max(w32, assert_plane_scores(o32[b, h].cpu().numpy(), ref, bound, wl.dtype,
+                                           f"{wl.name} -> f32 plane ({b},{h})", up))
+        g16 = o16[b, h].view(torch.int16).cpu().numpy().view(np.uint16)
+        w16 = max(w16, assert_plane_scores16(g16, ref, bound, wl.dtype, out16,
+                                             f"{wl.name} -> {out16} plane ({b},{h})", up))
+    print(f"{wl.name}: every element of all {B * NH} planes, max err/tol {w32:.3g} (f32 out), "
+          f"{w16:.3g} ({out16} out)")
