@@ -97,15 +97,20 @@ def trimul_inputs(B: int, T: int, NH: int, HS: int, dtype: str = "f32", seed: in
     return to_storage(x, dtype)
 
 
-def ramp_qk_inputs(B: int, T: int, NH: int, HS: int, q0, dtype: str = "f32", v_ramp: bool = False):
+def ramp_qk_inputs(B: int, T: int, NH: int, HS: int, q0, dtype: str = "f32", v_ramp: bool = False,
+                   v_seed: int | None = None):
     """Structured packed QKV: head entry 0 of Q is q0[nh] on every row, entry
-    0 of K is the row index t2, everything else is zero (with v_ramp, entry 0
-    of V is the row index too). The dot product of Q row t and K row t2 in
-    head nh is then q0[nh] * t2, the same ramp on every row. Values must be
-    exact in the storage type."""
+    0 of K is the row index t2, every other Q and K entry is zero. The dot
+    product of Q row t and K row t2 in head nh is then q0[nh] * t2, the same
+    ramp on every row, one product (exact in fp32 when it fits 24 bits). V is
+    zero, or N(0,1) drawn from v_seed; with v_ramp its entry 0 is the row
+    index. Q and K values should be exact in the storage type (a rounded key
+    index still gives one exact product, only not a ramp)."""
     x = np.zeros((B, T, 3, NH, HS), dtype=np.float32)
     x[:, :, 0, :, 0] = np.asarray(q0, dtype=np.float32)[None, None, :]
     x[:, :, 1, :, 0] = np.arange(T, dtype=np.float32)[None, :, None]
+    if v_seed is not None:
+        x[:, :, 2] = normal_f32(rng(v_seed), (B, T, NH, HS))
     if v_ramp:
         x[:, :, 2, :, 0] = np.arange(T, dtype=np.float32)[None, :, None]
     return to_storage(x.reshape(B, T, 3 * NH * HS), dtype)

@@ -12,9 +12,9 @@ import torch
 
 import causal_attention_score_amd as cas
 from causal_attention_score_amd import synth
-from gpu_util import (FILL, GUARD, assert_attention, assert_attention_online, assert_softmax, assert_softmax_stats,
-                      case, check_guards, online_logsum_extra,
-                      guarded_output, guarded_output16, to_device)
+from gpu_util import (FILL, GUARD, ROUND16, SENTINEL, SENTINEL16, SM_R, assert_attention, assert_attention_online,
+                      assert_softmax, assert_softmax_stats, case, check_guards, online_logsum_extra,
+                      guarded_output, guarded_output16, softmax_allowance, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -183,11 +183,30 @@ def test_softmax_unaligned_output(orc, launch, out_dtype, offset):
 @pytest.mark.parametrize("launch", LAUNCHES)
 def test_softmax_saturated(orc, launch):
     """Inputs scaled by 64: scores of order 1e3-1e4 (exp of a score overflows
-    fp32). The two statistics stay separate numbers, so nothing overflows."""
+    fp32). The two statistics stay separate numbers, so nothing overflows.
+    Statistics and log-probabilities are compared with their allowances. At
+    this scale the score allowance moves a probability by orders of magnitude,
+    so the probabilities are checked for what holds whatever the score error:
+    finite, the fill exact, and each row summing to one. Their values at this
+    scale are compared on exact scores (the slope-64 ramp rows)."""
     B, T, NH, HS = 1, 257, 2, 64
     qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=5) * np.float32(64.0)).astype(np.float32)
-    for mode in ("prob", "log"):
-        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="saturated", launch=launch)
+    check_case(orc, qkv, "f32", B, T, NH, HS, "log", label="saturated", launch=launch)
+    got, mx, ls = run_softmax(qkv, "f32", B, T, NH, HS, "prob", "f32", f"saturated {launch}", 0, launch)
+    _, mref, lref, bound = oracle_rows(orc, qkv, "f32", B, T, NH, HS, "prob")
+    t_idx = np.tile(np.arange(T), B * NH)
+    assert_softmax_stats(mx, ls, mref, lref, bound, t_idx, "f32", "saturated prob")
+    valid = np.arange(T)[None, :] <= t_idx[:, None]
+    assert np.all(got.view(np.uint32)[~valid] == 0), "fill above the diagonal"
+    p = got.astype(np.float64)
+    assert np.all(np.isfinite(p)) and np.all(p >= 0)
+    # sum_j p_j = 2^(-dL) sum_j exact_j (1 + e_j): the GPU's logsum of its own
+    # scores is within S + R (1 + L), each p_j within 2^-24 (2 + 5 |ln p_j|)
+    lnp = np.log(np.where(p > 0, p, 1.0))
+    n = t_idx + 1
+    lim = (n + 64) * 2.0 ** -24 + SM_R * (1 + np.abs(ls)) + (p * 2.0 ** -24 * (2 + 5 * np.abs(lnp))).sum(axis=1)
+    err = np.abs(p.sum(axis=1) - 1.0)
+    assert np.all(err <= lim), f"row sums: worst {float((err / lim).max()):.3g} of the allowance"
 
 
 def test_softmax_rejections():
@@ -233,14 +252,19 @@ def test_softmax_empty_and_side_stream(orc):
                                                        ("trimul_f16_B4_T4096_NH25_HS64", "log", "f16", True)])
 def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
     """The benchmark's score shapes, in the launch configuration the benchmark
-    times: every statistic of three planes and the fill of the whole output
-    checked; whole planes and rows of every seventh plane compared."""
+    times. The output starts as the sentinel (a NaN), so the fill above the
+    diagonal and finite values on and below it show that every element was
+    written. At T = 1024 every plane (statistics and rows) is compared; at
+    T = 4096 three whole planes and rows of every seventh plane."""
     wl = synth.WORKLOADS[name]
     B, T, NH, HS = wl.dims
     (qkv,) = wl.inputs()
     d = to_device(qkv, wl.dtype)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
-    out = torch.empty((B, NH, T, T), dtype=tdt, device="cuda")
+    if out_dtype == "f32":
+        out = torch.full((B, NH, T, T), SENTINEL, dtype=torch.int32, device="cuda").view(torch.float32)
+    else:
+        out = torch.full((B, NH, T, T), SENTINEL16, dtype=torch.int16, device="cuda").view(tdt)
     case(f"{wl.name} causal_softmax {mode} -> {out_dtype} full size, fused={fused}")
     _, mx, ls = cas.causal_softmax(d, NH, mode, out=out, fused=fused)
     torch.cuda.synchronize()
@@ -255,7 +279,8 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
     assert bool(torch.isfinite(out[..., ~up]).all()), "non-finite value on or below the diagonal"
     del up
     worst = 0.0
-    planes = [(0, 0), (B - 1, NH - 1), (B // 2, NH // 3)]
+    whole = T <= 1024
+    planes = [divmod(p, NH) for p in range(B * NH)] if whole else [(0, 0), (B - 1, NH - 1), (B // 2, NH // 3)]
     for (b, h) in planes:
         ref, mref, lref, bound = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, b, h, 0, T, wl.dtype, mode)
         t_idx = np.arange(T)
@@ -264,7 +289,7 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
                                                 bound, t_idx, wl.dtype, what))
         got = out[b, h].cpu().numpy() if out_dtype == "f32" else out[b, h].view(torch.int16).cpu().numpy()
         worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
-    for p in range(0, B * NH, 7):
+    for p in range(0, 0 if whole else B * NH, 7):
         b, h = divmod(p, NH)
         t0 = (p * 389) % (T - 8)
         ref, mref, lref, bound = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 8, wl.dtype,
@@ -277,7 +302,8 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
         blk = out[b, h, t0:t0 + 8]
         got = blk.cpu().numpy() if out_dtype == "f32" else blk.view(torch.int16).cpu().numpy()
         worst = max(worst, assert_softmax(got, ref, lref, bound, t_idx, wl.dtype, mode, out_dtype, what))
-    print(f"{wl.name} softmax {mode} -> {out_dtype} fused={fused}: sampled max err/tol {worst:.3g}")
+    print(f"{wl.name} softmax {mode} -> {out_dtype} fused={fused}: {'every plane' if whole else 'sampled'} "
+          f"max err/tol {worst:.3g}")
 
 
 # ------------------------------------------------------------ attention output
@@ -297,7 +323,9 @@ def run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats=False):
     cas.causal_attention(d, NH, y=flat.view(B, T, C), stats=(mx, ls))
     torch.cuda.synchronize()
     check_guards(buf, n)
-    return flat.view(B, T, C).cpu().numpy()
+    y = flat.view(B, T, C).cpu().numpy()
+    assert np.all(np.isfinite(y)), f"{label}: y not written whole (the sentinel is a NaN) or non-finite"
+    return y
 
 
 def check_attention(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, fused_stats=False, b_t=None):
@@ -336,11 +364,61 @@ def test_attention_ramp_rows_exact_scores(orc):
     check_attention(orc, qkv, "f32", B, T, NH, HS, "ramp", exact_scores=True)
 
 
-def test_attention_saturated_and_fused_stats(orc):
-    """Scores of order 1e3-1e4, statistics from the fused softmax launch."""
+# Saturated ramp rows: slopes 64 and 200 per key (row maxima up to 51200) and
+# -16, with one gentle slope beside them; exact scores in every input type
+# (q0 = 8 * slope is exact in bfloat16 and binary16, keys t2 <= 256 too), and
+# random value rows.
+SAT_SLOPES = [64.0, -16.0, 0.25, 200.0]
+
+
+@pytest.mark.parametrize("fused_stats", [False, True])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_attention_saturated_ramp(orc, dtype, fused_stats):
+    """Saturated rows with exact scores: only the exp / sum roundings (and, for
+    16-bit inputs, the rounding of p for the MFMA) are allowed, so every value
+    is pinned; statistics from the statistics launch or the fused softmax."""
+    B, T, NH, HS = 2, 257, 4, 64
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in SAT_SLOPES], dtype, v_seed=41)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "saturated ramp", exact_scores=True, fused_stats=fused_stats)
+
+
+def attention_hull_check(orc, y, qkv, dtype, B, T, NH, HS, what):
+    """y[t] is a weighted mean of V rows 0..t, whatever the weights: finite and
+    inside the per-column range of those rows, up to how far the kernel's
+    weights may miss summing to one -- the fp32 sums and roundings of the
+    exponentials and the log-sum, 2^-20 (t + 66 + ln(t + 1)), and for 16-bit
+    inputs the rounding of each weight to that format for the MFMA."""
+    V = orc.decode(qkv, dtype) if dtype != "f32" else np.asarray(qkv, np.float64)
+    V = V.reshape(B, T, 3, NH, HS)[:, :, 2]                                     # (B, T, NH, HS)
+    lo = np.minimum.accumulate(V, axis=1).reshape(B, T, NH * HS)
+    hi = np.maximum.accumulate(V, axis=1).reshape(B, T, NH * HS)
+    amax = np.maximum.accumulate(np.abs(V), axis=1).reshape(B, T, NH * HS)
+    u16, a16 = ROUND16[dtype] if dtype != "f32" else (0.0, 0.0)
+    t = np.arange(T)[None, :, None]
+    tol = amax * (u16 + 2.0 ** -20 * (t + 66 + np.log(t + 1.0))) + a16 * (t + 1) * amax
+    g = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    assert np.all((g >= lo - tol) & (g <= hi + tol)), f"{what}: output outside the range of the value rows"
+
+
+@pytest.mark.parametrize("dtype,scale", [("f32", 64.0), ("bf16", 16.0), ("f16", 16.0)])
+def test_attention_saturated_random_no_overflow(orc, dtype, scale):
+    """Random rows scaled to scores of order 1e2-1e4, where an unshifted
+    exponential overflows. The score allowance moves such weights by orders of
+    magnitude, so this checks what holds for any weights -- finite outputs
+    inside the range of the value rows, for both attention paths -- and the
+    row maxima against the oracle's within their allowance; values at this
+    scale are compared on exact scores (test_attention_saturated_ramp)."""
     B, T, NH, HS = 1, 257, 2, 64
-    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(64.0)).astype(np.float32)
-    check_attention(orc, qkv, "f32", B, T, NH, HS, "saturated", fused_stats=True)
+    qkv = synth.to_storage(synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(scale), dtype)
+    y2 = run_attention(qkv, dtype, B, T, NH, HS, "saturated random", fused_stats=True)
+    attention_hull_check(orc, y2, qkv, dtype, B, T, NH, HS, f"saturated random {dtype} two-pass")
+    y1, mx, _ = run_attention_fused(qkv, dtype, B, T, NH, HS, "saturated random")
+    attention_hull_check(orc, y1, qkv, dtype, B, T, NH, HS, f"saturated random {dtype} single pass")
+    for h in range(NH):
+        _, mref, lref, bd = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, 0, h, 0, T, dtype, "prob")
+        _, D, _, _ = softmax_allowance(bd, np.arange(T), dtype)
+        assert np.all(np.abs(mx[0, h] - mref) <= D), f"row maxima, head {h}"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -350,15 +428,6 @@ def test_attention_ragged_16bit(orc, T, HS, dtype):
     B, NH = 2, 2
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 7 + HS)
     check_attention(orc, qkv, dtype, B, T, NH, HS, "sweep")
-
-
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_attention_saturated_16bit_fused_stats(orc, dtype):
-    """Scores of order 1e2-1e3 (one dominant key per row, tiny p elsewhere:
-    f16's subnormal range), statistics from the fused softmax launch."""
-    B, T, NH, HS = 1, 200, 2, 64
-    qkv = synth.to_storage(synth.trimul_inputs(B, T, NH, HS, "f32", seed=9) * np.float32(16.0), dtype)
-    check_attention(orc, qkv, dtype, B, T, NH, HS, "saturated", fused_stats=True)
 
 
 def test_attention_rejections():
@@ -412,7 +481,10 @@ def run_attention_fused(qkv, dtype, B, T, NH, HS, label, y_offset=0):
     check_guards(ybuf, n + y_offset)
     check_guards(mbuf, B * NH * T)
     check_guards(lbuf, B * NH * T)
-    return (y.view(B, T, C).cpu().numpy(), mflat.view(B, NH, T).cpu().numpy(), lflat.view(B, NH, T).cpu().numpy())
+    res = (y.view(B, T, C).cpu().numpy(), mflat.view(B, NH, T).cpu().numpy(), lflat.view(B, NH, T).cpu().numpy())
+    for a, name in zip(res, ("y", "row_max", "row_logsum")):
+        assert np.all(np.isfinite(a)), f"{label}: {name} not written whole (the sentinel is a NaN) or non-finite"
+    return res
 
 
 def check_attention_fused(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, b_t=None, y_offset=0,
@@ -469,11 +541,23 @@ def test_attention_fused_ramp_rescales(orc):
     check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "ramp", exact_scores=True)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_attention_fused_saturated(orc, dtype):
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_attention_fused_saturated_ramp(orc, dtype):
+    """Saturated rows with exact scores in every input type (slopes 64, -16,
+    0.25 and 200 per key, random value rows): the offset moves on every step
+    of the steep rows and each weight is checked for value, including the
+    16-bit rounding of the weights for the MFMA."""
+    B, T, NH, HS = 2, 257, 4, 64
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in SAT_SLOPES], dtype, v_seed=43)
+    check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "saturated ramp", exact_scores=True)
+
+
+def test_attention_fused_saturated(orc):
+    """Random rows scaled by 16 (scores of order 1e2-1e3) in fp32, where the
+    score allowance still pins each weight to within a factor below 1.5."""
     B, T, NH, HS = 1, 257, 2, 64
-    qkv = synth.to_storage(synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(16.0), dtype)
-    check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "saturated")
+    qkv = (synth.trimul_inputs(B, T, NH, HS, "f32", seed=6) * np.float32(16.0)).astype(np.float32)
+    check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "saturated")
 
 
 def test_attention_fused_unaligned_y(orc):
