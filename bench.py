@@ -34,6 +34,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # dense MFMA
 METRIC = "useful TFLOP/s (gemm_nt, trimul_causal) + % of MI355X MFMA/HBM roofline"
+# Warm-up of the headline step lasts at least this long: launches timed within
+# the first few hundred milliseconds after the GPU leaves idle run slower while
+# its clocks ramp up.
+SETTLE_S = 0.5
+SUB_SETTLE_S = 0.25   # the same for each further workload (inputs are made on the host in between)
 
 
 def log(msg: str) -> None:
@@ -122,15 +127,23 @@ class Part:
             self.cas.trimul_causal(self.qkv, self.NH, out=self.out)
 
 
-def time_parts(parts, steps: int, warmup: int):
+def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
     """Warm up, then time `steps` steps; every part is bracketed by HIP events
-    on the stream it is launched on. Returns (ms per step, [mean ms per part],
-    wall ms per step, [median ms per part])."""
+    on the stream it is launched on. The warm-up is `warmup` steps, continued
+    (untimed) until `settle_s` seconds have passed, so the timed steps do not
+    run while the GPU's clocks are still ramping up from idle. Returns (ms per
+    step, [mean ms per part], wall ms per step, [median ms per part], warm-up
+    steps run)."""
     import torch
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < settle_s:
         for p in parts:
             p()
+        done += 1
+        if done >= warmup and done % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -149,7 +162,7 @@ def time_parts(parts, steps: int, warmup: int):
     each = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(len(parts))]
     per = [sum(e) / steps for e in each]
     med = [statistics.median(e) for e in each]
-    return total / steps, per, wall / steps, med
+    return total / steps, per, wall / steps, med, done
 
 
 def roofline_of(wl, ms: float, traffic_bytes, out_bytes: int = 4):
@@ -242,8 +255,8 @@ def softmax_timings(steps: int):
         log(f"softmax timing {key}")
         sp = SoftmaxParts(wl, mode, od)
         n = max(5, steps // (10 if T > 2048 else 2))
-        ms_step, (ms_st, ms_rows), _, _ = time_parts([sp.stats, sp.rows], n, 2)
-        _, (ms_fused,), _, _ = time_parts([sp.fused], n, 2)
+        ms_step, (ms_st, ms_rows), _, _, _ = time_parts([sp.stats, sp.rows], n, 2, SUB_SETTLE_S)
+        _, (ms_fused,), _, _, _ = time_parts([sp.fused], n, 2, SUB_SETTLE_S)
         ob = 4 if od == "f32" else 2
         rows_bytes = wl.algorithmic_bytes(ob) + 8 * B * NH * T
         st_bytes = wl.algorithmic_bytes(0) + 8 * B * NH * T
@@ -268,7 +281,7 @@ def softmax_timings(steps: int):
         }
         if mode == "prob" and od == "f32":
             # the attention output: softmax probabilities times V (statistics from the launch above)
-            _, (ms_att,), _, _ = time_parts([sp.attention], n, 2)
+            _, (ms_att,), _, _, _ = time_parts([sp.attention], n, 2, SUB_SETTLE_S)
             flops = 2 * wl.useful_flops()  # Q K^T and P V over the causal triangle
             out[key]["attention"] = {
                 "avg_launch_us": round(ms_att * 1e3, 2),
@@ -278,7 +291,7 @@ def softmax_timings(steps: int):
                              "frac": round(flops / (ms_att * 1e-3) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
                              "useful_flops": flops}}
             # the same output and the statistics in one pass (running maximum and sum)
-            _, (ms_one,), _, _ = time_parts([sp.attention_fused], n, 2)
+            _, (ms_one,), _, _, _ = time_parts([sp.attention_fused], n, 2, SUB_SETTLE_S)
             out[key]["attention_single_pass"] = {
                 "avg_launch_us": round(ms_one * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(flops / (ms_one * 1e-3) / 1e12, 2),
@@ -311,7 +324,7 @@ def local_padding_ab(steps: int):
                 os.environ["CAS_VARIANT"] = "predicated"
             else:
                 os.environ.pop("CAS_VARIANT", None)
-            _, (ms,), _, (md,) = time_parts([p], steps, 3)
+            _, (ms,), _, (md,), _ = time_parts([p], steps, 3, SUB_SETTLE_S)
             res[variant] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                             "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2)}
         os.environ.pop("CAS_VARIANT", None)
@@ -327,7 +340,7 @@ def local_padding_ab(steps: int):
         torch.cuda.empty_cache()
     wl = synth.WORKLOADS["trimul_f32_B16_T120_NH12_HS64"]
     p = Part(wl)
-    _, (ms,), _, (md,) = time_parts([p], steps, 3)
+    _, (ms,), _, (md,), _ = time_parts([p], steps, 3, SUB_SETTLE_S)
     out[wl.name] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                     "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                     "roofline": roofline_of(wl, ms, None)}
@@ -428,8 +441,8 @@ def main():
     wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
     log("preparing inputs")
     parts = [Part(wg), Part(wt)]
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, per, wall_ms, med = time_parts(parts, args.steps, args.warmup)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps (at least {SETTLE_S} s of them)")
+    ms_step, per, wall_ms, med, warm_done = time_parts(parts, args.steps, args.warmup, SETTLE_S)
     flops = wg.useful_flops() + wt.useful_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     dom = max(range(2), key=lambda i: per[i])
@@ -455,7 +468,7 @@ def main():
             key = name if out == "f32" else f"{name}_out_{out}"
             log(f"timing {key}")
             p = Part(wl, out)
-            _, (ms,), _, (md,) = time_parts([p], max(5, args.steps // 5), 2)
+            _, (ms,), _, (md,), _ = time_parts([p], max(5, args.steps // 5), 2, SUB_SETTLE_S)
             bf16[key] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2), "out_dtype": out,
                          "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
                          "roofline": roofline_of(wl, ms, None, 4 if out == "f32" else 2)}
@@ -477,7 +490,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_done, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,1) inputs of the pages' shapes)",
         "config": {"workload": "dense fp32 960x1024x770 + causal scores fp32 B=8 T=1024 NH=12 HS=64",
