@@ -56,12 +56,18 @@ def device_tensor(a, dtype):
 
 
 # Sources each profiled kernel is built from (its translation unit, what it
-# includes, and the host dispatch in front of it).
+# includes, and the host dispatch in front of it), keyed by the workload it is
+# profiled on.
 KERNEL_SOURCES = {
-    "trimul_f32_B8_T1024": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip", "trimul_f32.hip",
-                            "trimul_kernel.hpp"],
-    "gemm_nt_f32_960x1024x770": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip"],
+    "trimul_f32_B8_T1024_NH12_HS64": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip",
+                                      "trimul_f32.hip", "trimul_kernel.hpp"],
+    "dense_f32_960x1024x770": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip"],
+    "dense_bf16_4096": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip", "gemm_nt_wide.hip"],
+    "trimul_bf16_B4_T4096_NH25_HS64": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip",
+                                       "trimul_bf16.hip", "trimul_kernel.hpp"],
 }
+# Workloads whose kernels the counter runs profile (bench.py --traffic-probe).
+PROBED = tuple(KERNEL_SOURCES)
 
 
 def kernel_sources_digest(kernel: str) -> str:
@@ -74,11 +80,15 @@ def kernel_sources_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    `kernel`, if it was taken on the kernel's current sources; else None."""
+def read_counters(kernel: str):
+    """Counter figures of `kernel` from its committed rocprofv3 summary
+    (profiles/counters_<workload>.md), if they were taken on the kernel's
+    current sources; else None. Keys: hbm_bytes_per_launch (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
+    and where measured mfma_busy_frac, wait_frac, lds_bank_conflict_frac,
+    clock_ghz."""
     digest = kernel_sources_digest(kernel)
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -89,10 +99,13 @@ def read_traffic(kernel: str):
                 vals[k.strip()] = v.strip().strip("`")
     if vals.get("sources_digest") != digest:
         return None
-    try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    out = {}
+    for k in ("hbm_bytes_per_launch", "mfma_busy_frac", "wait_frac", "lds_bank_conflict_frac", "clock_ghz"):
+        try:
+            out[k] = float(vals[k])
+        except (KeyError, ValueError):
+            pass
+    return out or None
 
 
 class Part:
@@ -165,26 +178,32 @@ def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
     return total / steps, per, wall / steps, med, done
 
 
-def roofline_of(wl, ms: float, traffic_bytes, out_bytes: int = 4):
-    """Roofline entry of one kernel from its average launch time. `traffic` is
-    the measured HBM bytes per launch (rocprofv3 counters, committed under
-    profiles/) over the same launch time, in the unit of `achieved` when the
-    bound is HBM; null when no counters match the current kernel sources."""
+def roofline_of(wl, ms: float, counters=None, out_bytes: int = 4):
+    """Roofline entry of one kernel from its average launch time. `counters`
+    are the rocprofv3 figures committed under profiles/ for this kernel's
+    current sources (read_counters), or None. `traffic` is their HBM bytes per
+    launch over the same launch time, in GB/s (the unit of `achieved` when the
+    bound is HBM); `traffic_over_algorithmic` compares the bytes themselves.
+    `counters` also carries MFMA-busy and wait fractions where measured."""
     t = ms * 1e-3
+    tb = counters.get("hbm_bytes_per_launch") if counters else None
+    traffic = round(tb / t / 1e9, 1) if tb else None
+    extra = {"traffic": traffic, "traffic_bytes_per_launch": tb,
+             "counters": {k: v for k, v in counters.items() if k != "hbm_bytes_per_launch"} if counters else None}
     if wl.kind == "trimul_causal":
         achieved = wl.algorithmic_bytes(out_bytes) / t / 1e9
-        traffic = round(traffic_bytes / t / 1e9, 1) if traffic_bytes else None
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "traffic_bytes_per_launch": traffic_bytes,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), **extra,
+                "traffic_over_algorithmic": round(tb / wl.algorithmic_bytes(out_bytes), 4) if tb else None,
                 "kernel": f"trimul_causal {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
                 "algorithmic_bytes": wl.algorithmic_bytes(out_bytes)}
     achieved = wl.useful_flops() / t / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None, "traffic_bytes_per_launch": traffic_bytes,
+            "frac": round(achieved / peak, 4), **extra,
+            "traffic_over_algorithmic": round(tb / wl.algorithmic_bytes(), 4) if tb else None,
             "kernel": f"gemm_nt {wl.name}", "avg_launch_us": round(ms * 1e3, 2),
-            "useful_flops": wl.useful_flops()}
+            "useful_flops": wl.useful_flops(), "algorithmic_bytes": wl.algorithmic_bytes()}
 
 
 class SoftmaxParts:
@@ -343,7 +362,7 @@ def local_padding_ab(steps: int):
     _, (ms,), _, (md,), _ = time_parts([p], steps, 3, SUB_SETTLE_S)
     out[wl.name] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                     "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
-                    "roofline": roofline_of(wl, ms, None)}
+                    "roofline": roofline_of(wl, ms)}
     del p
     torch.cuda.empty_cache()
     return out
@@ -390,10 +409,11 @@ def cpu_baseline(budget_s: float = 12.0):
             "kind": "oracle", "seconds": round(dt, 2), "sample": sample + ", fp64 accumulation"}
 
 
-def traffic_probe() -> None:
-    """Kernels for the HBM-traffic counter runs (rocprofv3 --pmc FETCH_SIZE,
-    then WRITE_SIZE): one plain copy of 512 MiB, whose counters calibrate
-    the byte scale, then three launches of each part of the step."""
+def traffic_probe(names=PROBED) -> None:
+    """Kernels for the rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE,
+    then the SQ/GRBM busy counters, each a run of its own): one plain copy of
+    512 MiB, whose counters calibrate the byte scale, then three launches of
+    the kernel of each named workload, in the order given."""
     import torch
 
     from causal_attention_score_amd import synth
@@ -404,12 +424,14 @@ def traffic_probe() -> None:
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    for name in ("dense_f32_960x1024x770", "trimul_f32_B8_T1024_NH12_HS64"):
+    for name in names:
+        log(f"probe: 3 launches on {name}")
         p = Part(synth.WORKLOADS[name])
         for _ in range(3):
             p()
         torch.cuda.synchronize()
         del p
+        torch.cuda.empty_cache()
     print("traffic probe done", flush=True)
 
 
@@ -422,8 +444,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-ab", action="store_true", help="skip the local-padding A/B")
     ap.add_argument("--no-softmax", action="store_true", help="skip the causal-softmax timings")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="only launch the kernels for the rocprofv3 HBM-traffic counter runs")
+    ap.add_argument("--traffic-probe", nargs="*", metavar="WORKLOAD",
+                    help="only launch the kernels for the rocprofv3 counter runs (default: every profiled workload)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the hot path shards with no communication, "
@@ -434,8 +456,8 @@ def main():
 
     from causal_attention_score_amd import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.traffic_probe:
-        traffic_probe()
+    if args.traffic_probe is not None:
+        traffic_probe(tuple(args.traffic_probe) or PROBED)
         return
     wg = synth.WORKLOADS["dense_f32_960x1024x770"]
     wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
@@ -447,11 +469,10 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     dom = max(range(2), key=lambda i: per[i])
     dom_wl = [wg, wt][dom]
-    kname = "trimul_f32_B8_T1024" if dom_wl.kind == "trimul_causal" else "gemm_nt_f32_960x1024x770"
-    roof = roofline_of(dom_wl, per[dom], read_traffic(kname))
+    roof = roofline_of(dom_wl, per[dom], read_counters(dom_wl.name))
     parts_report = {wl.name: {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                               "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
-                              "roofline": roofline_of(wl, ms, None)}
+                              "roofline": roofline_of(wl, ms, read_counters(wl.name))}
                     for wl, ms, md in zip([wg, wt], per, med)}
     del parts
     torch.cuda.empty_cache()
@@ -471,7 +492,8 @@ def main():
             _, (ms,), _, (md,), _ = time_parts([p], max(5, args.steps // 5), 2, SUB_SETTLE_S)
             bf16[key] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2), "out_dtype": out,
                          "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2),
-                         "roofline": roofline_of(wl, ms, None, 4 if out == "f32" else 2)}
+                         "roofline": roofline_of(wl, ms, read_counters(name) if out == "f32" and name in KERNEL_SOURCES
+                                                 else None, 4 if out == "f32" else 2)}
             del p
             torch.cuda.empty_cache()
 

@@ -66,9 +66,11 @@ def test_roofline_scores_is_hbm_bound():
     assert r["achieved"] == pytest.approx(452_984_832 / 100e-6 / 1e9, rel=1e-4)
     assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, rel=1e-3)
     assert r["traffic"] is None
-    r = bench.roofline_of(wl, 0.1, 453_000_000)
+    r = bench.roofline_of(wl, 0.1, {"hbm_bytes_per_launch": 453_000_000.0, "mfma_busy_frac": 0.25})
     assert r["traffic"] == pytest.approx(4530.0, rel=1e-3)
     assert r["traffic_bytes_per_launch"] == 453_000_000
+    assert r["traffic_over_algorithmic"] == pytest.approx(453_000_000 / 452_984_832, rel=1e-4)
+    assert r["counters"] == {"mfma_busy_frac": 0.25}
 
 
 @pytest.mark.parametrize("name,peak", [("dense_f32_960x1024x770", 157.3), ("dense_bf16_4096", 2516.6),
@@ -88,13 +90,19 @@ def test_sources_digest_is_stable():
         assert d == bench.kernel_sources_digest(k)
 
 
-def test_read_traffic_only_for_matching_sources(tmp_path, monkeypatch):
+def test_read_counters_only_for_matching_sources(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
-    (tmp_path / "profiles" / "traffic_k.md").write_text(
-        "# summary\n\n- sources_digest: `0123456789abcdef`\n- hbm_bytes_per_launch: `453259002`\n")
+    (tmp_path / "profiles" / "counters_k.md").write_text(
+        "# summary\n\n- sources_digest: `0123456789abcdef`\n- hbm_bytes_per_launch: `453259002`\n"
+        "- mfma_busy_frac: `0.57`\n- wait_frac: `n/a`\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_sources_digest", lambda k: "0123456789abcdef")
-    assert bench.read_traffic("k") == 453259002.0
+    assert bench.read_counters("k") == {"hbm_bytes_per_launch": 453259002.0, "mfma_busy_frac": 0.57}
     monkeypatch.setattr(bench, "kernel_sources_digest", lambda k: "fedcba9876543210")
-    assert bench.read_traffic("k") is None
-    assert bench.read_traffic("missing") is None
+    assert bench.read_counters("k") is None
+    assert bench.read_counters("missing") is None
+
+
+def test_every_profiled_workload_is_a_workload():
+    for k in bench.KERNEL_SOURCES:
+        assert k in synth.WORKLOADS
