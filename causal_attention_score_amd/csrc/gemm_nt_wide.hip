@@ -14,11 +14,12 @@
 //  * Compute: the MFMA loop runs over whole tiles with no predicates.
 //  * Writeback: the only other place that looks at M and N.
 //
-// Data path. A workgroup holds four waves, one per SIMD, in a 2 x 2 grid;
-// each wave accumulates a 128 x 128 block as 4 x 4 MFMA tiles of 32 x 32
-// (v_mfma_f32_32x32x16_{bf16,f16}, 256 fp32 accumulators per lane, held in
-// the accumulation registers). Each k-chunk (BKB bytes of a row: 32 or 64
-// elements) of the 256 X rows and 256 W rows lands in LDS straight from the
+// Data path. By default a workgroup holds eight waves, two per SIMD, in a
+// 2 x 4 grid; each wave accumulates a 128 x 64 block as 4 x 2 MFMA tiles of
+// 32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}, 128 fp32 accumulators per lane; a
+// four-wave layout with 128 x 128 blocks exists for tuning). Each k-chunk
+// (BKB bytes of a row: 32 or 64 elements) of the 256 X rows and 256 W rows
+// lands in LDS straight from the
 // load unit: one load instruction fills 1 KB of LDS, lane i writing bytes
 // [16i, 16i + 16). A row's 16-byte pieces are stored XOR-swizzled, the loads
 // picking their source addresses to match, so the MFMA operand reads are free
@@ -95,6 +96,42 @@ template <int BKB, int S, int NW> struct Wide {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + blk * 1024), 16, (int)vo, 0, 0, 0);
     }
 };
+
+// Writeback of one wave's 128 x WN block: lane l, registers 4g .. 4g+3 of
+// block (a, b) hold row 32a + l % 32 and columns 32b + 8g + 4(l / 32) + 0..3
+// (row0 / col0: this lane's first row and column; r0 / c0: the block's): one
+// 16-byte store each where the rows are 16-byte aligned and the block lies
+// inside the matrix, else element by element, masked on the true M and N.
+template <int NB, int WN>
+__device__ __forceinline__ void write_tile(const f32x16 (&acc)[4][NB], float *Y, int64_t M, int64_t N, int64_t ldy,
+                                           int64_t row0, int64_t col0, int64_t r0, int64_t c0)
+{
+    float *yw = Y + row0 * ldy + col0;
+    const bool vec_ok = ((uintptr_t)Y % 16 == 0) && (ldy % 4 == 0);
+    if (vec_ok && r0 + 128 <= M && c0 + WN <= N) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4v v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+                    *reinterpret_cast<f32x4v *>(yw + 32 * a * ldy + 32 * b + 8 * g) = v;
+                }
+    } else {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const bool row_ok = row0 + 32 * a < M;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int cc = 32 * b + 8 * (r >> 2) + (r & 3);
+                    if (row_ok && col0 + cc < N) yw[32 * a * ldy + cc] = acc[a][b][r];
+                }
+        }
+    }
+}
 
 // NWN: waves along N (2: four waves with 128 x 128 blocks; 4: eight waves,
 // two per SIMD, with 128 x 64 blocks).
@@ -269,35 +306,173 @@ gemm_nt_wide_kernel(const char *__restrict__ X, const char *__restrict__ W, floa
     // Loads of chunks past the end may still be writing LDS.
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<0>);
 
-    // Writeback: lane l, registers 4g .. 4g+3 of block (a, b) hold row
-    // 32a + l % 32 and columns 32b + 8g + 4(l / 32) + 0..3 of this wave's
-    // block: one 16-byte store each where the row is 16-byte aligned.
-    const int64_t row0 = m0 + wm * 128 + r32, col0 = n0 + wn * WN + 4 * h;
-    float *yw = Y + row0 * ldy + col0;
-    const bool vec_ok = ((uintptr_t)Y % 16 == 0) && (ldy % 4 == 0);
-    if (vec_ok && m0 + wm * 128 + 128 <= M && n0 + wn * WN + WN <= N) {
+    write_tile<NB, WN>(acc, Y, M, N, ldy, m0 + wm * 128 + r32, n0 + wn * WN + 4 * h, m0 + wm * 128, n0 + wn * WN);
+}
+
+// The same product for shapes whose K is a whole number of ring turns
+// (K * ES a multiple of S * BKB bytes): the contraction needs no zero-fill, so
+// the fetch side has no per-chunk predicate at all. Each lane's load offsets
+// are computed once (rows past M or N get the out-of-range offset, as above)
+// and a chunk is selected by the load's scalar offset c * BKB; the loop is
+// unrolled over the S stages, so every LDS address is an immediate offset
+// from a base computed once, and the last S chunks are peeled so that no load
+// is issued past the end. The main loop then holds MFMAs, LDS reads, loads and
+// one barrier per chunk, with no vector-ALU instruction. The MFMA sequence
+// and the contraction order are the ring kernel's, so the results are the
+// same bit for bit.
+template <int V> using IC = std::integral_constant<int, V>;
+
+template <class E, int BKB, int S, int NWN>
+__global__ void __launch_bounds__(2 * NWN * 64)
+gemm_nt_wide_full_kernel(const char *__restrict__ X, const char *__restrict__ W, float *__restrict__ Y,
+                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                         int64_t tiles_m, int64_t tiles_n)
+{
+    constexpr int NW = 2 * NWN, WN = 256 / NWN, NB = WN / 32;
+    using G = Wide<BKB, S, NW>;
+    constexpr int ES = E::ES;
+    constexpr int MPS = 4 * NB, LPS = G::PC / G::NU, P = MPS / LPS;
+    static_assert(S == 4, "the loop body is unrolled for four stages");
+    static_assert(G::NU % 2 == 0 && LPS * G::NU == G::PC && MPS % LPS == 0, "load spread");
+    static_assert((S - 2) * G::PC + LPS <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[S * G::STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / NWN, wn = wave % NWN;
+
+    // XCD-aware raster, as in gemm_nt_wide_kernel.
+    const uint32_t ntm = (uint32_t)tiles_m, ntn = (uint32_t)tiles_n, nwg = ntm * ntn;
+    const uint32_t x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
+    const uint32_t pid = x * q8 + (x < r8 ? x : r8) + blockIdx.x / 8;
+    const uint32_t group = WGROUP_M * ntn;
+    const uint32_t first_m = (pid / group) * WGROUP_M;
+    const uint32_t gm = (ntm - first_m) < WGROUP_M ? (ntm - first_m) : WGROUP_M;
+    const uint32_t tm = __builtin_amdgcn_readfirstlane(first_m + (pid % group) % gm);
+    const uint32_t tn = __builtin_amdgcn_readfirstlane((pid % group) / gm);
+
+    const int64_t m0 = (int64_t)tm * WB, n0 = (int64_t)tn * WB;
+    const int rows_x = (int)(M - m0 < WB ? M - m0 : WB);
+    const int rows_w = (int)(N - n0 < WB ? N - n0 : WB);
+    const __amdgpu_buffer_rsrc_t rx = wide_rsrc(X + m0 * ldx * ES);
+    const __amdgpu_buffer_rsrc_t rw = wide_rsrc(W + n0 * ldw * ES);
+    const uint32_t ldxb = (uint32_t)(ldx * ES), ldwb = (uint32_t)(ldw * ES);
+    const int nk = (int)(K * ES / BKB); // a multiple of S, at least S (host)
+
+    // Load q of this wave (X tile's loads first, then W's): its lane offset
+    // within chunk 0; chunk c adds c * BKB through the scalar offset.
+    uint32_t vo[G::PC];
+    {
+        const int rsub = lane / G::SPR, slot = lane % G::SPR;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4v v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
-                    *reinterpret_cast<f32x4v *>(yw + 32 * a * ldy + 32 * b + 8 * g) = v;
-                }
-    } else {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const bool row_ok = row0 + 32 * a < M;
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int cc = 32 * b + 8 * (r >> 2) + (r & 3);
-                    if (row_ok && col0 + cc < N) yw[32 * a * ldy + cc] = acc[a][b][r];
-                }
+        for (int q = 0; q < G::PC; ++q) {
+            const int op = q / G::LOADS;
+            const int r = (wave * G::LOADS + q % G::LOADS) * G::ROWS_PER_LOAD + rsub;
+            vo[q] = r < (op ? rows_w : rows_x) ? (uint32_t)r * (op ? ldwb : ldxb) + (uint32_t)((slot ^ G::f(r)) * 16)
+                                               : WOOB;
         }
     }
+    auto load = [&](int c, int st, int q) {
+        const int op = q / G::LOADS;
+        char *dst = lds + st * G::STAGE + op * G::OPB + (wave * G::LOADS + q % G::LOADS) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rw : rx, (lds_void *)dst, 16, (int)vo[q], c * BKB, 0, 0);
+    };
+
+    // Fragment bases of k16 step u (piece h * NU + u of rows 32i + r32).
+    const int r32 = lane & 31, h = lane >> 5, fr = G::f(r32);
+    const char *xb[G::NU], *wb[G::NU];
+#pragma unroll
+    for (int u = 0; u < G::NU; ++u) {
+        const int pos = ((h * G::NU + u) ^ fr) * 16;
+        xb[u] = lds + (wm * 128 + r32) * BKB + pos;
+        wb[u] = lds + G::OPB + (wn * WN + r32) * BKB + pos;
+    }
+
+    f32x16 acc[4][NB];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
+    u32x4 fa[2][4], fb[2][NB];
+
+    // One k16 step: MPS MFMAs on fragment set fi; with rd, the fragments of
+    // step nu of stage nst read into set fi ^ 1 one after each of the first
+    // 4 + NB MFMAs (in the order that step takes them); nl loads (q0 on) of
+    // chunk lc into stage lst, one after every P MFMAs.
+    auto step = [&](int fi, int nst, int nu, bool rd, int lc, int lst, int q0, int nl) {
+        const char *xa = xb[nu] + nst * G::STAGE;
+        const char *wa = wb[nu] + nst * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < MPS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_chunk<E>(acc[i / NB][i % NB], fb[fi][i % NB], fa[fi][i / NB]);
+            if (rd) {
+                if (i == 0) fa[fi ^ 1][0] = *reinterpret_cast<const u32x4 *>(xa);
+                else if (i <= NB) fb[fi ^ 1][i - 1] = *reinterpret_cast<const u32x4 *>(wa + (i - 1) * 32 * BKB);
+                else if (i < 4 + NB) fa[fi ^ 1][i - NB] = *reinterpret_cast<const u32x4 *>(xa + (i - NB) * 32 * BKB);
+            }
+            if (nl > 0 && (i + 1) % P == 0 && (i + 1) / P <= nl) {
+                __builtin_amdgcn_sched_barrier(0);
+                load(lc, lst, q0 + (i + 1) / P - 1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    asm volatile("" ::"s"(Y), "s"(ldy)); // writeback arguments read before the loop (see above)
+    // Prologue: chunks 0 .. S-2 whole and the first LPS loads of chunk S-1.
+    for (int c = 0; c + 1 < S; ++c)
+        for (int q = 0; q < G::PC; ++q) load(c, c, q);
+    for (int q = 0; q < LPS; ++q) load(S - 1, S - 1, q);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<(S - 2) * G::PC + LPS>); // chunk 0 landed
+    plain_barrier();
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const u32x4 *>(xb[0] + i * 32 * BKB);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) fb[0][i] = *reinterpret_cast<const u32x4 *>(wb[0] + i * 32 * BKB);
+    }
+    // Chunk j in stage ST. During its steps 0 .. NU-2 the rest of chunk
+    // j + S - 1 is loaded (REST); its barrier waits until chunk j + 1 has
+    // landed, VM loads of later chunks may stay in flight; right after it the
+    // first LPS loads of chunk j + S go into stage ST, which no wave reads any
+    // more (NEXT). The last chunk has no barrier.
+    auto chunk = [&](int j, auto st_c, auto rest_c, auto next_c, auto vm_c, auto last_c) {
+        constexpr int ST = decltype(st_c)::value, VM = decltype(vm_c)::value;
+        constexpr bool REST = decltype(rest_c)::value, NEXT = decltype(next_c)::value;
+        constexpr bool LAST = decltype(last_c)::value;
+#pragma unroll
+        for (int u = 0; u < G::NU; ++u) {
+            const int fi = u & 1;
+            if (u + 1 < G::NU) {
+                step(fi, ST, u + 1, true, j + S - 1, (ST + S - 1) % S, LPS * (u + 1), REST ? LPS : 0);
+            } else if (!LAST) {
+                __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0<VM>);
+                plain_barrier();
+                step(fi, (ST + 1) % S, 0, true, j + S, ST, 0, NEXT ? LPS : 0);
+            } else {
+                step(fi, 0, 0, false, 0, 0, 0, 0);
+            }
+        }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    constexpr int VMS = (S - 2) * G::PC;
+    int j = 0;
+    for (; j + S < nk; j += S) {
+        chunk(j + 0, IC<0>{}, yes{}, yes{}, IC<VMS>{}, no{});
+        chunk(j + 1, IC<1>{}, yes{}, yes{}, IC<VMS>{}, no{});
+        chunk(j + 2, IC<2>{}, yes{}, yes{}, IC<VMS>{}, no{});
+        chunk(j + 3, IC<3>{}, yes{}, yes{}, IC<VMS>{}, no{});
+    }
+    // The last S chunks: only chunk nk - S still loads (the rest of chunk
+    // nk - 1); the barriers wait for what is left.
+    chunk(j + 0, IC<0>{}, yes{}, no{}, IC<VMS>{}, no{});
+    chunk(j + 1, IC<1>{}, no{}, no{}, IC<(S - 3) * G::PC>{}, no{});
+    chunk(j + 2, IC<2>{}, no{}, no{}, IC<0>{}, no{});
+    chunk(j + 3, IC<3>{}, no{}, no{}, IC<0>{}, yes{});
+
+    write_tile<NB, WN>(acc, Y, M, N, ldy, m0 + wm * 128 + r32, n0 + wn * WN + 4 * h, m0 + wm * 128, n0 + wn * WN);
 }
 
 } // namespace
@@ -321,8 +496,20 @@ hipError_t launch_wide_cfg(const GemmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-// CAS_GEMM_WIDE=<chunk bytes>x<stages>[w8] picks the k-chunk width, the
-// stage count and four or eight waves (tuning); see the default below.
+template <class E>
+hipError_t launch_wide_full(const GemmArgs &a, hipStream_t s)
+{
+    const int64_t tm = (a.M + WB - 1) / WB, tn = (a.N + WB - 1) / WB;
+    hipLaunchKernelGGL((gemm_nt_wide_full_kernel<E, 64, 4, 4>), dim3((unsigned)(tm * tn)), dim3(512), 0, s,
+                       (const char *)a.X, (const char *)a.W, a.Y, a.M, a.N, a.K, a.ldx, a.ldw, a.ldy, tm, tn);
+    return hipGetLastError();
+}
+
+// Default: eight waves, 64-byte k-chunks, four stages; the full-turn kernel
+// where K * 2 bytes is a multiple of the 256 bytes of one turn of the ring
+// (K % 128 == 0), else the ring kernel. CAS_GEMM_WIDE=<chunk bytes>x<stages>[w8]
+// picks another chunk width, stage count and four or eight waves of the ring
+// kernel (tuning); CAS_GEMM_WIDE=ring forces the ring kernel's default layout.
 template <class E>
 hipError_t launch_wide_elem(const GemmArgs &a, hipStream_t s)
 {
@@ -333,6 +520,7 @@ hipError_t launch_wide_elem(const GemmArgs &a, hipStream_t s)
     if (c == "64x4") return launch_wide_cfg<E, 64, 4, 2>(a, s);
     if (c == "128x2w8") return launch_wide_cfg<E, 128, 2, 4>(a, s);
     if (c == "64x3w8") return launch_wide_cfg<E, 64, 3, 4>(a, s);
+    if (c.empty() && a.K > 0 && (a.K * E::ES) % (4 * 64) == 0) return launch_wide_full<E>(a, s);
     return launch_wide_cfg<E, 64, 4, 4>(a, s);
 }
 } // namespace

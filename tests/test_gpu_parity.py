@@ -76,7 +76,38 @@ def test_gemm_wide_ragged(orc, monkeypatch, shape, dtype):
     assert_close(y, ref, bound, dtype, f"gemm wide {shape} {dtype}")
 
 
-@pytest.mark.parametrize("layout", ["64x4", "128x2", "64x3", "128x2w8", "64x3w8"])
+# K a multiple of 128 (whole turns of the four-stage ring): the full-turn
+# kernel, whose fetch has no per-chunk predicate; ragged M and N, one turn
+# (K = 128) and several.
+WIDE_FULL_SHAPES = [(300, 520, 256), (513, 260, 128), (256, 256, 512), (520, 513, 1024), (1, 300, 256),
+                    (600, 40, 384), (257, 255, 640), (768, 512, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE_FULL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_wide_full_turns(orc, monkeypatch, shape, dtype):
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, dtype, seed=M * 3 + N * 13 + K)
+    ref, bound = orc.gemm_nt(X, W, dtype)
+    y = run_gemm(X, W, dtype, M, N, K, "tile256 full turns")
+    assert_close(y, ref, bound, dtype, f"gemm wide full turns {shape} {dtype}")
+
+
+@pytest.mark.parametrize("shape", [(300, 520, 256), (520, 513, 1024)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_wide_full_turns_match_the_ring_kernel(monkeypatch, shape):
+    """The full-turn kernel issues the ring kernel's MFMAs in the same order
+    on the same fragments: the outputs are equal bit for bit."""
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    M, N, K = shape
+    X, W = synth.gemm_inputs(M, N, K, "bf16", seed=5)
+    full = run_gemm(X, W, "bf16", M, N, K, "full turns")
+    monkeypatch.setenv("CAS_GEMM_WIDE", "ring")
+    ring = run_gemm(X, W, "bf16", M, N, K, "ring")
+    assert_exact(full, ring, f"full turns vs ring {shape}")
+
+
+@pytest.mark.parametrize("layout", ["64x4", "128x2", "64x3", "128x2w8", "64x3w8", "ring"])
 @pytest.mark.parametrize("shape", [(300, 520, 136), (520, 513, 1032)], ids=lambda s: "x".join(map(str, s)))
 def test_gemm_wide_tuning_layouts(orc, monkeypatch, shape, layout):
     """The wide kernel's other chunk widths, stage counts and wave layouts
