@@ -234,12 +234,13 @@ CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t 
 
 namespace {
 
-// Shared checks of the two causal-softmax entry points: shapes, byte extents
-// of qkv (inb), of one statistics array (stb) and of the output (outb, for
-// out_bytes per element), the fused kernels' domain, and the 16-byte piece
-// width of the QKV rows (vec).
+// Shared checks of the causal-softmax and attention entry points: shapes,
+// byte extents of qkv (inb), of one statistics array (stb) and of the output
+// (outb, for out_bytes per element), the 16-byte piece width of the QKV rows
+// (vec), and which kernels serve the shape: the fast ones, or (*general) the
+// general-shape ones; outside both domains CAS_ERR_UNSUPPORTED.
 int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH, cas_dtype in_dtype, int out_bytes,
-                   int64_t *inb, int64_t *stb, int64_t *outb, int *vec)
+                   int64_t *inb, int64_t *stb, int64_t *outb, int *vec, bool *general)
 {
     if (B < 0 || T < 0 || C < 0 || NH < 0) return CAS_ERR_SHAPE;
     if (B == 0 || T == 0 || NH == 0) return 1; // nothing to do
@@ -260,10 +261,11 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     const int64_t nts = (T + 127) / 128;
     if (B * NH * (nts * (nts + 1) / 2) > INT32_MAX || cas::row_stats_workgroups(B, T, NH) > INT32_MAX)
         return CAS_ERR_SHAPE;
-    if (!cas::softmax_fits(T, HS, es, *vec)) return CAS_ERR_UNSUPPORTED;
-    // launches split by query block keep a grid below 2^32 work-items (256
-    // per workgroup) while the B * NH planes of one block fit in one grid
-    if (B * NH >= (INT64_C(1) << 23)) return CAS_ERR_UNSUPPORTED;
+    // the fast launches, split by query block, keep a grid below 2^32
+    // work-items (256 per workgroup) while the B * NH planes of one block fit
+    // in one grid
+    *general = !cas::softmax_fits(T, HS, es, *vec) || B * NH >= (INT64_C(1) << 23);
+    if (*general && !cas::general_softmax_fits(B, T, NH, HS, es, qkv)) return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
 }
 
@@ -294,7 +296,8 @@ CAS_EXPORT int cas_causal_row_stats(const void *qkv, float *row_max, float *row_
     if (!dtype_in_ok(in_dtype)) return CAS_ERR_DTYPE;
     int64_t inb, stb, outb;
     int vec = 1;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    bool general = false;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum) return CAS_ERR_NULL;
@@ -305,6 +308,7 @@ CAS_EXPORT int cas_causal_row_stats(const void *qkv, float *row_max, float *row_
     const int dc = device_check();
     if (dc != CAS_OK) return dc;
     const cas::TrimulArgs a = softmax_args(qkv, nullptr, row_max, row_logsum, B, T, C, NH, 4, 0);
+    if (general) return launch_status(cas::launch_gen_row_stats(a, in_dtype, (hipStream_t)stream));
     return launch_status(cas::launch_row_stats(a, in_dtype, (hipStream_t)stream));
 }
 
@@ -317,7 +321,8 @@ CAS_EXPORT int cas_causal_softmax(const void *qkv, const float *row_max, const f
     const int ob = elem_size(out_dtype);
     int64_t inb, stb, outb;
     int vec = 1;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec);
+    bool general = false;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum || !out) return CAS_ERR_NULL;
@@ -328,6 +333,7 @@ CAS_EXPORT int cas_causal_softmax(const void *qkv, const float *row_max, const f
     const int dc = device_check();
     if (dc != CAS_OK) return dc;
     const cas::TrimulArgs a = softmax_args(qkv, out, row_max, row_logsum, B, T, C, NH, ob, (int)out_dtype);
+    if (general) return launch_status(cas::launch_gen_softmax(a, in_dtype, mode, (hipStream_t)stream));
     return launch_status(cas::launch_softmax(a, in_dtype, mode, (hipStream_t)stream));
 }
 
@@ -340,7 +346,8 @@ CAS_EXPORT int cas_causal_softmax_fused(const void *qkv, void *out, float *row_m
     const int ob = elem_size(out_dtype);
     int64_t inb, stb, outb;
     int vec = 1;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec);
+    bool general = false;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, ob, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !out || !row_max || !row_logsum) return CAS_ERR_NULL;
@@ -354,6 +361,11 @@ CAS_EXPORT int cas_causal_softmax_fused(const void *qkv, void *out, float *row_m
     const int dc = device_check();
     if (dc != CAS_OK) return dc;
     const cas::TrimulArgs a = softmax_args(qkv, out, row_max, row_logsum, B, T, C, NH, ob, (int)out_dtype);
+    if (general) { // the statistics launch, then the rows launch, on the caller's stream
+        const hipError_t e = cas::launch_gen_row_stats(a, in_dtype, (hipStream_t)stream);
+        if (e != hipSuccess) return launch_status(e);
+        return launch_status(cas::launch_gen_softmax(a, in_dtype, mode, (hipStream_t)stream));
+    }
     return launch_status(cas::launch_softmax_fused(a, in_dtype, mode, (hipStream_t)stream));
 }
 
@@ -364,7 +376,8 @@ CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const
     if (!dtype_in_ok(in_dtype) || out_dtype != CAS_F32) return CAS_ERR_DTYPE;
     int64_t inb, stb, outb;
     int vec = 1;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    bool general = false;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum || !y) return CAS_ERR_NULL;
@@ -378,6 +391,7 @@ CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const
     if (dc != CAS_OK) return dc;
     cas::TrimulArgs a = softmax_args(qkv, y, row_max, row_logsum, B, T, C, NH, 4, 0);
     const hipStream_t st = (hipStream_t)stream;
+    if (general) return launch_status(cas::launch_gen_attention(a, in_dtype, false, st));
     switch (in_dtype) {
     case CAS_F32: return launch_status(cas::launch_attention_f32(a, st));
     case CAS_BF16: return launch_status(cas::launch_attention_bf16(a, st));
@@ -392,7 +406,8 @@ CAS_EXPORT int cas_causal_attention_fused(const void *qkv, void *y, float *row_m
     if (!dtype_in_ok(in_dtype) || out_dtype != CAS_F32) return CAS_ERR_DTYPE;
     int64_t inb, stb, outb;
     int vec = 1;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec);
+    bool general = false;
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !y || !row_max || !row_logsum) return CAS_ERR_NULL;
@@ -409,6 +424,7 @@ CAS_EXPORT int cas_causal_attention_fused(const void *qkv, void *y, float *row_m
     cas::TrimulArgs a = softmax_args(qkv, y, row_max, row_logsum, B, T, C, NH, 4, 0);
     a.vec_store = (uintptr_t)y % 16 == 0; // rows and head offsets are whole 16-byte pieces (C, HS multiples of 4)
     const hipStream_t st = (hipStream_t)stream;
+    if (general) return launch_status(cas::launch_gen_attention(a, in_dtype, true, st));
     switch (in_dtype) {
     case CAS_F32: return launch_status(cas::launch_attention_online_f32(a, st));
     case CAS_BF16: return launch_status(cas::launch_attention_online_bf16(a, st));
@@ -427,8 +443,8 @@ CAS_EXPORT const char *cas_status_string(int status)
     case CAS_ERR_DEVICE: return "the current HIP device is not a gfx950 (MI355X) GPU or is unavailable";
     case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
     case CAS_ERR_UNSUPPORTED:
-        return "valid arguments outside the kernels' domain (QKV rows not in 16-byte pieces, head over 256 bytes, "
-               "T >= 2^22, B * NH >= 2^23 for the softmax, or misaligned statistics)";
+        return "valid arguments outside the kernels' domain (softmax and attention: a head over 640 bytes with HS "
+               "rounded up to 32 elements, qkv off the element alignment, or statistics not 4-byte aligned)";
     case CAS_ERR_MODE: return "unknown softmax mode";
     default: return "unknown status";
     }

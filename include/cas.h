@@ -30,8 +30,9 @@
  *     BF16 or F16 with any input type. 16-bit inputs are raw bfloat16 / IEEE
  *     binary16 patterns.
  *   - The output byte range may not overlap an input byte range.
- *   - Any alignment is accepted (the softmax: see its domain); 16-byte aligned
- *     bases and pitches select wider loads and stores, with the same results.
+ *   - Any alignment is accepted (the softmax and attention: elements at their
+ *     natural alignment); 16-byte aligned bases and pitches select wider loads
+ *     and stores, with the same results.
  */
 #ifndef CAS_H
 #define CAS_H
@@ -154,12 +155,18 @@ int cas_trimul_causal(const void *qkv, void *out,
  *               outputs are the fp32 value rounded once more (to nearest
  *               even).
  *
- * Both: fp32 arithmetic; the scores are bit-identical to cas_trimul_causal's
- * (same products in the same order). Domain (else CAS_ERR_UNSUPPORTED, with
- * nothing written): QKV rows in 16-byte pieces (qkv 16-byte aligned, HS and
- * C times the element size multiples of 16), HS times the element size at
- * most 256 bytes, T < 2^22, B * NH < 2^23 (the planes of one query block in
- * one grid of under 2^32 work-items), and 4-byte aligned statistics. Other limits,
+ * Both: fp32 arithmetic. Two sets of kernels serve the calls:
+ *   - fast kernels where the QKV rows split into 16-byte pieces (qkv 16-byte
+ *     aligned, HS and C times the element size multiples of 16), HS times the
+ *     element size is at most 256 bytes, T < 2^22 and B * NH < 2^23; there
+ *     the scores are bit-identical to cas_trimul_causal's (same products in
+ *     the same order);
+ *   - general-shape kernels elsewhere (any HS, any base aligned to the
+ *     element size), with the same formulas and the same tolerance, up to
+ *     heads of 640 bytes once HS is rounded up to a multiple of 32 elements
+ *     (fp32 HS <= 160, 16-bit HS <= 320).
+ * Beyond that, or with statistics not 4-byte aligned: CAS_ERR_UNSUPPORTED,
+ * with nothing written. Other limits,
  * empty shapes and the no-overlap rule as for cas_trimul_causal: the
  * statistics written by cas_causal_row_stats may overlap neither qkv nor each
  * other, and out may overlap neither qkv nor the statistics it reads.
@@ -177,7 +184,9 @@ int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_l
  * Both softmax launches in one (the same outputs, statistics included):
  * each 128-row block of queries has its statistics computed and then its
  * rows written by the same workgroup, so the statistics work overlaps other
- * blocks' output stores instead of taking a launch of its own. Arguments,
+ * blocks' output stores instead of taking a launch of its own. (On general
+ * shapes the call enqueues the general statistics and rows kernels back to
+ * back on the stream.) Arguments,
  * modes, output types, domain and errors as for cas_causal_softmax, with
  * row_max / row_logsum written (as by cas_causal_row_stats) instead of read;
  * out, row_max and row_logsum may overlap neither qkv nor one another.
@@ -221,7 +230,10 @@ int cas_causal_attention(const void *qkv, const float *row_max, const float *row
  * row_max equals cas_causal_row_stats' bit for bit; row_logsum and y agree
  * with the two-pass results up to rounding (another summation order). For
  * 16-bit inputs the weights w_j are rounded to the input format for the
- * products with V; the sum uses them unrounded.
+ * products with V; the sum uses them unrounded. On general shapes (see
+ * cas_causal_softmax) the launch computes the statistics first, in two sweeps
+ * over the keys, writes them, and forms y from them as cas_causal_attention
+ * does.
  *   y   (B, T, C) fp32 (out_dtype must be CAS_F32), written whole, 16-byte
  *       stores when y is 16-byte aligned.
  * Domain, limits and empty shapes as for cas_causal_softmax; y and the 4-byte

@@ -31,11 +31,23 @@ def _gpu():
 LAUNCHES = ["two", "fused"]
 
 
-def run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, launch="two"):
+def device_qkv(qkv, dtype, B, T, NH, HS, offset=0):
+    """qkv on the device as a contiguous (B, T, 3C) tensor whose base lies
+    `offset` elements past an allocation's start (offset 1: a base that is
+    not 16-byte aligned)."""
+    d = to_device(qkv, dtype).reshape(-1)
+    if offset:
+        buf = torch.zeros(d.numel() + offset, dtype=d.dtype, device="cuda")
+        buf[offset:] = d
+        d = buf[offset:]
+    return d.view(B, T, 3 * NH * HS)
+
+
+def run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, launch="two", qkv_offset=0):
     """The softmax into guarded buffers, as two launches (row statistics, then
     softmax rows) or the fused one; returns (out rows (B*NH*T, T) as float32
     or raw uint16, row_max (B*NH*T,), row_logsum (B*NH*T,))."""
-    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    d = device_qkv(qkv, dtype, B, T, NH, HS, qkv_offset)
     ns = B * NH * T
     bm, mx = guarded_output(ns)
     bl, ls = guarded_output(ns)
@@ -77,8 +89,9 @@ def oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode):
 
 
 def check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", offset=0, exact_scores=False,
-               launch="two"):
-    got, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, f"{label} {launch}", offset, launch)
+               launch="two", qkv_offset=0):
+    got, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, f"{label} {launch}", offset, launch,
+                              qkv_offset)
     ref, mref, lref, bound = oracle_rows(orc, qkv, dtype, B, T, NH, HS, mode)
     t_idx = np.tile(np.arange(T), B * NH)
     what = f"{label} {mode} {dtype}->{out_dtype} B={B} T={T} NH={NH} HS={HS}"
@@ -210,7 +223,7 @@ def test_softmax_saturated(orc, launch):
 
 
 def test_softmax_rejections():
-    qkv = torch.zeros(2, 8, 3 * 2 * 5, device="cuda")        # HS = 5 fp32: 20-byte heads
+    qkv = torch.zeros(2, 8, 3 * 2 * 200, device="cuda")      # HS = 200 fp32: 800-byte heads
     for call in (lambda: cas.causal_softmax(qkv, 2), lambda: cas.causal_row_stats(qkv, 2)):
         with pytest.raises(cas.CasError) as e:
             call()
@@ -308,10 +321,10 @@ def test_workload_softmax_full_size(orc, name, mode, out_dtype, fused):
 
 # ------------------------------------------------------------ attention output
 
-def run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats=False):
+def run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats=False, qkv_offset=0):
     """Row statistics (two-launch or fused softmax), then the attention output
     into a guarded buffer; returns y (B, T, C)."""
-    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    d = device_qkv(qkv, dtype, B, T, NH, HS, qkv_offset)
     C = NH * HS
     if fused_stats:
         _, mx, ls = cas.causal_softmax(d, NH, "prob", fused=True)
@@ -328,11 +341,14 @@ def run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats=False):
     return y
 
 
-def check_attention(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, fused_stats=False, b_t=None):
+def check_attention(orc, qkv, dtype, B, T, NH, HS, label, exact_scores=False, fused_stats=False, b_t=None,
+                    qkv_offset=0, y=None):
     """GPU attention output against the oracle's, head by head. b_t: optional
-    list of (b, t0, t1) row ranges to compare (default: everything)."""
+    list of (b, t0, t1) row ranges to compare (default: everything). y: an
+    output already computed (else the two-pass launches run here)."""
     C = NH * HS
-    y = run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats)
+    if y is None:
+        y = run_attention(qkv, dtype, B, T, NH, HS, label, fused_stats, qkv_offset)
     V = np.abs(orc.decode(qkv, dtype).reshape(B, T, 3, NH, HS)[:, :, 2]) if dtype != "f32" else \
         np.abs(qkv.reshape(B, T, 3, NH, HS)[:, :, 2].astype(np.float64))
     worst = 0.0
@@ -431,11 +447,17 @@ def test_attention_ragged_16bit(orc, T, HS, dtype):
 
 
 def test_attention_rejections():
-    qkv = torch.zeros(2, 8, 3 * 2 * 4, device="cuda", dtype=torch.float16)
+    qkv = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)   # 672-byte heads
     mx = torch.zeros(2, 2, 8, device="cuda")
     with pytest.raises(cas.CasError) as e:
         cas.causal_attention(qkv, 2, stats=(mx, mx))
     assert e.value.status == -7
+    # an fp32 base that is not 4-byte aligned (raw pointer through the C ABI)
+    buf = torch.zeros(2 * 8 * 3 * 2 * 8 + 1, device="cuda")
+    y = torch.zeros(2, 8, 16, device="cuda")
+    st = cas.lib().cas_causal_attention(buf.data_ptr() + 2, mx.data_ptr(), mx.data_ptr(), y.data_ptr(), 2, 8, 16, 2,
+                                        cas.CAS_F32, cas.CAS_F32, cas._stream_ptr(buf.device))
+    assert st == -7
 
 
 def test_workload_attention_full_size(orc):
@@ -461,11 +483,11 @@ def test_workload_attention_bf16_full_size(orc):
 
 # ------------------------------------------------------- single-pass attention
 
-def run_attention_fused(qkv, dtype, B, T, NH, HS, label, y_offset=0):
+def run_attention_fused(qkv, dtype, B, T, NH, HS, label, y_offset=0, qkv_offset=0):
     """The single-pass attention into guarded buffers (y shifted by y_offset
     elements: 4 gives a y that is only 4-byte aligned); returns y (B, T, C)
     and the statistics (B, NH, T), as numpy."""
-    d = to_device(qkv, dtype).view(B, T, 3 * NH * HS)
+    d = device_qkv(qkv, dtype, B, T, NH, HS, qkv_offset)
     C = NH * HS
     n = B * T * C
     ybuf, yflat = guarded_output(n + y_offset)
@@ -572,7 +594,7 @@ def test_attention_fused_empty_and_rejections():
     assert y.numel() == 0 and mx.numel() == 0
     y2, _, _ = cas.causal_attention(qkv, 2)
     assert y2.numel() == 0
-    bad = torch.zeros(2, 8, 3 * 2 * 4, device="cuda", dtype=torch.float16)
+    bad = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)
     with pytest.raises(cas.CasError) as e:
         cas.causal_attention_fused(bad, 2)
     assert e.value.status == -7
@@ -594,3 +616,84 @@ def test_workload_attention_fused_bf16_full_size(orc):
     worst = check_attention_fused(orc, qkv, wl.dtype, B, T, NH, HS, wl.name,
                                   b_t=[(0, 0, 32), (2, 2040, 2060), (3, 4070, 4096)])
     print(f"{wl.name} fused attention: sampled max err/tol {worst:.3g}")
+
+
+# --------------------------------------------------- general shapes
+#
+# Heads whose rows do not split into 16-byte pieces (HS = 3 and 5 in fp32,
+# 12 in binary16, a base one element off alignment) or exceed 256 bytes
+# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels.
+
+GENERAL = [("f32", 3), ("f32", 5), ("f32", 80), ("bf16", 136), ("f16", 12), ("bf16", 3)]
+GENERAL_T = [1, 33, 64, 100, 300]
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("T", GENERAL_T)
+@pytest.mark.parametrize("dtype,HS", GENERAL, ids=lambda v: str(v))
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_general_shapes(orc, launch, dtype, HS, T, mode):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 19 + HS)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="general", launch=launch)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136), ("f32", 3)], ids=lambda v: str(v))
+def test_softmax_general_out16(orc, dtype, HS, out_dtype):
+    B, T, NH = 2, 130, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 7)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="general out16", launch="fused")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_misaligned_base(orc, launch, dtype):
+    """HS = 64 with qkv one element past a 16-byte boundary: the fast
+    kernels' domain needs 16-byte pieces, so the general kernels run."""
+    B, T, NH, HS = 2, 150, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=23)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="misaligned base", launch=launch, qkv_offset=1)
+
+
+@pytest.mark.parametrize("T", GENERAL_T)
+@pytest.mark.parametrize("dtype,HS", GENERAL, ids=lambda v: str(v))
+def test_attention_general_shapes(orc, dtype, HS, T):
+    """Both attention paths on general shapes: the two-pass launches, and the
+    one-launch entry point, which there computes the statistics first (two
+    sweeps over the keys) and then y as the two-pass path does -- so it is
+    held to the two-pass bound, and its row maxima to the statistics
+    launch's, bit for bit."""
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 29 + HS)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "general two-pass")
+    y, mx, ls = run_attention_fused(qkv, dtype, B, T, NH, HS, "general one launch")
+    mx2, ls2 = cas.causal_row_stats(to_device(qkv, dtype).view(B, T, 3 * NH * HS), NH)
+    assert np.array_equal(mx.view(np.uint32), mx2.cpu().numpy().view(np.uint32)), "row_max differs"
+    assert np.array_equal(ls.view(np.uint32), ls2.cpu().numpy().view(np.uint32)), "row_logsum differs"
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "general one launch", y=y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_attention_general_misaligned_base(orc, dtype):
+    B, T, NH, HS = 2, 97, 2, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=31)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "misaligned base", qkv_offset=1)
+    y, _, _ = run_attention_fused(qkv, dtype, B, T, NH, HS, "misaligned base one launch", qkv_offset=1)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "misaligned base one launch", y=y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_general_saturated_ramp(orc, dtype):
+    """Exact-score saturated rows (slopes 64, -16, 0.25, 200) on the general
+    kernels (HS = 64, where the scale 1/8 keeps every score exact, with a base
+    one element off alignment): statistics, probabilities and the attention
+    output pinned to exp / sum roundings only."""
+    B, T, NH, HS = 1, 257, 4, 64
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in SAT_SLOPES], dtype, v_seed=47)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="general ramp", exact_scores=True, launch="two",
+                   qkv_offset=1)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "general ramp", exact_scores=True, qkv_offset=1)
