@@ -790,12 +790,9 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
 // half h supplies 8 consecutive k-slots: MFMA j (of two per 32-key block)
 // takes, for k-slots 8h .. 8h + 7, keys 8(2j + i/4) + 4h + i%4 (i = 0..7),
 // which are score accumulators 8j .. 8j + 7 of that lane, so P again stays
-// in place. Those keys come in two runs of four, so V is staged transposed
-// (V^T[d][key], rows of AVT_PITCH bytes) and each operand is two 8-byte LDS
-// reads. The pitch 136 (34 dwords) puts the 32 d-rows an MFMA reads on 32
-// distinct bank pairs.
+// in place. Those keys come in two runs of four of one head column, which
+// the LDS transpose read delivers from V stored as read (below).
 // ---------------------------------------------------------------------------
-constexpr int AVT_PITCH = AKT * 2 + 8;
 
 // Two fp32 values rounded (nearest even) to the input format, a in the low
 // half: one packed conversion.
@@ -812,80 +809,106 @@ template <> __device__ __forceinline__ uint32_t pack16<KF16>(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, f16x2v));
 }
 
-// 16-bit staging. Waves 0 and 1 fetch the K tile: chunk t % NCH of rows
-// t / NCH + j (128 / NCH), j < NCH / 2 (t = tid % 128). Waves 2 and 3 fetch
-// the V tile as items of four consecutive rows 4g .. 4g + 3 of one chunk
-// (item t + 128 m, m < NCH / 8: chunk c = t % NCH, g = t / NCH + 8 m), so a
-// lane holds four keys of each of its eight head columns and writes them to
-// V^T as one 8-byte store per column: whole 4-key runs, no 2-byte stores.
-// Either way a lane stages NCH / 2 chunks. Rows past T and chunks past the
-// head read zero.
-template <int NCH> struct AStage16 {
-    u32x4 x[NCH / 2];
+// 16-bit staging. The K and V tiles go from HBM
+// straight into LDS (buffer loads with an LDS destination: no registers and no
+// VALU work on the way). One such wave load fills one kilobyte, lane i the
+// bytes 16i .. 16i + 15, so each lane fetches the global chunk that belongs at
+// its LDS position. K keeps the layout of the score reads (kswz). V is stored
+// key-major, chunk c of row r at position c ^ vswz(r), and the P V operand,
+// four consecutive keys of one head column per 8-byte register, comes out of
+// LDS through the transpose read ds_read_b64_tr_b16: within each group of 16
+// lanes, lane 4q + m receives element m of the 8 bytes that lanes
+// 4e + q (e = 0..3) address, as its elements e = 0..3. Rows past T are cut by
+// the size of the tile's buffer resource, chunks past the head by an
+// out-of-range offset; both read zero.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int NCH> __device__ __forceinline__ uint32_t vswz(uint32_t r)
+{
+    // A transpose read covers 4 rows x 64 bytes per 32 lanes and 4 rows x 32
+    // bytes per 16 lanes; with these chunk XORs the rows of either set fall in
+    // distinct banks (256 bytes of banks, rows of NCH * 16 bytes).
+    if constexpr (NCH == 8) return 2u * (r & 3u);
+    else return (0xCA60u >> (4u * (r & 3u))) & 15u;
+}
+
+// Per lane, the offset within the tile's rows of each of its NCH / 2 loads:
+// wave w fills kilobytes w * NCH / 4 .. of the K tile, then the same of V.
+template <int NCH> struct DStage16 {
+    uint32_t vo[NCH / 2];
 };
 
-// Row of load j for this lane: A + B_j (A per lane, B_j a constant of j and
-// of the lane's side).
-template <int NCH> __device__ __forceinline__ uint32_t a16_row(bool kside, uint32_t t, int j)
+template <int NCH>
+__device__ __forceinline__ void d16_init(DStage16<NCH> &st, int w, int lane, uint32_t ldb, uint32_t head_bytes)
 {
-    const uint32_t kb = (uint32_t)(j * (128 / NCH)), vb = (uint32_t)(32 * (j / 4) + (j % 4));
-    return (kside ? t / NCH : 4u * (t / NCH)) + (kside ? kb : vb);
+    constexpr uint32_t RB = NCH * 16, PER = NCH / 4, SH = NCH == 8 ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < NCH / 2; ++q) {
+        const bool kside = q < (int)PER;
+        const uint32_t o = ((uint32_t)w * PER + (uint32_t)q % PER) * 1024u + 16u * (uint32_t)lane;
+        const uint32_t r = o / RB, p = (o % RB) / 16u;
+        const uint32_t c = kside ? p ^ ((r >> SH) & (NCH - 1)) : p ^ vswz<NCH>(r); // the XORs are involutions
+        st.vo[q] = c * 16u < head_bytes ? r * ldb + c * 16u : OOB;
+    }
+}
+
+// A buffer resource over `rows` rows of pitch ldb from base: loads past them read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_rows(const char *base, uint32_t rows, uint32_t ldb)
+{
+    // Uniform, and visibly so (a saturating subtract for rows would otherwise
+    // put the size in a vector register and each load in a waterfall loop).
+    const uint64_t n = (uint64_t)rows * ldb;
+    const int size = __builtin_amdgcn_readfirstlane(n < 0x7FFFFFFFu ? (int)n : 0x7FFFFFFF);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, size, 0x00020000);
 }
 
 template <int NCH>
-__device__ __forceinline__ void a_fetch16(AStage16<NCH> &st, const char *kb0, const char *vb0, uint32_t J, uint32_t T,
-                                          uint32_t ldb, uint32_t head_bytes, int tid)
+__device__ __forceinline__ void d16_fetch(const DStage16<NCH> &st, char *kdst, char *vdst, const char *kb0,
+                                          const char *vb0, uint32_t J, uint32_t T, uint32_t ldb, int w)
 {
-    // Wave-uniform, and visibly so: from the wave's first lane. A per-lane
-    // test here would make the compiler build the buffer resource in a loop
-    // over the distinct values among the lanes (a waterfall) on every fetch.
-    const bool kside = __builtin_amdgcn_readfirstlane(tid) < 128;
-    const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at((kside ? kb0 : vb0) + (uint64_t)J * AKT * ldb);
-    const uint32_t lim = c * 16 < head_bytes ? T : 0u;
+    constexpr uint32_t PER = NCH / 4;
+    const uint32_t k0 = J * AKT, rows = k0 < T ? T - k0 : 0u;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_rows(kb0 + (uint64_t)k0 * ldb, rows, ldb);
+    const __amdgpu_buffer_rsrc_t rv = rsrc_rows(vb0 + (uint64_t)k0 * ldb, rows, ldb);
 #pragma unroll
-    for (int j = 0; j < NCH / 2; ++j) {
-        const uint32_t r = a16_row<NCH>(kside, t, j);
-        const uint32_t ok = 0u - (uint32_t)(J * AKT + r < lim);
-        const uint32_t vo = ((r * ldb + c * 16) & ok) | (OOB & ~ok);
-        st.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0);
+    for (int q = 0; q < NCH / 2; ++q) {
+        const bool kside = q < (int)PER;
+        char *dst = (kside ? kdst : vdst) + ((uint32_t)w * PER + (uint32_t)q % PER) * 1024u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kside ? rk : rv, (lds_void *)dst, 16, (int)st.vo[q], 0, 0, 0);
     }
 }
 
-template <int NCH> __device__ __forceinline__ void a_store16(const AStage16<NCH> &st, char *kbuf, char *vtbuf, int tid)
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p)
 {
-    const bool kside = __builtin_amdgcn_readfirstlane(tid) < 128;
-    const uint32_t t = (uint32_t)(tid & 127), c = t % NCH;
-    if (kside) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+}
+
+// The V operand addresses of this lane for key chunk 0, per head block nb:
+// lane (h, g = lane / 16 % 2, i = lane % 16) points at row 4h + i/4 of the
+// tile, column byte 64 nb + 32 g + 8 (i % 4). The transpose read then hands
+// it keys 4h .. 4h + 3 of head column 32 nb + lane % 32, the k-slots its p
+// occupies; rows 8 further give the other run of four, and chunk k0 adds
+// k0 rows (row r % 4 = i / 4 throughout, so the swizzle is the lane's own).
+template <int NCH, int NBV>
+__device__ __forceinline__ void v16_lanes(const char *(&vl)[NBV], const char *vbuf, int lane)
+{
+    constexpr uint32_t RB = NCH * 16;
+    const uint32_t h = (uint32_t)lane >> 5, i = (uint32_t)lane & 15u, e = i >> 2, q = i & 3u;
+    const uint32_t g = ((uint32_t)lane >> 4) & 1u;
 #pragma unroll
-        for (int j = 0; j < NCH / 2; ++j) {
-            const uint32_t r = a16_row<NCH>(true, t, j);
-            *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.x[j];
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < NCH / 8; ++m) {
-            const uint32_t g = t / NCH + 8u * (uint32_t)m; // keys 4g .. 4g + 3
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { // head columns 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
-                const uint32_t x0 = st.x[4 * m][e], x1 = st.x[4 * m + 1][e];
-                const uint32_t x2 = st.x[4 * m + 2][e], x3 = st.x[4 * m + 3][e];
-                char *d0 = vtbuf + (8u * c + 2u * (uint32_t)e) * AVT_PITCH + 8u * g;
-                *reinterpret_cast<u32x2 *>(d0) = u32x2{(x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16)};
-                *reinterpret_cast<u32x2 *>(d0 + AVT_PITCH) =
-                    u32x2{(x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u)};
-            }
-        }
-    }
+    for (int nb = 0; nb < NBV; ++nb)
+        vl[nb] = vbuf + (4u * h + e) * RB + 16u * ((4u * nb + 2u * g + (q >> 1)) ^ vswz<NCH>(e)) + 8u * (q & 1u);
 }
 
 template <class E, int NCH, int NBV, bool DIAG>
-__device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, const char *vtbuf,
+__device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
                                          const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
                                          uint32_t kabs0, uint32_t qabs)
 {
     f32x16 s[2];
-    const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    const uint32_t h = (uint32_t)(lane >> 5);
     attn_scores<E, NCH>(s, kbuf, qf, lane);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -895,59 +918,36 @@ __device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, 
             if (DIAG && kabs0 + 32u * b + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3) > qabs) p = 0.f;
             s[b][r] = p;
         }
+    const char *vl[NBV];
+    v16_lanes<NCH, NBV>(vl, vbuf, lane);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const u32x4 pa = {pack16<E>(s[b][8 * j + 0], s[b][8 * j + 1]), pack16<E>(s[b][8 * j + 2], s[b][8 * j + 3]),
                               pack16<E>(s[b][8 * j + 4], s[b][8 * j + 5]), pack16<E>(s[b][8 * j + 6], s[b][8 * j + 7])};
-            const uint32_t k0 = 32u * b + 16u * j + 4u * h; // keys k0 .. k0+3 and k0+8 .. k0+11
+            const uint32_t k0 = 32u * b + 16u * j; // keys k0 + 4h .. k0 + 4h + 3 and 8 further
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
-                const char *vr = vtbuf + (32u * nb + r32) * AVT_PITCH;
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + k0 * 2u);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + (k0 + 8u) * 2u);
+                const u32x2 lo = lds_read_tr16(vl[nb] + k0 * (NCH * 16));
+                const u32x2 hi = lds_read_tr16(vl[nb] + (k0 + 8u) * (NCH * 16));
                 mfma_chunk<E>(yacc[nb], pa, u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
         }
 }
 
 // One kernel for the three input types: the staging and the step differ
-// (fp32: V rows as read, 16-bit: V transposed, P rounded to the format).
+// (fp32: staged through registers, V rows padded; 16-bit: loaded straight
+// into LDS, V read back transposed, P rounded to the format).
 template <class E, int NCH> struct AttnCfg {
     static constexpr bool F32 = std::is_same<E, KF32>::value;
     static constexpr int ES = F32 ? 4 : 2;
     static constexpr int NBV = NCH * 16 / ES / 32; // 32-column blocks of the head (HS * ES <= NCH * 16 bytes)
-    static constexpr int VBYTES = F32 ? AKT * AV_PITCH : NBV * 32 * AVT_PITCH; // one V stage in LDS
-    static constexpr int MIN_WG = (!F32 && NCH == 8) ? 3 : 1; // workgroups per CU the registers must allow
+    static constexpr int VBYTES = AKT * AV_PITCH; // one fp32 V stage in LDS (16-bit: AKT * NCH * 16, as K)
+    // Workgroups per CU the registers must allow (LDS allows more). 16-bit,
+    // head <= 128 bytes: four, at 128 VGPRs, measured faster than three.
+    static constexpr int MIN_WG = (!F32 && NCH == 8) ? 4 : 1;
 };
-
-template <class E, int NCH>
-using AttnStage = typename std::conditional<AttnCfg<E, NCH>::F32, AStage<NCH>, AStage16<NCH>>::type;
-
-template <class E, int NCH>
-__device__ __forceinline__ void attn_fetch(AttnStage<E, NCH> &st, const char *kb0, const char *vb0, uint32_t J,
-                                           uint32_t T, uint32_t ldb, uint32_t head_bytes, int tid)
-{
-    if constexpr (AttnCfg<E, NCH>::F32) a_fetch<NCH>(st, kb0, vb0, J, T, ldb, head_bytes, tid);
-    else a_fetch16<NCH>(st, kb0, vb0, J, T, ldb, head_bytes, tid);
-}
-
-template <class E, int NCH>
-__device__ __forceinline__ void attn_stage(const AttnStage<E, NCH> &st, char *kbuf, char *vbuf, int tid)
-{
-    if constexpr (AttnCfg<E, NCH>::F32) a_store<NCH>(st, kbuf, vbuf, tid);
-    else a_store16<NCH>(st, kbuf, vbuf, tid);
-}
-
-template <class E, int NCH, int NBV, bool DIAG>
-__device__ __forceinline__ void attn_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
-                                          const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
-                                          uint32_t kabs0, uint32_t qabs)
-{
-    if constexpr (AttnCfg<E, NCH>::F32) a_step<NCH, NBV, DIAG>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, kabs0, qabs);
-    else a_step16<E, NCH, NBV, DIAG>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, kabs0, qabs);
-}
 
 template <class E, int NCH>
 __global__ void __launch_bounds__(STATS_THREADS, (AttnCfg<E, NCH>::MIN_WG))
@@ -957,8 +957,6 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
 {
     using Cfg = AttnCfg<E, NCH>;
     constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB, VBYTES = Cfg::VBYTES;
-    __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
-    __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1000,26 +998,58 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
         // 64-key tiles 0 .. 2I + 1: tiles below 2I lie wholly before the
         // block's first query; the last two hold the diagonal.
         const uint32_t nst = 2 * I + 2;
-        AttnStage<E, NCH> st;
-        attn_fetch<E, NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
-        attn_stage<E, NCH>(st, kbuf, vbuf, tid);
-        __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
-        tri::lds_barrier();
-        uint32_t J = 0;
-        for (; J + 2 < nst; ++J) {
-            attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-            attn_step<E, NCH, NBV, false>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls, lane,
-                                     J * AKT, qabs);
-            attn_stage<E, NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
+        if constexpr (Cfg::F32) {
+            __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
+            __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
+            AStage<NCH> st;
+            a_fetch<NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
+            a_store<NCH>(st, kbuf, vbuf, tid);
+            __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
             tri::lds_barrier();
+            uint32_t J = 0;
+            for (; J + 2 < nst; ++J) {
+                a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+                a_step<NCH, NBV, false>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls,
+                                        lane, J * AKT, qabs);
+                a_store<NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
+                tri::lds_barrier();
+            }
+            // the diagonal pair: J = nst - 2 (even, buffer 0), then nst - 1
+            a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+            a_step<NCH, NBV, true>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
+            a_store<NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
+            tri::lds_barrier();
+            a_step<NCH, NBV, true>(yacc, kbuf + KBYTES, vbuf + VBYTES, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+        } else {
+            // Direct staging into four named buffers, the loop unrolled by
+            // two (the single-pass kernel's scheme: no wait on the loads in
+            // flight before the reads of the current tile).
+            __shared__ __attribute__((aligned(16))) char k0s[KBYTES];
+            __shared__ __attribute__((aligned(16))) char k1s[KBYTES];
+            __shared__ __attribute__((aligned(16))) char v0s[KBYTES];
+            __shared__ __attribute__((aligned(16))) char v1s[KBYTES];
+            DStage16<NCH> ds;
+            d16_init<NCH>(ds, w, lane, ldb, head_bytes);
+            d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, 0, T, ldb, w);
+            __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q, statistics and tile 0 in place
+            tri::lds_barrier();
+            uint32_t J = 0;
+            for (; J + 2 < nst; J += 2) { // nst is even
+                d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
+                a_step16<E, NCH, NBV, false>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
+                __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
+                tri::lds_barrier();
+                d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, J + 2, T, ldb, w);
+                a_step16<E, NCH, NBV, false>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+                __builtin_amdgcn_s_waitcnt(0x70);
+                tri::lds_barrier();
+            }
+            d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
+            a_step16<E, NCH, NBV, true>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
+            __builtin_amdgcn_s_waitcnt(0x70);
+            tri::lds_barrier();
+            a_step16<E, NCH, NBV, true>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
         }
-        // the diagonal pair: J = nst - 2 (even, buffer 0), then nst - 1
-        attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-        attn_step<E, NCH, NBV, true>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
-        attn_stage<E, NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
-        tri::lds_barrier();
-        attn_step<E, NCH, NBV, true>(yacc, kbuf + KBYTES, vbuf + VBYTES, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
-        tri::lds_barrier();
         // y rows: lane holds query 32w + 8(r/4) + 4h + r%4 and column 32nb + lane%32
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb)
@@ -1069,18 +1099,33 @@ template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStre
 // ---------------------------------------------------------------------------
 constexpr float ONLINE_TAU = 8.f;
 
+
 struct OnlineRow {
     float mt; // largest dot product of the row so far (row_max = mt * scale)
     float ms; // offset of the exponentials: fl(m c) of an earlier maximum m <= mt
     float l;  // this lane half's sum of exp2(a c - ms) (the halves see disjoint keys)
 };
 
+// x of lane l combined with x of lane l ^ 32, in every lane, from one VALU
+// lane swap (v_permlane32_swap) instead of an LDS round trip: afterwards a
+// holds x of lanes l % 32 and b of lanes l % 32 + 32.
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]); // low half + high half in both: one order, one result
+}
+
 template <class E, int NCH, int NBV, bool DIAG>
 __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, const char *kbuf,
                                             const char *vbuf, const u32x4 (&qf)[NCH / 2], float c, int lane,
                                             uint32_t kabs0, uint32_t qabs)
 {
-    constexpr bool F32 = std::is_same<E, KF32>::value;
+    static_assert(std::is_same<E, KF32>::value, "fp32 step; online_step16 serves the 16-bit formats");
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
     f32x16 s[2];
     attn_scores<E, NCH>(s, kbuf, qf, lane);
@@ -1094,7 +1139,7 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
                 s[b][r] = -__builtin_inff();
             tmax = fmaxf(tmax, s[b][r]);
         }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)); // the row's other lane half: both take the same offset
+    tmax = halves_max(tmax); // the row's other lane half: both take the same offset
     rw.mt = fmaxf(rw.mt, tmax);
     const bool need = fmaf(tmax, c, -rw.ms) > ONLINE_TAU; // first step: ms = -inf
     if (__any(need)) {
@@ -1119,37 +1164,80 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
     rw.l += (part[0] + part[1]) + (part[2] + part[3]);
     // Y^T += V^T P^T: the A operand is V (as the B operand of the P V form),
     // the B operand this lane's p, in the same k-slots.
-    if constexpr (F32) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
 #pragma unroll
-                for (int nb = 0; nb < NBV; ++nb) {
-                    const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
-                    yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, s[b][j], yacc[nb], 0, 0, 0);
-                }
+            for (int nb = 0; nb < NBV; ++nb) {
+                const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
+                yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, s[b][j], yacc[nb], 0, 0, 0);
             }
-    } else {
+        }
+}
+
+// The 16-bit step: the scores and exponentials as in the fp32 step, then
+// P rounded to the input format and Y^T += V^T P^T with the V operand from
+// the transpose read.
+template <class E, int NCH, int NBV, bool DIAG>
+__device__ __forceinline__ void online_step16(f32x16 (&yacc)[NBV], OnlineRow &rw, const char *kbuf,
+                                              const char *vbuf, const u32x4 (&qf)[NCH / 2], float c, int lane,
+                                              uint32_t kabs0, uint32_t qabs)
+{
+    constexpr uint32_t RB = NCH * 16;
+    const uint32_t h = (uint32_t)(lane >> 5);
+    f32x16 s[2];
+    attn_scores<E, NCH>(s, kbuf, qf, lane);
+    // Keys after the query become -inf: no part in the maximum, exponential 0.
+    float tmax = -__builtin_inff();
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const u32x4 pb = {pack16<E>(s[b][8 * j + 0], s[b][8 * j + 1]),
-                                  pack16<E>(s[b][8 * j + 2], s[b][8 * j + 3]),
-                                  pack16<E>(s[b][8 * j + 4], s[b][8 * j + 5]),
-                                  pack16<E>(s[b][8 * j + 6], s[b][8 * j + 7])};
-                const uint32_t k0 = 32u * b + 16u * j + 4u * h; // keys k0 .. k0+3 and k0+8 .. k0+11
+        for (int r = 0; r < 16; ++r) {
+            if (DIAG && kabs0 + 32u * b + 8u * (r >> 2) + 4u * h + (uint32_t)(r & 3) > qabs)
+                s[b][r] = -__builtin_inff();
+            tmax = fmaxf(tmax, s[b][r]);
+        }
+    tmax = halves_max(tmax); // the row's other lane half: both take the same offset
+    rw.mt = fmaxf(rw.mt, tmax);
+    const bool need = fmaf(tmax, c, -rw.ms) > ONLINE_TAU; // first step: ms = -inf
+    if (__any(need)) {
+        const float msn = need ? pinned(tmax * c) : rw.ms;
+        const float alpha = __builtin_amdgcn_exp2f(rw.ms - msn); // 1 where the offset stays, 0 on the first step
+        rw.ms = msn;
+        rw.l *= alpha;
 #pragma unroll
-                for (int nb = 0; nb < NBV; ++nb) {
-                    const char *vr = vbuf + (32u * nb + r32) * AVT_PITCH;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + k0 * 2u);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + (k0 + 8u) * 2u);
-                    mfma_chunk<E>(yacc[nb], u32x4{lo[0], lo[1], hi[0], hi[1]}, pb);
-                }
-            }
+        for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yacc[nb][r] *= alpha;
     }
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -rw.ms));
+            s[b][r] = p;
+            part[r & 3] += p;
+        }
+    rw.l += (part[0] + part[1]) + (part[2] + part[3]);
+    const char *vl[NBV];
+    v16_lanes<NCH, NBV>(vl, vbuf, lane);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 pb = {pack16<E>(s[b][8 * j + 0], s[b][8 * j + 1]), pack16<E>(s[b][8 * j + 2], s[b][8 * j + 3]),
+                              pack16<E>(s[b][8 * j + 4], s[b][8 * j + 5]), pack16<E>(s[b][8 * j + 6], s[b][8 * j + 7])};
+            const uint32_t k0 = 32u * b + 16u * j; // keys k0 + 4h .. k0 + 4h + 3 and 8 further
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const u32x2 lo = lds_read_tr16(vl[nb] + k0 * RB);
+                const u32x2 hi = lds_read_tr16(vl[nb] + (k0 + 8u) * RB);
+                mfma_chunk<E>(yacc[nb], u32x4{lo[0], lo[1], hi[0], hi[1]}, pb);
+            }
+        }
 }
 
 template <class E, int NCH>
@@ -1159,9 +1247,8 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
                         uint32_t planes, uint32_t rank0, float scale, int vec_y)
 {
     using Cfg = AttnCfg<E, NCH>;
-    constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB, VBYTES = Cfg::VBYTES;
-    __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
-    __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
+    constexpr int RB = NCH * 16, NU = NCH / 2, NBV = Cfg::NBV, KBYTES = AKT * RB;
+    constexpr int VBYTES = Cfg::VBYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1197,27 +1284,62 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
 #pragma unroll
     for (int nb = 0; nb < NBV; ++nb) yacc[nb] = f32x16{};
     const uint32_t nst = 2 * I + 2; // 64-key tiles 0 .. 2I + 1; the last two hold the diagonal
-    AttnStage<E, NCH> st;
-    attn_fetch<E, NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
-    attn_stage<E, NCH>(st, kbuf, vbuf, tid);
-    __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q and tile 0 in place
-    tri::lds_barrier();
-    uint32_t J = 0;
-    for (; J + 2 < nst; ++J) {
-        attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-        online_step<E, NCH, NBV, false>(yacc, rw, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, c, lane,
-                                        J * AKT, qabs);
-        attn_stage<E, NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
+    if constexpr (Cfg::F32) {
+        __shared__ __attribute__((aligned(16))) char kbuf[2 * KBYTES];
+        __shared__ __attribute__((aligned(16))) char vbuf[2 * VBYTES];
+        AStage<NCH> st;
+        a_fetch<NCH>(st, kb0, vb0, 0, T, ldb, head_bytes, tid);
+        a_store<NCH>(st, kbuf, vbuf, tid);
+        __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q and tile 0 in place
         tri::lds_barrier();
+        uint32_t J = 0;
+        for (; J + 2 < nst; ++J) {
+            a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+            online_step<E, NCH, NBV, false>(yacc, rw, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, c,
+                                            lane, J * AKT, qabs);
+            a_store<NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
+            tri::lds_barrier();
+        }
+        a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
+        online_step<E, NCH, NBV, true>(yacc, rw, kbuf, vbuf, qf, c, lane, J * AKT, qabs);
+        a_store<NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
+        tri::lds_barrier();
+        online_step<E, NCH, NBV, true>(yacc, rw, kbuf + KBYTES, vbuf + VBYTES, qf, c, lane, (J + 1) * AKT, qabs);
+    } else {
+        // Tile J + 1 streams into the other buffer while step J runs; that
+        // buffer's last readers (step J - 1) passed the barrier before. The
+        // buffers are four separate arrays and the loop is unrolled by two,
+        // so that every LDS read names its buffer: the compiler then knows
+        // the loads in flight write elsewhere and does not wait for them.
+        __shared__ __attribute__((aligned(16))) char k0s[KBYTES];
+        __shared__ __attribute__((aligned(16))) char k1s[KBYTES];
+        __shared__ __attribute__((aligned(16))) char v0s[KBYTES];
+        __shared__ __attribute__((aligned(16))) char v1s[KBYTES];
+        DStage16<NCH> ds;
+        d16_init<NCH>(ds, w, lane, ldb, head_bytes);
+        d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, 0, T, ldb, w);
+        __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0): Q and tile 0 in place
+        tri::lds_barrier();
+        uint32_t J = 0;
+        for (; J + 2 < nst; J += 2) { // nst is even
+            d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
+            online_step16<E, NCH, NBV, false>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
+            __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
+            tri::lds_barrier();
+            d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, J + 2, T, ldb, w);
+            online_step16<E, NCH, NBV, false>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
+            __builtin_amdgcn_s_waitcnt(0x70);
+            tri::lds_barrier();
+        }
+        d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
+        online_step16<E, NCH, NBV, true>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
+        __builtin_amdgcn_s_waitcnt(0x70);
+        tri::lds_barrier();
+        online_step16<E, NCH, NBV, true>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
     }
-    attn_fetch<E, NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-    online_step<E, NCH, NBV, true>(yacc, rw, kbuf, vbuf, qf, c, lane, J * AKT, qabs);
-    attn_stage<E, NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
-    tri::lds_barrier();
-    online_step<E, NCH, NBV, true>(yacc, rw, kbuf + KBYTES, vbuf + VBYTES, qf, c, lane, (J + 1) * AKT, qabs);
 
     // y = Y / l and the statistics; the lane halves hold disjoint keys of one row.
-    const float lt = rw.l + __shfl_xor(rw.l, 32);
+    const float lt = halves_sum(rw.l);
     const float inv = 1.f / lt;
     if (qabs < T) {
         float *yr = y + ((uint64_t)b * T + qabs) * C + (uint64_t)nh * HS;
