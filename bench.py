@@ -435,6 +435,30 @@ def traffic_probe(names=PROBED) -> None:
     print("traffic probe done", flush=True)
 
 
+def attention_probe() -> None:
+    """Kernels for rocprofv3 counter runs of the attention kernels: three
+    launches of the single-pass attention, then three of the attention from
+    given statistics, on the 16-bit score workload (bf16 B4 T4096 NH25 HS64)."""
+    import torch
+
+    import causal_attention_score_amd as cas
+    from causal_attention_score_amd import synth
+    wl = synth.WORKLOADS["trimul_bf16_B4_T4096_NH25_HS64"]
+    (qkv,) = wl.inputs()
+    B, T, NH, HS = wl.dims
+    q = device_tensor(qkv, wl.dtype)
+    y = torch.empty((B, T, NH * HS), dtype=torch.float32, device="cuda")
+    mx = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+    ls = torch.empty_like(mx)
+    log("probe: 3 single-pass attention launches, then 3 from the statistics")
+    for _ in range(3):
+        cas.causal_attention_fused(q, NH, y=y, row_max=mx, row_logsum=ls)
+    for _ in range(3):
+        cas.causal_attention(q, NH, y=y, stats=(mx, ls))
+    torch.cuda.synchronize()
+    print("attention probe done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +470,8 @@ def main():
     ap.add_argument("--no-softmax", action="store_true", help="skip the causal-softmax timings")
     ap.add_argument("--traffic-probe", nargs="*", metavar="WORKLOAD",
                     help="only launch the kernels for the rocprofv3 counter runs (default: every profiled workload)")
+    ap.add_argument("--attention-probe", action="store_true",
+                    help="only launch the 16-bit attention kernels for the rocprofv3 counter runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the hot path shards with no communication, "
@@ -458,6 +484,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.traffic_probe is not None:
         traffic_probe(tuple(args.traffic_probe) or PROBED)
+        return
+    if args.attention_probe:
+        attention_probe()
         return
     wg = synth.WORKLOADS["dense_f32_960x1024x770"]
     wt = synth.WORKLOADS["trimul_f32_B8_T1024_NH12_HS64"]
