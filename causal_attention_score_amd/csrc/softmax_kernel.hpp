@@ -589,14 +589,308 @@ softmax_fused_kernel(const char *__restrict__ qkv, char *__restrict__ out, float
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined fused launch (16-bit inputs, heads of at most 128 bytes). The
+// walk of softmax_fused_kernel runs each block's statistics steps and then its
+// output steps; in the statistics steps nothing is stored. Here a step carries
+// up to two items: an output tile of block k and a statistics tile of block
+// k + 1, so the statistics of the next block are folded while the store
+// waves stream the current one's rows. Both items' Q and K rows sit in LDS
+// (two operand buffers: 2 x 32 KB at 128-byte heads). The statistics cursor
+// runs at most one block ahead of the output cursor, and a block's output
+// starts only after its statistics are complete (PWalk).
+// ---------------------------------------------------------------------------
+struct PWalk {
+    uint32_t nw, w, px, pbase, nt, rounds; // the deal, as in FWalk
+    uint32_t si, sJ, sPlane, sI;           // statistics cursor: block si, step sJ
+    uint32_t oi, oJ, oPlane, oI;           // output cursor
+    bool has_st, has_out;                  // this step's items
+
+    __device__ __forceinline__ void block(uint32_t i, uint32_t &plane, uint32_t &I) const
+    {
+        const uint32_t r = i < rounds ? (i + w) % rounds : 0;
+        const uint32_t k = r * nw + ((r & 1) ? nw - 1 - w : w);
+        const uint32_t rank = k / px;
+        I = nt - 1 - rank;
+        plane = pbase + (k - rank * px);
+    }
+    __device__ __forceinline__ void flags()
+    {
+        has_out = oi < rounds && si > oi;           // statistics of block oi complete
+        has_st = si < rounds && si <= oi + 1;       // at most one block ahead
+    }
+    __device__ __forceinline__ void init(uint32_t P, uint32_t nt_)
+    {
+        const uint32_t nwg = gridDim.x, x = blockIdx.x % 8, q8 = nwg / 8, r8 = nwg % 8;
+        nw = q8 + (x < r8 ? 1u : 0u);
+        w = blockIdx.x / 8;
+        pbase = (uint32_t)((uint64_t)P * x / 8);
+        px = (uint32_t)((uint64_t)P * (x + 1) / 8) - pbase;
+        nt = nt_;
+        const uint32_t nblk = px * nt, full = nblk / nw, rem = nblk - full * nw;
+        rounds = full + (((full & 1) ? nw - 1 - w : w) < rem ? 1u : 0u);
+        si = sJ = oi = oJ = 0;
+        sPlane = sI = 0;
+        if (rounds > 0) block(0, sPlane, sI); // px = 0 (an XCD without planes) gives no rounds
+        oPlane = sPlane;
+        oI = sI;
+        flags();
+    }
+    __device__ __forceinline__ bool valid() const { return oi < rounds; }
+    __device__ __forceinline__ void advance()
+    {
+        if (has_st && ++sJ > sI) {
+            ++si;
+            sJ = 0;
+            if (si < rounds) block(si, sPlane, sI);
+        }
+        if (has_out && ++oJ > oI) {
+            ++oi;
+            oJ = 0;
+            if (oi < rounds) block(oi, oPlane, oI);
+        }
+        flags();
+    }
+    __device__ __forceinline__ tri::Super st_item() const
+    {
+        tri::Super sp;
+        sp.plane = sPlane;
+        sp.T0 = sI * ST;
+        sp.S0 = sJ * ST;
+        sp.diag = sJ == sI;
+        return sp;
+    }
+    __device__ __forceinline__ tri::Super out_item() const
+    {
+        tri::Super sp;
+        sp.plane = oPlane;
+        sp.T0 = oI * ST;
+        sp.S0 = oJ * ST;
+        sp.diag = oJ == oI;
+        return sp;
+    }
+};
+
+template <class E, class O, class EP>
+__global__ void __launch_bounds__(tri::SUPER_THREADS)
+softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float *__restrict__ row_max,
+                    float *__restrict__ row_logsum, uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t P,
+                    uint32_t nt, float scale, int vec_store)
+{
+    using namespace tri;
+    constexpr int NCH = 8, RB = NCH * 16;
+    constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
+    __shared__ __attribute__((aligned(16))) char opb_st[OP_ROWS * RB];  // operand rows of the statistics item
+    __shared__ __attribute__((aligned(16))) char opb_out[OP_ROWS * RB]; // operand rows of the output item
+    __shared__ __attribute__((aligned(16))) char outb[NCOMP * OUT_BYTES];
+    __shared__ float part[2][NCOMP][3][64]; // per block parity and compute wave: m, ms, l of its 64 rows
+    __shared__ float stb[2 * ST];           // final statistics of the output block: [0, 128) max, [128, 256) logsum
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int role = wave / NCOMP; // 0 compute, 1 store, 2 loader
+    const int slot = wave % NCOMP;
+    const int sa = slot >> 1, sb = slot & 1;
+    char *my_out = outb + slot * OUT_BYTES;
+    const uint32_t TBY = T * (uint32_t)O::OB;
+    const uint32_t ldb = 3u * C * (uint32_t)E::ES;
+    const bool vec = vec_store != 0;
+    const float c = scale * LOG2E;
+
+    PWalk cur;
+    cur.init(P, nt);
+
+    // Every wave passes the same barriers: one after the prologue, then X and
+    // Y once per step, for as many steps as the walk has.
+    if (role == 2) {
+        const int cl = slot * 64 + lane;
+        Staged<NCH> ss, so;
+        // The item last staged in each buffer: a next item with the same
+        // plane and query block finds its Q rows already there.
+        uint32_t st_plane = ~0u, st_T0 = ~0u, out_plane = ~0u, out_T0 = ~0u;
+        if (cur.valid()) {
+            if (cur.has_st) {
+                const Super sp = cur.st_item();
+                stage_fetch<E, NCH>(ss, qkv, sp, T, C, NH, HS, ldb, cl);
+                stage_store<NCH>(ss, opb_st, cl);
+                st_plane = sp.plane;
+                st_T0 = sp.T0;
+            }
+            if (cur.has_out) {
+                const Super sp = cur.out_item();
+                stage_fetch<E, NCH>(so, qkv, sp, T, C, NH, HS, ldb, cl);
+                stage_store<NCH>(so, opb_out, cl);
+                out_plane = sp.plane;
+                out_T0 = sp.T0;
+            }
+        }
+        lds_barrier();
+        while (cur.valid()) {
+            cur.advance();
+            const bool more = cur.valid();
+            const bool nst = more && cur.has_st, nout = more && cur.has_out;
+            bool q_st = true, q_out = true;
+            if (nst) {
+                const Super sp = cur.st_item();
+                q_st = !(sp.plane == st_plane && sp.T0 == st_T0);
+                stage_fetch<E, NCH>(ss, qkv, sp, T, C, NH, HS, ldb, cl, q_st);
+                st_plane = sp.plane;
+                st_T0 = sp.T0;
+            }
+            if (nout) {
+                const Super sp = cur.out_item();
+                q_out = !(sp.plane == out_plane && sp.T0 == out_T0);
+                stage_fetch<E, NCH>(so, qkv, sp, T, C, NH, HS, ldb, cl, q_out);
+                out_plane = sp.plane;
+                out_T0 = sp.T0;
+            }
+            lds_barrier(); // X: operand rows of this step consumed
+            if (nst) stage_store<NCH>(ss, opb_st, cl, q_st);
+            if (nout) stage_store<NCH>(so, opb_out, cl, q_out);
+            lds_barrier(); // Y: operand rows of the next step in LDS
+        }
+    } else if (role == 0) {
+        const int r32 = lane & 31;
+        Run2 rn;
+        float mx[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
+        lds_barrier();
+        while (cur.valid()) {
+            const bool has_st = cur.has_st, has_out = cur.has_out;
+            const Super ss = cur.st_item(), so = cur.out_item();
+            const bool first_out = has_out && cur.oJ == 0, last_stats = has_st && cur.sJ == cur.sI;
+            const uint32_t opar = cur.oi & 1, spar = cur.si & 1;
+            cur.advance();
+            if (first_out) {
+                // The four waves' statistics of the output block, published at
+                // its last statistics step; both waves of a pair merge them in
+                // the same order, so they agree exactly.
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const int row = 32 * qb + r32;
+                    const int p0 = 2 * sa, p1 = 2 * sa + 1;
+                    float m = part[opar][p0][0][row], ms = part[opar][p0][1][row], l = part[opar][p0][2][row];
+                    stats_merge(m, ms, l, part[opar][p1][0][row], part[opar][p1][1][row], part[opar][p1][2][row], c);
+                    mx[qb] = m * scale;
+                    ls[qb] = (__builtin_amdgcn_logf(l) - fmaf(m, c, -ms)) * LN2;
+                    if (sb == 0 && lane < 32) {
+                        stb[64 * sa + row] = mx[qb];
+                        stb[ST + 64 * sa + row] = ls[qb];
+                    }
+                }
+            }
+            f32x16 acc[2][2];
+            if (has_st) {
+                if (ss.S0 == 0) { // a new block: statistics start empty
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        rn.m[qb] = -__builtin_inff();
+                        rn.ms[qb] = 0.f;
+                        rn.l[qb] = 0.f;
+                    }
+                }
+                const bool live = !(ss.diag && sa == 0 && sb == 1);
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+                if (live) {
+                    sub_mma<E, NCH>(acc, opb_st, sa, sb, lane);
+                    if (ss.diag && sa == sb) sub_stats_update<true>(acc, rn, c, lane);
+                    else sub_stats_update<false>(acc, rn, c, lane);
+                }
+                if (last_stats) { // merge the lane halves, publish for the block's first output step
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        stats_merge(rn.m[qb], rn.ms[qb], rn.l[qb], __shfl_xor(rn.m[qb], 32),
+                                    __shfl_xor(rn.ms[qb], 32), __shfl_xor(rn.l[qb], 32), c);
+                        if (lane < 32) {
+                            part[spar][slot][0][32 * qb + r32] = rn.m[qb];
+                            part[spar][slot][1][32 * qb + r32] = rn.ms[qb];
+                            part[spar][slot][2][32 * qb + r32] = rn.l[qb];
+                        }
+                    }
+                }
+            }
+            const bool live_out = has_out && !(so.diag && sa == 0 && sb == 1);
+            if (has_out) {
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+                if (live_out) sub_mma<E, NCH>(acc, opb_out, sa, sb, lane);
+            }
+            lds_barrier(); // X: operand rows consumed, previous tile read back
+            if (live_out) {
+                if (so.diag && sa == sb) subtile_to_lds<true, O, EP>(acc, my_out, scale, lane, mx, ls);
+                else subtile_to_lds<false, O, EP>(acc, my_out, scale, lane, mx, ls);
+            }
+            lds_barrier(); // Y: tile in LDS / partial statistics in LDS
+        }
+    } else {
+        lds_barrier();
+        Tile pm; // mirror of the previous output step, second half pending
+        bool pm_live = false, pm_full = false;
+        while (cur.valid()) {
+            const bool has_out = cur.has_out;
+            const Super sp = cur.out_item();
+            const bool first_out = has_out && cur.oJ == 0;
+            cur.advance();
+            const Tile tl = sub_tile<O>(sp, sa, sb, out, T);
+            const bool inside = tl.rl > 0 && tl.cl > 0;
+            const uint32_t tby = opaque_s(TBY);
+            const bool full = tl.rl == TB && tl.cl == TB;
+            lds_barrier(); // X
+            if (pm_live) {
+                if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+                else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
+            }
+            pm_live = false;
+            if (first_out) { // the block's statistics, written by the compute waves before X
+                const int cl = slot * 64 + lane;
+                const uint32_t row = sp.T0 + (uint32_t)(cl & (ST - 1));
+                if (row < T) (cl < ST ? row_max : row_logsum)[(uint64_t)sp.plane * T + row] = stb[cl];
+            }
+            lds_barrier(); // Y: tile in LDS
+            if (!has_out || !inside) continue;
+            stream_subtile<O, EP>(tl, sp.diag && sa == 0 && sb == 1, full, vec, my_out, T, tby, lane);
+            if (!tl.diag) { // first half of the mirror now, the second after the next X
+                pm = tl;
+                pm_live = true;
+                pm_full = full && vec;
+                if (pm_full) nan_mirror_o<0, O, true, EP>(tl, T, tby, lane, vec);
+                else nan_mirror_o<0, O, false, EP>(tl, T, tby, lane, vec);
+            }
+        }
+        if (pm_live) {
+            const uint32_t tby = opaque_s(TBY);
+            if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+            else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
+        }
+    }
+}
+
 template <class E, int NCH, class O, class EP> hipError_t launch_fused(const TrimulArgs &a, hipStream_t s)
 {
     auto kern = softmax_fused_kernel<E, NCH, O, EP>;
+    static ResidentSlots resident, resident_pipe;
+    ResidentSlots *rs = &resident;
     const int64_t nt = (a.T + ST - 1) / ST;
+    if constexpr (E::ES == 2 && NCH == 8) {
+        // The pipelined walk from 16 query blocks per plane on (measured,
+        // outputs bit-identical: bf16 B4 T4096 probabilities to bf16 727 ->
+        // 715 us, log-probabilities 737 -> 696 us, to fp32 1195 -> 1176 us;
+        // at B8 T1024, 8 blocks, 54.7 -> 57.0 us, so the plain walk there).
+        // CAS_SOFTMAX_FUSED=plain|pipe overrides the choice (tuning).
+        const char *env = std::getenv("CAS_SOFTMAX_FUSED");
+        const bool pipe = env && !std::strcmp(env, "pipe") ? true : env && !std::strcmp(env, "plain") ? false : nt >= 16;
+        if (pipe) {
+            kern = softmax_pipe_kernel<E, O, EP>;
+            rs = &resident_pipe;
+        }
+    }
     const int64_t P = a.B * a.NH;
-    static ResidentSlots resident;
     // Persistent grid; no more workgroups than row blocks (each XCD's share).
-    int64_t grid = resident_slots(resident, kern, tri::SUPER_THREADS);
+    int64_t grid = resident_slots(*rs, kern, tri::SUPER_THREADS);
     const int64_t blocks = P * nt;
     if (grid > 8 * ((blocks + 7) / 8)) grid = 8 * ((blocks + 7) / 8);
     if (grid < 8) grid = 8;

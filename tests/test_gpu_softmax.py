@@ -134,6 +134,32 @@ def test_softmax_ragged_16bit(orc, launch, T, HS, dtype, mode):
     check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="sweep16", launch=launch)
 
 
+# The fused launch has two walks for 16-bit inputs with heads of at most 128
+# bytes: the plain one (each block's statistics steps, then its output steps)
+# and the pipelined one (a block's output steps carry the next block's
+# statistics steps), chosen by the number of query blocks. Both are forced
+# here on ragged shapes, checked against the oracle and against each other:
+# they must agree bit for bit, statistics and every output byte included.
+PIPE_SHAPES = [(1, 1, 1, 64), (2, 65, 3, 64), (1, 300, 2, 40), (3, 1100, 2, 16), (2, 2049, 1, 64)]
+
+
+@pytest.mark.parametrize("out_dtype", ["same", "f32"])
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", PIPE_SHAPES, ids=lambda s: "B%dT%dNH%dHS%d" % s)
+def test_softmax_fused_pipelined_walk(orc, monkeypatch, shape, dtype, mode, out_dtype):
+    B, T, NH, HS = shape
+    od = dtype if out_dtype == "same" else out_dtype
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 13 + HS)
+    monkeypatch.setenv("CAS_SOFTMAX_FUSED", "pipe")
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, od, label="pipe walk", launch="fused")
+    got_p = run_softmax(qkv, dtype, B, T, NH, HS, mode, od, "pipe walk", launch="fused")
+    monkeypatch.setenv("CAS_SOFTMAX_FUSED", "plain")
+    got_q = run_softmax(qkv, dtype, B, T, NH, HS, mode, od, "plain walk", launch="fused")
+    for a, b in zip(got_p, got_q):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), f"walks differ at {shape}"
+
+
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("launch", LAUNCHES)
