@@ -141,12 +141,18 @@ class Part:
 
 
 def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
-    """Warm up, then time `steps` steps; every part is bracketed by HIP events
-    on the stream it is launched on. The warm-up is `warmup` steps, continued
-    (untimed) until `settle_s` seconds have passed, so the timed steps do not
-    run while the GPU's clocks are still ramping up from idle. Returns (ms per
-    step, [mean ms per part], wall ms per step, [median ms per part], warm-up
-    steps run)."""
+    """Warm up, then time `steps` steps (twice with several parts). The
+    warm-up is `warmup` steps,
+    continued (untimed) until `settle_s` seconds have passed, so the timed
+    steps do not run while the GPU's clocks are still ramping up from idle.
+    With several parts, the first timed pass brackets the steps with HIP
+    events at its two ends only: the step time. The second pass runs the same
+    steps with an event after every part, on the stream the parts are launched
+    on: the per-part times (an event between two launches adds a dispatch gap,
+    about 9 us per step for the two-kernel step, so these events stay out of
+    the step time). A single part is timed in one pass with an event after
+    every launch. Returns (ms per step, [mean ms per part], wall ms per step,
+    [median ms per part], warm-up steps run)."""
     import torch
     stream = torch.cuda.current_stream()
     t_warm = time.perf_counter()
@@ -158,20 +164,29 @@ def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
         if done >= warmup and done % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
+    single = len(parts) == 1
     t0 = time.perf_counter()
     start.record(stream)
     for s in range(steps):
-        ev[s][0].record(stream)
-        for i, p in enumerate(parts):
+        if single:
+            ev[s][0].record(stream)
+        for p in parts:
             p()
-            ev[s][i + 1].record(stream)
+        if single:
+            ev[s][1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     total = start.elapsed_time(stop)
+    if not single:
+        for s in range(steps):
+            ev[s][0].record(stream)
+            for i, p in enumerate(parts):
+                p()
+                ev[s][i + 1].record(stream)
+        torch.cuda.synchronize()
     each = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(len(parts))]
     per = [sum(e) / steps for e in each]
     med = [statistics.median(e) for e in each]

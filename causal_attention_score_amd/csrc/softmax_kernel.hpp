@@ -975,7 +975,8 @@ template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode,
 //    bytes apart, so the two keys an MFMA reads (4 apart) fall in different
 //    bank halves.
 //  * 16-bit inputs (v_mfma_f32_32x32x16): see the 16-bit section below (P
-//    rounded to the format, V staged transposed).
+//    rounded to the format; K and V loaded straight into LDS, the V operand
+//    read back through the LDS transpose read).
 // ---------------------------------------------------------------------------
 constexpr int AKT = 64;            // keys per attention step
 constexpr int AV_PITCH = 256 + 32; // LDS bytes per V row (HS * 4 <= 256)
