@@ -35,6 +35,8 @@
 // heads recompute the scores per group of columns.
 #pragma once
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "tile_engine.hpp"
 #include "trimul_kernel.hpp"
@@ -71,20 +73,29 @@ template <class E>
 __device__ __forceinline__ void stage_rows(char *lds, const char *__restrict__ base, int64_t ldb, int rows,
                                            const GenArgs &g, int lane)
 {
-    constexpr int ES = E::ES;
+    // Lane l takes elements l, l + 64, .. (M per row at most) of RG rows at a
+    // time: all their loads in flight, then the LDS writes (one load, wait
+    // and write per element left each load's latency exposed).
+    constexpr int ES = E::ES, M = (GMAX_HEAD / ES + 63) / 64, RG = ES == 4 ? 8 : 4;
+    using U = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
     const int nel = g.hsb / ES;
-    for (int r = 0; r < GB; ++r) {
-        const char *src = base + (int64_t)r * ldb;
-        for (int e = lane; e < nel; e += 64) {
-            const bool ok = r < rows && e < g.HS;
-            if constexpr (ES == 4) {
-                const uint32_t v = ok ? *reinterpret_cast<const uint32_t *>(src + e * 4) : 0u;
-                *reinterpret_cast<uint32_t *>(lds + r * g.pitch + e * 4) = v;
-            } else {
-                const uint16_t v = ok ? *reinterpret_cast<const uint16_t *>(src + e * 2) : (uint16_t)0;
-                *reinterpret_cast<uint16_t *>(lds + r * g.pitch + e * 2) = v;
+    for (int r0 = 0; r0 < GB; r0 += RG) {
+        U v[RG][M];
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int r = r0 + rr, e = lane + 64 * m;
+                const bool ok = r < rows && e < g.HS;
+                v[rr][m] = ok ? *reinterpret_cast<const U *>(base + (int64_t)r * ldb + e * ES) : (U)0;
             }
-        }
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int e = lane + 64 * m;
+                if (e < nel) *reinterpret_cast<U *>(lds + (r0 + rr) * g.pitch + e * ES) = v[rr][m];
+            }
     }
 }
 

@@ -62,39 +62,53 @@ template <int NCH> __device__ __forceinline__ uint32_t kswz(uint32_t r, uint32_t
     return (c ^ ((r >> SH) & (NCH - 1))) << 4;
 }
 
-// The 128 K rows of key tile J (rows J*128.. of the plane), NCH/2 chunks per
-// lane: lane tid takes chunk tid % NCH of rows q*RPJ + tid / NCH. Rows past T
-// and chunks past the head read zero.
-template <int NCH> struct KStage {
-    u32x4 v[NCH / 2];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A buffer resource over `rows` rows of pitch ldb from base: loads past them read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_rows(const char *base, uint32_t rows, uint32_t ldb)
+{
+    // Uniform, and visibly so (a saturating subtract for rows would otherwise
+    // put the size in a vector register and each load in a waterfall loop).
+    const uint64_t n = (uint64_t)rows * ldb;
+    const int size = __builtin_amdgcn_readfirstlane(n < 0x7FFFFFFFu ? (int)n : 0x7FFFFFFF);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, size, 0x00020000);
+}
+
+// The 128 K rows of key tile J (rows J*128.. of the plane) go from HBM
+// straight into LDS: buffer loads with an LDS destination, one kilobyte per
+// wave instruction (lane i fills bytes 16i .. 16i + 15 of it), so each lane
+// fetches the global chunk that belongs at its LDS position (chunk c of row r
+// at kswz(r, c); the XOR is an involution). Wave w fills kilobytes
+// w NCH/2 .. of the tile. Rows past T read zero through the size of the
+// tile's buffer resource, chunks past the head through an out-of-range offset.
+template <int NCH> struct KDirect {
+    uint32_t vo[NCH / 2]; // per lane: offset within the tile's rows of each of its loads
 };
 
 template <int NCH>
-__device__ __forceinline__ void k_fetch(KStage<NCH> &st, const char *kb0, uint32_t J, uint32_t T, uint32_t ldb,
-                                        uint32_t head_bytes, int tid)
+__device__ __forceinline__ void kd_init(KDirect<NCH> &st, int w, int lane, uint32_t ldb, uint32_t head_bytes)
 {
-    constexpr int RPJ = STATS_THREADS / NCH;
-    const __amdgpu_buffer_rsrc_t rk = rsrc_at(kb0 + (uint64_t)J * ST * ldb);
-    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
-    const uint32_t lim = c * 16 < head_bytes ? T : 0u; // a chunk past the head reads zero
+    constexpr uint32_t RB = NCH * 16, PER = NCH / 2, SH = NCH == 8 ? 1 : 0;
 #pragma unroll
-    for (int q = 0; q < NCH / 2; ++q) {
-        const uint32_t r = (uint32_t)(q * RPJ) + r0;
-        const uint32_t ok = 0u - (uint32_t)(J * ST + r < lim);
-        const uint32_t vo = ((r * ldb + c * 16) & ok) | (OOB & ~ok);
-        st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)vo, 0, 0);
+    for (int q = 0; q < (int)PER; ++q) {
+        const uint32_t o = ((uint32_t)w * PER + (uint32_t)q) * 1024u + 16u * (uint32_t)lane;
+        const uint32_t r = o / RB, p = (o % RB) / 16u;
+        const uint32_t c = p ^ ((r >> SH) & (NCH - 1));
+        st.vo[q] = c * 16u < head_bytes ? r * ldb + c * 16u : OOB;
     }
 }
 
-template <int NCH> __device__ __forceinline__ void k_store(const KStage<NCH> &st, char *kb, int tid)
+template <int NCH>
+__device__ __forceinline__ void kd_fetch(const KDirect<NCH> &st, char *dst, const char *kb0, uint32_t J, uint32_t T,
+                                         uint32_t ldb, int w)
 {
-    constexpr int RPJ = STATS_THREADS / NCH;
-    const uint32_t c = (uint32_t)(tid % NCH), r0 = (uint32_t)(tid / NCH);
+    constexpr uint32_t PER = NCH / 2;
+    const uint32_t k0 = J * ST, rows = k0 < T ? T - k0 : 0u;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_rows(kb0 + (uint64_t)k0 * ldb, rows, ldb);
 #pragma unroll
-    for (int q = 0; q < NCH / 2; ++q) {
-        const uint32_t r = (uint32_t)(q * RPJ) + r0;
-        *reinterpret_cast<u32x4 *>(kb + r * (NCH * 16) + kswz<NCH>(r, c)) = st.v[q];
-    }
+    for (int q = 0; q < (int)PER; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dst + ((uint32_t)w * PER + (uint32_t)q) * 1024u), 16,
+                                                 (int)st.vo[q], 0, 0, 0);
 }
 
 // acc[kb] += K rows 32kb.. of the LDS tile times this wave's Q rows: lane
@@ -211,7 +225,11 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
                  float scale)
 {
     constexpr int RB = NCH * 16, NU = NCH / 2;
-    __shared__ __attribute__((aligned(16))) char kbuf[2 * ST * RB];
+    // Two named buffers (and the loop unrolled by two) so that every LDS read
+    // names its buffer: the compiler then knows the loads in flight write the
+    // other one and does not wait for them before the reads.
+    __shared__ __attribute__((aligned(16))) char k0s[ST * RB];
+    __shared__ __attribute__((aligned(16))) char k1s[ST * RB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -245,28 +263,37 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
         }
 
         RowRun rr{-__builtin_inff(), 0.f, 0.f};
-        KStage<NCH> st;
-        k_fetch<NCH>(st, kb0, 0, T, ldb, head_bytes, tid);
-        k_store<NCH>(st, kbuf, tid);
+        KDirect<NCH> kd;
+        kd_init<NCH>(kd, w, lane, ldb, head_bytes);
+        kd_fetch<NCH>(kd, k0s, kb0, 0, T, ldb, w);
         // Every load so far (Q fragments included) has landed: the loop's
         // waits then only ever concern the key tile fetched a step ahead.
         __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) lgkmcnt(0)
         tri::lds_barrier();
-        for (uint32_t J = 0; J < I; ++J) { // key tiles left of the diagonal: nothing masked
-            k_fetch<NCH>(st, kb0, J + 1, T, ldb, head_bytes, tid);
+        // Key tiles left of the diagonal (nothing masked): tile J in k<J % 2>,
+        // tile J + 1 loading into the other buffer meanwhile.
+        auto step = [&](const char *cur, char *next, uint32_t J) {
+            kd_fetch<NCH>(kd, next, kb0, J + 1, T, ldb, w);
             f32x16 acc[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
-            k_mma<E, NCH>(acc, kbuf + (J & 1) * (ST * RB), qf, lane);
+            k_mma<E, NCH>(acc, cur, qf, lane);
             stats_update<4>(acc, rr, c, lane);
-            k_store<NCH>(st, kbuf + ((J + 1) & 1) * (ST * RB), tid);
-            tri::lds_barrier(); // tile J + 1 written; tile J's reads done before it is rewritten
+            __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
+            tri::lds_barrier();                 // every wave's part; tile J's reads done before it is rewritten
+        };
+        uint32_t J = 0;
+        for (;;) {
+            if (J >= I) break;
+            step(k0s, k1s, J++);
+            if (J >= I) break;
+            step(k1s, k0s, J++);
         }
-        {   // the diagonal tile J = I
+        {   // the diagonal tile J = I (no loads in flight: the buffer may be chosen at run time)
             f32x16 acc[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
-            k_mma<E, NCH>(acc, kbuf + (I & 1) * (ST * RB), qf, lane);
+            k_mma<E, NCH>(acc, (I & 1) ? k1s : k0s, qf, lane);
             switch (w) {
             case 0: stats_update<0>(acc, rr, c, lane); break;
             case 1: stats_update<1>(acc, rr, c, lane); break;
@@ -1116,7 +1143,6 @@ template <> __device__ __forceinline__ uint32_t pack16<KF16>(float a, float b)
 // 4e + q (e = 0..3) address, as its elements e = 0..3. Rows past T are cut by
 // the size of the tile's buffer resource, chunks past the head by an
 // out-of-range offset; both read zero.
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -1149,15 +1175,6 @@ __device__ __forceinline__ void d16_init(DStage16<NCH> &st, int w, int lane, uin
     }
 }
 
-// A buffer resource over `rows` rows of pitch ldb from base: loads past them read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_rows(const char *base, uint32_t rows, uint32_t ldb)
-{
-    // Uniform, and visibly so (a saturating subtract for rows would otherwise
-    // put the size in a vector register and each load in a waterfall loop).
-    const uint64_t n = (uint64_t)rows * ldb;
-    const int size = __builtin_amdgcn_readfirstlane(n < 0x7FFFFFFFu ? (int)n : 0x7FFFFFFF);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, size, 0x00020000);
-}
 
 template <int NCH>
 __device__ __forceinline__ void d16_fetch(const DStage16<NCH> &st, char *kdst, char *vdst, const char *kb0,
