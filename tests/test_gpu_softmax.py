@@ -103,6 +103,23 @@ def check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype="f32", label="", o
 SM_T = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_softmax_default_launch(dtype):
+    """Without stats or fused, the binding takes the two launches for fp32
+    inputs and the fused launch for 16-bit inputs: outputs and statistics
+    equal those of that explicit choice bit for bit."""
+    B, T, NH, HS = 2, 200, 3, 64
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=17)
+    d = to_device(qkv, dtype).view(B, T, -1)
+    case(f"softmax default launch {dtype}")
+    want = dtype != "f32"
+    got = cas.causal_softmax(d, NH, "prob")
+    ref = cas.causal_softmax(d, NH, "prob", fused=want)
+    torch.cuda.synchronize()
+    for g, r, name in zip(got, ref, ("probabilities", "row_max", "row_logsum")):
+        assert torch.equal(g.view(torch.int32), r.view(torch.int32)), f"{name} differ from fused={want}"
+
+
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("HS", [8, 16, 40, 64])
 @pytest.mark.parametrize("T", SM_T)
