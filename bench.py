@@ -61,7 +61,7 @@ def device_tensor(a, dtype):
 KERNEL_SOURCES = {
     "trimul_f32_B8_T1024_NH12_HS64": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip",
                                       "trimul_f32.hip", "trimul_kernel.hpp"],
-    "dense_f32_960x1024x770": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip"],
+    "dense_f32_960x1024x770": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip", "gemm_nt_direct.hip"],
     "dense_bf16_4096": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "gemm_nt.hip", "gemm_nt_wide.hip"],
     "trimul_bf16_B4_T4096_NH25_HS64": ["cas_api.hip", "launch.hpp", "tile_engine.hpp", "trimul.hip",
                                        "trimul_bf16.hip", "trimul_kernel.hpp"],
@@ -343,7 +343,10 @@ def local_padding_ab(steps: int):
     MFMA loop (CAS_VARIANT=predicated), on the 1024-wide layer, on the
     DietCode shape (H = 2304), and on DietCode's BatchMatmulNT heads
     (192 x 120 x 120 x 64, full-size LDS tiles at T = 120); plus the causal
-    scores of those heads (ragged T)."""
+    scores of those heads (ragged T). Both arms run the register-ring engine
+    (CAS_GEMM_F32=ring), the one kernel that has both forms; the default
+    fp32 path, loads straight into LDS (local padding only), is timed beside
+    them as "direct"."""
     import torch
 
     from causal_attention_score_amd import synth
@@ -353,15 +356,18 @@ def local_padding_ab(steps: int):
         log(f"local-padding A/B on {name}")
         p = Part(wl)
         res = {}
-        for variant in ("local_padding", "predicated"):
+        for variant in ("local_padding", "predicated", "direct"):
+            os.environ.pop("CAS_VARIANT", None)
+            os.environ.pop("CAS_GEMM_F32", None)
+            if variant != "direct":
+                os.environ["CAS_GEMM_F32"] = "ring"
             if variant == "predicated":
                 os.environ["CAS_VARIANT"] = "predicated"
-            else:
-                os.environ.pop("CAS_VARIANT", None)
             _, (ms,), _, (md,), _ = time_parts([p], steps, 3, SUB_SETTLE_S)
             res[variant] = {"avg_launch_us": round(ms * 1e3, 2), "median_launch_us": round(md * 1e3, 2),
                             "useful_tflops": round(wl.useful_flops() / (ms * 1e-3) / 1e12, 2)}
         os.environ.pop("CAS_VARIANT", None)
+        os.environ.pop("CAS_GEMM_F32", None)
         res["speedup"] = round(res["predicated"]["avg_launch_us"] / res["local_padding"]["avg_launch_us"], 3)
         if name.endswith("2304x770"):
             res["pages_context"] = ("DietCode on NVIDIA RTX: 0.98 vs 11.6 TFLOP/s (3090), 0.43 vs 5.27 (2080 Ti), "

@@ -11,6 +11,9 @@
 // walked in groups of GROUP_M tile rows so that neighbouring workgroups share
 // X and W panels in L2.
 #include "launch.hpp"
+
+#include <cstdlib>
+#include <cstring>
 #include "tile_engine.hpp"
 
 namespace cas {
@@ -159,6 +162,12 @@ hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStr
     if (elem != E_F32 && !a.predicated && a.batch == 1 && gemm_wide_fits(a, 2, vec) &&
         (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256)))
         return launch_gemm_wide(a, elem, s);
+    // fp32 on 64 x 64 tiles: loads straight into LDS where the rows allow
+    // (CAS_GEMM_F32=ring keeps the register-ring engine, e.g. to compare).
+    if (elem == E_F32 && pick_tile(a, tile) == GEMM_TILE_64 && gemm_direct_fits(a, elem, vec)) {
+        const char *v = std::getenv("CAS_GEMM_F32");
+        if (!v || std::strcmp(v, "ring") != 0) return launch_gemm_direct(a, s);
+    }
     switch (elem) {
     case E_F32: return launch_elem<KF32>(a, vec, tile, s);
     case E_BF16: return launch_elem<KBF16>(a, vec, tile, s);

@@ -69,6 +69,11 @@ bool gemm_wide_fits(const GemmArgs &a, int es, int vec);
 int64_t gemm_wide_workgroups(const GemmArgs &a);
 hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s);
 
+// 64 x 64 fp32 tiles with loads straight into LDS (gemm_nt_direct.hip): rows
+// and bases 8-byte aligned (vec >= 2), not predicated.
+bool gemm_direct_fits(const GemmArgs &a, int elem, int vec);
+hipError_t launch_gemm_direct(const GemmArgs &a, hipStream_t s);
+
 hipError_t launch_trimul(const TrimulArgs &a, int elem, int vec, hipStream_t s);
 int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);
 

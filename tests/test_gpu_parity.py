@@ -199,6 +199,41 @@ def test_gemm_strided_misaligned(orc, dtype):
     assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
 
 
+# fp32 on 64 x 64 tiles with loads straight into LDS (rows 8-byte aligned):
+# K below, at and just past one 32-float chunk, K % 4 == 2 (a 16-byte piece
+# straddles K and reads past the row), and row pitches whose padding holds
+# NaN, which must not reach the products. The register-ring engine
+# (CAS_GEMM_F32=ring) forms the same products in the same order: bit for bit.
+DIRECT_SHAPES = [(1, 1, 2), (70, 90, 98), (64, 64, 32), (65, 63, 34), (130, 200, 96), (257, 255, 770),
+                 (40, 300, 1026)]
+
+
+@pytest.mark.parametrize("shape", DIRECT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_direct_nan_padding_and_ring(orc, monkeypatch, shape):
+    M, N, K = shape
+    ldx, ldw = K + 2, K + 6  # even pitches: 8-byte-aligned rows
+    g = np.random.default_rng(M * 31 + K)
+    Xf = np.full(M * ldx, np.nan, np.float32)
+    Wf = np.full(N * ldw, np.nan, np.float32)
+    Xf.reshape(M, ldx)[:, :K] = g.standard_normal((M, K))
+    Wf.reshape(N, ldw)[:, :K] = g.standard_normal((N, K))
+    ref, bound = orc.gemm_nt(Xf, Wf, "f32", M=M, N=N, K=K, ldx=ldx, ldw=ldw, ldy=N)
+    x = to_device(Xf, "f32").as_strided((M, K), (ldx, 1))
+    w = to_device(Wf, "f32").as_strided((N, K), (ldw, 1))
+    got = {}
+    for engine in ("direct", "ring"):
+        if engine == "ring":
+            monkeypatch.setenv("CAS_GEMM_F32", "ring")
+        buf, flat = guarded_output(M * N)
+        case(f"gemm fp32 {engine} {shape} NaN pitch padding")
+        cas.gemm_nt(x, w, out=flat.view(M, N))
+        torch.cuda.synchronize()
+        check_guards(buf, M * N)
+        got[engine] = flat.view(M, N).cpu().numpy()
+    assert_close(got["direct"], ref, bound, "f32", f"gemm direct {shape}")
+    assert np.array_equal(got["direct"].view(np.uint32), got["ring"].view(np.uint32)), "direct and ring differ"
+
+
 @pytest.mark.parametrize("tile,ldx", [("64", 8_000_000), ("64", 9_000_000), ("128", 4_000_000), ("128", 4_500_000)])
 def test_gemm_huge_row_pitch(orc, monkeypatch, tile, ldx):
     """Row pitches near the 31-bit offset range: the register-ring loop
