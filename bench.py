@@ -140,7 +140,7 @@ class Part:
             self.cas.trimul_causal(self.qkv, self.NH, out=self.out)
 
 
-def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
+def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0, per_launch: bool = True):
     """Warm up, then time `steps` steps (twice with several parts). The
     warm-up is `warmup` steps,
     continued (untimed) until `settle_s` seconds have passed, so the timed
@@ -151,8 +151,10 @@ def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
     on: the per-part times (an event between two launches adds a dispatch gap,
     about 9 us per step for the two-kernel step, so these events stay out of
     the step time). A single part is timed in one pass with an event after
-    every launch. Returns (ms per step, [mean ms per part], wall ms per step,
-    [median ms per part], warm-up steps run)."""
+    every launch, or with per_launch=False like a step (events at the two
+    ends only; the per-part figures are then the step's). Returns (ms per
+    step, [mean ms per part], wall ms per step, [median ms per part], warm-up
+    steps run)."""
     import torch
     stream = torch.cuda.current_stream()
     t_warm = time.perf_counter()
@@ -166,7 +168,7 @@ def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
-    single = len(parts) == 1
+    single = len(parts) == 1 and per_launch
     t0 = time.perf_counter()
     start.record(stream)
     for s in range(steps):
@@ -180,6 +182,8 @@ def time_parts(parts, steps: int, warmup: int, settle_s: float = 0.0):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     total = start.elapsed_time(stop)
+    if len(parts) == 1 and not per_launch:
+        return total / steps, [total / steps], wall / steps, [total / steps], done
     if not single:
         for s in range(steps):
             ev[s][0].record(stream)
@@ -291,13 +295,16 @@ def softmax_timings(steps: int):
         n = max(5, steps // (10 if T > 2048 else 2))
         ms_step, (ms_st, ms_rows), _, _, _ = time_parts([sp.stats, sp.rows], n, 2, SUB_SETTLE_S)
         _, (ms_fused,), _, _, _ = time_parts([sp.fused], n, 2, SUB_SETTLE_S)
+        # the fused launch timed like the two-launch step (events at the ends
+        # only), for a like-for-like comparison of the two paths
+        ms_fused_step, _, _, _, _ = time_parts([sp.fused], n, 2, SUB_SETTLE_S, per_launch=False)
         ob = 4 if od == "f32" else 2
         rows_bytes = wl.algorithmic_bytes(ob) + 8 * B * NH * T
         st_bytes = wl.algorithmic_bytes(0) + 8 * B * NH * T
         scores = B * NH * T * (T + 1) // 2
         out[key] = {
             "step_us": round(ms_step * 1e3, 2),
-            "fused": {"avg_launch_us": round(ms_fused * 1e3, 2),
+            "fused": {"avg_launch_us": round(ms_fused * 1e3, 2), "step_us": round(ms_fused_step * 1e3, 2),
                       "roofline": {"bound": "hbm", "achieved": round(rows_bytes / (ms_fused * 1e-3) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(rows_bytes / (ms_fused * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
