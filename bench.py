@@ -352,8 +352,8 @@ def local_padding_ab(steps: int):
     (192 x 120 x 120 x 64, full-size LDS tiles at T = 120); plus the causal
     scores of those heads (ragged T). Both arms run the register-ring engine
     (CAS_GEMM_F32=ring), the one kernel that has both forms; the default
-    fp32 path, loads straight into LDS (local padding only), is timed beside
-    them as "direct"."""
+    fp32 path (loads straight into LDS where that kernel applies, local
+    padding only) is timed beside them as "default"."""
     import torch
 
     from causal_attention_score_amd import synth
@@ -363,10 +363,10 @@ def local_padding_ab(steps: int):
         log(f"local-padding A/B on {name}")
         p = Part(wl)
         res = {}
-        for variant in ("local_padding", "predicated", "direct"):
+        for variant in ("local_padding", "predicated", "default"):
             os.environ.pop("CAS_VARIANT", None)
             os.environ.pop("CAS_GEMM_F32", None)
-            if variant != "direct":
+            if variant != "default":
                 os.environ["CAS_GEMM_F32"] = "ring"
             if variant == "predicated":
                 os.environ["CAS_VARIANT"] = "predicated"
