@@ -506,6 +506,7 @@ def main():
               "so one GPU's share is what is measured; --gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from causal_attention_score_amd import synth
@@ -583,6 +584,8 @@ def main():
         "local_padding_ab": ab,
         "wall_ms_per_step": round(wall_ms, 5),
         "device": torch.cuda.get_device_name(0),
+        # the seeded input streams (numpy PCG64) are not guaranteed stable across numpy versions
+        "numpy": np.__version__,
         "sources_digest": {k: kernel_sources_digest(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
