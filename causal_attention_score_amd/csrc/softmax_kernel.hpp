@@ -698,8 +698,12 @@ struct PWalk {
     }
 };
 
-template <class E, class O, class EP>
-__global__ void __launch_bounds__(tri::SUPER_THREADS)
+// SPLIT: four more waves (1024 threads). The statistics items go to waves
+// 12 .. 15 and the compute waves keep the output items, so the two run side
+// by side on each SIMD instead of one after the other in one wave; the
+// arithmetic and its order are unchanged.
+template <class E, class O, class EP, bool SPLIT>
+__global__ void __launch_bounds__(SPLIT ? tri::SUPER_THREADS + tri::NCOMP_THREADS : tri::SUPER_THREADS)
 softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float *__restrict__ row_max,
                     float *__restrict__ row_logsum, uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t P,
                     uint32_t nt, float scale, int vec_store)
@@ -715,7 +719,7 @@ softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float 
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int role = wave / NCOMP; // 0 compute, 1 store, 2 loader
+    const int role = wave / NCOMP; // 0 compute, 1 store, 2 loader, 3 statistics (SPLIT)
     const int slot = wave % NCOMP;
     const int sa = slot >> 1, sb = slot & 1;
     char *my_out = outb + slot * OUT_BYTES;
@@ -776,13 +780,18 @@ softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float 
             if (nout) stage_store<NCH>(so, opb_out, cl, q_out);
             lds_barrier(); // Y: operand rows of the next step in LDS
         }
-    } else if (role == 0) {
+    } else if (role == 0 || role == 3) {
+        // Without SPLIT the compute waves take both items of a step; with it
+        // role 0 takes the output item and role 3 the statistics item, each
+        // in a loop of its own (so neither holds the other's invariants).
+        auto compute_loop = [&](auto with_st, auto with_out) {
+        constexpr bool DO_ST = decltype(with_st)::value, DO_OUT = decltype(with_out)::value;
         const int r32 = lane & 31;
         Run2 rn;
         float mx[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
         lds_barrier();
         while (cur.valid()) {
-            const bool has_st = cur.has_st, has_out = cur.has_out;
+            const bool has_st = DO_ST && cur.has_st, has_out = DO_OUT && cur.has_out;
             const Super ss = cur.st_item(), so = cur.out_item();
             const bool first_out = has_out && cur.oJ == 0, last_stats = has_st && cur.sJ == cur.sI;
             const uint32_t opar = cur.oi & 1, spar = cur.si & 1;
@@ -853,6 +862,15 @@ softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float 
             }
             lds_barrier(); // Y: tile in LDS / partial statistics in LDS
         }
+        };
+        using yes = std::true_type;
+        using no = std::false_type;
+        if constexpr (SPLIT) {
+            if (role == 3) compute_loop(yes{}, no{});
+            else compute_loop(no{}, yes{});
+        } else {
+            compute_loop(yes{}, yes{});
+        }
     } else {
         lds_barrier();
         Tile pm; // mirror of the previous output step, second half pending
@@ -899,29 +917,38 @@ softmax_pipe_kernel(const char *__restrict__ qkv, char *__restrict__ out, float 
 template <class E, int NCH, class O, class EP> hipError_t launch_fused(const TrimulArgs &a, hipStream_t s)
 {
     auto kern = softmax_fused_kernel<E, NCH, O, EP>;
-    static ResidentSlots resident, resident_pipe;
+    static ResidentSlots resident, resident_pipe, resident_split;
     ResidentSlots *rs = &resident;
+    int threads = tri::SUPER_THREADS;
     const int64_t nt = (a.T + ST - 1) / ST;
     if constexpr (E::ES == 2 && NCH == 8) {
         // The pipelined walk from 16 query blocks per plane on (measured,
         // outputs bit-identical: bf16 B4 T4096 probabilities to bf16 727 ->
         // 715 us, log-probabilities 737 -> 696 us, to fp32 1195 -> 1176 us;
         // at B8 T1024, 8 blocks, 54.7 -> 57.0 us, so the plain walk there).
-        // CAS_SOFTMAX_FUSED=plain|pipe overrides the choice (tuning).
+        // With fp32 output the walk's statistics items go to waves of their
+        // own (SPLIT: 1192.7 -> 1149.8 us, bit-identical); with 16-bit output
+        // the two time alike (712.6 / 716.5 us), so the 768-thread kernel.
+        // CAS_SOFTMAX_FUSED=plain|pipe|split overrides the choice (tuning).
         const char *env = std::getenv("CAS_SOFTMAX_FUSED");
         const bool pipe = env && !std::strcmp(env, "pipe") ? true : env && !std::strcmp(env, "plain") ? false : nt >= 16;
-        if (pipe) {
-            kern = softmax_pipe_kernel<E, O, EP>;
+        const bool split = env ? !std::strcmp(env, "split") : pipe && std::is_same<O, tri::OF32>::value;
+        if (split) {
+            kern = softmax_pipe_kernel<E, O, EP, true>;
+            rs = &resident_split;
+            threads = tri::SUPER_THREADS + tri::NCOMP_THREADS;
+        } else if (pipe) {
+            kern = softmax_pipe_kernel<E, O, EP, false>;
             rs = &resident_pipe;
         }
     }
     const int64_t P = a.B * a.NH;
     // Persistent grid; no more workgroups than row blocks (each XCD's share).
-    int64_t grid = resident_slots(*rs, kern, tri::SUPER_THREADS);
+    int64_t grid = resident_slots(*rs, kern, threads);
     const int64_t blocks = P * nt;
     if (grid > 8 * ((blocks + 7) / 8)) grid = 8 * ((blocks + 7) / 8);
     if (grid < 8) grid = 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(tri::SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, s, (const char *)a.qkv, (char *)a.out,
                        const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)P, (uint32_t)nt, a.scale,
                        (int)a.vec_store);

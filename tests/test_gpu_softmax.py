@@ -160,17 +160,22 @@ def test_softmax_ragged_16bit(orc, launch, T, HS, dtype, mode):
 PIPE_SHAPES = [(1, 1, 1, 64), (2, 65, 3, 64), (1, 300, 2, 40), (3, 1100, 2, 16), (2, 2049, 1, 64)]
 
 
+@pytest.mark.parametrize("walk", ["pipe", "split"])
 @pytest.mark.parametrize("out_dtype", ["same", "f32"])
 @pytest.mark.parametrize("mode", ["prob", "log"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", PIPE_SHAPES, ids=lambda s: "B%dT%dNH%dHS%d" % s)
-def test_softmax_fused_pipelined_walk(orc, monkeypatch, shape, dtype, mode, out_dtype):
+def test_softmax_fused_pipelined_walk(orc, monkeypatch, shape, dtype, mode, out_dtype, walk):
+    """The pipelined walk (statistics of the next query block beside the
+    outputs of the current one), in the compute waves themselves ("pipe") or
+    on waves of their own ("split"): against the oracle, and bit for bit
+    against the plain walk."""
     B, T, NH, HS = shape
     od = dtype if out_dtype == "same" else out_dtype
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 13 + HS)
-    monkeypatch.setenv("CAS_SOFTMAX_FUSED", "pipe")
-    check_case(orc, qkv, dtype, B, T, NH, HS, mode, od, label="pipe walk", launch="fused")
-    got_p = run_softmax(qkv, dtype, B, T, NH, HS, mode, od, "pipe walk", launch="fused")
+    monkeypatch.setenv("CAS_SOFTMAX_FUSED", walk)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, od, label=f"{walk} walk", launch="fused")
+    got_p = run_softmax(qkv, dtype, B, T, NH, HS, mode, od, f"{walk} walk", launch="fused")
     monkeypatch.setenv("CAS_SOFTMAX_FUSED", "plain")
     got_q = run_softmax(qkv, dtype, B, T, NH, HS, mode, od, "plain walk", launch="fused")
     for a, b in zip(got_p, got_q):
