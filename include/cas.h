@@ -33,6 +33,13 @@
  *   - Any alignment is accepted (the softmax and attention: elements at their
  *     natural alignment); 16-byte aligned bases and pitches select wider loads
  *     and stores, with the same results.
+ *   - Kernel variants are chosen by shape, dtype and alignment. Environment
+ *     variables read at each call override the choice for tests and tuning:
+ *     CAS_GEMM_TILE, CAS_GEMM_F32, CAS_GEMM_WIDE, CAS_VARIANT (gemm_nt and
+ *     batch_matmul_nt), CAS_TRIMUL_KERNEL, CAS_TRIMUL_PASS (trimul_causal and
+ *     the softmax rows) and CAS_SOFTMAX_FUSED (cas_causal_softmax_fused).
+ *     Every variant meets the same accuracy bounds; those with another
+ *     accumulation order may differ from the default in the last bits.
  */
 #ifndef CAS_H
 #define CAS_H
