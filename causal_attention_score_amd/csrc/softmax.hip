@@ -21,6 +21,13 @@ bool softmax_fits(int64_t T, int64_t HS, int es, int vec)
     return vec * es >= 16 && HS * es <= 256 && T < (int64_t(1) << 22);
 }
 
+bool stats_fits(int64_t T, int64_t HS, int es, int vec)
+{
+    // The row-statistics and attention kernels also take fp32 heads of up to
+    // 512 bytes (32 pieces per row).
+    return softmax_fits(T, HS, es, vec) || (es == 4 && vec * es >= 16 && HS * es <= 512 && T < (int64_t(1) << 22));
+}
+
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH)
 {
     const int64_t nt = (T + 127) / 128; // 128-row query blocks, one per workgroup

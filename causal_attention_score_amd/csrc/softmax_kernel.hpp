@@ -987,6 +987,9 @@ template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a,
 template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStream_t s)
 {
     if (a.HS * E::ES <= 128) return launch_row_stats_nch<E, 8>(a, s);
+    if constexpr (std::is_same<E, KF32>::value) { // fp32 heads of 257 .. 512 bytes
+        if (a.HS * E::ES > 256) return launch_row_stats_nch<E, 32>(a, s);
+    }
     return launch_row_stats_nch<E, 16>(a, s);
 }
 
@@ -1033,7 +1036,10 @@ template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode,
 //    read back through the LDS transpose read).
 // ---------------------------------------------------------------------------
 constexpr int AKT = 64;            // keys per attention step
-constexpr int AV_PITCH = 256 + 32; // LDS bytes per V row (HS * 4 <= 256)
+// LDS bytes per fp32 V row: the head row (at least 256 bytes) plus 32, so
+// that rows 4 apart (the two lane halves of a P V operand read) start 32
+// banks apart.
+template <int NCH> constexpr int av_pitch() { return (NCH * 16 > 256 ? NCH * 16 : 256) + 32; }
 
 template <int NCH> struct AStage {
     u32x4 k[NCH / 4], v[NCH / 4];
@@ -1069,7 +1075,7 @@ template <int NCH> __device__ __forceinline__ void a_store(const AStage<NCH> &st
     for (int q = 0; q < NCH / 4; ++q) {
         const uint32_t r = (uint32_t)(q * RPJ) + r0;
         *reinterpret_cast<u32x4 *>(kbuf + r * (NCH * 16) + kswz<NCH>(r, c)) = st.k[q];
-        *reinterpret_cast<u32x4 *>(vbuf + r * AV_PITCH + c * 16) = st.v[q];
+        *reinterpret_cast<u32x4 *>(vbuf + r * av_pitch<NCH>() + c * 16) = st.v[q];
     }
 }
 
@@ -1127,7 +1133,7 @@ __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, co
             const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
-                const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
+                const float v = *reinterpret_cast<const float *>(vbuf + key * av_pitch<NCH>() + (32u * nb + r32) * 4u);
                 yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[b][j], v, yacc[nb], 0, 0, 0);
             }
         }
@@ -1282,7 +1288,7 @@ template <class E, int NCH> struct AttnCfg {
     static constexpr bool F32 = std::is_same<E, KF32>::value;
     static constexpr int ES = F32 ? 4 : 2;
     static constexpr int NBV = NCH * 16 / ES / 32; // 32-column blocks of the head (HS * ES <= NCH * 16 bytes)
-    static constexpr int VBYTES = AKT * AV_PITCH; // one fp32 V stage in LDS (16-bit: AKT * NCH * 16, as K)
+    static constexpr int VBYTES = AKT * av_pitch<NCH>(); // one fp32 V stage in LDS (16-bit: AKT * NCH * 16, as K)
     // Workgroups per CU the registers must allow (LDS allows more). 16-bit,
     // head <= 128 bytes: four, at 128 VGPRs, measured faster than three.
     static constexpr int MIN_WG = (!F32 && NCH == 8) ? 4 : 1;
@@ -1414,6 +1420,9 @@ template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a,
 template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStream_t s)
 {
     if (a.HS * AttnCfg<E, 8>::ES <= 128) return launch_attention_nch<E, 8>(a, s);
+    if constexpr (std::is_same<E, KF32>::value) { // fp32 heads of 257 .. 512 bytes
+        if (a.HS * E::ES > 256) return launch_attention_nch<E, 32>(a, s);
+    }
     return launch_attention_nch<E, 16>(a, s);
 }
 
@@ -1510,7 +1519,7 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
             const uint32_t key = 32u * b + 8u * (j >> 2) + 4u * h + (uint32_t)(j & 3);
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
-                const float v = *reinterpret_cast<const float *>(vbuf + key * AV_PITCH + (32u * nb + r32) * 4u);
+                const float v = *reinterpret_cast<const float *>(vbuf + key * av_pitch<NCH>() + (32u * nb + r32) * 4u);
                 yacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, s[b][j], yacc[nb], 0, 0, 0);
             }
         }
@@ -1717,8 +1726,13 @@ template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, 
                                const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (float *)a.out,
                                (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0,
                                a.scale, (int)a.vec_store);
-        else
+        else if (a.HS * AttnCfg<E, 8>::ES <= 256)
             hipLaunchKernelGGL((attention_online_kernel<E, 16>), grid, dim3(STATS_THREADS), 0, s,
+                               (const char *)a.qkv, const_cast<float *>(a.row_max),
+                               const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
+                               (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+        else if constexpr (std::is_same<E, KF32>::value) // fp32 heads of 257 .. 512 bytes
+            hipLaunchKernelGGL((attention_online_kernel<E, 32>), grid, dim3(STATS_THREADS), 0, s,
                                (const char *)a.qkv, const_cast<float *>(a.row_max),
                                const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
                                (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);

@@ -670,9 +670,12 @@ def test_workload_attention_fused_bf16_full_size(orc):
 #
 # Heads whose rows do not split into 16-byte pieces (HS = 3 and 5 in fp32,
 # 12 in binary16, a base one element off alignment) or exceed 256 bytes
-# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels.
+# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels; fp32
+# heads of up to 512 bytes in 16-byte pieces (HS = 80) take the fast row
+# statistics and attention kernels (32 pieces per row), tested below too.
 
 GENERAL = [("f32", 3), ("f32", 5), ("f32", 80), ("bf16", 136), ("f16", 12), ("bf16", 3)]
+GENERAL_ATT = [g for g in GENERAL if g != ("f32", 80)]
 GENERAL_T = [1, 33, 64, 100, 300]
 
 
@@ -707,7 +710,7 @@ def test_softmax_misaligned_base(orc, launch, dtype):
 
 
 @pytest.mark.parametrize("T", GENERAL_T)
-@pytest.mark.parametrize("dtype,HS", GENERAL, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,HS", GENERAL_ATT, ids=lambda v: str(v))
 def test_attention_general_shapes(orc, dtype, HS, T):
     """Both attention paths on general shapes: the two-pass launches, and the
     one-launch entry point, which there computes the statistics first (two
@@ -722,6 +725,28 @@ def test_attention_general_shapes(orc, dtype, HS, T):
     assert np.array_equal(mx.view(np.uint32), mx2.cpu().numpy().view(np.uint32)), "row_max differs"
     assert np.array_equal(ls.view(np.uint32), ls2.cpu().numpy().view(np.uint32)), "row_logsum differs"
     check_attention(orc, qkv, dtype, B, T, NH, HS, "general one launch", y=y)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 300])
+@pytest.mark.parametrize("HS", [68, 80, 128])
+def test_attention_wide_heads_f32(orc, HS, T):
+    """fp32 heads of 257 .. 512 bytes (32 pieces per row): the two-pass
+    attention (statistics launch, then y) and the single pass, on the fast
+    kernels; row maxima bit for bit against the statistics launch."""
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 37 + HS)
+    check_attention(orc, qkv, "f32", B, T, NH, HS, "wide heads two-pass")
+    check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "wide heads")
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_wide_heads_f32(orc, launch):
+    """fp32 HS = 128: the fast statistics launch beside the general softmax
+    rows (two launches), and the general fused launch."""
+    B, T, NH, HS = 2, 200, 2, 128
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=41)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="wide heads", launch=launch)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
