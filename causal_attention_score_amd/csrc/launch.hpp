@@ -81,8 +81,8 @@ int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);
 // then the softmax rows (mode 0 log-probabilities, 1 probabilities) into
 // a.out. Both need softmax_fits(); vec as for launch_trimul.
 bool softmax_fits(int64_t T, int64_t HS, int es, int vec);
-// The row statistics and the attention output: softmax_fits(), or fp32 heads
-// of up to 512 bytes in 16-byte pieces.
+// The row statistics and the attention output: softmax_fits(), or heads of up
+// to 512 bytes in 16-byte pieces.
 bool stats_fits(int64_t T, int64_t HS, int es, int vec);
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH);
 hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
@@ -99,6 +99,10 @@ hipError_t launch_attention_f16(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_attention_online_f32(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_attention_online_bf16(const TrimulArgs &a, hipStream_t s);
 hipError_t launch_attention_online_f16(const TrimulArgs &a, hipStream_t s);
+// 16-bit heads of 257 .. 512 bytes (softmax_wide16.hip), elem E_BF16 or E_F16.
+hipError_t launch_row_stats_wide16(const TrimulArgs &a, int elem, hipStream_t s);
+hipError_t launch_attention_wide16(const TrimulArgs &a, int elem, hipStream_t s);
+hipError_t launch_attention_online_wide16(const TrimulArgs &a, int elem, hipStream_t s);
 
 // General shapes (softmax_general.hip): heads whose rows do not split into
 // 16-byte pieces or exceed 256 bytes, up to general_softmax_fits(). The same

@@ -23,9 +23,9 @@ bool softmax_fits(int64_t T, int64_t HS, int es, int vec)
 
 bool stats_fits(int64_t T, int64_t HS, int es, int vec)
 {
-    // The row-statistics and attention kernels also take fp32 heads of up to
-    // 512 bytes (32 pieces per row).
-    return softmax_fits(T, HS, es, vec) || (es == 4 && vec * es >= 16 && HS * es <= 512 && T < (int64_t(1) << 22));
+    // The row-statistics and attention kernels also take heads of up to 512
+    // bytes (32 pieces per row).
+    return softmax_fits(T, HS, es, vec) || (vec * es >= 16 && HS * es <= 512 && T < (int64_t(1) << 22));
 }
 
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH)

@@ -987,8 +987,9 @@ template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a,
 template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStream_t s)
 {
     if (a.HS * E::ES <= 128) return launch_row_stats_nch<E, 8>(a, s);
-    if constexpr (std::is_same<E, KF32>::value) { // fp32 heads of 257 .. 512 bytes
-        if (a.HS * E::ES > 256) return launch_row_stats_nch<E, 32>(a, s);
+    if (a.HS * E::ES > 256) { // heads of 257 .. 512 bytes
+        if constexpr (std::is_same<E, KF32>::value) return launch_row_stats_nch<E, 32>(a, s);
+        else return launch_row_stats_wide16(a, std::is_same<E, KBF16>::value ? E_BF16 : E_F16, s);
     }
     return launch_row_stats_nch<E, 16>(a, s);
 }
@@ -1185,7 +1186,8 @@ template <int NCH> __device__ __forceinline__ uint32_t vswz(uint32_t r)
     // bytes per 16 lanes; with these chunk XORs the rows of either set fall in
     // distinct banks (256 bytes of banks, rows of NCH * 16 bytes).
     if constexpr (NCH == 8) return 2u * (r & 3u);
-    else return (0xCA60u >> (4u * (r & 3u))) & 15u;
+    else if constexpr (NCH == 16) return (0xCA60u >> (4u * (r & 3u))) & 15u;
+    else return 4u * (r & 3u); // 512-byte rows: the four rows' 64-byte groups at 0, 64, 128, 192 bytes
 }
 
 // Per lane, the offset within the tile's rows of each of its NCH / 2 loads:
@@ -1420,8 +1422,9 @@ template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a,
 template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStream_t s)
 {
     if (a.HS * AttnCfg<E, 8>::ES <= 128) return launch_attention_nch<E, 8>(a, s);
-    if constexpr (std::is_same<E, KF32>::value) { // fp32 heads of 257 .. 512 bytes
-        if (a.HS * E::ES > 256) return launch_attention_nch<E, 32>(a, s);
+    if (a.HS * E::ES > 256) { // heads of 257 .. 512 bytes
+        if constexpr (std::is_same<E, KF32>::value) return launch_attention_nch<E, 32>(a, s);
+        else return launch_attention_wide16(a, std::is_same<E, KBF16>::value ? E_BF16 : E_F16, s);
     }
     return launch_attention_nch<E, 16>(a, s);
 }
@@ -1720,6 +1723,10 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
 // a.vec_store), the statistics into a.row_max / a.row_logsum.
 template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, hipStream_t s)
 {
+    if constexpr (!std::is_same<E, KF32>::value) { // 16-bit heads of 257 .. 512 bytes
+        if (a.HS * E::ES > 256)
+            return launch_attention_online_wide16(a, std::is_same<E, KBF16>::value ? E_BF16 : E_F16, s);
+    }
     return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
         if (a.HS * AttnCfg<E, 8>::ES <= 128)
             hipLaunchKernelGGL((attention_online_kernel<E, 8>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
@@ -1736,6 +1743,28 @@ template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, 
                                (const char *)a.qkv, const_cast<float *>(a.row_max),
                                const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
                                (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+    });
+}
+
+// 16-bit heads of 257 .. 512 bytes (32 pieces per row): the kernels of the
+// launchers above, compiled in their own translation unit
+// (softmax_wide16.hip) without the VGPR-only MFMA form, so that their 8 x 16
+// output accumulators can live in the accumulation registers.
+template <class E> hipError_t launch_row_stats_wide16_impl(const TrimulArgs &a, hipStream_t s)
+{
+    return launch_row_stats_nch<E, 32>(a, s);
+}
+template <class E> hipError_t launch_attention_wide16_impl(const TrimulArgs &a, hipStream_t s)
+{
+    return launch_attention_nch<E, 32>(a, s);
+}
+template <class E> hipError_t launch_attention_online_wide16_impl(const TrimulArgs &a, hipStream_t s)
+{
+    return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
+        hipLaunchKernelGGL((attention_online_kernel<E, 32>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+                           const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (float *)a.out,
+                           (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale,
+                           (int)a.vec_store);
     });
 }
 

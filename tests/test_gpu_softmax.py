@@ -670,12 +670,13 @@ def test_workload_attention_fused_bf16_full_size(orc):
 #
 # Heads whose rows do not split into 16-byte pieces (HS = 3 and 5 in fp32,
 # 12 in binary16, a base one element off alignment) or exceed 256 bytes
-# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels; fp32
-# heads of up to 512 bytes in 16-byte pieces (HS = 80) take the fast row
-# statistics and attention kernels (32 pieces per row), tested below too.
+# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels; heads
+# of up to 512 bytes in 16-byte pieces (fp32 HS = 80, bf16 HS = 136) take the
+# fast row statistics and attention kernels (32 pieces per row), tested below
+# too, and heads over 512 bytes (fp32 HS = 160) stay on the general kernels.
 
 GENERAL = [("f32", 3), ("f32", 5), ("f32", 80), ("bf16", 136), ("f16", 12), ("bf16", 3)]
-GENERAL_ATT = [g for g in GENERAL if g != ("f32", 80)]
+GENERAL_ATT = [g for g in GENERAL if g not in (("f32", 80), ("bf16", 136))] + [("f32", 160)]
 GENERAL_T = [1, 33, 64, 100, 300]
 
 
@@ -737,6 +738,20 @@ def test_attention_wide_heads_f32(orc, HS, T):
     qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=T * 37 + HS)
     check_attention(orc, qkv, "f32", B, T, NH, HS, "wide heads two-pass")
     check_attention_fused(orc, qkv, "f32", B, T, NH, HS, "wide heads")
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 300])
+@pytest.mark.parametrize("HS", [136, 192, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attention_wide_heads_16bit(orc, dtype, HS, T):
+    """16-bit heads of 257 .. 512 bytes (32 pieces per row, kernels built with
+    their output accumulators in the accumulation registers): both attention
+    paths against the oracle, row maxima bit for bit against the statistics
+    launch."""
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 43 + HS)
+    check_attention(orc, qkv, dtype, B, T, NH, HS, "wide heads two-pass")
+    check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "wide heads")
 
 
 @pytest.mark.parametrize("launch", LAUNCHES)
