@@ -238,11 +238,10 @@ namespace {
 // byte extents of qkv (inb), of one statistics array (stb) and of the output
 // (outb, for out_bytes per element), the 16-byte piece width of the QKV rows
 // (vec), and which kernels serve the shape: the fast ones, or (*general) the
-// general-shape ones; outside both domains CAS_ERR_UNSUPPORTED. wide: the
-// entry point's fast kernels also take fp32 heads of up to 512 bytes (the
-// row statistics and the attention output), else heads of up to 256.
+// general-shape ones; outside both domains CAS_ERR_UNSUPPORTED. The fast
+// kernels take heads of up to 512 bytes in 16-byte pieces.
 int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH, cas_dtype in_dtype, int out_bytes,
-                   int64_t *inb, int64_t *stb, int64_t *outb, int *vec, bool *general, bool wide = false)
+                   int64_t *inb, int64_t *stb, int64_t *outb, int *vec, bool *general)
 {
     if (B < 0 || T < 0 || C < 0 || NH < 0) return CAS_ERR_SHAPE;
     if (B == 0 || T == 0 || NH == 0) return 1; // nothing to do
@@ -266,7 +265,7 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     // the fast launches, split by query block, keep a grid below 2^32
     // work-items (256 per workgroup) while the B * NH planes of one block fit
     // in one grid
-    const bool fast = wide ? cas::stats_fits(T, HS, es, *vec) : cas::softmax_fits(T, HS, es, *vec);
+    const bool fast = cas::softmax_fits(T, HS, es, *vec);
     *general = !fast || B * NH >= (INT64_C(1) << 23);
     if (*general && !cas::general_softmax_fits(B, T, NH, HS, es, qkv)) return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
@@ -300,7 +299,7 @@ CAS_EXPORT int cas_causal_row_stats(const void *qkv, float *row_max, float *row_
     int64_t inb, stb, outb;
     int vec = 1;
     bool general = false;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general, true);
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum) return CAS_ERR_NULL;
@@ -380,7 +379,7 @@ CAS_EXPORT int cas_causal_attention(const void *qkv, const float *row_max, const
     int64_t inb, stb, outb;
     int vec = 1;
     bool general = false;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general, true);
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !row_max || !row_logsum || !y) return CAS_ERR_NULL;
@@ -410,7 +409,7 @@ CAS_EXPORT int cas_causal_attention_fused(const void *qkv, void *y, float *row_m
     int64_t inb, stb, outb;
     int vec = 1;
     bool general = false;
-    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general, true);
+    const int rc = softmax_checks(qkv, B, T, C, NH, in_dtype, 0, &inb, &stb, &outb, &vec, &general);
     if (rc == 1) return CAS_OK;
     if (rc == CAS_ERR_SHAPE) return rc;
     if (!qkv || !y || !row_max || !row_logsum) return CAS_ERR_NULL;

@@ -79,11 +79,9 @@ int64_t trimul_workgroups(int64_t B, int64_t T, int64_t NH);
 
 // Causal softmax (softmax.hip): row statistics into a.row_max / a.row_logsum,
 // then the softmax rows (mode 0 log-probabilities, 1 probabilities) into
-// a.out. Both need softmax_fits(); vec as for launch_trimul.
+// a.out. Both need softmax_fits() (heads of up to 512 bytes in 16-byte
+// pieces); vec as for launch_trimul.
 bool softmax_fits(int64_t T, int64_t HS, int es, int vec);
-// The row statistics and the attention output: softmax_fits(), or heads of up
-// to 512 bytes in 16-byte pieces.
-bool stats_fits(int64_t T, int64_t HS, int es, int vec);
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH);
 hipError_t launch_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
 hipError_t launch_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s);

@@ -16,16 +16,10 @@ hipError_t launch_softmax_fused_f16(const TrimulArgs &a, int mode, hipStream_t s
 
 bool softmax_fits(int64_t T, int64_t HS, int es, int vec)
 {
-    // The super-tile score kernel's domain: rows in 16-byte pieces, heads of
-    // at most 256 bytes, tile offsets within 31-bit buffer ranges.
-    return vec * es >= 16 && HS * es <= 256 && T < (int64_t(1) << 22);
-}
-
-bool stats_fits(int64_t T, int64_t HS, int es, int vec)
-{
-    // The row-statistics and attention kernels also take heads of up to 512
-    // bytes (32 pieces per row).
-    return softmax_fits(T, HS, es, vec) || (vec * es >= 16 && HS * es <= 512 && T < (int64_t(1) << 22));
+    // Rows in 16-byte pieces, heads of at most 512 bytes (the three-role
+    // kernels up to 256, the wide variants and the per-wave tile kernel
+    // above), tile offsets within 31-bit buffer ranges.
+    return vec * es >= 16 && HS * es <= 512 && T < (int64_t(1) << 22);
 }
 
 int64_t row_stats_workgroups(int64_t B, int64_t T, int64_t NH)

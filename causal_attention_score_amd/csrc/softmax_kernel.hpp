@@ -967,8 +967,16 @@ template <class E, class EP> hipError_t launch_fused_ep(const TrimulArgs &a, hip
 
 // Both launches in one (softmax_fused_kernel); statistics written through
 // a.row_max / a.row_logsum, the rows through a.out.
+template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStream_t s);
+template <class E> hipError_t launch_softmax_impl(const TrimulArgs &a, int mode, hipStream_t s);
+
 template <class E> hipError_t launch_softmax_fused_impl(const TrimulArgs &a, int mode, hipStream_t s)
 {
+    if (a.HS * E::ES > 256) { // heads of 257 .. 512 bytes: the statistics launch, then the rows launch
+        const hipError_t e = launch_row_stats_impl<E>(a, s);
+        if (e != hipSuccess) return e;
+        return launch_softmax_impl<E>(a, mode, s);
+    }
     if (mode == 0) return launch_fused_ep<E, tri::EpLog>(a, s);
     return launch_fused_ep<E, tri::EpProb>(a, s);
 }
@@ -994,10 +1002,12 @@ template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStre
     return launch_row_stats_nch<E, 16>(a, s);
 }
 
-// Softmax rows: the three-role score kernel with the softmax epilogue.
+// Softmax rows: the three-role score kernel with the softmax epilogue; heads
+// of 257 .. 512 bytes on the per-wave tile kernel with the same epilogue.
 // mode 0: log-probabilities, 1: probabilities.
 template <class E, class EP> hipError_t launch_softmax_ep(const TrimulArgs &a, hipStream_t s)
 {
+    if (a.HS * E::ES > 256) return tri::launch_tile_ep<E, EP>(a, s);
     const bool narrow = a.HS * E::ES <= 128;
     if (a.out_kind == 1)
         return narrow ? tri::launch_super<E, 8, tri::OBF16, EP>(a, s) : tri::launch_super<E, 16, tri::OBF16, EP>(a, s);

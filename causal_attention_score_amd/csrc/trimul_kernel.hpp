@@ -134,6 +134,7 @@ struct Tile {
     const char *k; // K row s0 of (b, nh)
     char *o;       // out plane (b, nh)
     int64_t t0, s0;
+    int64_t sr;    // index of row t0 in the (B, NH, T) row statistics
     int rl, cl;    // rows / columns of the tile inside the plane (<= 64)
     bool diag;
 };
@@ -153,6 +154,7 @@ __device__ __forceinline__ Tile make_tile(const char *qkv, float *out, int64_t i
     const int64_t C3 = 3 * C;
     tl.t0 = i * TB;
     tl.s0 = j * TB;
+    tl.sr = plane * T + tl.t0;
     tl.q = qkv + ((b * T + tl.t0) * C3 + nh * HS) * es;
     tl.k = qkv + ((b * T + tl.s0) * C3 + C + nh * HS) * es;
     tl.o = reinterpret_cast<char *>(out) + plane * T * T * ob;
@@ -243,24 +245,42 @@ __device__ __forceinline__ void mma_pass(f32x16 (&acc)[2][2], const Operand<U> &
     }
 }
 
-// Scaled, masked tile -> LDS, row-major 64 x 64 fp32.
-__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, bool diag, int lane)
+template <class EP> __device__ __forceinline__ float epilogue(float a, float scale, float mx, float ls);
+
+// Scaled, masked tile -> LDS, row-major 64 x 64 fp32. EP other than the
+// scores: the softmax epilogue of each element, st holding the tile rows'
+// statistics (st[row] the row maximum, st[TB + row] the logsum), and that
+// epilogue's fill right of the diagonal.
+template <class EP = EpScore>
+__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[2][2], char *lds, float scale, bool diag, int lane,
+                                            const float *st = nullptr)
 {
-    const float qnan = __uint_as_float(QNAN_BITS);
+    const float fill = __uint_as_float(fill32<EP>());
     const int c0 = lane & 31, h4 = 4 * (lane >> 5);
     const uint32_t lo = opaque((uint32_t)(h4 * TB + c0) * 4);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = mb * 32 + 8 * (r >> 2) + (r & 3); // uniform part of the row
-                const int row = rr + h4, col = nb * 32 + c0;
-                float v = acc[mb][nb][r] * scale;
-                if (diag && col > row) v = qnan;
-                *reinterpret_cast<float *>(lds + lo + (uint32_t)(rr * TB + nb * 32) * 4) = v;
+        for (int q = 0; q < 4; ++q) {
+            f32x4v mx4 = {}, ls4 = {}; // rows mb*32 + 8q + h4 .. + 3
+            if constexpr (EP::KIND != 0) {
+                mx4 = *reinterpret_cast<const f32x4v *>(st + mb * 32 + 8 * q + h4);
+                ls4 = *reinterpret_cast<const f32x4v *>(st + TB + mb * 32 + 8 * q + h4);
             }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    const int rr = mb * 32 + 8 * q + e; // uniform part of the row
+                    const int row = rr + h4, col = nb * 32 + c0;
+                    float v;
+                    if constexpr (EP::KIND == 0) v = acc[mb][nb][r] * scale;
+                    else v = epilogue<EP>(acc[mb][nb][r], scale, mx4[e], ls4[e]);
+                    if (diag && col > row) v = fill;
+                    *reinterpret_cast<float *>(lds + lo + (uint32_t)(rr * TB + nb * 32) * 4) = v;
+                }
+        }
 }
 
 // LDS tile -> rows [t0, t0+rl) x columns [s0, s0+cl) of the plane. FULL:
@@ -291,11 +311,11 @@ __device__ __forceinline__ void lds_to_out(const char *lds, const Tile &tl, uint
 // NaN over the mirror tile (j, i): rows [s0, s0+cl) x columns [t0, t0+rl).
 // H = 0 or 1 writes only the first or the second half of the mirror's rows,
 // H = -1 all of them.
-template <bool FULL, int H = -1>
+template <bool FULL, int H = -1, class EP = EpScore>
 __device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane, bool vec4)
 {
     constexpr int R0 = H == 1 ? TB / 2 : 0, R1 = H == 0 ? TB / 2 : TB; // mirror rows [R0, R1)
-    const float qnan = __uint_as_float(QNAN_BITS);
+    const float qnan = __uint_as_float(fill32<EP>()); // the scores' NaN, or the softmax fill
     char *dst = tl.o + ((uint64_t)tl.s0 * (T4 / 4) + (uint64_t)tl.t0) * 4;
     if (FULL || vec4) {
         const f32x4v n4 = {qnan, qnan, qnan, qnan};
@@ -325,11 +345,11 @@ __device__ __forceinline__ void lds_to_out16(const char *lds, const Tile &tl, in
     }
 }
 
-template <class O>
+template <class O, class EP = EpScore>
 __device__ __forceinline__ void nan_mirror16(const Tile &tl, int64_t T, int lane)
 {
     for (int s = 0; s < TB; ++s)
-        if (s < tl.cl && lane < tl.rl) st_nt16(tl.o + ((tl.s0 + s) * T + tl.t0 + lane) * 2, O::NAN16);
+        if (s < tl.cl && lane < tl.rl) st_nt16(tl.o + ((tl.s0 + s) * T + tl.t0 + lane) * 2, fill16<O, EP>());
 }
 
 // One step of a compute wave: the P register passes of tile `tl` (operands of
@@ -337,9 +357,15 @@ __device__ __forceinline__ void nan_mirror16(const Tile &tl, int64_t T, int lane
 // pass the first pass of `nx` when has_next -- into the other buffer, then the
 // scaled, masked tile to LDS. Afterwards nx's first pass sits in ops[(SB+P)%2].
 // P == 0: any number of passes, each fetched and then multiplied (no prefetch).
-template <class E, int U, bool VEC16, int P, int SB>
+//
+// Softmax epilogue (EP other than EpScore): mxv / lsv are the statistics of
+// row t0 + lane, loaded before the passes so their latency hides behind the
+// MFMAs; the wave puts them in its slot st (64 maxima, then 64 logsums) for
+// the cross-lane reads of tile_to_lds.
+template <class E, int U, bool VEC16, int P, int SB, class EP = EpScore>
 __device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile &tl, const Tile &nx, bool has_next,
-                                             char *lds, uint32_t ldb, int64_t HS, float scale, int lane)
+                                             char *lds, uint32_t ldb, int64_t HS, float scale, int lane,
+                                             float *st = nullptr, float mxv = 0.f, float lsv = 0.f)
 {
     constexpr int64_t PASS = (int64_t)U * 32 / E::ES;
     f32x16 acc[2][2];
@@ -367,16 +393,29 @@ __device__ __forceinline__ void compute_tile(Operand<U> (&ops)[2][2], const Tile
             mma_pass<E, U>(acc, ops[cur][0], ops[cur][1]);
         }
     }
-    tile_to_lds(acc, lds, scale, tl.diag, lane);
+    if constexpr (EP::KIND != 0) {
+        // One wave writes and reads its slot: LDS keeps a wave's accesses in
+        // order, the fences keep the compiler from moving them.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        st[lane] = mxv;
+        st[TB + lane] = lsv;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    }
+    tile_to_lds<EP>(acc, lds, scale, tl.diag, lane, st);
 }
 
-template <class E, int U, bool VEC16, int P>
+// EP other than EpScore: the causal softmax rows (log-probabilities or
+// probabilities) from the per-row statistics row_max / row_logsum (B, NH, T).
+template <class E, int U, bool VEC16, int P, class EP = EpScore>
 __global__ void __launch_bounds__(NTHREADS)
 trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, int64_t C, int64_t NH, int64_t HS,
-              int64_t L, int64_t items, float scale, int vec_store, int out_kind)
+              int64_t L, int64_t items, float scale, int vec_store, int out_kind, const float *__restrict__ row_max,
+              const float *__restrict__ row_logsum)
 {
     constexpr int ES = E::ES;
+    constexpr bool SM = EP::KIND != 0;
     __shared__ __attribute__((aligned(16))) char lds[NCOMP * 2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float stl[SM ? NCOMP * 2 * TB : 4]; // per compute wave: 64 max, 64 logsum
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -419,10 +458,20 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
                         const bool has_next = m + 1 < steps && nid < hi;
                         const Tile nx = make_tile(qkv, out, has_next ? nid : id, L, T, C, NH, HS, ES);
                         char *buf = my_lds + (m & 1) * TILE_BYTES;
+                        float mxv = 0.f, lsv = 0.f; // statistics of row t0 + lane (softmax)
+                        if constexpr (SM) {
+                            if (lane < tl.rl) {
+                                mxv = row_max[tl.sr + lane];
+                                lsv = row_logsum[tl.sr + lane];
+                            }
+                        }
+                        float *st = stl + (SM ? slot * 2 * TB : 0);
                         if (half == 0 || (P & 1) == 0)
-                            compute_tile<E, U, VEC16, P, 0>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane);
+                            compute_tile<E, U, VEC16, P, 0, EP>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane, st,
+                                                                mxv, lsv);
                         else
-                            compute_tile<E, U, VEC16, P, 1>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane);
+                            compute_tile<E, U, VEC16, P, 1, EP>(ops, tl, nx, has_next, buf, ldb, HS, scale, lane, st,
+                                                                mxv, lsv);
                         tl = nx;
                         id = nid;
                     }
@@ -439,10 +488,10 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
                     const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
                     if (out_kind == 1) {
                         lds_to_out16<OBF16>(buf, tl, T, lane);
-                        if (!tl.diag) nan_mirror16<OBF16>(tl, T, lane);
+                        if (!tl.diag) nan_mirror16<OBF16, EP>(tl, T, lane);
                     } else {
                         lds_to_out16<OF16>(buf, tl, T, lane);
-                        if (!tl.diag) nan_mirror16<OF16>(tl, T, lane);
+                        if (!tl.diag) nan_mirror16<OF16, EP>(tl, T, lane);
                     }
                 } else if (pid < hi) {
                     const Tile tl = make_tile(qkv, out, pid, L, T, C, NH, HS, ES);
@@ -450,10 +499,10 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
                     const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
                     if (tl.rl == TB && tl.cl == TB && vec4) {
                         lds_to_out<true>(buf, tl, t4, lane, vec4);
-                        if (!tl.diag) nan_mirror<true>(tl, t4, lane, vec4);
+                        if (!tl.diag) nan_mirror<true, -1, EP>(tl, t4, lane, vec4);
                     } else {
                         lds_to_out<false>(buf, tl, t4, lane, vec4);
-                        if (!tl.diag) nan_mirror<false>(tl, t4, lane, vec4);
+                        if (!tl.diag) nan_mirror<false, -1, EP>(tl, t4, lane, vec4);
                     }
                 }
             }
@@ -1019,10 +1068,10 @@ inline int pick_u(int64_t HS, int es)
     return 1;
 }
 
-template <class E, int U, bool VEC16, int P>
+template <class E, int U, bool VEC16, int P, class EP = EpScore>
 hipError_t launch_cfg(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_kernel<E, U, VEC16, P>;
+    auto kern = trimul_kernel<E, U, VEC16, P, EP>;
     const int64_t nt = (a.T + TB - 1) / TB;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -1034,8 +1083,18 @@ hipError_t launch_cfg(const TrimulArgs &a, hipStream_t s)
     if (grid > want) grid = want;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHREADS), 0, s, (const char *)a.qkv, (float *)a.out, a.T, a.C,
-                       a.NH, a.HS, L, items, a.scale, (int)a.vec_store, a.out_kind);
+                       a.NH, a.HS, L, items, a.scale, (int)a.vec_store, a.out_kind, a.row_max, a.row_logsum);
     return hipGetLastError();
+}
+
+// Softmax rows (EP = EpLog or EpProb) on the tile kernel, for heads of 257 ..
+// 512 bytes in 16-byte pieces: three or four 128-byte register passes.
+template <class E, class EP> hipError_t launch_tile_ep(const TrimulArgs &a, hipStream_t s)
+{
+    const int64_t P = (a.HS * E::ES + 127) / 128;
+    if (P == 3) return launch_cfg<E, 4, true, 3, EP>(a, s);
+    if (P == 4) return launch_cfg<E, 4, true, 4, EP>(a, s);
+    return hipErrorInvalidValue;
 }
 
 // Passes per head: P = ceil(HS*ES / (32*U)). Prefetching variants exist for

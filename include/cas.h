@@ -165,7 +165,7 @@ int cas_trimul_causal(const void *qkv, void *out,
  * Both: fp32 arithmetic. Two sets of kernels serve the calls:
  *   - fast kernels where the QKV rows split into 16-byte pieces (qkv 16-byte
  *     aligned, HS and C times the element size multiples of 16), HS times the
- *     element size is at most 256 bytes, T < 2^22 and B * NH < 2^23; there
+ *     element size is at most 512 bytes, T < 2^22 and B * NH < 2^23; there
  *     the scores are bit-identical to cas_trimul_causal's (same products in
  *     the same order);
  *   - general-shape kernels elsewhere (any HS, any base aligned to the
@@ -192,8 +192,8 @@ int cas_causal_softmax(const void *qkv, const float *row_max, const float *row_l
  * each 128-row block of queries has its statistics computed and then its
  * rows written by the same workgroup, so the statistics work overlaps other
  * blocks' output stores instead of taking a launch of its own. (On general
- * shapes the call enqueues the general statistics and rows kernels back to
- * back on the stream.) Arguments,
+ * shapes, and for heads of 257 .. 512 bytes, the call enqueues the
+ * statistics and rows kernels back to back on the stream.) Arguments,
  * modes, output types, domain and errors as for cas_causal_softmax, with
  * row_max / row_logsum written (as by cas_causal_row_stats) instead of read;
  * out, row_max and row_logsum may overlap neither qkv nor one another.

@@ -669,14 +669,14 @@ def test_workload_attention_fused_bf16_full_size(orc):
 # --------------------------------------------------- general shapes
 #
 # Heads whose rows do not split into 16-byte pieces (HS = 3 and 5 in fp32,
-# 12 in binary16, a base one element off alignment) or exceed 256 bytes
-# (HS = 80 in fp32, 136 in bfloat16) run on the general-shape kernels; heads
-# of up to 512 bytes in 16-byte pieces (fp32 HS = 80, bf16 HS = 136) take the
-# fast row statistics and attention kernels (32 pieces per row), tested below
-# too, and heads over 512 bytes (fp32 HS = 160) stay on the general kernels.
+# 12 in binary16, a base one element off alignment) or exceed 512 bytes
+# (HS = 160 in fp32) run on the general-shape kernels. Heads of 257 .. 512
+# bytes in 16-byte pieces (fp32 HS = 80, bf16 HS = 136) take the fast
+# kernels' wide variants (32 pieces per row) and, for the softmax rows, the
+# per-wave tile kernel with the softmax epilogue: the wide-head tests below.
 
-GENERAL = [("f32", 3), ("f32", 5), ("f32", 80), ("bf16", 136), ("f16", 12), ("bf16", 3)]
-GENERAL_ATT = [g for g in GENERAL if g not in (("f32", 80), ("bf16", 136))] + [("f32", 160)]
+GENERAL = [("f32", 3), ("f32", 5), ("f32", 160), ("f16", 12), ("bf16", 3)]
+GENERAL_ATT = GENERAL
 GENERAL_T = [1, 33, 64, 100, 300]
 
 
@@ -691,7 +691,7 @@ def test_softmax_general_shapes(orc, launch, dtype, HS, T, mode):
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136), ("f32", 3)], ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,HS", [("f32", 160), ("f32", 3)], ids=lambda v: str(v))
 def test_softmax_general_out16(orc, dtype, HS, out_dtype):
     B, T, NH = 2, 130, 2
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 7)
@@ -754,14 +754,69 @@ def test_attention_wide_heads_16bit(orc, dtype, HS, T):
     check_attention_fused(orc, qkv, dtype, B, T, NH, HS, "wide heads")
 
 
+WIDE_SM = [("f32", 68), ("f32", 80), ("f32", 128), ("bf16", 136), ("bf16", 256), ("f16", 192)]
+
+
+@pytest.mark.parametrize("mode", ["prob", "log"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 300])
+@pytest.mark.parametrize("dtype,HS", WIDE_SM, ids=lambda v: str(v))
 @pytest.mark.parametrize("launch", LAUNCHES)
-def test_softmax_wide_heads_f32(orc, launch):
-    """fp32 HS = 128: the fast statistics launch beside the general softmax
-    rows (two launches), and the general fused launch."""
-    B, T, NH, HS = 2, 200, 2, 128
-    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=41)
+def test_softmax_wide_heads(orc, launch, dtype, HS, T, mode):
+    """Heads of 257 .. 512 bytes (three or four 128-byte register passes):
+    the wide statistics launch and the tile kernel's softmax rows, as two
+    launches and through the fused entry point (the same two launches)."""
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 53 + HS)
+    check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide heads", launch=launch)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136)], ids=lambda v: str(v))
+def test_softmax_wide_heads_out16(orc, dtype, HS, out_dtype):
+    B, T, NH = 2, 130, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 11)
     for mode in ("prob", "log"):
-        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="wide heads", launch=launch)
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="wide heads out16", launch="two")
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_softmax_wide_heads_unaligned_output(orc, offset):
+    """Output rows not in 16-byte pieces (T = 97, and a base one element
+    off): the tile kernel's masked per-element stores."""
+    B, T, NH, HS = 1, 97, 3, 96
+    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=59)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="wide heads unaligned", offset=offset)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_softmax_wide_heads_saturated_ramp(orc, launch, dtype):
+    """Exact-score saturated ramp rows on 512-byte heads (HS = 256, scale
+    1/16 exact): only the exp / log / sum roundings are allowed."""
+    B, T, NH, HS = 1, 257, 4, 256
+    qkv = synth.ramp_qk_inputs(B, T, NH, HS, [16.0 * a for a in SAT_SLOPES], dtype)
+    for mode in ("prob", "log"):
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide ramp", exact_scores=True, launch=launch)
+
+
+@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("bf16", 136), ("f16", 256)], ids=lambda v: str(v))
+def test_softmax_wide_heads_stats_match_the_score_kernel(orc, dtype, HS):
+    """Wide heads: the statistics launch and the tile kernel form every
+    score alike, bit for bit (row maxima equal the largest scores of
+    cas_trimul_causal's rows, and the largest log-probability of a row is
+    exactly -row_logsum)."""
+    B, T, NH = 2, 200, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 3)
+    d = to_device(qkv, dtype).view(B, T, -1)
+    case(f"wide stats vs scores {dtype} HS={HS}")
+    sc = cas.trimul_causal(d, NH)
+    low = torch.tril(torch.ones(T, T, dtype=torch.bool, device="cuda"))
+    smax = torch.where(low, sc, torch.full_like(sc, -float("inf"))).amax(dim=-1)
+    lp, mx, ls = cas.causal_softmax(d, NH, "log", fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(smax.view(torch.int32), mx.view(torch.int32)), "row_max"
+    assert torch.equal(lp.amax(dim=-1).view(torch.int32), (-ls).view(torch.int32)), "max lp"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
