@@ -352,6 +352,53 @@ __device__ __forceinline__ void nan_mirror16(const Tile &tl, int64_t T, int lane
         if (s < tl.cl && lane < tl.rl) st_nt16(tl.o + ((tl.s0 + s) * T + tl.t0 + lane) * 2, fill16<O, EP>());
 }
 
+// The same with 16-byte stores, for output rows in 16-byte pieces (T a
+// multiple of 8, base 16-byte aligned; the tile's row and column counts are
+// then multiples of 8 too): lane l covers columns 8(l%8) .. +7 of rows
+// l/8 + 8s, eight rows of the tile per store instruction.
+__device__ __forceinline__ uint32_t pack16(OBF16, float a, float b)
+{
+    const uint32_t lo = __float_as_uint(a) == QNAN_BITS ? OBF16::NAN16 : round16(OBF16{}, a);
+    const uint32_t hi = __float_as_uint(b) == QNAN_BITS ? OBF16::NAN16 : round16(OBF16{}, b);
+    return lo | (hi << 16);
+}
+__device__ __forceinline__ uint32_t pack16(OF16, float a, float b)
+{
+    const uint32_t lo = __float_as_uint(a) == QNAN_BITS ? OF16::NAN16 : round16(OF16{}, a);
+    const uint32_t hi = __float_as_uint(b) == QNAN_BITS ? OF16::NAN16 : round16(OF16{}, b);
+    return lo | (hi << 16);
+}
+
+template <class O>
+__device__ __forceinline__ void lds_to_out16v(const char *lds, const Tile &tl, int64_t T, int lane)
+{
+    const int c = (lane & 7) * 8, r8 = lane >> 3;
+    char *dst = tl.o + ((tl.t0 + r8) * T + tl.s0 + c) * 2;
+#pragma unroll
+    for (int s = 0; s < TB / 8; ++s) {
+        const int row = r8 + 8 * s;
+        const f32x4v a = *reinterpret_cast<const f32x4v *>(lds + (row * TB + c) * 4);
+        const f32x4v b = *reinterpret_cast<const f32x4v *>(lds + (row * TB + c + 4) * 4);
+        const u32x4 v = {pack16(O{}, a[0], a[1]), pack16(O{}, a[2], a[3]), pack16(O{}, b[0], b[1]),
+                         pack16(O{}, b[2], b[3])};
+        if (row < tl.rl && c < tl.cl)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + (int64_t)(8 * s) * T * 2));
+    }
+}
+
+template <class O, class EP = EpScore>
+__device__ __forceinline__ void nan_mirror16v(const Tile &tl, int64_t T, int lane)
+{
+    const int c = (lane & 7) * 8, r8 = lane >> 3;
+    constexpr uint32_t F = fill_dw<O, EP>();
+    const u32x4 v = {F, F, F, F};
+    char *dst = tl.o + ((tl.s0 + r8) * T + tl.t0 + c) * 2;
+#pragma unroll
+    for (int s = 0; s < TB / 8; ++s)
+        if (r8 + 8 * s < tl.cl && c < tl.rl)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + (int64_t)(8 * s) * T * 2));
+}
+
 // One step of a compute wave: the P register passes of tile `tl` (operands of
 // pass 0 already in ops[SB]), prefetching each next pass -- and after the last
 // pass the first pass of `nx` when has_next -- into the other buffer, then the
@@ -486,7 +533,15 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
                 if (pid < hi && out_kind != 0) { // 16-bit output (out_kind is uniform)
                     const Tile tl = make_tile(qkv, out, pid, L, T, C, NH, HS, ES, 2);
                     const char *buf = my_lds + ((n - 1) & 1) * TILE_BYTES;
-                    if (out_kind == 1) {
+                    if (vec4) { // rows in 16-byte pieces
+                        if (out_kind == 1) {
+                            lds_to_out16v<OBF16>(buf, tl, T, lane);
+                            if (!tl.diag) nan_mirror16v<OBF16, EP>(tl, T, lane);
+                        } else {
+                            lds_to_out16v<OF16>(buf, tl, T, lane);
+                            if (!tl.diag) nan_mirror16v<OF16, EP>(tl, T, lane);
+                        }
+                    } else if (out_kind == 1) {
                         lds_to_out16<OBF16>(buf, tl, T, lane);
                         if (!tl.diag) nan_mirror16<OBF16, EP>(tl, T, lane);
                     } else {

@@ -517,9 +517,11 @@ def test_trimul_out16_exact(orc, monkeypatch, dtype, out_dtype, kernel):
                     exact16=orc.round16(ref, out_dtype))
 
 
+@pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
-def test_trimul_out16_unaligned(orc, out_dtype):
+def test_trimul_out16_unaligned(orc, monkeypatch, out_dtype, kernel):
     """Output one element past a 16-byte boundary: the per-element stores."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
     B, T, NH, HS = 2, 136, 2, 64
     qkv = synth.trimul_inputs(B, T, NH, HS, "bf16", seed=77)
     ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, "bf16")

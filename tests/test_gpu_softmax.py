@@ -770,10 +770,13 @@ def test_softmax_wide_heads(orc, launch, dtype, HS, T, mode):
     check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide heads", launch=launch)
 
 
+@pytest.mark.parametrize("T", [130, 200])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136)], ids=lambda v: str(v))
-def test_softmax_wide_heads_out16(orc, dtype, HS, out_dtype):
-    B, T, NH = 2, 130, 2
+def test_softmax_wide_heads_out16(orc, dtype, HS, out_dtype, T):
+    """16-bit output rows: per-element stores (T = 130) and 16-byte stores
+    (T = 200, rows in 16-byte pieces)."""
+    B, NH = 2, 2
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 11)
     for mode in ("prob", "log"):
         check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="wide heads out16", launch="two")
