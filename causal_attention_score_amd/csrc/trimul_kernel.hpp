@@ -332,9 +332,10 @@ __device__ __forceinline__ void nan_mirror(const Tile &tl, uint32_t T4, int lane
 }
 
 // 16-bit output from the tile kernel's fp32 LDS tile (row-major, TB floats
-// per row): one element per lane and row, rounded on the way out, the fp32
-// mask pattern turned into the format's quiet NaN. (This kernel serves the
-// unaligned and wide-head shapes; the super-tile kernel has the fast path.)
+// per row), for output rows not in 16-byte pieces: one element per lane and
+// row, rounded on the way out, the fp32 mask pattern turned into the
+// format's quiet NaN. (This kernel serves the unaligned and wide-head
+// shapes; the super-tile kernel has the fast path.)
 template <class O>
 __device__ __forceinline__ void lds_to_out16(const char *lds, const Tile &tl, int64_t T, int lane)
 {
