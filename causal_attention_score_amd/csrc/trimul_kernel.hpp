@@ -662,20 +662,22 @@ template <int NCH> struct Staged {
 
 // Coalesced fetch of the 256 operand rows of super-tile `sp` (loader lane
 // cl = wave*64 + lane of 256): chunk j*256 + cl is row (j*256 + cl) / NCH,
-// chunk (cl % NCH). Rows past T and chunks past the head read zero.
+// chunk (cl % NCH). Rows past T and chunks past the head read zero. hoff:
+// the first head byte fetched (the second half of a wide head).
 template <class E, int NCH>
 __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, const Super &sp, uint32_t T, uint32_t C,
-                                            uint32_t NH, uint32_t HS, uint32_t ldb, int cl, bool with_q = true)
+                                            uint32_t NH, uint32_t HS, uint32_t ldb, int cl, bool with_q = true,
+                                            uint32_t hoff = 0)
 {
     constexpr int ES = E::ES;
     constexpr int RPJ = NCOMP_THREADS / NCH; // rows per j
     const uint32_t b = sp.plane / NH, nh = sp.plane - b * NH;
     const uint64_t rowq = (uint64_t)b * T + sp.T0, rowk = (uint64_t)b * T + sp.S0;
-    const char *qb = qkv + (rowq * (3u * C) + (uint64_t)nh * HS) * ES;
-    const char *kb = qkv + (rowk * (3u * C) + C + (uint64_t)nh * HS) * ES;
+    const char *qb = qkv + (rowq * (3u * C) + (uint64_t)nh * HS) * ES + hoff;
+    const char *kb = qkv + (rowk * (3u * C) + C + (uint64_t)nh * HS) * ES + hoff;
     const __amdgpu_buffer_rsrc_t rq = rsrc_at(qb), rk = rsrc_at(kb);
     const uint32_t c = (uint32_t)(cl % NCH), r0 = (uint32_t)(cl / NCH);
-    const uint32_t lim = c * 16 < HS * ES ? T : 0u; // a chunk past the head reads zero
+    const uint32_t lim = hoff + c * 16 < HS * ES ? T : 0u; // a chunk past the head reads zero
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const bool isq = j < NCH / 2; // uniform: rows 0..127 are Q, 128..255 K
@@ -939,12 +941,20 @@ __device__ __forceinline__ void stream_subtile(const Tile &tl, bool all_masked, 
     }
 }
 
-template <class E, int NCH, class O, class EP = EpScore>
+// HV = 2: heads of 257 .. 512 bytes in two halves of NCH * 16 = 256 bytes.
+// Each super-tile then takes two steps, one per half of the head: the
+// loaders stage the Q and K rows' first half, then their second half, and
+// the compute waves keep accumulating into the same registers, so every
+// score sums the same products in the same order as with one whole-row
+// step. The tile goes to LDS after the second step; the store waves stream
+// it during the next item's first step and its mirror during the second.
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store,
                     const float *__restrict__ row_max, const float *__restrict__ row_logsum, int runs)
 {
+    static_assert(HV == 1 || HV == 2, "one or two head halves");
     constexpr int RB = NCH * 16;
     constexpr int PITCH = out_pitch<O>(), OUT_BYTES = TB * PITCH;
     constexpr bool SM = EP::KIND != 0; // softmax: per-row statistics ride along with the operand rows
@@ -1003,13 +1013,19 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         }
         lds_barrier(); // operand rows of step 0 in LDS
         for (uint32_t n = 0; n < steps; ++n) {
+            if constexpr (HV == 2) { // item n's second half, then the next item's first
+                stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl, true, RB);
+                lds_barrier(); // X: first half consumed
+                stage_store<NCH>(st, opb, cl);
+                lds_barrier(); // Y: second half in LDS
+            }
             const bool more = n + 1 < steps;
             bool with_q = true; // the next item's Q rows differ from this one's
             if (more) {
                 const Super was = cur.item();
                 cur.advance();
                 const Super nx = cur.item();
-                with_q = !(nx.plane == was.plane && nx.T0 == was.T0);
+                if constexpr (HV == 1) with_q = !(nx.plane == was.plane && nx.T0 == was.T0);
                 stage_fetch<E, NCH>(st, qkv, nx, T, C, NH, HS, ldb, cl, with_q);
                 if constexpr (SM) sv = stat_fetch(row_max, row_logsum, nx, T, cl);
             }
@@ -1040,6 +1056,11 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+            if constexpr (HV == 2) { // the head's first half
+                if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
+                lds_barrier(); // X: first half consumed
+                lds_barrier(); // Y: second half in LDS
+            }
             if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
             lds_barrier(); // X: operand rows consumed, previous tile read back
             if (live) {
@@ -1059,6 +1080,20 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             const bool inside = tl.rl > 0 && tl.cl > 0; // else the sub-tile lies past the plane edge
             const uint32_t tby = opaque_s(TBY);
             const bool full = tl.rl == TB && tl.cl == TB;
+            if constexpr (HV == 2) { // the whole mirror of the previous item during this item's first step
+                lds_barrier(); // X: first half consumed
+                lds_barrier(); // Y: second half in LDS
+                if (pm_live) {
+                    if (pm_full) {
+                        nan_mirror_o<0, O, true, EP>(pm, T, tby, lane, vec);
+                        nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
+                    } else {
+                        nan_mirror_o<0, O, false, EP>(pm, T, tby, lane, vec);
+                        nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
+                    }
+                }
+                pm_live = false;
+            }
             lds_barrier(); // X
             if (pm_live) { // second half of the previous step's mirror: needs nothing from LDS
                 if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
@@ -1069,26 +1104,32 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
             if (!inside) continue;
             // Sub-tile (0, 1) of a diagonal super-tile lies wholly above the diagonal.
             stream_subtile<O, EP>(tl, sp.diag && sa == 0 && sb == 1, full, vec, my_out, T, tby, lane);
-            if (!tl.diag) { // first half of the mirror now, the second after the next X
+            if (!tl.diag) { // HV = 1: first half of the mirror now, the second after the next X
                 pm = tl;
                 pm_live = true;
                 pm_full = full && vec;
-                if (pm_full) nan_mirror_o<0, O, true, EP>(tl, T, tby, lane, vec);
-                else nan_mirror_o<0, O, false, EP>(tl, T, tby, lane, vec);
+                if constexpr (HV == 1) {
+                    if (pm_full) nan_mirror_o<0, O, true, EP>(tl, T, tby, lane, vec);
+                    else nan_mirror_o<0, O, false, EP>(tl, T, tby, lane, vec);
+                }
             }
         }
         if (pm_live) {
             const uint32_t tby = opaque_s(TBY);
+            if constexpr (HV == 2) {
+                if (pm_full) nan_mirror_o<0, O, true, EP>(pm, T, tby, lane, vec);
+                else nan_mirror_o<0, O, false, EP>(pm, T, tby, lane, vec);
+            }
             if (pm_full) nan_mirror_o<1, O, true, EP>(pm, T, tby, lane, vec);
             else nan_mirror_o<1, O, false, EP>(pm, T, tby, lane, vec);
         }
     }
 }
 
-template <class E, int NCH, class O, class EP = EpScore>
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1>
 hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_super_kernel<E, NCH, O, EP>;
+    auto kern = trimul_super_kernel<E, NCH, O, EP, HV>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -1100,8 +1141,9 @@ hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
     // super-tile rows: there the saved Q-row reloads outweigh the scattered
     // writes (fp32 B8 T1024: 85.8 -> 82.8 us; B8 T2048: 321 -> 309 us; B32
     // T512: 88.6 -> 89.9 us). The store-bound 16-bit inputs lose with them
-    // (bf16 B4 T4096 to bf16: 577 -> 659 us).
-    const int runs = std::is_same<E, KF32>::value && nt >= 8;
+    // (bf16 B4 T4096 to bf16: 577 -> 659 us). Two head halves (HV = 2)
+    // reload the Q rows anyway.
+    const int runs = HV == 1 && std::is_same<E, KF32>::value && nt >= 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SUPER_THREADS), 0, s, (const char *)a.qkv, (char *)a.out,
                        (uint32_t)a.T,
                        (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, (uint32_t)L, (uint32_t)items, a.scale,
@@ -1185,6 +1227,17 @@ hipError_t launch_u(const TrimulArgs &a, hipStream_t s)
     }
 }
 
+// Heads of 257 .. 512 bytes: the super-tile kernel in two 256-byte halves
+// multiplies the second half whole, zeros included. For 16-bit inputs (the
+// launch bound by its stores) that always pays; for fp32 inputs, bound by
+// the MFMAs, only from 385 bytes on, where the tile kernel's 128-byte passes
+// multiply as many zeros (fp32 B4 T2048 NH12: HS 80 253 us on the tile
+// kernel against 278 in two halves; HS 128 335 against 273 us).
+template <class E> bool two_halves_pay(int64_t HS)
+{
+    return !std::is_same<E, KF32>::value || HS * E::ES > 384;
+}
+
 template <class E>
 hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
 {
@@ -1198,8 +1251,15 @@ hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
     const bool ids_fit = a.B * a.NH * (nts * (nts + 1) / 2) <= INT32_MAX;
     // The super-tile kernel's buffer offsets within a 64-row tile reach 256 T
     // bytes, under the 2^31 range of its buffer resources for T < 2^22.
-    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 256 && a.T < (int64_t(1) << 22);
+    // Heads of 257 .. 512 bytes take it in two halves of 256 (two_halves_pay).
+    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.T < (int64_t(1) << 22) &&
+                          (a.HS * E::ES <= 256 || (a.HS * E::ES <= 512 && two_halves_pay<E>(a.HS)));
     if (super_ok && !force_tile) {
+        if (a.HS * E::ES > 256) {
+            if (a.out_kind == 1) return launch_super<E, 16, OBF16, EpScore, 2>(a, s);
+            if (a.out_kind == 2) return launch_super<E, 16, OF16, EpScore, 2>(a, s);
+            return launch_super<E, 16, OF32, EpScore, 2>(a, s);
+        }
         const bool narrow = a.HS * E::ES <= 128;
         if (a.out_kind == 1) return narrow ? launch_super<E, 8, OBF16>(a, s) : launch_super<E, 16, OBF16>(a, s);
         if (a.out_kind == 2) return narrow ? launch_super<E, 8, OF16>(a, s) : launch_super<E, 16, OF16>(a, s);

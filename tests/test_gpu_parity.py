@@ -474,6 +474,37 @@ def test_trimul_ragged_16bit(orc, monkeypatch, T, HS, dtype, kernel):
     assert_scores(out, ref, bound, dtype, f"trimul {dtype} T={T} HS={HS}")
 
 
+WIDE_HEADS = [("f32", 100), ("f32", 112), ("f32", 128), ("bf16", 136), ("bf16", 200), ("bf16", 256), ("f16", 144)]
+
+
+@pytest.mark.parametrize("T", [1, 65, 128, 129, 300])
+@pytest.mark.parametrize("dtype,HS", WIDE_HEADS, ids=lambda v: str(v))
+def test_trimul_wide_heads_two_halves(orc, monkeypatch, T, dtype, HS):
+    """Heads of 257 .. 512 bytes (the second half whole or partial): the
+    super-tile kernel in two head halves against the oracle, and bit for bit
+    against the per-wave tile kernel, which forms the same products in the
+    same order."""
+    B, NH = 2, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 71 + HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul(qkv, dtype, B, T, NH, HS, "two halves")
+    assert_scores(out, ref, bound, dtype, f"trimul two halves {dtype} T={T} HS={HS}")
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+    out_t = run_trimul(qkv, dtype, B, T, NH, HS, "two halves, tile kernel")
+    assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype,HS", [("f32", 100), ("bf16", 256)], ids=lambda v: str(v))
+def test_trimul_wide_heads_out16(orc, dtype, HS, out_dtype):
+    for T in (200, 257):
+        B, NH = 2, 2
+        qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 73 + HS)
+        ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+        out = run_trimul16(qkv, dtype, out_dtype, B, T, NH, HS, "two halves out16")
+        assert_scores16(out, ref, bound, dtype, out_dtype, f"trimul two halves {dtype}->{out_dtype} T={T} HS={HS}")
+
+
 @pytest.mark.parametrize("kernel", ["super", "tile"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_trimul_exact_small_integers(orc, monkeypatch, dtype, kernel):

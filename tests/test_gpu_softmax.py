@@ -770,6 +770,29 @@ def test_softmax_wide_heads(orc, launch, dtype, HS, T, mode):
     check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide heads", launch=launch)
 
 
+@pytest.mark.parametrize("dtype,HS", [("f32", 100), ("bf16", 256)], ids=lambda v: str(v))
+def test_softmax_wide_heads_kernels_agree(orc, monkeypatch, dtype, HS):
+    """The wide-head softmax rows from the super-tile kernel (two head
+    halves) equal those of the per-wave tile kernel bit for bit, both
+    modes, fp32 and bf16 output."""
+    B, T, NH = 2, 200, 2
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 29)
+    for mode in ("prob", "log"):
+        for out_dtype in ("f32", "bf16"):
+            got = {}
+            for kernel in ("super", "tile"):
+                if kernel == "tile":
+                    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+                else:
+                    monkeypatch.delenv("CAS_TRIMUL_KERNEL", raising=False)
+                got[kernel] = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, f"kernels agree {kernel}")
+            for a, b in zip(got["super"], got["tile"]):
+                assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), \
+                    f"{mode} {out_dtype}: kernels differ"
+    monkeypatch.delenv("CAS_TRIMUL_KERNEL", raising=False)
+    check_case(orc, qkv, dtype, B, T, NH, HS, "prob", label="wide heads super")
+
+
 @pytest.mark.parametrize("T", [130, 200])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136)], ids=lambda v: str(v))
