@@ -805,14 +805,17 @@ def test_softmax_wide_heads_out16(orc, dtype, HS, out_dtype, T):
         check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="wide heads out16", launch="two")
 
 
+@pytest.mark.parametrize("dtype,HS", [("f32", 96), ("f32", 100), ("bf16", 136)], ids=lambda v: str(v))
 @pytest.mark.parametrize("offset", [0, 1])
-def test_softmax_wide_heads_unaligned_output(orc, offset):
+def test_softmax_wide_heads_unaligned_output(orc, offset, dtype, HS):
     """Output rows not in 16-byte pieces (T = 97, and a base one element
-    off): the tile kernel's masked per-element stores."""
-    B, T, NH, HS = 1, 97, 3, 96
-    qkv = synth.trimul_inputs(B, T, NH, HS, "f32", seed=59)
+    off): the masked per-element stores of the tile kernel (fp32 HS 96) and
+    of the super-tile kernel in two head halves (fp32 HS 100, bf16 HS 136)."""
+    B, T, NH = 1, 97, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=59 + HS)
     for mode in ("prob", "log"):
-        check_case(orc, qkv, "f32", B, T, NH, HS, mode, label="wide heads unaligned", offset=offset)
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide heads unaligned", offset=offset)
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, "bf16", label="wide heads unaligned", offset=offset)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
