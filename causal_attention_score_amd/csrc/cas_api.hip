@@ -267,7 +267,7 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     // in one grid
     const bool fast = cas::softmax_fits(T, HS, es, *vec);
     *general = !fast || B * NH >= (INT64_C(1) << 23);
-    if (*general && !cas::general_softmax_fits(B, T, NH, HS, es, qkv)) return CAS_ERR_UNSUPPORTED;
+    if (*general && !cas::general_softmax_fits(B, T, NH, es, qkv)) return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
 }
 

@@ -103,11 +103,11 @@ hipError_t launch_attention_wide16(const TrimulArgs &a, int elem, hipStream_t s)
 hipError_t launch_attention_online_wide16(const TrimulArgs &a, int elem, hipStream_t s);
 
 // General shapes (softmax_general.hip): heads whose rows do not split into
-// 16-byte pieces or exceed 256 bytes, up to general_softmax_fits(). The same
-// outputs as above: row statistics; softmax rows (a.out_kind picks the output
-// type); the attention output, with the statistics computed and written first
-// when with_stats, else read.
-bool general_softmax_fits(int64_t B, int64_t T, int64_t NH, int64_t HS, int es, const void *qkv);
+// 16-byte pieces or exceed 512 bytes, any head size, within
+// general_softmax_fits(). The same outputs as above: row statistics; softmax
+// rows (a.out_kind picks the output type); the attention output, with the
+// statistics computed and written first when with_stats, else read.
+bool general_softmax_fits(int64_t B, int64_t T, int64_t NH, int es, const void *qkv);
 hipError_t launch_gen_row_stats(const TrimulArgs &a, int elem, hipStream_t s);
 hipError_t launch_gen_softmax(const TrimulArgs &a, int elem, int mode, hipStream_t s);
 hipError_t launch_gen_attention(const TrimulArgs &a, int elem, bool with_stats, hipStream_t s);

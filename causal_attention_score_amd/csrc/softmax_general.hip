@@ -15,7 +15,13 @@ gen::GenArgs gen_args(const TrimulArgs &a, int es)
     g.C = a.C;
     g.NH = a.NH;
     g.HS = (int)a.HS;
-    g.hsb = (int)((a.HS + 31) / 32 * 32 * es); // whole 32-column blocks of the attention output
+    // Chunks of whole 32-column blocks of the attention output, at most
+    // GMAX_HEAD bytes (fp32 160, 16-bit 320 elements: at least the NDB * 32
+    // columns of one attention pass).
+    const int64_t hs32 = (a.HS + 31) / 32 * 32, cap = gen::GMAX_HEAD / es / 32 * 32;
+    g.hch = (int)(hs32 < cap ? hs32 : cap);
+    g.nch = (int)((a.HS + g.hch - 1) / g.hch);
+    g.hsb = g.hch * es;
     g.pitch = g.hsb + 16;
     g.nqb = (uint32_t)((a.T + gen::GB - 1) / gen::GB);
     g.scale = a.scale;
@@ -59,12 +65,12 @@ template <class E, bool STATS> hipError_t attention_e(const TrimulArgs &a, hipSt
 
 } // namespace
 
-bool general_softmax_fits(int64_t B, int64_t T, int64_t NH, int64_t HS, int es, const void *qkv)
+bool general_softmax_fits(int64_t B, int64_t T, int64_t NH, int es, const void *qkv)
 {
-    // Head rows staged whole (three tiles of 32 rows within 64 KB of LDS),
-    // elements at their natural alignment, one workgroup per 32-row block.
-    return (HS + 31) / 32 * 32 * es <= gen::GMAX_HEAD && (uintptr_t)qkv % es == 0 &&
-           B * NH * ((T + gen::GB - 1) / gen::GB) <= INT32_MAX;
+    // Any head size (rows staged in chunks of at most GMAX_HEAD bytes, three
+    // tiles of 32 rows within 64 KB of LDS), elements at their natural
+    // alignment, one workgroup per 32-row block.
+    return (uintptr_t)qkv % es == 0 && B * NH * ((T + gen::GB - 1) / gen::GB) <= INT32_MAX;
 }
 
 hipError_t launch_gen_row_stats(const TrimulArgs &a, int elem, hipStream_t s)

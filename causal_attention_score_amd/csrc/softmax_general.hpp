@@ -1,9 +1,9 @@
 // softmax_general.hpp -- the causal softmax (row statistics, softmax rows) and
 // the attention output for QKV rows outside the fast kernels' domain: heads
 // whose rows do not split into 16-byte pieces (HS = 3 in fp32, misaligned
-// bases) and heads over 256 bytes (HS = 80 in fp32, 136 in bfloat16), up to
-// 640 bytes per head row rounded up to 32 elements (three staged tiles stay
-// within 64 KB of LDS).
+// bases) and heads over 512 bytes, of any size: a head row is staged in
+// chunks of at most 640 bytes (fp32 160, 16-bit 320 elements), so three
+// staged tiles stay within 64 KB of LDS.
 //
 // Semantics are those of the fast path (smallem "Kernels GPU", its softmax
 // section: row_stats reduces a row to its maximum and ln sum exp(x - max),
@@ -20,7 +20,10 @@
 // is a whole number of 32-byte MFMA steps and of 32-column output blocks
 // (local padding: the contraction runs over full steps, the zeros add
 // nothing). Scores come from MFMAs as D = K Q^T, so lane l holds query
-// l % 32 and keys 8g + 4(l / 32) + e of the tile in register 4g + e.
+// l % 32 and keys 8g + 4(l / 32) + e of the tile in register 4g + e. A head
+// longer than one chunk is taken chunk after chunk, the Q and K chunks
+// staged together, the products accumulating in the same registers: the
+// same sums in the same order as one whole-row pass.
 //
 // Statistics take two sweeps over the key tiles: the row maximum of the raw
 // dot products mt, then l = sum exp2(a c - ms) against ms = fl(mt c),
@@ -45,7 +48,7 @@ namespace cas {
 namespace gen {
 
 constexpr int GB = 32;          // query rows per workgroup, keys per step
-constexpr int GMAX_HEAD = 640;  // bytes of one head row
+constexpr int GMAX_HEAD = 640;  // bytes of one staged head chunk
 constexpr int NDB = 4;          // 32-column blocks of the attention output per pass
 constexpr float GLOG2E = 1.44269504088896340736f;
 constexpr float GLN2 = 0.693147180559945309417f;
@@ -54,7 +57,9 @@ struct GenArgs {
     const char *qkv;
     int64_t B, T, C, NH;
     int HS;
-    int hsb;       // bytes of a staged row: HS rounded up to 32 elements (zero-padded)
+    int hch;       // elements of one staged head chunk: HS rounded up to 32, at most GMAX_HEAD bytes
+    int nch;       // chunks per head row
+    int hsb;       // bytes of a staged row chunk (hch elements, zero-padded past the head)
     int pitch;     // LDS row pitch: hsb + 16
     uint32_t nqb;  // 32-row query blocks per plane
     float scale;
@@ -66,12 +71,12 @@ __device__ __forceinline__ float pin(float v)
     return v;
 }
 
-// Rows [0, 32) of a head at `base` (row pitch ldb bytes; rows at or past
-// `rows` and elements at or past HS become zero) -> LDS rows of `pitch`
-// bytes, hsb bytes each.
+// Elements [e0, e0 + hch) of rows [0, 32) of a head at `base` (row pitch
+// ldb bytes; rows at or past `rows` and elements at or past HS become zero)
+// -> LDS rows of `pitch` bytes, hsb bytes each.
 template <class E>
 __device__ __forceinline__ void stage_rows(char *lds, const char *__restrict__ base, int64_t ldb, int rows,
-                                           const GenArgs &g, int lane)
+                                           const GenArgs &g, int lane, int e0 = 0)
 {
     // Lane l takes elements l, l + 64, .. (M per row at most) of RG rows at a
     // time: all their loads in flight, then the LDS writes (one load, wait
@@ -86,8 +91,8 @@ __device__ __forceinline__ void stage_rows(char *lds, const char *__restrict__ b
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int r = r0 + rr, e = lane + 64 * m;
-                const bool ok = r < rows && e < g.HS;
-                v[rr][m] = ok ? *reinterpret_cast<const U *>(base + (int64_t)r * ldb + e * ES) : (U)0;
+                const bool ok = r < rows && e < nel && e0 + e < g.HS;
+                v[rr][m] = ok ? *reinterpret_cast<const U *>(base + (int64_t)r * ldb + (int64_t)(e0 + e) * ES) : (U)0;
             }
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr)
@@ -99,20 +104,19 @@ __device__ __forceinline__ void stage_rows(char *lds, const char *__restrict__ b
     }
 }
 
-// Raw dot products of the staged key tile with the staged query block:
-// register 4g + e of lane l is key 8g + 4(l / 32) + e against query l % 32.
-// Step c takes chunk 2c + h of both rows (h = l / 32, the MFMA k-slot).
+// Raw dot products of the staged key tile with the staged query block,
+// added to acc: register 4g + e of lane l is key 8g + 4(l / 32) + e against
+// query l % 32. Step c takes chunk 2c + h of both rows (h = l / 32, the
+// MFMA k-slot).
 template <class E>
-__device__ __forceinline__ f32x16 score_tile(const char *ldk, const char *ldq, const GenArgs &g, int lane)
+__device__ __forceinline__ void score_acc(f32x16 &acc, const char *ldk, const char *ldq, const GenArgs &g, int lane)
 {
     const int r = lane & 31, h = lane >> 5;
-    f32x16 acc = {};
     for (int c = 0; c < g.hsb / 32; ++c) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(ldk + r * g.pitch + (2 * c + h) * 16);
         const u32x4 b = *reinterpret_cast<const u32x4 *>(ldq + r * g.pitch + (2 * c + h) * 16);
         mfma_chunk<E>(acc, a, b);
     }
-    return acc;
 }
 
 __device__ __forceinline__ int key_of(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -146,6 +150,34 @@ __device__ __forceinline__ Block block_of(const GenArgs &g)
     return k;
 }
 
+// Q rows of the block at ldq for the whole launch when the head is one
+// chunk; longer heads stage them chunk by chunk with the keys (tile_scores).
+template <class E>
+__device__ __forceinline__ void stage_queries(char *ldq, const Block &bk, const GenArgs &g, int lane)
+{
+    if (g.nch == 1) stage_rows<E>(ldq, bk.q, bk.ldb, bk.qrows, g, lane);
+}
+
+// Raw dot products of key tile s0 with the block's queries: the K rows (and
+// for a head of several chunks the Q rows) staged chunk by chunk, the
+// products of every chunk accumulating in the same registers.
+template <class E>
+__device__ __forceinline__ f32x16 tile_scores(const GenArgs &g, const Block &bk, int64_t s0, char *ldq, char *ldk,
+                                              int lane)
+{
+    const int krows = (int)(g.T - s0 < GB ? g.T - s0 : GB);
+    f32x16 acc = {};
+    for (int ch = 0; ch < g.nch; ++ch) {
+        const int e0 = ch * g.hch;
+        __syncthreads();
+        if (g.nch > 1) stage_rows<E>(ldq, bk.q, bk.ldb, bk.qrows, g, lane, e0);
+        stage_rows<E>(ldk, bk.k + s0 * bk.ldb, bk.ldb, krows, g, lane, e0);
+        __syncthreads();
+        score_acc<E>(acc, ldk, ldq, g, lane);
+    }
+    return acc;
+}
+
 // The statistics of the lane's query row (two sweeps over key tiles
 // 0 .. the block's own): the raw maximum mt, the offset ms = fl(mt c) and
 // l = sum exp2(a c - ms), both lane halves combined. Q staged at ldq.
@@ -160,10 +192,7 @@ __device__ __forceinline__ void row_stats(const GenArgs &g, const Block &bk, cha
     mt = -__builtin_inff();
     for (int j = 0; j < ntk; ++j) {
         const int64_t s0 = (int64_t)j * GB;
-        __syncthreads();
-        stage_rows<E>(ldk, bk.k + s0 * bk.ldb, bk.ldb, (int)(g.T - s0 < GB ? g.T - s0 : GB), g, lane);
-        __syncthreads();
-        const f32x16 acc = score_tile<E>(ldk, ldq, g, lane);
+        const f32x16 acc = tile_scores<E>(g, bk, s0, ldq, ldk, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t key = s0 + key_of(r, h);
@@ -175,10 +204,7 @@ __device__ __forceinline__ void row_stats(const GenArgs &g, const Block &bk, cha
     l = 0.f;
     for (int j = 0; j < ntk; ++j) {
         const int64_t s0 = (int64_t)j * GB;
-        __syncthreads();
-        stage_rows<E>(ldk, bk.k + s0 * bk.ldb, bk.ldb, (int)(g.T - s0 < GB ? g.T - s0 : GB), g, lane);
-        __syncthreads();
-        const f32x16 acc = score_tile<E>(ldk, ldq, g, lane);
+        const f32x16 acc = tile_scores<E>(g, bk, s0, ldq, ldk, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t key = s0 + key_of(r, h);
@@ -196,7 +222,7 @@ __global__ void __launch_bounds__(64) gen_stats_kernel(GenArgs g, float *__restr
     const int lane = threadIdx.x;
     const Block bk = block_of<E>(g);
     char *ldq = glds, *ldk = glds + GB * g.pitch;
-    stage_rows<E>(ldq, bk.q, bk.ldb, bk.qrows, g, lane);
+    stage_queries<E>(ldq, bk, g, lane);
     float mt, ms, l;
     row_stats<E>(g, bk, ldq, ldk, lane, mt, ms, l);
     const int q = lane & 31;
@@ -229,7 +255,7 @@ __global__ void __launch_bounds__(64) gen_rows_kernel(GenArgs g, const float *__
     const int lane = threadIdx.x, h = lane >> 5;
     const Block bk = block_of<E>(g);
     char *ldq = glds, *ldk = glds + GB * g.pitch;
-    stage_rows<E>(ldq, bk.q, bk.ldb, bk.qrows, g, lane);
+    stage_queries<E>(ldq, bk, g, lane);
     const int q = lane & 31;
     const int64_t t = bk.t0 + q;
     const bool row_ok = q < bk.qrows;
@@ -240,10 +266,7 @@ __global__ void __launch_bounds__(64) gen_rows_kernel(GenArgs g, const float *__
     for (int j = 0; j < ntk; ++j) {
         const int64_t s0 = (int64_t)j * GB;
         if (j <= own) {
-            __syncthreads();
-            stage_rows<E>(ldk, bk.k + s0 * bk.ldb, bk.ldb, (int)(g.T - s0 < GB ? g.T - s0 : GB), g, lane);
-            __syncthreads();
-            const f32x16 acc = score_tile<E>(ldk, ldq, g, lane);
+            const f32x16 acc = tile_scores<E>(g, bk, s0, ldq, ldk, lane);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t key = s0 + key_of(r, h);
@@ -274,9 +297,10 @@ template <> __device__ __forceinline__ uint32_t pack2<KF16>(float a, float b)
 }
 
 // Y^T[d][q] += sum over the tile's keys of V[key][d] p[q][key], for the
-// column blocks [db0, db0 + NDB) of the head. ldv: the staged value rows.
+// nb <= NDB column blocks staged at ldv (the value rows from the pass's
+// first column on).
 template <class E>
-__device__ __forceinline__ void pv_tile(f32x16 (&yt)[NDB], const float (&p)[16], const char *ldv, int db0, int nb,
+__device__ __forceinline__ void pv_tile(f32x16 (&yt)[NDB], const float (&p)[16], const char *ldv, int nb,
                                         const GenArgs &g, int lane)
 {
     const int d = lane & 31, h = lane >> 5;
@@ -287,7 +311,7 @@ __device__ __forceinline__ void pv_tile(f32x16 (&yt)[NDB], const float (&p)[16],
 #pragma unroll
             for (int i = 0; i < NDB; ++i) {
                 if (i >= nb) break; // past the head's last 32-column block
-                const float v = *reinterpret_cast<const float *>(vrow + ((db0 + i) * 32 + d) * 4);
+                const float v = *reinterpret_cast<const float *>(vrow + (i * 32 + d) * 4);
                 yt[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, p[r], yt[i], 0, 0, 0);
             }
         }
@@ -301,7 +325,7 @@ __device__ __forceinline__ void pv_tile(f32x16 (&yt)[NDB], const float (&p)[16],
 #pragma unroll
             for (int i = 0; i < NDB; ++i) {
                 if (i >= nb) break;
-                const int col = ((db0 + i) * 32 + d) * 2;
+                const int col = (i * 32 + d) * 2;
                 uint32_t w[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
@@ -327,7 +351,7 @@ __global__ void __launch_bounds__(64) gen_attention_kernel(GenArgs g, float *__r
     const int lane = threadIdx.x, h = lane >> 5;
     const Block bk = block_of<E>(g);
     char *ldq = glds, *ldk = glds + GB * g.pitch, *ldv = glds + 2 * GB * g.pitch;
-    stage_rows<E>(ldq, bk.q, bk.ldb, bk.qrows, g, lane);
+    stage_queries<E>(ldq, bk, g, lane);
     const int q = lane & 31;
     const int64_t t = bk.t0 + q;
     const bool row_ok = q < bk.qrows;
@@ -355,18 +379,19 @@ __global__ void __launch_bounds__(64) gen_attention_kernel(GenArgs g, float *__r
         for (int j = 0; j < ntk; ++j) {
             const int64_t s0 = (int64_t)j * GB;
             const int krows = (int)(g.T - s0 < GB ? g.T - s0 : GB);
+            // the value rows' columns of this pass (hch >= NDB * 32 whenever
+            // the head needs more than one pass), then the scores, whose
+            // first barrier also orders these writes after the last pass's reads
             __syncthreads();
-            stage_rows<E>(ldk, bk.k + s0 * bk.ldb, bk.ldb, krows, g, lane);
-            stage_rows<E>(ldv, bk.v + s0 * bk.ldb, bk.ldb, krows, g, lane);
-            __syncthreads();
-            const f32x16 acc = score_tile<E>(ldk, ldq, g, lane);
+            stage_rows<E>(ldv, bk.v + s0 * bk.ldb, bk.ldb, krows, g, lane, db0 * 32);
+            const f32x16 acc = tile_scores<E>(g, bk, s0, ldq, ldk, lane);
             float p[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t key = s0 + key_of(r, h);
                 p[r] = (key <= t && key < g.T) ? tri::epilogue<tri::EpProb>(acc[r], g.scale, mx, ls) : 0.f;
             }
-            pv_tile<E>(yt, p, ldv, db0, ndb - db0 < NDB ? ndb - db0 : NDB, g, lane);
+            pv_tile<E>(yt, p, ldv, ndb - db0 < NDB ? ndb - db0 : NDB, g, lane);
         }
         // lane: query q, head columns 32 (db0 + i) + 8(r/4) + 4h + r%4
         if (row_ok) {

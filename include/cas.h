@@ -169,10 +169,10 @@ int cas_trimul_causal(const void *qkv, void *out,
  *     the scores are bit-identical to cas_trimul_causal's (same products in
  *     the same order);
  *   - general-shape kernels elsewhere (any HS, any base aligned to the
- *     element size), with the same formulas and the same tolerance, up to
- *     heads of 640 bytes once HS is rounded up to a multiple of 32 elements
- *     (fp32 HS <= 160, 16-bit HS <= 320).
- * Beyond that, or with statistics not 4-byte aligned: CAS_ERR_UNSUPPORTED,
+ *     element size), with the same formulas and the same tolerance, for
+ *     any head size (rows staged in chunks of at most 640 bytes).
+ * With elements off their natural alignment, or with statistics not 4-byte
+ * aligned: CAS_ERR_UNSUPPORTED,
  * with nothing written. Other limits,
  * empty shapes and the no-overlap rule as for cas_trimul_causal: the
  * statistics written by cas_causal_row_stats may overlap neither qkv nor each

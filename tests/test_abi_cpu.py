@@ -175,8 +175,6 @@ def test_attention_rejections(L):
     assert at(L, B=-1) == ESHAPE
     assert at(L, C=10, NH=3) == ESHAPE
     assert at(L, y=None) == ENULL and at(L, qkv=None) == ENULL and at(L, mx=None) == ENULL
-    assert at(L, C=3 * 161, NH=3) == EUNSUP                 # HS = 161 fp32: 644-byte heads (768 padded)
-    assert at(L, ind=F16, C=3 * 336, NH=3) == EUNSUP        # HS = 336 binary16: 672-byte heads
     assert at(L, qkv=PX + 2) == EUNSUP                      # fp32 elements off their 4-byte alignment
     assert at(L, y=PX + 16) == EALIAS                       # y inside qkv
     assert at(L, y=PY + 64) == EALIAS                       # y over the statistics
@@ -189,6 +187,8 @@ def test_attention_rejections(L):
         assert at(L, ind=F16, C=12) == EDEV                 # 8-byte heads of a 16-bit type
         assert at(L, C=15, NH=3) == EDEV                    # 20-byte heads
         assert at(L, C=3 * 160, NH=3) == EDEV               # HS = 160 fp32: 640-byte heads
+        assert at(L, C=3 * 161, NH=3) == EDEV               # HS = 161 fp32: 644-byte heads, staged in chunks
+        assert at(L, ind=F16, C=3 * 336, NH=3) == EDEV      # HS = 336 binary16: 672-byte heads
         assert at(L, B=2**23, T=1, C=4, NH=1) == EDEV       # past the fast kernels' grid limits
 
 
@@ -204,7 +204,6 @@ def test_attention_fused_rejections(L):
     assert af(L, C=10, NH=3) == ESHAPE
     assert af(L, y=None) == ENULL and af(L, qkv=None) == ENULL and af(L, mx=None) == ENULL
     assert af(L, ls=None) == ENULL
-    assert af(L, C=3 * 161, NH=3) == EUNSUP                 # heads over 640 bytes (padded)
     assert af(L, qkv=PX + 2) == EUNSUP                      # fp32 elements off their alignment
     assert af(L, mx=PY + 2) == EUNSUP and af(L, y=PZ + 2) == EUNSUP
     # three outputs: none over qkv or over another; (B, T, C) fp32 y spans 480 bytes, statistics 120
@@ -220,6 +219,7 @@ def test_attention_fused_rejections(L):
         assert af(L, ind=BF16, C=24) == EDEV
         assert af(L, ind=F16, C=12) == EDEV                 # general shapes
         assert af(L, C=15, NH=3) == EDEV
+        assert af(L, C=3 * 161, NH=3) == EDEV               # heads over 640 bytes, staged in chunks
         assert af(L, B=2**23, T=1, C=4, NH=1) == EDEV
 
 
@@ -234,8 +234,6 @@ def test_softmax_rejections(L):
         assert f(L, B=2**40, T=2**20) == ESHAPE
         assert f(L, B=1, T=4, C=2**22, NH=2) == ESHAPE
         # outside both the fast and the general kernels' domains (valid arguments otherwise)
-        assert f(L, C=3 * 161, NH=3, ind=F32) == EUNSUP    # HS = 161 fp32: 644-byte heads (768 padded)
-        assert f(L, C=3 * 336, NH=3, ind=BF16) == EUNSUP   # HS = 336 bf16: 672-byte heads
         assert f(L, qkv=PX + 2) == EUNSUP                  # fp32 elements off their 4-byte alignment
         assert f(L, mx=PY + 2) == EUNSUP                   # misaligned statistics
         assert f(L, B=0) == OK and f(L, T=0) == OK and f(L, NH=0, C=0) == OK
@@ -275,7 +273,10 @@ def test_softmax_valid_calls_reach_the_device_check(L):
         assert f(L, C=15, NH=3) == EDEV                    # HS = 5 fp32: 20-byte heads
         assert f(L, C=3 * 80, NH=3, ind=F32) == EDEV       # HS = 80 fp32: 320-byte heads
         assert f(L, C=3 * 136, NH=3, ind=BF16) == EDEV     # HS = 136 bf16: 272-byte heads
-        assert f(L, C=3 * 160, NH=3, ind=F32) == EDEV      # 640-byte heads: the largest accepted
+        assert f(L, C=3 * 160, NH=3, ind=F32) == EDEV      # HS = 160 fp32: 640-byte heads, one chunk
+        assert f(L, C=3 * 161, NH=3, ind=F32) == EDEV      # HS = 161 fp32: two chunks
+        assert f(L, C=3 * 336, NH=3, ind=BF16) == EDEV     # HS = 336 bf16: 672-byte heads
+        assert f(L, C=3 * 1024, NH=3, ind=F32) == EDEV     # HS = 1024 fp32: 4 KB heads
         assert f(L, B=1, T=2**22, C=12, NH=3) == EDEV      # past the fast kernels' T limit
         assert f(L, B=2**23, T=1, C=4, NH=1) == EDEV       # past the fast kernels' grid limits
 

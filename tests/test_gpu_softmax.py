@@ -670,12 +670,14 @@ def test_workload_attention_fused_bf16_full_size(orc):
 #
 # Heads whose rows do not split into 16-byte pieces (HS = 3 and 5 in fp32,
 # 12 in binary16, a base one element off alignment) or exceed 512 bytes
-# (HS = 160 in fp32) run on the general-shape kernels. Heads of 257 .. 512
+# (HS = 160 in fp32; 161 and 333 in fp32 and 336 in bfloat16, staged in two
+# or three chunks of at most 640 bytes) run on the general-shape kernels. Heads of 257 .. 512
 # bytes in 16-byte pieces (fp32 HS = 80, bf16 HS = 136) take the fast
 # kernels' wide variants (32 pieces per row) and, for the softmax rows, the
 # per-wave tile kernel with the softmax epilogue: the wide-head tests below.
 
-GENERAL = [("f32", 3), ("f32", 5), ("f32", 160), ("f16", 12), ("bf16", 3)]
+GENERAL = [("f32", 3), ("f32", 5), ("f32", 160), ("f32", 161), ("f32", 333), ("f16", 12), ("bf16", 3),
+           ("bf16", 336)]
 GENERAL_ATT = GENERAL
 GENERAL_T = [1, 33, 64, 100, 300]
 
