@@ -445,8 +445,8 @@ CAS_EXPORT const char *cas_status_string(int status)
     case CAS_ERR_DEVICE: return "the current HIP device is not a gfx950 (MI355X) GPU or is unavailable";
     case CAS_ERR_HIP: return "HIP launch failed (see cas_last_hip_error)";
     case CAS_ERR_UNSUPPORTED:
-        return "valid arguments outside the kernels' domain (softmax and attention: a head over 640 bytes with HS "
-               "rounded up to 32 elements, qkv off the element alignment, or statistics not 4-byte aligned)";
+        return "valid arguments outside the kernels' domain (softmax and attention: qkv off the element "
+               "alignment, or statistics not 4-byte aligned)";
     case CAS_ERR_MODE: return "unknown softmax mode";
     default: return "unknown status";
     }

@@ -568,8 +568,9 @@ trimul_kernel(const char *__restrict__ qkv, float *__restrict__ out, int64_t T, 
 }
 
 // ---------------------------------------------------------------------------
-// Super-tile kernel (rows 16-byte aligned, HS*ES <= 256 bytes): a workgroup
-// step is one 128x128 super-tile (I, J <= I). Its 128 Q rows and 128 K rows
+// Super-tile kernel (rows 16-byte aligned, HS*ES <= 256 bytes, or up to 512
+// in two halves, HV below): a workgroup step is one 128x128 super-tile
+// (I, J <= I). Its 128 Q rows and 128 K rows
 // are fetched once, with coalesced 16-byte loads (8 or 16 lanes per row), into
 // an XOR-swizzled LDS operand buffer: chunk c of row r sits at position
 // c ^ (r % 8), so the MFMA operand reads (32 rows, one chunk) and the row
@@ -1242,9 +1243,9 @@ template <class E>
 hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
 {
     // Super-tile kernel wherever it applies (16-byte aligned rows, heads of
-    // at most 256 bytes): measured ahead of the per-wave tile kernel for every
-    // input type. CAS_TRIMUL_KERNEL=tile forces the tile kernel (tests and
-    // tuning).
+    // at most 256 bytes, or up to 512 in two halves where that pays):
+    // measured ahead of the per-wave tile kernel for every input type.
+    // CAS_TRIMUL_KERNEL=tile forces the tile kernel (tests and tuning).
     const char *kv = std::getenv("CAS_TRIMUL_KERNEL");
     const bool force_tile = kv && std::strcmp(kv, "tile") == 0;
     const int64_t nts = (a.T + ST - 1) / ST;
