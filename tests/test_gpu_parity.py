@@ -494,6 +494,23 @@ def test_trimul_wide_heads_two_halves(orc, monkeypatch, T, dtype, HS):
     assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
 
 
+@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("bf16", 256), ("bf16", 136)], ids=lambda v: str(v))
+def test_trimul_wide_heads_many_items(orc, monkeypatch, dtype, HS):
+    """Two head halves over many super-tiles per workgroup (B2 T1024 NH8:
+    576 items on a grid of at most one workgroup per CU), so every
+    workgroup walks several items (operand halves, mirror and output buffer
+    handed on from item to item): the whole output against the oracle, and
+    bit for bit against the tile kernel."""
+    B, T, NH = 2, 1024, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 81)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul(qkv, dtype, B, T, NH, HS, "two halves many items")
+    assert_scores(out, ref, bound, dtype, f"trimul two halves many items {dtype} HS={HS}")
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+    out_t = run_trimul(qkv, dtype, B, T, NH, HS, "two halves many items, tile kernel")
+    assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,HS", [("f32", 100), ("bf16", 256)], ids=lambda v: str(v))
 def test_trimul_wide_heads_out16(orc, dtype, HS, out_dtype):

@@ -795,6 +795,36 @@ def test_softmax_wide_heads_kernels_agree(orc, monkeypatch, dtype, HS):
     check_case(orc, qkv, dtype, B, T, NH, HS, "prob", label="wide heads super")
 
 
+@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("bf16", 256)], ids=lambda v: str(v))
+def test_softmax_wide_heads_many_items(orc, monkeypatch, dtype, HS):
+    """Wide-head softmax rows over many super-tiles per workgroup (B2 T1024
+    NH8): bit for bit against the tile kernel, both modes, fp32 and bf16
+    output, and sampled rows of the plane against the oracle."""
+    B, T, NH = 2, 1024, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 83)
+    for mode in ("prob", "log"):
+        for out_dtype in ("f32", "bf16"):
+            got = {}
+            for kernel in ("super", "tile"):
+                if kernel == "tile":
+                    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+                else:
+                    monkeypatch.delenv("CAS_TRIMUL_KERNEL", raising=False)
+                got[kernel] = run_softmax(qkv, dtype, B, T, NH, HS, mode, out_dtype, f"many items {kernel}")
+            for a, b in zip(got["super"], got["tile"]):
+                assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), \
+                    f"{mode} {out_dtype}: kernels differ"
+    monkeypatch.delenv("CAS_TRIMUL_KERNEL", raising=False)
+    out, mx, ls = run_softmax(qkv, dtype, B, T, NH, HS, "prob", "f32", "many items oracle rows")
+    for b, h, t0 in [(0, 0, 0), (1, 5, 500), (1, 7, 992)]:
+        ref, mref, lref, bound = orc.causal_softmax_rows(qkv, B, T, NH * HS, NH, b, h, t0, t0 + 32, dtype, "prob")
+        r0 = (b * NH + h) * T + t0
+        t_idx = np.arange(t0, t0 + 32)
+        what = f"many items {dtype} HS={HS} b={b} h={h} t0={t0}"
+        assert_softmax_stats(mx[r0:r0 + 32], ls[r0:r0 + 32], mref, lref, bound, t_idx, dtype, what)
+        assert_softmax(out[r0:r0 + 32], ref, lref, bound, t_idx, dtype, "prob", "f32", what)
+
+
 @pytest.mark.parametrize("T", [130, 200])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,HS", [("f32", 80), ("bf16", 136)], ids=lambda v: str(v))
