@@ -1003,17 +1003,17 @@ template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStre
 }
 
 // Softmax rows: the three-role score kernel with the softmax epilogue; heads
-// of 257 .. 512 bytes in two halves where that pays, else (and with
-// CAS_TRIMUL_KERNEL=tile) on the per-wave tile kernel with the same
-// epilogue. mode 0: log-probabilities, 1: probabilities.
+// of 257 .. 512 bytes in two halves (CAS_TRIMUL_KERNEL=tile: on the per-wave
+// tile kernel with the same epilogue). mode 0: log-probabilities, 1:
+// probabilities.
 template <class E, class EP> hipError_t launch_softmax_ep(const TrimulArgs &a, hipStream_t s)
 {
     if (a.HS * E::ES > 256) {
         const char *kv = std::getenv("CAS_TRIMUL_KERNEL");
-        if ((kv && std::strcmp(kv, "tile") == 0) || !tri::two_halves_pay<E>(a.HS)) return tri::launch_tile_ep<E, EP>(a, s);
-        if (a.out_kind == 1) return tri::launch_super<E, 16, tri::OBF16, EP, 2>(a, s);
-        if (a.out_kind == 2) return tri::launch_super<E, 16, tri::OF16, EP, 2>(a, s);
-        return tri::launch_super<E, 16, tri::OF32, EP, 2>(a, s);
+        if (kv && std::strcmp(kv, "tile") == 0) return tri::launch_tile_ep<E, EP>(a, s);
+        if (a.out_kind == 1) return tri::launch_two_halves<E, tri::OBF16, EP>(a, s);
+        if (a.out_kind == 2) return tri::launch_two_halves<E, tri::OF16, EP>(a, s);
+        return tri::launch_two_halves<E, tri::OF32, EP>(a, s);
     }
     const bool narrow = a.HS * E::ES <= 128;
     if (a.out_kind == 1)

@@ -727,11 +727,13 @@ __device__ __forceinline__ Frag read_frag(const char *krow, const char *qrow, in
 // diagonal sub-tile the block (kb=1, qb=0) lies above the diagonal; it is
 // computed anyway and masked to NaN on the way out: a branch around its MFMAs
 // would make the compiler copy the accumulators, waiting on the matrix pipe.
-template <class E, int NCH>
+// NU: the chunk pairs multiplied (fewer than NCH / 2 when the rest of the
+// staged rows is known to be zero).
+template <class E, int NCH, int NU = NCH / 2>
 __device__ __forceinline__ void sub_mma(f32x16 (&acc)[2][2], const char *opb, int a, int b, int lane)
 {
     constexpr int RB = NCH * 16;
-    constexpr int NU = NCH / 2;
+    static_assert(NU >= 1 && NU <= NCH / 2, "chunk pairs of the staged rows");
     const int r32 = lane & 31, h = lane >> 5, xr = r32 & 7;
     const char *qrow = opb + (a * TB + r32) * RB;
     const char *krow = opb + (ST + b * TB + r32) * RB;
@@ -947,9 +949,11 @@ __device__ __forceinline__ void stream_subtile(const Tile &tl, bool all_masked, 
 // loaders stage the Q and K rows' first half, then their second half, and
 // the compute waves keep accumulating into the same registers, so every
 // score sums the same products in the same order as with one whole-row
-// step. The tile goes to LDS after the second step; the store waves stream
-// it during the next item's first step and its mirror during the second.
-template <class E, int NCH, class O, class EP = EpScore, int HV = 1>
+// step. NU2: the chunk pairs of the second half multiplied (NCH / 4 when the
+// head ends within its first 128 bytes: the rest is zero). The tile goes to
+// LDS after the second step; the store waves stream it during the next
+// item's first step and its mirror during the second.
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store,
@@ -1062,7 +1066,7 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
                 lds_barrier(); // X: first half consumed
                 lds_barrier(); // Y: second half in LDS
             }
-            if (live) sub_mma<E, NCH>(acc, opb, sa, sb, lane);
+            if (live) sub_mma<E, NCH, HV == 2 ? NU2 : NCH / 2>(acc, opb, sa, sb, lane);
             lds_barrier(); // X: operand rows consumed, previous tile read back
             if (live) {
                 if (sp.diag && sa == sb) subtile_to_lds<true, O, EP>(acc, my_out, scale, lane, mx, ls);
@@ -1127,10 +1131,10 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
     }
 }
 
-template <class E, int NCH, class O, class EP = EpScore, int HV = 1>
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2>
 hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_super_kernel<E, NCH, O, EP, HV>;
+    auto kern = trimul_super_kernel<E, NCH, O, EP, HV, NU2>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -1228,15 +1232,13 @@ hipError_t launch_u(const TrimulArgs &a, hipStream_t s)
     }
 }
 
-// Heads of 257 .. 512 bytes: the super-tile kernel in two 256-byte halves
-// multiplies the second half whole, zeros included. For 16-bit inputs (the
-// launch bound by its stores) that always pays; for fp32 inputs, bound by
-// the MFMAs, only from 385 bytes on, where the tile kernel's 128-byte passes
-// multiply as many zeros (fp32 B4 T2048 NH12: HS 80 253 us on the tile
-// kernel against 278 in two halves; HS 128 335 against 273 us).
-template <class E> bool two_halves_pay(int64_t HS)
+// Heads of 257 .. 512 bytes: the super-tile kernel in two 256-byte halves,
+// the second multiplied over 128 bytes when the head ends there (as many
+// chunks as the tile kernel's 128-byte passes take), else whole.
+template <class E, class O, class EP> hipError_t launch_two_halves(const TrimulArgs &a, hipStream_t s)
 {
-    return !std::is_same<E, KF32>::value || HS * E::ES > 384;
+    if (a.HS * E::ES <= 384) return launch_super<E, 16, O, EP, 2, 4>(a, s);
+    return launch_super<E, 16, O, EP, 2, 8>(a, s);
 }
 
 template <class E>
@@ -1252,14 +1254,13 @@ hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
     const bool ids_fit = a.B * a.NH * (nts * (nts + 1) / 2) <= INT32_MAX;
     // The super-tile kernel's buffer offsets within a 64-row tile reach 256 T
     // bytes, under the 2^31 range of its buffer resources for T < 2^22.
-    // Heads of 257 .. 512 bytes take it in two halves of 256 (two_halves_pay).
-    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.T < (int64_t(1) << 22) &&
-                          (a.HS * E::ES <= 256 || (a.HS * E::ES <= 512 && two_halves_pay<E>(a.HS)));
+    // Heads of 257 .. 512 bytes take it in two halves of 256.
+    const bool super_ok = ids_fit && vec * E::ES >= 16 && a.HS * E::ES <= 512 && a.T < (int64_t(1) << 22);
     if (super_ok && !force_tile) {
         if (a.HS * E::ES > 256) {
-            if (a.out_kind == 1) return launch_super<E, 16, OBF16, EpScore, 2>(a, s);
-            if (a.out_kind == 2) return launch_super<E, 16, OF16, EpScore, 2>(a, s);
-            return launch_super<E, 16, OF32, EpScore, 2>(a, s);
+            if (a.out_kind == 1) return launch_two_halves<E, OBF16, EpScore>(a, s);
+            if (a.out_kind == 2) return launch_two_halves<E, OF16, EpScore>(a, s);
+            return launch_two_halves<E, OF32, EpScore>(a, s);
         }
         const bool narrow = a.HS * E::ES <= 128;
         if (a.out_kind == 1) return narrow ? launch_super<E, 8, OBF16>(a, s) : launch_super<E, 16, OBF16>(a, s);

@@ -474,7 +474,7 @@ def test_trimul_ragged_16bit(orc, monkeypatch, T, HS, dtype, kernel):
     assert_scores(out, ref, bound, dtype, f"trimul {dtype} T={T} HS={HS}")
 
 
-WIDE_HEADS = [("f32", 100), ("f32", 112), ("f32", 128), ("bf16", 136), ("bf16", 200), ("bf16", 256), ("f16", 144)]
+WIDE_HEADS = [("f32", 68), ("f32", 96), ("f32", 100), ("f32", 112), ("f32", 128), ("bf16", 136), ("bf16", 200), ("bf16", 256), ("f16", 144)]
 
 
 @pytest.mark.parametrize("T", [1, 65, 128, 129, 300])
@@ -494,7 +494,7 @@ def test_trimul_wide_heads_two_halves(orc, monkeypatch, T, dtype, HS):
     assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
 
 
-@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("bf16", 256), ("bf16", 136)], ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("f32", 80), ("bf16", 256), ("bf16", 136)], ids=lambda v: str(v))
 def test_trimul_wide_heads_many_items(orc, monkeypatch, dtype, HS):
     """Two head halves over many super-tiles per workgroup (B2 T1024 NH8:
     576 items on a grid of at most one workgroup per CU), so every

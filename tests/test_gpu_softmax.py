@@ -772,7 +772,7 @@ def test_softmax_wide_heads(orc, launch, dtype, HS, T, mode):
     check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="wide heads", launch=launch)
 
 
-@pytest.mark.parametrize("dtype,HS", [("f32", 100), ("bf16", 256)], ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,HS", [("f32", 100), ("f32", 80), ("bf16", 256), ("bf16", 136)], ids=lambda v: str(v))
 def test_softmax_wide_heads_kernels_agree(orc, monkeypatch, dtype, HS):
     """The wide-head softmax rows from the super-tile kernel (two head
     halves) equal those of the per-wave tile kernel bit for bit, both
@@ -795,7 +795,7 @@ def test_softmax_wide_heads_kernels_agree(orc, monkeypatch, dtype, HS):
     check_case(orc, qkv, dtype, B, T, NH, HS, "prob", label="wide heads super")
 
 
-@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("bf16", 256)], ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,HS", [("f32", 128), ("f32", 80), ("bf16", 256)], ids=lambda v: str(v))
 def test_softmax_wide_heads_many_items(orc, monkeypatch, dtype, HS):
     """Wide-head softmax rows over many super-tiles per workgroup (B2 T1024
     NH8): bit for bit against the tile kernel, both modes, fp32 and bf16
