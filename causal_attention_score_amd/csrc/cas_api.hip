@@ -103,6 +103,26 @@ int pick_vec(int es, const int64_t *lens, int nlens, const void *const *ptrs, in
     return 1;
 }
 
+// Widest 16-byte-or-narrower piece of the packed QKV rows for the score,
+// softmax and attention kernels: from the head and row lengths alone when
+// the base sits at its element alignment. Their buffer loads of 16 bytes
+// take any base alignment (every row then shares the base's offset within a
+// 16-byte line); a base off its element alignment gets single elements.
+int pick_vec_qkv(int es, int64_t HS, int64_t C, const void *qkv)
+{
+    if ((uintptr_t)qkv % (uintptr_t)es != 0) return 1;
+    const int64_t lens[2] = {HS, C};
+    return pick_vec(es, lens, 2, nullptr, 0);
+}
+
+// CAS_SOFTMAX_KERNEL=general puts the causal softmax and attention on the
+// general-shape kernels (tests and tuning).
+bool force_general_softmax()
+{
+    const char *v = std::getenv("CAS_SOFTMAX_KERNEL");
+    return v && std::strcmp(v, "general") == 0;
+}
+
 // CAS_GEMM_TILE=64|128|256 forces the dense tile shape (tests and tuning;
 // 256 applies where its kernel does, see gemm_wide_fits); anything else leaves
 // the automatic choice.
@@ -226,9 +246,7 @@ CAS_EXPORT int cas_trimul_causal(const void *qkv, void *out, int64_t B, int64_t 
     a.scale = (float)(1.0 / std::sqrt((double)HS)); // nearest fp32 to 1/sqrt(HS)
     a.vec_store = ((T * ob) % 16 == 0) && ((uintptr_t)out % 16 == 0);
     a.out_kind = (int)out_dtype;
-    const int64_t lens[2] = {HS, C};
-    const void *ptrs[1] = {qkv};
-    const int vec = pick_vec(es, lens, 2, ptrs, 1);
+    const int vec = pick_vec_qkv(es, HS, C, qkv);
     return launch_status(cas::launch_trimul(a, in_dtype, vec, (hipStream_t)stream));
 }
 
@@ -256,9 +274,7 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     if (*inb >= (INT64_C(1) << 62) || *outb >= (INT64_C(1) << 62)) return CAS_ERR_SHAPE;
     if (c3 * es >= (INT64_C(1) << 24) || T >= (INT64_C(1) << 24)) return CAS_ERR_SHAPE;
     const int64_t HS = C / NH;
-    const int64_t lens[2] = {HS, C};
-    const void *ptrs[1] = {qkv};
-    *vec = qkv ? pick_vec(es, lens, 2, ptrs, 1) : 1;
+    *vec = qkv ? pick_vec_qkv(es, HS, C, qkv) : 1;
     const int64_t nts = (T + 127) / 128;
     if (B * NH * (nts * (nts + 1) / 2) > INT32_MAX || cas::row_stats_workgroups(B, T, NH) > INT32_MAX)
         return CAS_ERR_SHAPE;
@@ -266,7 +282,7 @@ int softmax_checks(const void *qkv, int64_t B, int64_t T, int64_t C, int64_t NH,
     // work-items (256 per workgroup) while the B * NH planes of one block fit
     // in one grid
     const bool fast = cas::softmax_fits(T, HS, es, *vec);
-    *general = !fast || B * NH >= (INT64_C(1) << 23);
+    *general = !fast || B * NH >= (INT64_C(1) << 23) || force_general_softmax();
     if (*general && !cas::general_softmax_fits(B, T, NH, es, qkv)) return CAS_ERR_UNSUPPORTED;
     return CAS_OK;
 }

@@ -32,12 +32,16 @@
  *   - The output byte range may not overlap an input byte range.
  *   - Any alignment is accepted (the softmax and attention: elements at their
  *     natural alignment); 16-byte aligned bases and pitches select wider loads
- *     and stores, with the same results.
+ *     and stores, with the same results. For the packed QKV rows only the
+ *     head and row lengths decide: a qkv base at its element alignment but
+ *     not on a 16-byte boundary still takes 16-byte pieces.
  *   - Kernel variants are chosen by shape, dtype and alignment. Environment
  *     variables read at each call override the choice for tests and tuning:
  *     CAS_GEMM_TILE, CAS_GEMM_F32, CAS_GEMM_WIDE, CAS_VARIANT (gemm_nt and
  *     batch_matmul_nt), CAS_TRIMUL_KERNEL, CAS_TRIMUL_PASS (trimul_causal and
- *     the softmax rows) and CAS_SOFTMAX_FUSED (cas_causal_softmax_fused).
+ *     the softmax rows), CAS_SOFTMAX_FUSED (cas_causal_softmax_fused) and
+ *     CAS_SOFTMAX_KERNEL=general (the general-shape softmax and attention
+ *     kernels).
  *     Every variant meets the same accuracy bounds; those with another
  *     accumulation order may differ from the default in the last bits.
  */
@@ -163,8 +167,8 @@ int cas_trimul_causal(const void *qkv, void *out,
  *               even).
  *
  * Both: fp32 arithmetic. Two sets of kernels serve the calls:
- *   - fast kernels where the QKV rows split into 16-byte pieces (qkv 16-byte
- *     aligned, HS and C times the element size multiples of 16), HS times the
+ *   - fast kernels where the QKV rows split into 16-byte pieces (qkv at its
+ *     element alignment, HS and C times the element size multiples of 16), HS times the
  *     element size is at most 512 bytes, T < 2^22 and B * NH < 2^23; there
  *     the scores are bit-identical to cas_trimul_causal's (same products in
  *     the same order);

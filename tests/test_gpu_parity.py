@@ -577,21 +577,30 @@ def test_trimul_out16_unaligned(orc, monkeypatch, out_dtype, kernel):
     assert_scores16(out, ref, bound, "bf16", out_dtype, f"trimul unaligned ->{out_dtype}")
 
 
+@pytest.mark.parametrize("kernel", ["super", "tile"])
+@pytest.mark.parametrize("HS", [16, 64, 128])
+@pytest.mark.parametrize("offset", [1, 3])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_trimul_misaligned_base(orc, dtype):
-    """qkv one element past a 16-byte boundary: the narrow fetch variant."""
-    B, T, NH, HS = 2, 70, 2, 16
+def test_trimul_misaligned_base(orc, monkeypatch, dtype, offset, HS, kernel):
+    """qkv `offset` elements past a 16-byte boundary: the 16-byte pieces are
+    loaded at the base's offset within a line. Against the oracle, and bit for
+    bit against the same input at an aligned base."""
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", kernel)
+    B, T, NH = 2, 70, 2
     n = B * T * 3 * NH * HS
-    flat = synth.to_storage(synth.normal_f32(synth.rng(3), (n + 1,)), dtype)
-    qkv = flat[1:].reshape(B, T, 3 * NH * HS)
+    flat = synth.to_storage(synth.normal_f32(synth.rng(3 + HS), (n + offset,)), dtype)
+    qkv = flat[offset:].reshape(B, T, 3 * NH * HS)
     ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
     d = to_device(flat, dtype)
     buf, o = guarded_output(B * NH * T * T)
-    case(f"trimul misaligned {dtype}")
-    cas.trimul_causal(d[1:].view(B, T, -1), NH, out=o.view(B, NH, T, T))
+    case(f"trimul misaligned {dtype} offset={offset} HS={HS} {kernel}")
+    cas.trimul_causal(d[offset:].view(B, T, -1), NH, out=o.view(B, NH, T, T))
     torch.cuda.synchronize()
     check_guards(buf, B * NH * T * T)
-    assert_scores(o.view(B, NH, T, T).cpu().numpy(), ref, bound, dtype, f"trimul misaligned {dtype}")
+    got = o.view(B, NH, T, T).cpu().numpy()
+    assert_scores(got, ref, bound, dtype, f"trimul misaligned {dtype} offset={offset} HS={HS}")
+    aligned = run_trimul(qkv, dtype, B, T, NH, HS, "aligned twin")
+    assert np.array_equal(got.view(np.uint32), aligned.view(np.uint32)), "misaligned base changes the scores"
 
 
 def test_trimul_5d_input_and_side_stream(orc):

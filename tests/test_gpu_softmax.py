@@ -701,15 +701,28 @@ def test_softmax_general_out16(orc, dtype, HS, out_dtype):
         check_case(orc, qkv, dtype, B, T, NH, HS, mode, out_dtype, label="general out16", launch="fused")
 
 
+KERNELS = ["fast", "general"]
+
+
+def use_kernels(monkeypatch, kernel):
+    if kernel == "general":
+        monkeypatch.setenv("CAS_SOFTMAX_KERNEL", "general")
+    else:
+        monkeypatch.delenv("CAS_SOFTMAX_KERNEL", raising=False)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("launch", LAUNCHES)
-def test_softmax_misaligned_base(orc, launch, dtype):
+def test_softmax_misaligned_base(orc, monkeypatch, launch, dtype, kernel):
     """HS = 64 with qkv one element past a 16-byte boundary: the fast
-    kernels' domain needs 16-byte pieces, so the general kernels run."""
+    kernels (16-byte pieces at the base's offset) and the general ones."""
+    use_kernels(monkeypatch, kernel)
     B, T, NH, HS = 2, 150, 2, 64
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=23)
     for mode in ("prob", "log"):
-        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label="misaligned base", launch=launch, qkv_offset=1)
+        check_case(orc, qkv, dtype, B, T, NH, HS, mode, label=f"misaligned base {kernel}", launch=launch,
+                   qkv_offset=1)
 
 
 @pytest.mark.parametrize("T", GENERAL_T)
@@ -880,8 +893,10 @@ def test_softmax_wide_heads_stats_match_the_score_kernel(orc, dtype, HS):
     assert torch.equal(lp.amax(dim=-1).view(torch.int32), (-ls).view(torch.int32)), "max lp"
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_attention_general_misaligned_base(orc, dtype):
+def test_attention_misaligned_base(orc, monkeypatch, dtype, kernel):
+    use_kernels(monkeypatch, kernel)
     B, T, NH, HS = 2, 97, 2, 64
     qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=31)
     check_attention(orc, qkv, dtype, B, T, NH, HS, "misaligned base", qkv_offset=1)
@@ -889,12 +904,15 @@ def test_attention_general_misaligned_base(orc, dtype):
     check_attention(orc, qkv, dtype, B, T, NH, HS, "misaligned base one launch", y=y)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_general_saturated_ramp(orc, dtype):
-    """Exact-score saturated rows (slopes 64, -16, 0.25, 200) on the general
-    kernels (HS = 64, where the scale 1/8 keeps every score exact, with a base
-    one element off alignment): statistics, probabilities and the attention
-    output pinned to exp / sum roundings only."""
+def test_general_saturated_ramp(orc, monkeypatch, dtype, kernel):
+    """Exact-score saturated rows (slopes 64, -16, 0.25, 200) with a base one
+    element off alignment, on the general kernels and on the fast ones (HS =
+    64, where the scale 1/8 keeps every score exact): statistics,
+    probabilities and the attention output pinned to exp / sum roundings
+    only."""
+    use_kernels(monkeypatch, kernel)
     B, T, NH, HS = 1, 257, 4, 64
     qkv = synth.ramp_qk_inputs(B, T, NH, HS, [8.0 * a for a in SAT_SLOPES], dtype, v_seed=47)
     for mode in ("prob", "log"):
