@@ -158,10 +158,13 @@ int64_t gemm_nt_workgroups(const GemmArgs &a, int /*elem*/, int tile)
 
 hipError_t launch_gemm_nt(const GemmArgs &a, int elem, int vec, int tile, hipStream_t s)
 {
-    // 256 x 256 tiles where every CU gets one (M = N = 4096 and up).
-    if (elem != E_F32 && !a.predicated && a.batch == 1 && gemm_wide_fits(a, 2, vec) &&
-        (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256)))
-        return launch_gemm_wide(a, elem, s);
+    // 256 x 256 tiles where every CU gets one (M = N = 4096 and up); rows
+    // not in 16-byte pieces take them too, with a tail kernel for K % 8.
+    if (elem != E_F32 && !a.predicated && a.batch == 1 &&
+        (tile == GEMM_TILE_256 || (tile == GEMM_TILE_AUTO && gemm_wide_workgroups(a) >= 256))) {
+        if (gemm_wide_fits(a, 2, vec)) return launch_gemm_wide(a, elem, s);
+        if (gemm_wide_fits_unaligned(a, 2)) return launch_gemm_wide_unaligned(a, elem, s);
+    }
     // fp32 on 64 x 64 tiles: loads straight into LDS where the rows allow
     // (CAS_GEMM_F32=ring keeps the register-ring engine, e.g. to compare).
     if (elem == E_F32 && pick_tile(a, tile) == GEMM_TILE_64 && gemm_direct_fits(a, elem, vec)) {

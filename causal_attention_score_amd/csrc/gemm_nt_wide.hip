@@ -530,4 +530,96 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s)
     return elem == E_BF16 ? launch_wide_elem<KBF16>(a, s) : launch_wide_elem<KF16>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Rows not in 16-byte pieces (an odd pitch, a base off a 16-byte boundary, K
+// not a multiple of 8). The load unit's 16-byte buffer loads take any element
+// alignment, so the wide kernel runs over the first K8 = K - K % 8 columns,
+// whose pieces all lie inside their rows; the last r = K % 8 columns are then
+// added by a tail kernel, y += sum_{j < r} x[m][K8 + j] w[n][K8 + j], one
+// fused multiply-add per column in column order (the same products; the
+// tolerance of fp32 accumulation covers the order).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int KT_B = 64; // output block edge of the tail kernel
+
+// A 16-bit element's value in fp32 (exact for both formats).
+template <class E> __device__ __forceinline__ float to_f32(uint16_t bits);
+template <> __device__ __forceinline__ float to_f32<KBF16>(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+template <> __device__ __forceinline__ float to_f32<KF16>(uint16_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+template <class E>
+__global__ void __launch_bounds__(256) gemm_ktail_kernel(const char *__restrict__ X, const char *__restrict__ W,
+                                                          float *__restrict__ Y, int64_t M, int64_t N, int64_t K8,
+                                                          int r, int64_t ldx, int64_t ldw, int64_t ldy, int64_t tn)
+{
+    using U = uint16_t;
+    __shared__ float xs[KT_B][8];
+    __shared__ float ws[KT_B][8];
+    const int tid = threadIdx.x;
+    const int64_t bm = blockIdx.x / tn, bn = blockIdx.x - bm * tn;
+    const int64_t m0 = bm * KT_B, n0 = bn * KT_B;
+    // the tail columns of the block's 64 X rows and 64 W rows, as fp32 (zero past M / N)
+    for (int i = tid; i < 2 * KT_B * 8; i += 256) {
+        const int side = i / (KT_B * 8), row = (i / 8) % KT_B, j = i % 8;
+        float v = 0.f;
+        if (j < r) {
+            if (side == 0 && m0 + row < M)
+                v = to_f32<E>(*reinterpret_cast<const U *>(X + ((m0 + row) * ldx + K8 + j) * 2));
+            else if (side == 1 && n0 + row < N)
+                v = to_f32<E>(*reinterpret_cast<const U *>(W + ((n0 + row) * ldw + K8 + j) * 2));
+        }
+        (side == 0 ? xs : ws)[row][j] = v;
+    }
+    __syncthreads();
+    const int c = tid % KT_B, rq = tid / KT_B; // column c; rows rq, rq + 4, ..
+    const int64_t n = n0 + c;
+    if (n >= N) return;
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = ws[c][j];
+    for (int i = rq; i < KT_B; i += 4) {
+        const int64_t m = m0 + i;
+        if (m >= M) break;
+        float *y = Y + m * ldy + n;
+        float v = *y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < r) v = __builtin_fmaf(xs[i][j], w[j], v);
+        *y = v;
+    }
+}
+
+template <class E> hipError_t launch_ktail(const GemmArgs &a, int64_t K8, hipStream_t s)
+{
+    const int64_t tm = (a.M + KT_B - 1) / KT_B, tn = (a.N + KT_B - 1) / KT_B;
+    hipLaunchKernelGGL((gemm_ktail_kernel<E>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, (const char *)a.X,
+                       (const char *)a.W, a.Y, a.M, a.N, K8, (int)(a.K - K8), a.ldx, a.ldw, a.ldy, tn);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool gemm_wide_fits_unaligned(const GemmArgs &a, int es)
+{
+    // 16-bit elements at their alignment, at least one 8-column piece, and
+    // the same 31-bit tile offsets as gemm_wide_fits; the tail grid in 2^32.
+    const int64_t kt = ((a.M + KT_B - 1) / KT_B) * ((a.N + KT_B - 1) / KT_B);
+    return es == 2 && (uintptr_t)a.X % 2 == 0 && (uintptr_t)a.W % 2 == 0 && a.K >= 8 &&
+           a.ldx * es * WB + a.K * es < (int64_t(1) << 31) && a.ldw * es * WB + a.K * es < (int64_t(1) << 31) &&
+           kt <= UINT32_MAX;
+}
+
+hipError_t launch_gemm_wide_unaligned(const GemmArgs &a, int elem, hipStream_t s)
+{
+    GemmArgs b = a;
+    b.K = a.K - a.K % 8;
+    const hipError_t e = launch_gemm_wide(b, elem, s);
+    if (e != hipSuccess || b.K == a.K) return e;
+    return elem == E_BF16 ? launch_ktail<KBF16>(a, b.K, s) : launch_ktail<KF16>(a, b.K, s);
+}
+
 } // namespace cas

@@ -68,6 +68,11 @@ int64_t gemm_nt_workgroups(const GemmArgs &a, int elem, int tile);
 bool gemm_wide_fits(const GemmArgs &a, int es, int vec);
 int64_t gemm_wide_workgroups(const GemmArgs &a);
 hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s);
+// The same kernel for 16-bit rows not in 16-byte pieces (elements at their
+// alignment, K >= 8): the first K - K % 8 columns, then a tail kernel adding
+// the last K % 8 into Y.
+bool gemm_wide_fits_unaligned(const GemmArgs &a, int es);
+hipError_t launch_gemm_wide_unaligned(const GemmArgs &a, int elem, hipStream_t s);
 
 // 64 x 64 fp32 tiles with loads straight into LDS (gemm_nt_direct.hip): rows
 // and bases 8-byte aligned (vec >= 2), not predicated.

@@ -76,6 +76,35 @@ def test_gemm_wide_ragged(orc, monkeypatch, shape, dtype):
     assert_close(y, ref, bound, dtype, f"gemm wide {shape} {dtype}")
 
 
+# 16-bit rows not in 16-byte pieces on 256 x 256 tiles: K not a multiple of 8
+# (the wide kernel over the first K - K % 8 columns, a tail kernel adding the
+# rest), row pitches above K, and bases one element off a 16-byte boundary.
+# (M, N, K, base offset in elements, pitch padding in elements)
+WIDE_UNALIGNED = [(300, 520, 771, 0, 0), (257, 255, 9, 0, 0), (600, 40, 1023, 1, 3), (513, 260, 264, 1, 1),
+                  (256, 256, 130, 0, 5), (1024, 1024, 1023, 0, 0), (520, 513, 4097, 0, 0), (64, 300, 15, 1, 0)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE_UNALIGNED, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_wide_unaligned(orc, monkeypatch, shape, dtype):
+    monkeypatch.setenv("CAS_GEMM_TILE", "256")
+    M, N, K, off, pad = shape
+    ldx, ldw = K + pad, K + pad + 2
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    Xf = synth.to_storage(g.standard_normal((M * ldx + off,)).astype(np.float32), dtype)
+    Wf = synth.to_storage(g.standard_normal((N * ldw + off,)).astype(np.float32), dtype)
+    ref, bound = orc.gemm_nt(Xf[off:], Wf[off:], dtype, M=M, N=N, K=K, ldx=ldx, ldw=ldw, ldy=N)
+    dx, dw = to_device(Xf, dtype), to_device(Wf, dtype)
+    x = dx[off:].as_strided((M, K), (ldx, 1))
+    w = dw[off:].as_strided((N, K), (ldw, 1))
+    buf, flat = guarded_output(M * N)
+    case(f"gemm wide unaligned {shape} {dtype}")
+    cas.gemm_nt(x, w, out=flat.view(M, N))
+    torch.cuda.synchronize()
+    check_guards(buf, M * N)
+    assert_close(flat.view(M, N).cpu().numpy(), ref, bound, dtype, f"gemm wide unaligned {shape} {dtype}")
+
+
 # K a multiple of 128 (whole turns of the four-stage ring): the full-turn
 # kernel, whose fetch has no per-chunk predicate; ragged M and N, one turn
 # (K = 128) and several.
