@@ -11,8 +11,8 @@
 // an LDS write per 8 bytes for rows of 770 floats, which are only 8-byte
 // aligned, plus the out-of-range selects) costs MFMA time. Here each 16-byte
 // piece of a row goes from HBM straight into LDS with one buffer load per
-// kilobyte per wave (the load unit accepts 16-byte pieces at 8-byte-aligned
-// addresses), and the main loop holds MFMAs, LDS reads, these loads, one
+// kilobyte per wave (the load unit accepts 16-byte pieces at any 4-byte
+// aligned address), and the main loop holds MFMAs, LDS reads, these loads, one
 // barrier per chunk and scalar arithmetic only.
 //
 // Stage model (same docstring: Fetch, Compute, Writeback), with local padding:
@@ -256,13 +256,15 @@ gemm_nt_direct_kernel(const char *__restrict__ X, const char *__restrict__ W, fl
 
 bool gemm_direct_fits(const GemmArgs &a, int elem, int vec)
 {
-    // fp32, rows and bases 8-byte aligned (vec >= 2), 64-row tile offsets
-    // under 2^31 bytes. Its 64 KB of LDS hold two workgroups per CU against
+    // fp32 elements at their alignment (the load unit takes 16-byte pieces at
+    // any element alignment), 64-row tile offsets under 2^31 bytes. Its 64 KB of LDS hold two workgroups per CU against
     // the register-ring engine's four, so with more than 512 workgroups it
     // pays only on long contractions (measured: 192 heads of 120 x 120, 768
     // workgroups, K = 64 .. 256: 10.1 .. 18.7 us on the ring against 11.2 ..
     // 20.1 us; 960 x 2304 x 770, 540 workgroups: 43.4 against 47.1 us).
-    if (elem != E_F32 || a.predicated || vec < 2 || a.K <= 0) return false;
+    (void)vec;
+    if (elem != E_F32 || a.predicated || a.K <= 0 || (uintptr_t)a.X % 4 != 0 || (uintptr_t)a.W % 4 != 0)
+        return false;
     if (a.ldx * 4 * DT + a.K * 4 >= (int64_t(1) << 31) || a.ldw * 4 * DT + a.K * 4 >= (int64_t(1) << 31))
         return false;
     const int64_t wgs = ((a.M + DT - 1) / DT) * ((a.N + DT - 1) / DT) * a.batch;

@@ -228,19 +228,25 @@ def test_gemm_strided_misaligned(orc, dtype):
     assert_close(h[:, :N], ref[:, :N], bound[:, :N], dtype, "gemm strided")
 
 
-# fp32 on 64 x 64 tiles with loads straight into LDS (rows 8-byte aligned):
-# K below, at and just past one 32-float chunk, K % 4 == 2 (a 16-byte piece
-# straddles K and reads past the row), and row pitches whose padding holds
-# NaN, which must not reach the products. The register-ring engine
-# (CAS_GEMM_F32=ring) forms the same products in the same order: bit for bit.
+# fp32 on 64 x 64 tiles with loads straight into LDS: K below, at and just
+# past one 32-float chunk, K % 4 != 0 (a 16-byte piece straddles K and reads
+# past the row), row pitches even (8-byte-aligned rows) and odd (4-byte
+# aligned: the load unit takes the pieces at any element alignment), and
+# padding that holds NaN, which must not reach the products. The
+# register-ring engine (CAS_GEMM_F32=ring) forms the same products in the
+# same order: bit for bit.
 DIRECT_SHAPES = [(1, 1, 2), (70, 90, 98), (64, 64, 32), (65, 63, 34), (130, 200, 96), (257, 255, 770),
-                 (40, 300, 1026)]
+                 (40, 300, 1026), (1, 1, 1), (65, 63, 33), (257, 255, 771), (40, 300, 1025)]
 
 
+@pytest.mark.parametrize("pitch", ["even", "odd"])
 @pytest.mark.parametrize("shape", DIRECT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_gemm_direct_nan_padding_and_ring(orc, monkeypatch, shape):
+def test_gemm_direct_nan_padding_and_ring(orc, monkeypatch, shape, pitch):
     M, N, K = shape
-    ldx, ldw = K + 2, K + 6  # even pitches: 8-byte-aligned rows
+    if pitch == "even":
+        ldx, ldw = (K + 2, K + 6) if K % 2 == 0 else (K + 1, K + 5)
+    else:
+        ldx, ldw = (K + 1, K + 3) if K % 2 == 0 else (K, K + 2)
     g = np.random.default_rng(M * 31 + K)
     Xf = np.full(M * ldx, np.nan, np.float32)
     Wf = np.full(N * ldw, np.nan, np.float32)
