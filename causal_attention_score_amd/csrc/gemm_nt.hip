@@ -141,11 +141,27 @@ int pick_tile(const GemmArgs &a, int tile)
     return t128 >= 256 ? GEMM_TILE_128 : GEMM_TILE_64;
 }
 
+// The register ring fetches through buffer loads, which take pieces at any
+// element alignment (the base's and pitches' own alignment then does not
+// matter): where the ring applies, the piece width comes from K alone.
+template <class E, int BM>
+int ring_vec(const GemmArgs &a, int vec)
+{
+    constexpr int ES = E::ES;
+    if ((uintptr_t)a.X % ES != 0 || (uintptr_t)a.W % ES != 0) return vec;
+    constexpr int64_t BKB = GemmBK<E>::v * ES;
+    const int64_t lim = INT64_C(0x7FFFFFFF);
+    if (BM * a.ldx * ES + BKB > lim || BM * a.ldw * ES + BKB > lim) return vec; // no ring: pointer loads
+    for (int v = 16 / ES; v > vec; v /= 2)
+        if (a.K % v == 0 && (BM == 64 || v * ES == 16)) return v;
+    return vec;
+}
+
 template <class E>
 hipError_t launch_elem(const GemmArgs &a, int vec, int tile, hipStream_t s)
 {
-    if (pick_tile(a, tile) == GEMM_TILE_128) return launch_vec<E, 128, 128>(a, vec, s);
-    return launch_vec<E, 64, 64>(a, vec, s);
+    if (pick_tile(a, tile) == GEMM_TILE_128) return launch_vec<E, 128, 128>(a, ring_vec<E, 128>(a, vec), s);
+    return launch_vec<E, 64, 64>(a, ring_vec<E, 64>(a, vec), s);
 }
 
 } // namespace
