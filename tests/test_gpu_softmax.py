@@ -270,12 +270,24 @@ def test_softmax_saturated(orc, launch):
     assert np.all(err <= lim), f"row sums: worst {float((err / lim).max()):.3g} of the allowance"
 
 
-def test_softmax_rejections():
-    qkv = torch.zeros(2, 8, 3 * 2 * 200, device="cuda")      # HS = 200 fp32: 800-byte heads
-    for call in (lambda: cas.causal_softmax(qkv, 2), lambda: cas.causal_row_stats(qkv, 2)):
-        with pytest.raises(cas.CasError) as e:
-            call()
-        assert e.value.status == -7
+def test_softmax_big_heads_and_rejections():
+    """HS = 200 fp32 (800-byte heads, staged in two chunks) is served: zero
+    inputs give uniform rows. An fp32 base off its 4-byte alignment is
+    rejected, with nothing written."""
+    qkv = torch.zeros(2, 8, 3 * 2 * 200, device="cuda")
+    for fused in (False, True):
+        p, mx, ls = cas.causal_softmax(qkv, 2, fused=fused)
+        torch.cuda.synchronize()
+        assert torch.equal(mx, torch.zeros_like(mx)), "row maxima of zero scores"
+        assert bool((p.sum(-1) - 1).abs().max() < 1e-6), "rows sum to one"
+    buf = torch.zeros(2 * 8 * 3 * 2 * 8 + 1, device="cuda")
+    mx = torch.full((2, 2, 8), 7.0, device="cuda")
+    ls = torch.full((2, 2, 8), 7.0, device="cuda")
+    st = cas.lib().cas_causal_row_stats(buf.data_ptr() + 2, mx.data_ptr(), ls.data_ptr(), 2, 8, 16, 2,
+                                        cas.CAS_F32, cas._stream_ptr(buf.device))
+    assert st == -7
+    torch.cuda.synchronize()
+    assert bool((mx == 7.0).all()) and bool((ls == 7.0).all()), "a rejected call wrote"
     with pytest.raises(ValueError):
         cas.causal_softmax(torch.zeros(2, 8, 3 * 2 * 8, device="cuda"), 2, mode="softmax")
 
@@ -495,11 +507,12 @@ def test_attention_ragged_16bit(orc, T, HS, dtype):
 
 
 def test_attention_rejections():
-    qkv = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)   # 672-byte heads
+    # 672-byte binary16 heads are served (staged in chunks): zero values give zero y
+    qkv = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)
     mx = torch.zeros(2, 2, 8, device="cuda")
-    with pytest.raises(cas.CasError) as e:
-        cas.causal_attention(qkv, 2, stats=(mx, mx))
-    assert e.value.status == -7
+    y0, _, _ = cas.causal_attention(qkv, 2, stats=(mx, mx))
+    torch.cuda.synchronize()
+    assert bool((y0 == 0).all())
     # an fp32 base that is not 4-byte aligned (raw pointer through the C ABI)
     buf = torch.zeros(2 * 8 * 3 * 2 * 8 + 1, device="cuda")
     y = torch.zeros(2, 8, 16, device="cuda")
@@ -642,10 +655,16 @@ def test_attention_fused_empty_and_rejections():
     assert y.numel() == 0 and mx.numel() == 0
     y2, _, _ = cas.causal_attention(qkv, 2)
     assert y2.numel() == 0
-    bad = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)
-    with pytest.raises(cas.CasError) as e:
-        cas.causal_attention_fused(bad, 2)
-    assert e.value.status == -7
+    big = torch.zeros(2, 8, 3 * 2 * 336, device="cuda", dtype=torch.float16)  # 672-byte heads: served
+    yb, mxb, _ = cas.causal_attention_fused(big, 2)
+    torch.cuda.synchronize()
+    assert bool((yb == 0).all()) and bool((mxb == 0).all())
+    buf = torch.zeros(2 * 8 * 3 * 2 * 8 + 1, device="cuda")  # an fp32 base off its 4-byte alignment
+    y = torch.zeros(2, 8, 16, device="cuda")
+    m2, l2 = torch.zeros(2, 2, 8, device="cuda"), torch.zeros(2, 2, 8, device="cuda")
+    st = cas.lib().cas_causal_attention_fused(buf.data_ptr() + 2, y.data_ptr(), m2.data_ptr(), l2.data_ptr(),
+                                              2, 8, 16, 2, cas.CAS_F32, cas.CAS_F32, cas._stream_ptr(buf.device))
+    assert st == -7
 
 
 def test_workload_attention_fused_full_size(orc):
