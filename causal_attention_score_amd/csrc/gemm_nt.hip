@@ -160,7 +160,23 @@ int ring_vec(const GemmArgs &a, int vec)
 template <class E>
 hipError_t launch_elem(const GemmArgs &a, int vec, int tile, hipStream_t s)
 {
-    if (pick_tile(a, tile) == GEMM_TILE_128) return launch_vec<E, 128, 128>(a, ring_vec<E, 128>(a, vec), s);
+    if (pick_tile(a, tile) == GEMM_TILE_128) {
+        // The 128 x 128 ring needs 16-byte pieces; for K not a multiple of
+        // them it runs over the first K0 = K - K % VMAX columns and the tail
+        // kernel adds the rest (fp32 4096^2 x 4095: the two-stage loop with
+        // 4-byte loads before).
+        constexpr int VMAX = 16 / E::ES;
+        GemmArgs b = a;
+        b.K = a.K - a.K % VMAX;
+        if (a.K % VMAX != 0 && b.K > 0 && !a.predicated && a.batch == 1 && gemm_ktail_fits(a) &&
+            ring_vec<E, 128>(b, 1) == VMAX) {
+            const hipError_t e = launch_vec<E, 128, 128>(b, VMAX, s);
+            if (e != hipSuccess) return e;
+            return launch_gemm_ktail(a, std::is_same<E, KF32>::value ? E_F32
+                                        : std::is_same<E, KBF16>::value ? E_BF16 : E_F16, b.K, s);
+        }
+        return launch_vec<E, 128, 128>(a, ring_vec<E, 128>(a, vec), s);
+    }
     return launch_vec<E, 64, 64>(a, ring_vec<E, 64>(a, vec), s);
 }
 

@@ -537,18 +537,23 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s)
 // whose pieces all lie inside their rows; the last r = K % 8 columns are then
 // added by a tail kernel, y += sum_{j < r} x[m][K8 + j] w[n][K8 + j], one
 // fused multiply-add per column in column order (the same products; the
-// tolerance of fp32 accumulation covers the order).
+// tolerance of fp32 accumulation covers the order). The fp32 register ring
+// on 128 x 128 tiles uses the same tail kernel for K % 4 (gemm_nt.hip).
 // ---------------------------------------------------------------------------
 namespace {
 
 constexpr int KT_B = 64; // output block edge of the tail kernel
 
-// A 16-bit element's value in fp32 (exact for both formats).
-template <class E> __device__ __forceinline__ float to_f32(uint16_t bits);
-template <> __device__ __forceinline__ float to_f32<KBF16>(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
-template <> __device__ __forceinline__ float to_f32<KF16>(uint16_t bits)
+// An element's value in fp32 (exact for every input format).
+template <class E> __device__ __forceinline__ float elem_f32(const char *p);
+template <> __device__ __forceinline__ float elem_f32<KF32>(const char *p) { return *reinterpret_cast<const float *>(p); }
+template <> __device__ __forceinline__ float elem_f32<KBF16>(const char *p)
 {
-    return (float)__builtin_bit_cast(_Float16, bits);
+    return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
+}
+template <> __device__ __forceinline__ float elem_f32<KF16>(const char *p)
+{
+    return (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t *>(p));
 }
 
 template <class E>
@@ -556,7 +561,7 @@ __global__ void __launch_bounds__(256) gemm_ktail_kernel(const char *__restrict_
                                                           float *__restrict__ Y, int64_t M, int64_t N, int64_t K8,
                                                           int r, int64_t ldx, int64_t ldw, int64_t ldy, int64_t tn)
 {
-    using U = uint16_t;
+    constexpr int ES = E::ES;
     __shared__ float xs[KT_B][8];
     __shared__ float ws[KT_B][8];
     const int tid = threadIdx.x;
@@ -568,9 +573,9 @@ __global__ void __launch_bounds__(256) gemm_ktail_kernel(const char *__restrict_
         float v = 0.f;
         if (j < r) {
             if (side == 0 && m0 + row < M)
-                v = to_f32<E>(*reinterpret_cast<const U *>(X + ((m0 + row) * ldx + K8 + j) * 2));
+                v = elem_f32<E>(X + ((m0 + row) * ldx + K8 + j) * ES);
             else if (side == 1 && n0 + row < N)
-                v = to_f32<E>(*reinterpret_cast<const U *>(W + ((n0 + row) * ldw + K8 + j) * 2));
+                v = elem_f32<E>(W + ((n0 + row) * ldw + K8 + j) * ES);
         }
         (side == 0 ? xs : ws)[row][j] = v;
     }
@@ -619,7 +624,21 @@ hipError_t launch_gemm_wide_unaligned(const GemmArgs &a, int elem, hipStream_t s
     b.K = a.K - a.K % 8;
     const hipError_t e = launch_gemm_wide(b, elem, s);
     if (e != hipSuccess || b.K == a.K) return e;
-    return elem == E_BF16 ? launch_ktail<KBF16>(a, b.K, s) : launch_ktail<KF16>(a, b.K, s);
+    return launch_gemm_ktail(a, elem, b.K, s);
+}
+
+bool gemm_ktail_fits(const GemmArgs &a)
+{
+    return ((a.M + KT_B - 1) / KT_B) * ((a.N + KT_B - 1) / KT_B) <= UINT32_MAX;
+}
+
+hipError_t launch_gemm_ktail(const GemmArgs &a, int elem, int64_t K0, hipStream_t s)
+{
+    switch (elem) {
+    case E_F32: return launch_ktail<KF32>(a, K0, s);
+    case E_BF16: return launch_ktail<KBF16>(a, K0, s);
+    default: return launch_ktail<KF16>(a, K0, s);
+    }
 }
 
 } // namespace cas

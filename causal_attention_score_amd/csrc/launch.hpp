@@ -73,6 +73,9 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int elem, hipStream_t s);
 // the last K % 8 into Y.
 bool gemm_wide_fits_unaligned(const GemmArgs &a, int es);
 hipError_t launch_gemm_wide_unaligned(const GemmArgs &a, int elem, hipStream_t s);
+// Y += X[:, K0:K] W[:, K0:K]^T for the last K - K0 < 8 columns (batch 1).
+bool gemm_ktail_fits(const GemmArgs &a);
+hipError_t launch_gemm_ktail(const GemmArgs &a, int elem, int64_t K0, hipStream_t s);
 
 // 64 x 64 fp32 tiles with loads straight into LDS (gemm_nt_direct.hip): rows
 // and bases 8-byte aligned (vec >= 2), not predicated.

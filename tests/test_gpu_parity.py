@@ -105,6 +105,31 @@ def test_gemm_wide_unaligned(orc, monkeypatch, shape, dtype):
     assert_close(flat.view(M, N).cpu().numpy(), ref, bound, dtype, f"gemm wide unaligned {shape} {dtype}")
 
 
+# The 128 x 128 register ring for K not a multiple of its 16-byte pieces: the
+# ring over the first K - K % (16 / es) columns, then the tail kernel; pitches
+# above K and bases one element off a 16-byte boundary.
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(300, 520, 771, 0, 0), (257, 255, 9, 1, 3), (129, 300, 130, 1, 0),
+                                   (640, 384, 1023, 0, 1)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_ring128_ktail(orc, monkeypatch, shape, dtype):
+    monkeypatch.setenv("CAS_GEMM_TILE", "128")
+    M, N, K, off, pad = shape
+    ldx, ldw = K + pad, K + pad + 1
+    g = np.random.default_rng(M * 5 + N * 7 + K)
+    Xf = synth.to_storage(g.standard_normal((M * ldx + off,)).astype(np.float32), dtype)
+    Wf = synth.to_storage(g.standard_normal((N * ldw + off,)).astype(np.float32), dtype)
+    ref, bound = orc.gemm_nt(Xf[off:], Wf[off:], dtype, M=M, N=N, K=K, ldx=ldx, ldw=ldw, ldy=N)
+    dx, dw = to_device(Xf, dtype), to_device(Wf, dtype)
+    x = dx[off:].as_strided((M, K), (ldx, 1))
+    w = dw[off:].as_strided((N, K), (ldw, 1))
+    buf, flat = guarded_output(M * N)
+    case(f"gemm ring128 k-tail {shape} {dtype}")
+    cas.gemm_nt(x, w, out=flat.view(M, N))
+    torch.cuda.synchronize()
+    check_guards(buf, M * N)
+    assert_close(flat.view(M, N).cpu().numpy(), ref, bound, dtype, f"gemm ring128 k-tail {shape} {dtype}")
+
+
 # K a multiple of 128 (whole turns of the four-stage ring): the full-turn
 # kernel, whose fetch has no per-chunk predicate; ragged M and N, one turn
 # (K = 128) and several.
