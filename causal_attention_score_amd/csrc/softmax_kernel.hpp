@@ -114,13 +114,15 @@ __device__ __forceinline__ void kd_fetch(const KDirect<NCH> &st, char *dst, cons
 // acc[kb] += K rows 32kb.. of the LDS tile times this wave's Q rows: lane
 // (r32, h) supplies chunk 2u + h of K row 32kb + r32 and of its Q row (the
 // same chunk permutation on both operands, so each product appears once).
-template <class E, int NCH>
+// NQ: the chunk pairs multiplied (fewer than NCH / 2 when the rest of the
+// head row is zero: heads of 257 .. 384 bytes on 32-chunk rows take 12).
+template <class E, int NCH, int NQ = NCH / 2>
 __device__ __forceinline__ void k_mma(f32x16 (&acc)[4], const char *kb, const u32x4 (&qf)[NCH / 2], int lane)
 {
     constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 #pragma unroll
-    for (int u = 0; u < NCH / 2; ++u) {
+    for (int u = 0; u < NQ; ++u) {
         u32x4 kf[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -218,7 +220,7 @@ template <class F> hipError_t launch_longest_first(const TrimulArgs &a, hipStrea
     return hipSuccess;
 }
 
-template <class E, int NCH>
+template <class E, int NCH, int NQ = NCH / 2>
 __global__ void __launch_bounds__(STATS_THREADS)
 row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, float *__restrict__ row_logsum,
                  uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt, uint32_t planes, uint32_t rank0,
@@ -255,7 +257,7 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
             const uint32_t row = 32u * w + r32;
             const bool row_ok = t0 + row < T;
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
+            for (int u = 0; u < NQ; ++u) {
                 const uint32_t ch = 2u * u + h;
                 const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
                 qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
@@ -277,7 +279,7 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
             f32x16 acc[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
-            k_mma<E, NCH>(acc, cur, qf, lane);
+            k_mma<E, NCH, NQ>(acc, cur, qf, lane);
             stats_update<4>(acc, rr, c, lane);
             __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
             tri::lds_barrier();                 // every wave's part; tile J's reads done before it is rewritten
@@ -293,7 +295,7 @@ row_stats_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, floa
             f32x16 acc[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
-            k_mma<E, NCH>(acc, (I & 1) ? k1s : k0s, qf, lane);
+            k_mma<E, NCH, NQ>(acc, (I & 1) ? k1s : k0s, qf, lane);
             switch (w) {
             case 0: stats_update<0>(acc, rr, c, lane); break;
             case 1: stats_update<1>(acc, rr, c, lane); break;
@@ -981,10 +983,10 @@ template <class E> hipError_t launch_softmax_fused_impl(const TrimulArgs &a, int
     return launch_fused_ep<E, tri::EpProb>(a, s);
 }
 
-template <class E, int NCH> hipError_t launch_row_stats_nch(const TrimulArgs &a, hipStream_t s)
+template <class E, int NCH, int NQ = NCH / 2> hipError_t launch_row_stats_nch(const TrimulArgs &a, hipStream_t s)
 {
     return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
-        hipLaunchKernelGGL((row_stats_kernel<E, NCH>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+        hipLaunchKernelGGL((row_stats_kernel<E, NCH, NQ>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
                            const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (uint32_t)a.T,
                            (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale);
     });
@@ -996,7 +998,8 @@ template <class E> hipError_t launch_row_stats_impl(const TrimulArgs &a, hipStre
 {
     if (a.HS * E::ES <= 128) return launch_row_stats_nch<E, 8>(a, s);
     if (a.HS * E::ES > 256) { // heads of 257 .. 512 bytes
-        if constexpr (std::is_same<E, KF32>::value) return launch_row_stats_nch<E, 32>(a, s);
+        if constexpr (std::is_same<E, KF32>::value)
+            return a.HS * E::ES <= 384 ? launch_row_stats_nch<E, 32, 12>(a, s) : launch_row_stats_nch<E, 32>(a, s);
         else return launch_row_stats_wide16(a, std::is_same<E, KBF16>::value ? E_BF16 : E_F16, s);
     }
     return launch_row_stats_nch<E, 16>(a, s);
@@ -1104,13 +1107,13 @@ template <int NCH> __device__ __forceinline__ void a_store(const AStage<NCH> &st
 // Scores of this wave's 32 queries against the tile's 64 keys: D = K Q^T
 // per 32-key block b, so s[b][r] is the dot product of query lane%32 and key
 // 32b + 8(r/4) + 4(lane/32) + r%4 (unscaled).
-template <class E, int NCH>
+template <class E, int NCH, int NQ = NCH / 2>
 __device__ __forceinline__ void attn_scores(f32x16 (&s)[2], const char *kbuf, const u32x4 (&qf)[NCH / 2], int lane)
 {
     constexpr int RB = NCH * 16;
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 #pragma unroll
-    for (int u = 0; u < NCH / 2; ++u) {
+    for (int u = 0; u < NQ; ++u) {
         u32x4 kf[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -1125,14 +1128,14 @@ __device__ __forceinline__ void attn_scores(f32x16 (&s)[2], const char *kbuf, co
     }
 }
 
-template <int NCH, int NBV, bool DIAG>
+template <int NCH, int NBV, bool DIAG, int NQ = NCH / 2>
 __device__ __forceinline__ void a_step(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
                                        const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
                                        uint32_t kabs0, uint32_t qabs)
 {
     f32x16 s[2];
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-    attn_scores<KF32, NCH>(s, kbuf, qf, lane);
+    attn_scores<KF32, NCH, NQ>(s, kbuf, qf, lane);
     // p, in place, as the softmax-rows kernel forms it
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -1266,14 +1269,14 @@ __device__ __forceinline__ void v16_lanes(const char *(&vl)[NBV], const char *vb
         vl[nb] = vbuf + (4u * h + e) * RB + 16u * ((4u * nb + 2u * g + (q >> 1)) ^ vswz<NCH>(e)) + 8u * (q & 1u);
 }
 
-template <class E, int NCH, int NBV, bool DIAG>
+template <class E, int NCH, int NBV, bool DIAG, int NQ = NCH / 2>
 __device__ __forceinline__ void a_step16(f32x16 (&yacc)[NBV], const char *kbuf, const char *vbuf,
                                          const u32x4 (&qf)[NCH / 2], float scale, float mx, float ls, int lane,
                                          uint32_t kabs0, uint32_t qabs)
 {
     f32x16 s[2];
     const uint32_t h = (uint32_t)(lane >> 5);
-    attn_scores<E, NCH>(s, kbuf, qf, lane);
+    attn_scores<E, NCH, NQ>(s, kbuf, qf, lane);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1313,7 +1316,7 @@ template <class E, int NCH> struct AttnCfg {
     static constexpr int MIN_WG = (!F32 && NCH == 8) ? 4 : 1;
 };
 
-template <class E, int NCH>
+template <class E, int NCH, int NQ = NCH / 2>
 __global__ void __launch_bounds__(STATS_THREADS, (AttnCfg<E, NCH>::MIN_WG))
 attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max,
                  const float *__restrict__ row_logsum, float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH,
@@ -1346,7 +1349,7 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
             const uint32_t row = 32u * w + r32;
             const bool row_ok = t0 + row < T;
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
+            for (int u = 0; u < NQ; ++u) {
                 const uint32_t ch = 2u * u + h;
                 const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
                 qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
@@ -1373,17 +1376,18 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
             uint32_t J = 0;
             for (; J + 2 < nst; ++J) {
                 a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-                a_step<NCH, NBV, false>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls,
+                a_step<NCH, NBV, false, NQ>(yacc, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, scale, mx, ls,
                                         lane, J * AKT, qabs);
                 a_store<NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
                 tri::lds_barrier();
             }
             // the diagonal pair: J = nst - 2 (even, buffer 0), then nst - 1
             a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-            a_step<NCH, NBV, true>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
+            a_step<NCH, NBV, true, NQ>(yacc, kbuf, vbuf, qf, scale, mx, ls, lane, J * AKT, qabs);
             a_store<NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
             tri::lds_barrier();
-            a_step<NCH, NBV, true>(yacc, kbuf + KBYTES, vbuf + VBYTES, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+            a_step<NCH, NBV, true, NQ>(yacc, kbuf + KBYTES, vbuf + VBYTES, qf, scale, mx, ls, lane, (J + 1) * AKT,
+                                       qabs);
         } else {
             // Direct staging into four named buffers, the loop unrolled by
             // two (the single-pass kernel's scheme: no wait on the loads in
@@ -1400,19 +1404,19 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
             uint32_t J = 0;
             for (; J + 2 < nst; J += 2) { // nst is even
                 d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
-                a_step16<E, NCH, NBV, false>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
+                a_step16<E, NCH, NBV, false, NQ>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
                 __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
                 tri::lds_barrier();
                 d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, J + 2, T, ldb, w);
-                a_step16<E, NCH, NBV, false>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+                a_step16<E, NCH, NBV, false, NQ>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
                 __builtin_amdgcn_s_waitcnt(0x70);
                 tri::lds_barrier();
             }
             d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
-            a_step16<E, NCH, NBV, true>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
+            a_step16<E, NCH, NBV, true, NQ>(yacc, k0s, v0s, qf, scale, mx, ls, lane, J * AKT, qabs);
             __builtin_amdgcn_s_waitcnt(0x70);
             tri::lds_barrier();
-            a_step16<E, NCH, NBV, true>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
+            a_step16<E, NCH, NBV, true, NQ>(yacc, k1s, v1s, qf, scale, mx, ls, lane, (J + 1) * AKT, qabs);
         }
         // y rows: lane holds query 32w + 8(r/4) + 4h + r%4 and column 32nb + lane%32
 #pragma unroll
@@ -1426,10 +1430,10 @@ attention_kernel(const char *__restrict__ qkv, const float *__restrict__ row_max
     }
 }
 
-template <class E, int NCH> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
+template <class E, int NCH, int NQ = NCH / 2> hipError_t launch_attention_nch(const TrimulArgs &a, hipStream_t s)
 {
     return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
-        hipLaunchKernelGGL((attention_kernel<E, NCH>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+        hipLaunchKernelGGL((attention_kernel<E, NCH, NQ>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
                            a.row_max, a.row_logsum, (float *)a.out, (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH,
                            (uint32_t)a.HS, nt, planes, rank0, a.scale);
     });
@@ -1440,7 +1444,8 @@ template <class E> hipError_t launch_attention_impl(const TrimulArgs &a, hipStre
 {
     if (a.HS * AttnCfg<E, 8>::ES <= 128) return launch_attention_nch<E, 8>(a, s);
     if (a.HS * E::ES > 256) { // heads of 257 .. 512 bytes
-        if constexpr (std::is_same<E, KF32>::value) return launch_attention_nch<E, 32>(a, s);
+        if constexpr (std::is_same<E, KF32>::value)
+            return a.HS * E::ES <= 384 ? launch_attention_nch<E, 32, 12>(a, s) : launch_attention_nch<E, 32>(a, s);
         else return launch_attention_wide16(a, std::is_same<E, KBF16>::value ? E_BF16 : E_F16, s);
     }
     return launch_attention_nch<E, 16>(a, s);
@@ -1488,7 +1493,7 @@ __device__ __forceinline__ float halves_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]); // low half + high half in both: one order, one result
 }
 
-template <class E, int NCH, int NBV, bool DIAG>
+template <class E, int NCH, int NBV, bool DIAG, int NQ = NCH / 2>
 __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, const char *kbuf,
                                             const char *vbuf, const u32x4 (&qf)[NCH / 2], float c, int lane,
                                             uint32_t kabs0, uint32_t qabs)
@@ -1496,7 +1501,7 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
     static_assert(std::is_same<E, KF32>::value, "fp32 step; online_step16 serves the 16-bit formats");
     const uint32_t r32 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
     f32x16 s[2];
-    attn_scores<E, NCH>(s, kbuf, qf, lane);
+    attn_scores<E, NCH, NQ>(s, kbuf, qf, lane);
     // Keys after the query become -inf: no part in the maximum, exponential 0.
     float tmax = -__builtin_inff();
 #pragma unroll
@@ -1548,7 +1553,7 @@ __device__ __forceinline__ void online_step(f32x16 (&yacc)[NBV], OnlineRow &rw, 
 // The 16-bit step: the scores and exponentials as in the fp32 step, then
 // P rounded to the input format and Y^T += V^T P^T with the V operand from
 // the transpose read.
-template <class E, int NCH, int NBV, bool DIAG>
+template <class E, int NCH, int NBV, bool DIAG, int NQ = NCH / 2>
 __device__ __forceinline__ void online_step16(f32x16 (&yacc)[NBV], OnlineRow &rw, const char *kbuf,
                                               const char *vbuf, const u32x4 (&qf)[NCH / 2], float c, int lane,
                                               uint32_t kabs0, uint32_t qabs)
@@ -1556,7 +1561,7 @@ __device__ __forceinline__ void online_step16(f32x16 (&yacc)[NBV], OnlineRow &rw
     constexpr uint32_t RB = NCH * 16;
     const uint32_t h = (uint32_t)(lane >> 5);
     f32x16 s[2];
-    attn_scores<E, NCH>(s, kbuf, qf, lane);
+    attn_scores<E, NCH, NQ>(s, kbuf, qf, lane);
     // Keys after the query become -inf: no part in the maximum, exponential 0.
     float tmax = -__builtin_inff();
 #pragma unroll
@@ -1608,7 +1613,7 @@ __device__ __forceinline__ void online_step16(f32x16 (&yacc)[NBV], OnlineRow &rw
         }
 }
 
-template <class E, int NCH>
+template <class E, int NCH, int NQ = NCH / 2>
 __global__ void __launch_bounds__(STATS_THREADS, (AttnCfg<E, NCH>::MIN_WG))
 attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_max, float *__restrict__ row_logsum,
                         float *__restrict__ y, uint32_t T, uint32_t C, uint32_t NH, uint32_t HS, uint32_t nt,
@@ -1641,7 +1646,7 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
         const uint32_t row = 32u * w + r32;
         const bool row_ok = t0 + row < T;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
+        for (int u = 0; u < NQ; ++u) {
             const uint32_t ch = 2u * u + h;
             const uint32_t vo = (row_ok && ch * 16 < head_bytes) ? row * ldb + ch * 16 : OOB;
             qf[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)vo, 0, 0);
@@ -1663,16 +1668,16 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
         uint32_t J = 0;
         for (; J + 2 < nst; ++J) {
             a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-            online_step<E, NCH, NBV, false>(yacc, rw, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, c,
+            online_step<E, NCH, NBV, false, NQ>(yacc, rw, kbuf + (J & 1) * KBYTES, vbuf + (J & 1) * VBYTES, qf, c,
                                             lane, J * AKT, qabs);
             a_store<NCH>(st, kbuf + ((J + 1) & 1) * KBYTES, vbuf + ((J + 1) & 1) * VBYTES, tid);
             tri::lds_barrier();
         }
         a_fetch<NCH>(st, kb0, vb0, J + 1, T, ldb, head_bytes, tid);
-        online_step<E, NCH, NBV, true>(yacc, rw, kbuf, vbuf, qf, c, lane, J * AKT, qabs);
+        online_step<E, NCH, NBV, true, NQ>(yacc, rw, kbuf, vbuf, qf, c, lane, J * AKT, qabs);
         a_store<NCH>(st, kbuf + KBYTES, vbuf + VBYTES, tid);
         tri::lds_barrier();
-        online_step<E, NCH, NBV, true>(yacc, rw, kbuf + KBYTES, vbuf + VBYTES, qf, c, lane, (J + 1) * AKT, qabs);
+        online_step<E, NCH, NBV, true, NQ>(yacc, rw, kbuf + KBYTES, vbuf + VBYTES, qf, c, lane, (J + 1) * AKT, qabs);
     } else {
         // Tile J + 1 streams into the other buffer while step J runs; that
         // buffer's last readers (step J - 1) passed the barrier before. The
@@ -1691,19 +1696,19 @@ attention_online_kernel(const char *__restrict__ qkv, float *__restrict__ row_ma
         uint32_t J = 0;
         for (; J + 2 < nst; J += 2) { // nst is even
             d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
-            online_step16<E, NCH, NBV, false>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
+            online_step16<E, NCH, NBV, false, NQ>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
             __builtin_amdgcn_s_waitcnt(0x70); // this wave's part of tile J + 1 in LDS
             tri::lds_barrier();
             d16_fetch<NCH>(ds, k0s, v0s, kb0, vb0, J + 2, T, ldb, w);
-            online_step16<E, NCH, NBV, false>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
+            online_step16<E, NCH, NBV, false, NQ>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
             __builtin_amdgcn_s_waitcnt(0x70);
             tri::lds_barrier();
         }
         d16_fetch<NCH>(ds, k1s, v1s, kb0, vb0, J + 1, T, ldb, w);
-        online_step16<E, NCH, NBV, true>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
+        online_step16<E, NCH, NBV, true, NQ>(yacc, rw, k0s, v0s, qf, c, lane, J * AKT, qabs);
         __builtin_amdgcn_s_waitcnt(0x70);
         tri::lds_barrier();
-        online_step16<E, NCH, NBV, true>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
+        online_step16<E, NCH, NBV, true, NQ>(yacc, rw, k1s, v1s, qf, c, lane, (J + 1) * AKT, qabs);
     }
 
     // y = Y / l and the statistics; the lane halves hold disjoint keys of one row.
@@ -1755,11 +1760,18 @@ template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, 
                                (const char *)a.qkv, const_cast<float *>(a.row_max),
                                const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
                                (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
-        else if constexpr (std::is_same<E, KF32>::value) // fp32 heads of 257 .. 512 bytes
-            hipLaunchKernelGGL((attention_online_kernel<E, 32>), grid, dim3(STATS_THREADS), 0, s,
-                               (const char *)a.qkv, const_cast<float *>(a.row_max),
-                               const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
-                               (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+        else if constexpr (std::is_same<E, KF32>::value) { // fp32 heads of 257 .. 512 bytes
+            if (a.HS * E::ES <= 384)
+                hipLaunchKernelGGL((attention_online_kernel<E, 32, 12>), grid, dim3(STATS_THREADS), 0, s,
+                                   (const char *)a.qkv, const_cast<float *>(a.row_max),
+                                   const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
+                                   (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+            else
+                hipLaunchKernelGGL((attention_online_kernel<E, 32>), grid, dim3(STATS_THREADS), 0, s,
+                                   (const char *)a.qkv, const_cast<float *>(a.row_max),
+                                   const_cast<float *>(a.row_logsum), (float *)a.out, (uint32_t)a.T, (uint32_t)a.C,
+                                   (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale, (int)a.vec_store);
+        }
     });
 }
 
@@ -1767,22 +1779,28 @@ template <class E> hipError_t launch_attention_online_impl(const TrimulArgs &a, 
 // launchers above, compiled in their own translation unit
 // (softmax_wide16.hip) without the VGPR-only MFMA form, so that their 8 x 16
 // output accumulators can live in the accumulation registers.
+// Heads of at most 384 bytes multiply 12 of the row's 16 chunk pairs.
 template <class E> hipError_t launch_row_stats_wide16_impl(const TrimulArgs &a, hipStream_t s)
 {
-    return launch_row_stats_nch<E, 32>(a, s);
+    return a.HS * E::ES <= 384 ? launch_row_stats_nch<E, 32, 12>(a, s) : launch_row_stats_nch<E, 32>(a, s);
 }
 template <class E> hipError_t launch_attention_wide16_impl(const TrimulArgs &a, hipStream_t s)
 {
-    return launch_attention_nch<E, 32>(a, s);
+    return a.HS * E::ES <= 384 ? launch_attention_nch<E, 32, 12>(a, s) : launch_attention_nch<E, 32>(a, s);
 }
-template <class E> hipError_t launch_attention_online_wide16_impl(const TrimulArgs &a, hipStream_t s)
+template <class E, int NQ> hipError_t launch_attention_online_wide16_nq(const TrimulArgs &a, hipStream_t s)
 {
     return launch_longest_first(a, s, [&](dim3 grid, uint32_t nt, uint32_t planes, uint32_t rank0) {
-        hipLaunchKernelGGL((attention_online_kernel<E, 32>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
+        hipLaunchKernelGGL((attention_online_kernel<E, 32, NQ>), grid, dim3(STATS_THREADS), 0, s, (const char *)a.qkv,
                            const_cast<float *>(a.row_max), const_cast<float *>(a.row_logsum), (float *)a.out,
                            (uint32_t)a.T, (uint32_t)a.C, (uint32_t)a.NH, (uint32_t)a.HS, nt, planes, rank0, a.scale,
                            (int)a.vec_store);
     });
+}
+template <class E> hipError_t launch_attention_online_wide16_impl(const TrimulArgs &a, hipStream_t s)
+{
+    return a.HS * E::ES <= 384 ? launch_attention_online_wide16_nq<E, 12>(a, s)
+                               : launch_attention_online_wide16_nq<E, 16>(a, s);
 }
 
 } // namespace sm
