@@ -664,8 +664,11 @@ template <int NCH> struct Staged {
 // Coalesced fetch of the 256 operand rows of super-tile `sp` (loader lane
 // cl = wave*64 + lane of 256): chunk j*256 + cl is row (j*256 + cl) / NCH,
 // chunk (cl % NCH). Rows past T and chunks past the head read zero. hoff:
-// the first head byte fetched (the second half of a wide head).
-template <class E, int NCH>
+// the first head byte fetched (the second half of a wide head). PART: a head
+// row that ends inside a 16-byte piece; that piece's bytes past the head
+// (the next head's, or the next slot's: never past the packed row) are
+// zeroed in registers.
+template <class E, int NCH, bool PART = false>
 __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, const Super &sp, uint32_t T, uint32_t C,
                                             uint32_t NH, uint32_t HS, uint32_t ldb, int cl, bool with_q = true,
                                             uint32_t hoff = 0)
@@ -687,6 +690,19 @@ __device__ __forceinline__ void stage_fetch(Staged<NCH> &st, const char *qkv, co
         const uint32_t ok = 0u - (uint32_t)((isq ? sp.T0 : sp.S0) + rin < lim); // all ones in range
         const uint32_t vo = ((rin * ldb + c * 16) & ok) | (OOB & ~ok);
         st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(isq ? rq : rk, (int)vo, 0, 0);
+    }
+    if constexpr (PART) {
+        const uint32_t cb = hoff + c * 16, hb = HS * ES; // the lane's piece, the head's bytes
+        if (cb < hb && hb < cb + 16) {
+            u32x4 keep;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t b0 = cb + 4u * w; // bytes b0 .. b0 + 3 of the row
+                keep[w] = b0 + 4 <= hb ? 0xFFFFFFFFu : b0 >= hb ? 0u : (1u << (8u * (hb - b0))) - 1u;
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) st.v[j] &= keep;
+        }
     }
 }
 
@@ -953,7 +969,7 @@ __device__ __forceinline__ void stream_subtile(const Tile &tl, bool all_masked, 
 // head ends within its first 128 bytes: the rest is zero). The tile goes to
 // LDS after the second step; the store waves stream it during the next
 // item's first step and its mirror during the second.
-template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2>
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2, bool PART = false>
 __global__ void __launch_bounds__(SUPER_THREADS)
 trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32_t T, uint32_t C, uint32_t NH,
                     uint32_t HS, uint32_t L, uint32_t items, float scale, int vec_store,
@@ -1011,7 +1027,7 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         Staged<NCH> st;
         float sv = 0.f;
         if (steps > 0) {
-            stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
+            stage_fetch<E, NCH, PART>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl);
             if constexpr (SM) sv = stat_fetch(row_max, row_logsum, cur.item(), T, cl);
             stage_store<NCH>(st, opb, cl);
             if constexpr (SM) stb[cl] = sv;
@@ -1019,7 +1035,7 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
         lds_barrier(); // operand rows of step 0 in LDS
         for (uint32_t n = 0; n < steps; ++n) {
             if constexpr (HV == 2) { // item n's second half, then the next item's first
-                stage_fetch<E, NCH>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl, true, RB);
+                stage_fetch<E, NCH, PART>(st, qkv, cur.item(), T, C, NH, HS, ldb, cl, true, RB);
                 lds_barrier(); // X: first half consumed
                 stage_store<NCH>(st, opb, cl);
                 lds_barrier(); // Y: second half in LDS
@@ -1031,7 +1047,7 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
                 cur.advance();
                 const Super nx = cur.item();
                 if constexpr (HV == 1) with_q = !(nx.plane == was.plane && nx.T0 == was.T0);
-                stage_fetch<E, NCH>(st, qkv, nx, T, C, NH, HS, ldb, cl, with_q);
+                stage_fetch<E, NCH, PART>(st, qkv, nx, T, C, NH, HS, ldb, cl, with_q);
                 if constexpr (SM) sv = stat_fetch(row_max, row_logsum, nx, T, cl);
             }
             lds_barrier(); // X: operand rows of step n consumed
@@ -1131,10 +1147,10 @@ trimul_super_kernel(const char *__restrict__ qkv, char *__restrict__ out, uint32
     }
 }
 
-template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2>
+template <class E, int NCH, class O, class EP = EpScore, int HV = 1, int NU2 = NCH / 2, bool PART = false>
 hipError_t launch_super(const TrimulArgs &a, hipStream_t s)
 {
-    auto kern = trimul_super_kernel<E, NCH, O, EP, HV, NU2>;
+    auto kern = trimul_super_kernel<E, NCH, O, EP, HV, NU2, PART>;
     const int64_t nt = (a.T + ST - 1) / ST;
     const int64_t L = nt * (nt + 1) / 2;
     const int64_t items = a.B * a.NH * L;
@@ -1241,6 +1257,18 @@ template <class E, class O, class EP> hipError_t launch_two_halves(const TrimulA
     return launch_super<E, 16, O, EP, 2, 8>(a, s);
 }
 
+// A head that ends inside a 16-byte piece (qkv at its element alignment,
+// HS * ES not a multiple of 16): the same kernels, that piece's bytes past
+// the head zeroed in the loader waves' registers (PART).
+template <class E, class O> hipError_t launch_part(const TrimulArgs &a, hipStream_t s)
+{
+    const int64_t hb = a.HS * E::ES;
+    if (hb > 384) return launch_super<E, 16, O, EpScore, 2, 8, true>(a, s);
+    if (hb > 256) return launch_super<E, 16, O, EpScore, 2, 4, true>(a, s);
+    if (hb > 128) return launch_super<E, 16, O, EpScore, 1, 8, true>(a, s);
+    return launch_super<E, 8, O, EpScore, 1, 4, true>(a, s);
+}
+
 template <class E>
 hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
 {
@@ -1266,6 +1294,13 @@ hipError_t launch_elem_impl(const TrimulArgs &a, int vec, hipStream_t s)
         if (a.out_kind == 1) return narrow ? launch_super<E, 8, OBF16>(a, s) : launch_super<E, 16, OBF16>(a, s);
         if (a.out_kind == 2) return narrow ? launch_super<E, 8, OF16>(a, s) : launch_super<E, 16, OF16>(a, s);
         return narrow ? launch_super<E, 8, OF32>(a, s) : launch_super<E, 16, OF32>(a, s);
+    }
+    const bool part_ok = ids_fit && vec * E::ES < 16 && (uintptr_t)a.qkv % E::ES == 0 && a.HS * E::ES <= 512 &&
+                         a.T < (int64_t(1) << 22);
+    if (part_ok && !force_tile) {
+        if (a.out_kind == 1) return launch_part<E, OBF16>(a, s);
+        if (a.out_kind == 2) return launch_part<E, OF16>(a, s);
+        return launch_part<E, OF32>(a, s);
     }
     // 16-byte chunks need base, pitch and head offsets 16-byte aligned and
     // HS*ES a multiple of 16 (vec = elements that divide all of them).

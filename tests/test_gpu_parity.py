@@ -571,6 +571,43 @@ def test_trimul_wide_heads_many_items(orc, monkeypatch, dtype, HS):
     assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
 
 
+# Heads that end inside a 16-byte piece (fp32 HS not a multiple of 4, 16-bit
+# HS not a multiple of 8), up to 512 bytes: the super-tile kernel with the
+# last piece's bytes past the head zeroed in registers (one and two head
+# halves), against the oracle and bit for bit against the tile kernel's
+# element-wise fetch.
+PART_HEADS = [("f32", 1), ("f32", 3), ("f32", 50), ("f32", 66), ("f32", 127), ("bf16", 3), ("bf16", 36),
+              ("bf16", 100), ("bf16", 129), ("bf16", 190), ("f16", 12), ("f16", 250)]
+
+
+@pytest.mark.parametrize("T", [1, 65, 300])
+@pytest.mark.parametrize("dtype,HS", PART_HEADS, ids=lambda v: str(v))
+def test_trimul_partial_piece_heads(orc, monkeypatch, T, dtype, HS):
+    B, NH = 2, 3
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=T * 89 + HS)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul(qkv, dtype, B, T, NH, HS, "partial piece")
+    assert_scores(out, ref, bound, dtype, f"trimul partial piece {dtype} T={T} HS={HS}")
+    monkeypatch.setenv("CAS_TRIMUL_KERNEL", "tile")
+    out_t = run_trimul(qkv, dtype, B, T, NH, HS, "partial piece, tile kernel")
+    assert np.array_equal(out.view(np.uint32), out_t.view(np.uint32)), "super-tile and tile kernels differ"
+
+
+@pytest.mark.parametrize("dtype,HS", [("f32", 66), ("bf16", 100)], ids=lambda v: str(v))
+def test_trimul_partial_piece_many_items_and_out16(orc, dtype, HS):
+    """Partial-piece heads over many super-tiles per workgroup (B2 T1024 NH8),
+    the whole output against the oracle, and bf16 output."""
+    B, T, NH = 2, 1024, 8
+    qkv = synth.trimul_inputs(B, T, NH, HS, dtype, seed=HS + 91)
+    ref, bound = orc.trimul_causal(qkv, B, T, NH * HS, NH, dtype)
+    out = run_trimul(qkv, dtype, B, T, NH, HS, "partial piece many items")
+    assert_scores(out, ref, bound, dtype, f"trimul partial piece many items {dtype} HS={HS}")
+    q2 = synth.trimul_inputs(2, 300, 2, HS, dtype, seed=HS + 93)
+    ref2, bound2 = orc.trimul_causal(q2, 2, 300, 2 * HS, 2, dtype)
+    out16 = run_trimul16(q2, dtype, "bf16", 2, 300, 2, HS, "partial piece out16")
+    assert_scores16(out16, ref2, bound2, dtype, "bf16", f"trimul partial piece {dtype}->bf16 HS={HS}")
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,HS", [("f32", 100), ("bf16", 256)], ids=lambda v: str(v))
 def test_trimul_wide_heads_out16(orc, dtype, HS, out_dtype):
